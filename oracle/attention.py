@@ -1,0 +1,86 @@
+"""Scaled dot-product attention for one new query over cached keys/values (fp64).
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+Three independent paths:
+  * decode_row       -- the definition for one query over L cached positions;
+  * full_causal      -- recompute all rows with the causal mask, no cache;
+  * cached_decode    -- the naive cached loop: concatenate the new k, v and attend the new q.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def decode_row(q, K, V, scale) -> np.ndarray:
+    """softmax(scale * q . K^T) . V for one query over L cached positions, in fp64.
+
+    q: [D]; K, V: [L, D] (any real dtype, widened exactly to fp64); scale: a float, used as the
+    exact fp64 value of the number passed. Returns [D] fp64.
+
+    The new query attends every cached position, its own included, with no mask: in the cached
+    path causality holds by construction ("LLM Inference Acceleration -- KV Cache", section 3.1,
+    the Attention class writes the new k/v at start_pos and then reads [0, start_pos+seqlen);
+    "From Neuron to GPT -- KV cache chapter", cached attention layer: no causal mask with a
+    cache). The softmax is taken in higher precision than the stored values (section 3.1 casts
+    the scores to float before the softmax); here fp64.
+
+    L = 0 gives the zero vector (nothing to attend).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    if K.shape[0] == 0:
+        return np.zeros(V.shape[1], dtype=np.float64)
+    s = (K @ q) * float(scale)
+    m = s.max()
+    p = np.exp(s - m)
+    return (p @ V) / p.sum()
+
+
+def full_causal(Q, K, V, scale, start_pos: int = 0) -> np.ndarray:
+    """Recompute attention for a chunk of queries against all keys, with the causal mask.
+
+    Q: [T, D] holds queries for positions start_pos .. start_pos+T-1; K, V: [start_pos+T, D].
+    Row i may attend positions 0 .. start_pos+i. The mask is the upper-triangular -inf matrix
+    with diagonal offset start_pos+1, added to the scaled scores before the row softmax
+    ("LLM Inference Acceleration -- KV Cache", section 2.1, the two worked steps; section 3.1,
+    Transformer.forward builds triu(-inf, diagonal=start_pos+1) when seqlen > 1).
+    Returns [T, D] fp64.
+    """
+    Q = np.asarray(Q, dtype=np.float64)
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    T = Q.shape[0]
+    S = K.shape[0]
+    if S != start_pos + T:
+        raise ValueError("keys must cover every position up to the last query")
+    scores = (Q @ K.T) * float(scale)
+    mask = np.triu(np.full((T, S), -np.inf), k=start_pos + 1)
+    scores = scores + mask
+    m = scores.max(axis=1, keepdims=True)
+    p = np.exp(scores - m)
+    return (p @ V) / p.sum(axis=1, keepdims=True)
+
+
+def cached_decode(Qs, Ks, Vs, scale, prefix_K=None, prefix_V=None) -> np.ndarray:
+    """The naive cached path: for each step, append the new k, v to the cache by concatenation
+    and attend the new q over the whole cache.
+
+    Qs, Ks, Vs: [T, D] -- the new token's q, k, v at each of T steps. prefix_K/prefix_V: [P, D]
+    entries already cached (optional). Returns [T, D]: the output row of each step.
+
+    Follows "KV Cache Mechanism Explained", section 3.2 (forward_with_cache: concatenate the
+    cached K/V with K_new/V_new, store it back, attend Q_new) and section 4 (the cache grows by
+    exactly one entry per generated token).
+    """
+    Qs = np.asarray(Qs, dtype=np.float64)
+    D = Qs.shape[1]
+    K_cache = np.zeros((0, D)) if prefix_K is None else np.asarray(prefix_K, dtype=np.float64)
+    V_cache = np.zeros((0, D)) if prefix_V is None else np.asarray(prefix_V, dtype=np.float64)
+    rows = []
+    for t in range(Qs.shape[0]):
+        K_cache = np.concatenate([K_cache, np.asarray(Ks[t:t + 1], dtype=np.float64)], axis=0)
+        V_cache = np.concatenate([V_cache, np.asarray(Vs[t:t + 1], dtype=np.float64)], axis=0)
+        rows.append(decode_row(Qs[t], K_cache, V_cache, scale))
+    return np.stack(rows) if rows else np.zeros((0, D))

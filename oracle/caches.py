@@ -1,0 +1,119 @@
+"""Cache storage models and decode through them (fp64 arithmetic).
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+ContigCache: one [B, H, S_max, D] array for K and one for V per layer, preallocated to the
+maximum length ("LLM Inference Acceleration -- KV Cache", section 3.1, cache_k/cache_v sized
+max_batch x max_seq; "KV Cache Mechanism Explained", section 6.2, item 2 -- preallocate the
+cache). The new token of sequence b is written at position len_b, then the query attends
+positions [0, len_b] (section 3.1: write at start_pos, read up to start_pos + seqlen).
+
+PagedCache: K and V pools [num_blocks, H, 16, D] per layer; token t of a sequence lives in
+physical block table[t // 16] at in-block slot t % 16 ("KV Cache and PagedAttention", section
+2.1 and section 3.2: gather the sequence's blocks through its block table). Writes go to slots
+(physical_block * 16 + offset). Copy-on-write copies whole blocks (section 3.3). An fp8 pool keeps
+uint8 e4m3 codes plus one fp32 scale per block for K and one for V (codecs module).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .attention import decode_row
+from .codecs import e4m3_decode, fp8_write_token
+
+BS = 16
+_NP = {"f32": np.float32, "f16": np.float16}
+
+
+class ContigCache:
+    def __init__(self, B: int, H: int, S_max: int, D: int, dtype: str, fill=0.0):
+        self.B, self.H, self.S_max, self.D = B, H, S_max, D
+        self.K = np.full((B, H, S_max, D), fill, dtype=_NP[dtype])
+        self.V = np.full((B, H, S_max, D), fill, dtype=_NP[dtype])
+
+    def append(self, pos, k_new, v_new) -> None:
+        """k_new, v_new: [B, n, H, D]; token t of sequence b goes to position pos[b] + t.
+        Positions outside [0, S_max) are skipped."""
+        n = k_new.shape[1]
+        for b in range(self.B):
+            for t in range(n):
+                p = int(pos[b]) + t
+                if 0 <= p < self.S_max:
+                    self.K[b, :, p, :] = k_new[b, t]
+                    self.V[b, :, p, :] = v_new[b, t]
+
+    def decode(self, q, lens, scale) -> np.ndarray:
+        """q: [B, H, D]; lens[b]: attended length (the new token included). Returns [B, H, D]."""
+        out = np.zeros((self.B, self.H, self.D))
+        for b in range(self.B):
+            L = int(lens[b])
+            for h in range(self.H):
+                out[b, h] = decode_row(q[b, h], self.K[b, h, :L], self.V[b, h, :L], scale)
+        return out
+
+
+class PagedCache:
+    def __init__(self, num_blocks: int, H: int, D: int, dtype: str, fill=0.0):
+        self.N, self.H, self.D, self.dtype = num_blocks, H, D, dtype
+        if dtype == "e4m3":
+            self.K = np.zeros((num_blocks, H, BS, D), dtype=np.uint8)
+            self.V = np.zeros((num_blocks, H, BS, D), dtype=np.uint8)
+            self.k_scale = np.zeros(num_blocks, dtype=np.float32)
+            self.v_scale = np.zeros(num_blocks, dtype=np.float32)
+        else:
+            self.K = np.full((num_blocks, H, BS, D), fill, dtype=_NP[dtype])
+            self.V = np.full((num_blocks, H, BS, D), fill, dtype=_NP[dtype])
+            self.k_scale = self.v_scale = None
+
+    def copy_blocks(self, pairs) -> None:
+        """Copy every (src, dst) block: all 16 slots of K and V, and the fp8 scales."""
+        for s, d in pairs:
+            self.K[d] = self.K[s]
+            self.V[d] = self.V[s]
+            if self.k_scale is not None:
+                self.k_scale[d] = self.k_scale[s]
+                self.v_scale[d] = self.v_scale[s]
+
+    def write(self, slots, k_new, v_new) -> None:
+        """k_new, v_new: [n, H, D]; entry i goes to slot slots[i]; entries are applied in order."""
+        for i, slot in enumerate(slots):
+            blk, off = divmod(int(slot), BS)
+            if self.dtype == "e4m3":
+                self.k_scale[blk] = fp8_write_token(self.K[blk], self.k_scale[blk], off, k_new[i])
+                self.v_scale[blk] = fp8_write_token(self.V[blk], self.v_scale[blk], off, v_new[i])
+            else:
+                self.K[blk, :, off, :] = k_new[i]
+                self.V[blk, :, off, :] = v_new[i]
+
+    def values(self, pool: str, blk: int) -> np.ndarray:
+        """Stored values of one block, [H, 16, D] fp64."""
+        if self.dtype == "e4m3":
+            codes = self.K[blk] if pool == "k" else self.V[blk]
+            s = self.k_scale[blk] if pool == "k" else self.v_scale[blk]
+            return e4m3_decode(codes) * np.float64(s)
+        return (self.K[blk] if pool == "k" else self.V[blk]).astype(np.float64)
+
+    def gather(self, table, L: int):
+        """K, V of one sequence, [H, L, D] fp64, read token by token through its block table."""
+        K = np.zeros((self.H, L, self.D))
+        V = np.zeros((self.H, L, self.D))
+        cache = {}
+        for t in range(L):
+            blk, off = int(table[t // BS]), t % BS
+            if blk not in cache:
+                cache[blk] = (self.values("k", blk), self.values("v", blk))
+            K[:, t, :] = cache[blk][0][:, off, :]
+            V[:, t, :] = cache[blk][1][:, off, :]
+        return K, V
+
+    def decode(self, q, tables, lens, scale, heads=None) -> np.ndarray:
+        """q: [B, H, D]; tables: [B, max_blocks]; lens[b]: attended length. Returns [B, H, D]
+        (only the listed heads are computed when `heads` is given; the rest stay 0)."""
+        B = len(lens)
+        out = np.zeros((B, self.H, self.D))
+        hs = range(self.H) if heads is None else heads
+        for b in range(B):
+            K, V = self.gather(tables[b], int(lens[b]))
+            for h in hs:
+                out[b, h] = decode_row(q[b, h], K[h], V[h], scale)
+        return out

@@ -1,0 +1,115 @@
+"""Number formats of the cache: fp16 and OCP fp8-e4m3, and the per-block fp8 write rule.
+
+TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
+
+The pages store the cache in fp16 ("KV Cache Mechanism Explained", section 3.1; "KV Cache and
+PagedAttention", section 1.1 and section 5.2) and mention compressing it to fp8 e4m3 with a
+scaling factor ("KV Cache Mechanism Explained", section 8, item 3 -- mixed-precision cache; the
+snippet there casts to torch.float8_e4m3fn and derives a scale from abs().max()). The printed
+snippet is garbled (it takes the max after the cast and divides by the int8 limit 127), so the
+rule below is the reading taken for a per-block fp32 scale:
+
+  * e4m3 here is the OCP "fn" variant: 1 sign, 4 exponent (bias 7), 3 mantissa bits; exponent 0
+    is subnormal; S.1111.111 is NaN; there is no infinity; the largest finite magnitude is 448.
+  * enc(y): round y to the nearest finite e4m3 value, ties to the even code, magnitudes beyond
+    448 saturate to 448, the sign bit is kept (so -0 and small negatives give 0x80).
+  * A block holds one fp32 scale for K (and one for V) covering every head of the block. Tokens
+    are written one at a time in order. Writing in-block slot 0 starts a fresh block (scale 0).
+    For a new token x (all heads): s_new = fp32(max|x| / 448); if s_new > scale, the codes
+    already in slots [0, off) are re-quantised as enc(fp32(fp32(dec(c) * old) / s_new)) and the
+    scale becomes s_new; then the token is stored as enc(fp32(x / scale)). While the scale is 0
+    (every value written so far is +-0) a value is stored as a signed zero code.
+  * The stored value of a code c in a block with scale s is dec(c) * s.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+E4M3_MAX = 448.0
+E4M3_NAN = 0x7F
+
+
+def f16_round(x) -> np.ndarray:
+    """Round to IEEE binary16, nearest even (NumPy's conversion)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float16)
+
+
+def e4m3_decode_table() -> np.ndarray:
+    """float64 value of every one of the 256 e4m3 codes, from the OCP definition."""
+    out = np.empty(256, dtype=np.float64)
+    for code in range(256):
+        sign = -1.0 if code & 0x80 else 1.0
+        e = (code >> 3) & 0xF
+        m = code & 0x7
+        if e == 0xF and m == 0x7:
+            out[code] = np.nan
+        elif e == 0:
+            out[code] = sign * (m / 8.0) * 2.0 ** -6
+        else:
+            out[code] = sign * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return out
+
+
+_DEC = e4m3_decode_table()
+# magnitudes of the finite non-negative codes 0x00 .. 0x7E, increasing with the code
+_MAGS = _DEC[:0x7F].copy()
+
+
+def e4m3_decode(codes) -> np.ndarray:
+    return _DEC[np.asarray(codes, dtype=np.uint8)]
+
+
+def e4m3_encode(y) -> np.ndarray:
+    """Nearest finite e4m3 code to each value of y (ties to the even code, saturating at 448,
+    sign bit kept, NaN -> 0x7F with the sign). Brute force over all 127 magnitudes."""
+    y = np.asarray(y, dtype=np.float64)
+    flat = y.reshape(-1)
+    out = np.empty(flat.shape, dtype=np.uint8)
+    step = 4096
+    for i in range(0, flat.size, step):
+        v = flat[i:i + step]
+        a = np.abs(v)
+        nan = np.isnan(v)
+        a = np.where(nan, 0.0, a)
+        a = np.minimum(a, E4M3_MAX)          # saturation: beyond 448 (and inf) -> 448
+        dist = np.abs(a[:, None] - _MAGS[None, :])
+        dmin = dist.min(axis=1, keepdims=True)
+        cand = dist == dmin
+        # at most two candidates and they are adjacent codes; prefer the even one
+        even = cand & ((np.arange(0x7F) % 2) == 0)[None, :]
+        pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
+        code = pick.astype(np.uint8)
+        code = np.where(nan, np.uint8(E4M3_NAN), code)
+        code = code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+        out[i:i + step] = code
+    return out.reshape(y.shape)
+
+
+def _enc_scaled(y32: np.ndarray, s: np.float32) -> np.ndarray:
+    """Codes of fp32 values y32 under fp32 scale s (s == 0 stores signed zeros)."""
+    if s == 0:
+        return np.where(np.signbit(y32), np.uint8(0x80), np.uint8(0)).astype(np.uint8)
+    q = (y32 / np.float32(s)).astype(np.float32)   # IEEE binary32 division, nearest even
+    return e4m3_encode(q)
+
+
+def fp8_write_token(codes: np.ndarray, scale, off: int, x) -> np.float32:
+    """Write one token into an fp8 block, per the rule in the module docstring.
+
+    codes: uint8 [H, block_size, D] of one physical block (modified in place);
+    scale: the block's current fp32 scale; off: in-block slot of the token;
+    x: the token's values, [H, D], exactly representable in fp32.
+    Returns the block's new fp32 scale.
+    """
+    x32 = np.asarray(x, dtype=np.float32)
+    s = np.float32(0.0) if off == 0 else np.float32(scale)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    s_new = np.float32(amax / np.float32(E4M3_MAX))
+    if s_new > s:
+        if off > 0:
+            old = np.float32(s)
+            y = (e4m3_decode(codes[:, :off, :]).astype(np.float32) * old).astype(np.float32)
+            codes[:, :off, :] = _enc_scaled(y, s_new)
+        s = s_new
+    codes[:, off, :] = _enc_scaled(x32, s)
+    return np.float32(s)

@@ -1,0 +1,173 @@
+"""Pins for oracle.codecs (CPU only): fp16 and OCP e4m3 against their definitions and against
+torch's conversion routines, and the per-block fp8 write rule against its stated properties."""
+import numpy as np
+import pytest
+import torch
+
+from oracle.codecs import (E4M3_MAX, e4m3_decode, e4m3_decode_table, e4m3_encode, f16_round,
+                           fp8_write_token)
+
+
+def test_e4m3_decode_spot_values():
+    t = e4m3_decode_table()
+    assert t[0x7E] == 448.0 and t[0xFE] == -448.0
+    assert t[0x38] == 1.0
+    assert t[0x08] == 2.0 ** -6          # smallest normal
+    assert t[0x01] == 2.0 ** -9          # smallest subnormal
+    assert t[0x07] == 7 * 2.0 ** -9
+    assert t[0x77] == 240.0
+    assert np.isnan(t[0x7F]) and np.isnan(t[0xFF])
+    assert t[0x00] == 0.0 and np.signbit(t[0x80])
+    fin = t[:0x7F]
+    assert np.all(np.diff(fin) > 0)
+    assert np.count_nonzero(~np.isnan(t)) == 254
+
+
+def test_e4m3_decode_matches_torch_all_codes():
+    codes = torch.arange(256, dtype=torch.uint8)
+    ref = codes.view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = e4m3_decode_table()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3_encode_matches_torch_on_every_fp16_in_range():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    h = h[np.isfinite(h)]
+    h = h[np.abs(h.astype(np.float64)) < 464.0]    # torch does not saturate beyond this
+    ours = e4m3_encode(h.astype(np.float64))
+    ref = torch.from_numpy(h.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(ours, ref)
+
+
+def test_e4m3_encode_saturates_and_keeps_sign():
+    x = np.array([448.0, 463.99, 464.0, 500.0, 1e6, np.inf, -1e6, -np.inf])
+    np.testing.assert_array_equal(e4m3_encode(x),
+                                  [0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0x7E, 0xFE, 0xFE])
+    assert e4m3_encode(np.array([np.nan]))[0] & 0x7F == 0x7F
+    np.testing.assert_array_equal(e4m3_encode(np.array([-0.0, -1e-9, 0.0, 1e-9])),
+                                  [0x80, 0x80, 0x00, 0x00])
+
+
+def test_e4m3_encode_is_nearest_with_even_ties():
+    rng = np.random.default_rng(3)
+    y = rng.uniform(-460, 460, 20000) * np.exp2(rng.integers(-14, 1, 20000))
+    c = e4m3_encode(y)
+    err = np.abs(e4m3_decode(c) - y)
+    table = e4m3_decode_table()[:0x7F]
+    best = np.abs(np.abs(y)[:, None] - table[None, :]).min(axis=1)
+    np.testing.assert_array_equal(err, best)
+    # exact midpoints: 1 + 1/16 lies between 1.0 (0x38) and 1.125 (0x39) -> even code 0x38
+    assert e4m3_encode(np.array([1.0625]))[0] == 0x38
+    assert e4m3_encode(np.array([1.1875]))[0] == 0x3A   # between 0x39 and 0x3A -> 0x3A
+    assert e4m3_encode(np.array([2.0 ** -10]))[0] == 0x00   # half of the smallest subnormal
+    assert e4m3_encode(np.array([3 * 2.0 ** -10]))[0] == 0x02
+
+
+def test_f16_round_all_codes_roundtrip_and_ties():
+    h = np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    fin = np.isfinite(h)
+    back = f16_round(h[fin].astype(np.float64))
+    np.testing.assert_array_equal(back.view(np.uint16), h[fin].view(np.uint16))
+    assert f16_round(1 + 2.0 ** -11) == 1.0
+    assert f16_round(1 + 3 * 2.0 ** -11) == 1 + 2.0 ** -9
+
+
+def _block(H=3, D=8):
+    return np.zeros((H, 16, D), dtype=np.uint8)
+
+
+def test_fp8_first_token_scale_and_extreme_code():
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 8)).astype(np.float32)
+    codes = _block()
+    s = fp8_write_token(codes, 0.0, 0, x)
+    amax = np.float32(np.abs(x).max())
+    assert s == np.float32(amax / np.float32(448.0))
+    i = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert codes[i[0], 0, i[1]] & 0x7F == 0x7E
+    # every value within half an e4m3 step (relative 2^-4 for normals) of the input
+    vals = e4m3_decode(codes[:, 0, :]) * np.float64(s)
+    bound = np.maximum(np.abs(x) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 1e-6)
+    assert np.all(np.abs(vals - x) <= bound)
+
+
+def test_fp8_single_token_codes_match_torch_quantiser():
+    rng = np.random.default_rng(12)
+    x = (rng.standard_normal((4, 16)) * 3).astype(np.float16).astype(np.float32)
+    codes = np.zeros((4, 16, 16), dtype=np.uint8)
+    s = fp8_write_token(codes, 0.0, 0, x)
+    q = torch.from_numpy(x) / torch.tensor(s, dtype=torch.float32)
+    ref = q.clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes[:, 0, :], ref)
+
+
+def test_fp8_smaller_token_leaves_earlier_codes_untouched():
+    rng = np.random.default_rng(13)
+    codes = _block()
+    x0 = rng.standard_normal((3, 8)).astype(np.float32) * 4
+    s0 = fp8_write_token(codes, 0.0, 0, x0)
+    before = codes[:, 0, :].copy()
+    x1 = x0 * np.float32(0.25)
+    s1 = fp8_write_token(codes, s0, 1, x1)
+    assert s1 == s0
+    np.testing.assert_array_equal(codes[:, 0, :], before)
+
+
+def test_fp8_growing_scale_requantises_earlier_tokens():
+    rng = np.random.default_rng(14)
+    codes = _block()
+    x0 = rng.standard_normal((3, 8)).astype(np.float32)
+    s0 = fp8_write_token(codes, 0.0, 0, x0)
+    c0 = codes[:, 0, :].copy()
+    x1 = rng.standard_normal((3, 8)).astype(np.float32) * 10
+    s1 = fp8_write_token(codes, s0, 1, x1)
+    assert s1 == np.float32(np.float32(np.abs(x1).max()) / np.float32(448))
+    assert s1 > s0
+    # the first token stays within one step at the old scale plus one at the new scale
+    v0 = e4m3_decode(codes[:, 0, :]) * np.float64(s1)
+    bound = (np.maximum(np.abs(x0) * 2.0 ** -4, 2.0 ** -10 * s0)
+             + np.maximum(np.abs(x0) * 1.07 * 2.0 ** -4, 2.0 ** -10 * s1)) * (1 + 1e-6)
+    assert np.all(np.abs(v0 - x0) <= bound)
+    # the earlier token is requantised from its stored codes (dequantise at the old scale, then
+    # quantise at the new one); torch's fp8 conversion does the rounding here
+    deq = torch.from_numpy(c0).view(torch.float8_e4m3fn).to(torch.float32) * float(s0)
+    ref = (deq / float(s1)).clamp(-448, 448).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    np.testing.assert_array_equal(codes[:, 0, :], ref)
+
+
+def test_fp8_slot_zero_restarts_block_and_zero_tokens():
+    codes = _block()
+    big = np.full((3, 8), 100.0, dtype=np.float32)
+    s = fp8_write_token(codes, 0.0, 0, big)
+    # a later write at slot 0 ignores the stale scale
+    small = np.full((3, 8), 0.5, dtype=np.float32)
+    s2 = fp8_write_token(codes, s, 0, small)
+    assert s2 == np.float32(np.float32(0.5) / np.float32(448))
+    # an all-zero first token keeps scale 0 and signed-zero codes; a later token sets the scale
+    codes = _block()
+    z = np.zeros((3, 8), dtype=np.float32)
+    z[0, 0] = -0.0
+    s = fp8_write_token(codes, 0.0, 0, z)
+    assert s == 0.0 and np.all((codes[:, 0, :] & 0x7F) == 0)
+    s = fp8_write_token(codes, s, 1, small)
+    assert s > 0 and np.all((codes[:, 0, :] & 0x7F) == 0)
+    assert np.all(codes[:, 1, :] == 0x7E)
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_fp8_token_sequential_error_vs_unquantised(seed):
+    """A 16-token block of N(0,1) fp16 data stays within the fp8 tolerance band of 3e-2 relative
+    to typical magnitudes once all requantisations are done."""
+    rng = np.random.default_rng(seed)
+    H, D = 4, 32
+    xs = rng.standard_normal((16, H, D)).astype(np.float16).astype(np.float32)
+    codes = np.zeros((H, 16, D), dtype=np.uint8)
+    s = 0.0
+    for t in range(16):
+        s = fp8_write_token(codes, s, t, xs[t])
+    vals = e4m3_decode(codes) * np.float64(s)           # [H, 16, D]
+    err = np.abs(vals - xs.transpose(1, 0, 2))
+    assert err.max() < 0.5 and err.mean() < 0.05
+    # the scale is the block maximum over all written tokens / 448
+    assert s == np.float32(np.float32(np.abs(xs).max()) / np.float32(448))

@@ -1,0 +1,129 @@
+"""Seeded synthetic inputs and workload shapes for decode attention over a KV cache.
+
+This module is shared by the tests, the benchmark and the smoke check. It holds random draws and
+shape bookkeeping only: no attention arithmetic, no cache layout logic and no codec. Both the CPU
+oracle and the HIP path receive the arrays produced here and nothing else in common.
+
+Value distribution: K, V and Q entries are standard normal, drawn in float32 from a seeded
+generator and, for fp16 workloads, rounded to fp16 (round to nearest even) by NumPy or torch.
+
+Workload shapes follow the pages' model dimensions:
+  * tiny character GPT: 6 heads x 64-dim heads, context 256 (From Neuron to GPT, "KV cache"
+    chapter, trainer section: 6 blocks, 6 heads, embedding 384, context 256);
+  * LLaMA-7B: 32 layers x 32 heads x 128 (KV Cache Mechanism Explained, section 3.1);
+  * LLaMA-13B: 40 layers x 40 heads x 128 (KV Cache and PagedAttention, section 1.1);
+  * parallel sampling: 8 candidates, 1024-token prompt, 128 generated tokens (KV Cache and
+    PagedAttention, section 5.1).
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+BLOCK_SIZE = 16
+
+
+def rng(seed: int) -> np.random.Generator:
+    return np.random.default_rng(seed)
+
+
+def normal_f32(gen: np.random.Generator, shape) -> np.ndarray:
+    """Standard normal float32 draws."""
+    return gen.standard_normal(size=shape, dtype=np.float32)
+
+
+def normal(gen: np.random.Generator, shape, dtype: str) -> np.ndarray:
+    """Standard normal draws stored in `dtype` ("f32" or "f16")."""
+    x = normal_f32(gen, shape)
+    if dtype == "f32":
+        return x
+    if dtype == "f16":
+        return x.astype(np.float16)
+    raise ValueError(dtype)
+
+
+def uniform_lengths(gen: np.random.Generator, n: int, lo: int, hi: int) -> np.ndarray:
+    """n integers drawn uniformly from the closed range [lo, hi]."""
+    return gen.integers(lo, hi + 1, size=n).astype(np.int64)
+
+
+def permutation(gen: np.random.Generator, n: int) -> np.ndarray:
+    return gen.permutation(n).astype(np.int32)
+
+
+def torch_normal(shape, dtype, device, seed: int):
+    """Standard normal tensor drawn on `device` by torch's seeded generator (large workloads
+    whose inputs are generated in device memory). Returns a tensor of `dtype`."""
+    import torch
+
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    x = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+    return x.to(dtype)
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    kind: str                 # "contig" or "paged"
+    layers: int
+    batch: int
+    heads: int
+    head_dim: int
+    kv_dtype: str             # "f32", "f16", "e4m3"
+    q_dtype: str
+    seed: int
+    # contiguous: capacity per sequence; paged: unused
+    s_max: int = 0
+    # attended length after the append (contig / fp8): every sequence has this length
+    ctx: int = 0
+    # paged with drawn lengths: closed range of the attended length
+    ctx_lo: int = 0
+    ctx_hi: int = 0
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(1.0 / math.sqrt(self.head_dim)))
+
+
+TINY_GPT = Workload(
+    name="tiny-gpt-6x64-f32-contig-ctx256", kind="contig", layers=1, batch=1, heads=6,
+    head_dim=64, kv_dtype="f32", q_dtype="f32", seed=1, s_max=256, ctx=256,
+    extra={"prefill": 16, "decode_steps": 240})
+
+LLAMA7B_CONTIG = Workload(
+    name="llama7b-32x32x128-f16-contig-b16-ctx2048", kind="contig", layers=32, batch=16,
+    heads=32, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=2, s_max=2048, ctx=2048)
+
+LLAMA13B_PAGED = Workload(
+    name="llama13b-40x40x128-f16-paged16-b32-ctxU64-2048", kind="paged", layers=40, batch=32,
+    heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=3, ctx_lo=64, ctx_hi=2048)
+
+PARALLEL_SAMPLING = Workload(
+    name="parallel-sampling-8x(1024+128)-40x128-f16-paged16", kind="paged", layers=1, batch=8,
+    heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=4,
+    extra={"prompt": 1024, "generate": 128, "cow_variant_prompt": 1020})
+
+LONGCTX_FP8 = Workload(
+    name="llama7b-32x32x128-e4m3-paged16-b64-ctx4096", kind="paged", layers=32, batch=64,
+    heads=32, head_dim=128, kv_dtype="e4m3", q_dtype="f16", seed=5, ctx=4096)
+
+ALL = [TINY_GPT, LLAMA7B_CONTIG, LLAMA13B_PAGED, PARALLEL_SAMPLING, LONGCTX_FP8]
+
+
+def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
+    """Attended lengths of the LLaMA-13B paged batch: uniform in [ctx_lo, ctx_hi]."""
+    g = rng(w.seed if seed is None else seed)
+    return uniform_lengths(g, w.batch, w.ctx_lo, w.ctx_hi)
+
+
+def llama13b_pool_order(num_blocks: int, seed: int) -> np.ndarray:
+    """Shuffled physical-block order for the LLaMA-13B paged pool (a seeded permutation)."""
+    return permutation(rng(seed + 1000), num_blocks)
+
+
+def blocks_for(n_tokens: int, block_size: int = BLOCK_SIZE) -> int:
+    return -(-int(n_tokens) // block_size)
