@@ -1,0 +1,259 @@
+/*
+ * kvc.h -- decode attention over a growing KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * One new query per sequence attends every cached position of that sequence:
+ *     out[b,h,:] = softmax(scale * q[b,h,:] . K[b,h,0:L_b,:]^T) . V[b,h,0:L_b,:]
+ * where L_b counts the token appended in this step. Two cache layouts are served by one
+ * kernel body: a contiguous [B, H, S_max, D] cache per layer, and a paged cache whose
+ * sequences reach fixed 16-token physical blocks through per-sequence block tables.
+ *
+ * Pages cited (titles as printed, with their own section numbers):
+ *   "LLM Inference Acceleration -- KV Cache" (大模型推理加速——KV Cache篇)
+ *   "KV Cache Mechanism Explained" (KV缓存机制解析：优化大型语言模型推理性能)
+ *   "From Neuron to GPT -- KV cache chapter" (键值缓存)
+ *   "KV Cache and PagedAttention" (KV Cache与PagedAttention：大模型推理显存优化方案)
+ *
+ * General rules
+ *   - Every call returns kvc_status. Nothing aborts and no C++ exception crosses this ABI.
+ *   - Host-pool calls (kvc_pool_*, kvc_alloc ... kvc_check) touch host memory only, are not
+ *     thread-safe for one pool (serialise calls per pool), and give the strong guarantee: a call
+ *     that fails leaves the pool exactly as it was.
+ *   - Device calls never allocate device memory. Every array they take is caller-owned device
+ *     memory unless marked "host". They are stream-ordered on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream) and return once the work is queued. Arguments are
+ *     validated on the host before anything is launched (KVC_E_INVALID / KVC_E_UNSUPPORTED, and
+ *     nothing is queued); a launch failure reported by the runtime gives KVC_E_HIP. Faults
+ *     inside kernels surface at the caller's next synchronisation.
+ *   - Device arrays must be 16-byte aligned and densely packed in the stated layouts.
+ *   - Kernels read device-side lengths and block ids defensively: lengths are clamped to
+ *     [0, capacity] and a block id outside [0, num_blocks) makes that block contribute nothing,
+ *     so malformed tables cannot make a kernel read outside the pools.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum kvc_status {
+  KVC_OK = 0,
+  KVC_E_INVALID = -1,     /* bad argument (null pointer, bad size, misaligned, short buffer) */
+  KVC_E_OOM = -2,         /* the block pool has no free block for the request */
+  KVC_E_NOSEQ = -3,       /* the sequence id is not live */
+  KVC_E_CAPACITY = -4,    /* a sequence would exceed max_blocks_per_seq blocks */
+  KVC_E_UNSUPPORTED = -5, /* valid but not implemented combination (dtype, head_dim) */
+  KVC_E_HIP = -6          /* the HIP runtime reported an error */
+} kvc_status;
+
+typedef enum kvc_dtype {
+  KVC_F32 = 0,  /* IEEE binary32 */
+  KVC_F16 = 1,  /* IEEE binary16 */
+  KVC_E4M3 = 2  /* OCP fp8 e4m3 ("fn": bias 7, max 448, no inf, 0x7F/0xFF NaN); cache only */
+} kvc_dtype;
+
+#define KVC_BLOCK_SIZE 16
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *kvc_status_str(kvc_status s);
+
+/* ==================================================================================== *
+ * Host-side block pool ("KV Cache and PagedAttention", sections 2.1, 2.2, 3.1, 3.3, 5.1;
+ * "LLM Inference Acceleration -- KV Cache", section 6.1).
+ *
+ * The pool tracks, for num_blocks physical blocks of KVC_BLOCK_SIZE token slots, a reference
+ * count per block, and per live sequence its length and block table (logical block i holds
+ * tokens 16i .. 16i+15). One table per sequence serves every layer: each layer has its own
+ * K/V pool arrays indexed by the same physical block ids. The pool never touches device
+ * memory; device-side effects of its decisions are carried out by kvc_copy_blocks and
+ * kvc_write_paged.
+ *
+ * Allocation is first fit: the first free block in pool order (section 3.1 chooses first fit).
+ * Pool order is block id order, or a caller-given permutation (a shuffled pool).
+ * Sequence ids are the lowest non-negative id not in use.
+ * ==================================================================================== */
+typedef struct kvc_pool kvc_pool; /* opaque */
+
+typedef struct kvc_pool_stats {
+  int32_t num_blocks;    /* physical blocks in the pool */
+  int32_t used;          /* blocks with refcount > 0 */
+  int32_t free_blocks;   /* blocks with refcount == 0 */
+  int32_t shared;        /* blocks with refcount > 1 */
+  int32_t num_seqs;      /* live sequences */
+  int32_t reserved;
+  int64_t cow_copies;    /* copy-on-write copies emitted since creation */
+  int64_t tokens;        /* sum of live sequence lengths (shared prefixes counted per sequence) */
+  int64_t slots_logical; /* sum over live sequences of 16 x table entries */
+} kvc_pool_stats;
+
+/* Create a pool. block_size must be KVC_BLOCK_SIZE. order: host int32[num_blocks], a
+ * permutation of 0..num_blocks-1 giving the first-fit search order, or NULL for id order
+ * (copied; the caller keeps ownership). On success *out owns the pool (kvc_pool_destroy). */
+kvc_status kvc_pool_create(int32_t num_blocks, int32_t block_size, int32_t max_blocks_per_seq,
+                           const int32_t *order, kvc_pool **out);
+void kvc_pool_destroy(kvc_pool *pool);
+
+/* New empty sequence (length 0, no blocks). *seq_out receives its id. */
+kvc_status kvc_alloc(kvc_pool *pool, int32_t *seq_out);
+
+/* Reserve n_tokens new token slots at the end of each listed sequence, in list order, all tokens
+ * of seqs[0] first. For each token, at length L: if L % 16 == 0 a fresh block is taken (first
+ * fit, refcount 1); otherwise, if the last block is shared (refcount > 1), copy-on-write takes a
+ * fresh block, records the pair (old, new), drops one reference to the old block and repoints
+ * the table (section 3.3); the token's slot is block*16 + L%16.
+ *   seqs:        host int32[n_seqs] (a sequence may appear more than once)
+ *   slots_out:   host int64[n_seqs * n_tokens]; slots_out[i*n_tokens + j] is token j of seqs[i]
+ *   cow_src_out, cow_dst_out: host int32[cow_cap]; the copy pairs, in the order they arose.
+ *                Copies must be carried out (kvc_copy_blocks) before the writes of this call.
+ *   cow_cap:     must be >= n_seqs (each sequence copies at most once per call)
+ *   n_cow_out:   host; receives the number of pairs
+ * Errors: KVC_E_NOSEQ (a listed id is not live), KVC_E_CAPACITY (a table would exceed
+ * max_blocks_per_seq), KVC_E_OOM (no free block), KVC_E_INVALID. On error nothing changes. */
+kvc_status kvc_append(kvc_pool *pool, const int32_t *seqs, int32_t n_seqs, int32_t n_tokens,
+                      int64_t *slots_out, int32_t *cow_src_out, int32_t *cow_dst_out,
+                      int32_t cow_cap, int32_t *n_cow_out);
+
+/* New sequence sharing all of parent's blocks: same length, same table, one more reference on
+ * every block (parallel sampling, section 5.1). *child_out receives its id. */
+kvc_status kvc_fork(kvc_pool *pool, int32_t parent, int32_t *child_out);
+
+/* End a sequence: one reference fewer on each of its blocks; blocks reaching 0 become free
+ * (their device contents are left as they are). */
+kvc_status kvc_free(kvc_pool *pool, int32_t seq);
+
+/* Block tables and lengths of the listed sequences.
+ *   tables_out: host int32[n_seqs][max_blocks_per_seq], unused entries set to -1
+ *   lens_out:   host int32[n_seqs] (may be NULL) */
+kvc_status kvc_block_table(const kvc_pool *pool, const int32_t *seqs, int32_t n_seqs,
+                           int32_t *tables_out, int32_t *lens_out);
+
+kvc_status kvc_stats(const kvc_pool *pool, kvc_pool_stats *out);
+
+/* Check the pool's invariants ("KV Cache and PagedAttention", section 6.2: leaks show up as
+ * wrong reference counts): every refcount equals the number of table entries naming the block,
+ * every table has exactly ceil(len/16) entries, within capacity, in range, without repeats.
+ * Returns KVC_OK or KVC_E_INVALID. */
+kvc_status kvc_check(const kvc_pool *pool);
+
+/* ==================================================================================== *
+ * Device side: cache writes.
+ * ==================================================================================== */
+
+/* One layer of a paged cache (device pointers owned by the caller).
+ *   k_pool, v_pool: [num_blocks][num_heads][16][head_dim] elements of kv_dtype
+ *   k_scale, v_scale: float[num_blocks], one fp32 scale per block for K and for V, covering all
+ *                     heads of the block (KVC_E4M3 only; NULL otherwise). The stored value of
+ *                     code c in block p is e4m3(c) * scale[p]. */
+typedef struct kvc_paged_layer {
+  kvc_dtype kv_dtype;
+  int32_t num_blocks;
+  int32_t num_heads;
+  int32_t head_dim; /* 64 or 128 */
+  void *k_pool;
+  void *v_pool;
+  float *k_scale;
+  float *v_scale;
+} kvc_paged_layer;
+
+/* Contiguous append ("LLM Inference Acceleration -- KV Cache", section 3.1: the new k/v are
+ * stored at start_pos before attention reads the cache).
+ *   k_cache, v_cache: [B][H][S_max][D] of dtype (KVC_F32 or KVC_F16)
+ *   pos:   device int32[B], first position written for each sequence
+ *   k_new, v_new: [B][n_tok][H][D] of dtype (token-major, as projections produce them)
+ * Writes K[b,h,pos[b]+t,:] = k_new[b,t,h,:] for t < n_tok; positions outside [0, S_max) are
+ * skipped. D is 64 or 128. */
+kvc_status kvc_append_contig(void *k_cache, void *v_cache, kvc_dtype dtype, int32_t B, int32_t H,
+                             int32_t S_max, int32_t D, const int32_t *pos, int32_t n_tok,
+                             const void *k_new, const void *v_new, void *stream);
+
+/* Carry out copy-on-write pairs ("KV Cache and PagedAttention", section 3.3, copy_block): for
+ * each i < n, block dst[i] of K and V (and its fp8 scales) becomes a copy of block src[i].
+ * src, dst: device int32[n]. All pairs are done in one launch. A pair naming a block outside
+ * [0, num_blocks) is skipped. The dst blocks of one call must be distinct and no dst may be a src
+ * (kvc_append's pairs satisfy both). */
+kvc_status kvc_copy_blocks(const kvc_paged_layer *layer, const int32_t *src, const int32_t *dst,
+                           int32_t n, void *stream);
+
+/* Store new tokens' K and V at their slots (slot = block*16 + offset, from kvc_append).
+ *   slots: device int64[n_tok]; k_new, v_new: [n_tok][H][D] of new_dtype
+ *   f32/f16 pools: new_dtype must equal kv_dtype; a plain copy.
+ *   e4m3 pools: new_dtype is KVC_F16 or KVC_F32; tokens are quantised one at a time in slot-array
+ *     order with the per-block running-maximum rule: writing offset 0 starts the block afresh
+ *     (scale 0); for a token x, s_new = fp32(max|x| / 448); if s_new exceeds the block's scale,
+ *     codes already in offsets [0, off) are requantised as e4m3(fp32(fp32(e4m3(c) * old) /
+ *     s_new)) and the scale becomes s_new; the token is stored as e4m3(fp32(x / scale)), rounded
+ *     to nearest even and saturated to +-448 (signed zero while the scale is 0). ("KV Cache
+ *     Mechanism Explained", section 8, item 3: fp8 e4m3 cache with a scaling factor.) All
+ *     entries that target one block must be adjacent in `slots`; inputs must be finite.
+ * Entries with a slot outside [0, 16*num_blocks) are skipped. */
+kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, int32_t n_tok,
+                           const void *k_new, const void *v_new, kvc_dtype new_dtype,
+                           void *stream);
+
+/* ==================================================================================== *
+ * Device side: decode attention.
+ *
+ * Pass 1 splits the work of all (sequence, head) pairs -- H * sum_b ceil(L_b/16) blocks of 16
+ * positions -- into equal contiguous chunks, one per wavefront of a grid sized to the GPU. Each
+ * wavefront runs an online softmax (running max and running sum) over its chunk and either
+ * writes the finished output row (when it saw the whole sequence-head) or a partial state
+ * (max, sum, unnormalised output) to the workspace. Pass 2 combines the partial states of
+ * every sequence-head that was split. Accumulation is fp32; scores are never rounded below
+ * fp32 ("LLM Inference Acceleration -- KV Cache", section 3.1 takes the softmax in float).
+ *
+ * Common arguments
+ *   q:        [B][H][D] of q_dtype (KVC_F32 or KVC_F16)
+ *   ctx_lens: device int32[B], L_b = positions attended by sequence b (its new token included);
+ *             clamped to [0, capacity]; L_b = 0 gives a zero output row
+ *   max_ctx:  host upper bound of every L_b (sizes the grid; need not be tight)
+ *   scale:    multiplies q.k (normally 1/sqrt(D))
+ *   out:      [B][H][D] of out_dtype (KVC_F32 or KVC_F16), rounded to nearest even
+ *   workspace: device buffer of at least kvc_decode_workspace_bytes(B, H, D) bytes, 256-byte
+ *             aligned, owned by the caller; its contents need no initialisation and are
+ *             overwritten. Calls that overlap in time must use different workspaces.
+ * Supported: D in {64, 128}; kv dtype f32/f16 (contiguous) and f32/f16/e4m3 (paged).
+ * ==================================================================================== */
+size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D);
+
+/* Contiguous cache: k_cache, v_cache [B][H][S_max][D] of kv_dtype (capacity = S_max). */
+kvc_status kvc_decode_attn_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+                                  const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                  int32_t B, int32_t H, int32_t S_max, int32_t D, int32_t max_ctx,
+                                  float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                  size_t ws_bytes, void *stream);
+
+/* Paged cache ("KV Cache and PagedAttention", section 3.2: gather each sequence's blocks
+ * through its block table). block_tables: device int32[B][max_blocks_per_seq] (from
+ * kvc_block_table); capacity = 16 * max_blocks_per_seq. H and D come from the layer. */
+kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *ctx_lens, int32_t B, int32_t max_ctx, float scale,
+                                 void *out, kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream);
+
+/* The two passes as separate launches, for callers that time or schedule them apart.
+ * kvc_decode_attn_{contig,paged} == the matching *_partial call followed by kvc_decode_merge
+ * on the same stream, workspace and out. Pass 1 leaves a record of its split in the workspace;
+ * kvc_decode_merge must follow it with the same B, H, D and out before the workspace is reused. */
+kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+                                     const void *v_cache, kvc_dtype kv_dtype,
+                                     const int32_t *ctx_lens, int32_t B, int32_t H, int32_t S_max,
+                                     int32_t D, int32_t max_ctx, float scale, void *out,
+                                     kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                     void *stream);
+kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
+                                    const kvc_paged_layer *layer, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                    int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                    void *workspace, size_t ws_bytes, void *stream);
+kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
+                            void *workspace, size_t ws_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

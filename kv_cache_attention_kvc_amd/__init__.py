@@ -1,0 +1,421 @@
+"""Python binding of libkvc: decode attention over a KV cache on AMD MI355X (gfx950).
+
+Argument marshalling only: every step runs in libkvc (host block pool in C++, cache writes and
+attention in HIP kernels). torch is used for device memory and streams. The library must have
+been built (`python -m kv_cache_attention_kvc_amd.csrc.build`); importing works without it, but
+the first call raises if libkvc.so is missing -- there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "KvcError", "load_library", "library_path", "Pool", "PagedLayer",
+    "F32", "F16", "E4M3", "BLOCK_SIZE", "workspace_bytes",
+    "append_contig", "copy_blocks", "write_paged", "decode_attn_contig", "decode_attn_paged",
+    "decode_partial_contig", "decode_partial_paged", "decode_merge", "EXPORTS",
+]
+
+F32, F16, E4M3 = 0, 1, 2
+BLOCK_SIZE = 16
+_STATUS = {0: "KVC_OK", -1: "KVC_E_INVALID", -2: "KVC_E_OOM", -3: "KVC_E_NOSEQ",
+           -4: "KVC_E_CAPACITY", -5: "KVC_E_UNSUPPORTED", -6: "KVC_E_HIP"}
+
+# every symbol include/kvc.h declares
+EXPORTS = [
+    "kvc_status_str", "kvc_pool_create", "kvc_pool_destroy", "kvc_alloc", "kvc_append",
+    "kvc_fork", "kvc_free", "kvc_block_table", "kvc_stats", "kvc_check", "kvc_append_contig",
+    "kvc_copy_blocks", "kvc_write_paged", "kvc_decode_workspace_bytes", "kvc_decode_attn_contig",
+    "kvc_decode_attn_paged", "kvc_decode_partial_contig", "kvc_decode_partial_paged",
+    "kvc_decode_merge",
+]
+
+
+class KvcError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = status
+        name = _STATUS.get(status, str(status))
+        msg = _lib().kvc_status_str(status).decode() if _LIB is not None else name
+        super().__init__(f"{where}: {name} ({msg})" if where else f"{name} ({msg})")
+
+
+class PoolStats(ctypes.Structure):
+    _fields_ = [("num_blocks", ctypes.c_int32), ("used", ctypes.c_int32),
+                ("free_blocks", ctypes.c_int32), ("shared", ctypes.c_int32),
+                ("num_seqs", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("cow_copies", ctypes.c_int64), ("tokens", ctypes.c_int64),
+                ("slots_logical", ctypes.c_int64)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("kv_dtype", ctypes.c_int), ("num_blocks", ctypes.c_int32),
+                ("num_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("k_pool", ctypes.c_void_p), ("v_pool", ctypes.c_void_p),
+                ("k_scale", ctypes.c_void_p), ("v_scale", ctypes.c_void_p)]
+
+
+_LIB: Optional[ctypes.CDLL] = None
+_P = ctypes.c_void_p
+_I32, _I64, _F = ctypes.c_int32, ctypes.c_int64, ctypes.c_float
+_PI32 = ctypes.POINTER(ctypes.c_int32)
+_PI64 = ctypes.POINTER(ctypes.c_int64)
+
+
+def library_path() -> str:
+    return os.environ.get("KVC_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libkvc.so")
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libkvc.so and declare its signatures. Raises if it has not been built."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"libkvc.so not found at {path}; build it with "
+                           "`python -m kv_cache_attention_kvc_amd.csrc.build`")
+    lib = ctypes.CDLL(path)
+    sig = {
+        "kvc_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "kvc_pool_create": (ctypes.c_int, [_I32, _I32, _I32, _P, ctypes.POINTER(_P)]),
+        "kvc_pool_destroy": (None, [_P]),
+        "kvc_alloc": (ctypes.c_int, [_P, _PI32]),
+        "kvc_append": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _P, _I32, _PI32]),
+        "kvc_fork": (ctypes.c_int, [_P, _I32, _PI32]),
+        "kvc_free": (ctypes.c_int, [_P, _I32]),
+        "kvc_block_table": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
+        "kvc_stats": (ctypes.c_int, [_P, ctypes.POINTER(PoolStats)]),
+        "kvc_check": (ctypes.c_int, [_P]),
+        "kvc_append_contig": (ctypes.c_int, [_P, _P, ctypes.c_int, _I32, _I32, _I32, _I32, _P,
+                                             _I32, _P, _P, _P]),
+        "kvc_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_Layer), _P, _P, _I32, _P]),
+        "kvc_write_paged": (ctypes.c_int, [ctypes.POINTER(_Layer), _P, _I32, _P, _P, ctypes.c_int,
+                                           _P]),
+        "kvc_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
+        "kvc_decode_attn_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32,
+                                                  _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P,
+                                                  ctypes.c_size_t, _P]),
+        "kvc_decode_partial_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
+                                                     _I32, _I32, _I32, _I32, _I32, _F, _P,
+                                                     ctypes.c_int, _P, ctypes.c_size_t, _P]),
+        "kvc_decode_attn_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P, _I32,
+                                                 _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
+                                                 ctypes.c_size_t, _P]),
+        "kvc_decode_partial_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P,
+                                                    _I32, _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
+                                                    ctypes.c_size_t, _P]),
+        "kvc_decode_merge": (ctypes.c_int, [_I32, _I32, _I32, _P, ctypes.c_int, _P,
+                                            ctypes.c_size_t, _P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _lib() -> ctypes.CDLL:
+    return _LIB if _LIB is not None else load_library()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KvcError(status, where)
+
+
+# ---------------------------------------------------------------------------------------------
+# Host block pool
+# ---------------------------------------------------------------------------------------------
+class Pool:
+    """Host-side block pool: first fit, refcounts, fork, copy-on-write (libkvc C++)."""
+
+    def __init__(self, num_blocks: int, max_blocks_per_seq: int, order=None,
+                 block_size: int = BLOCK_SIZE):
+        lib = _lib()
+        self.num_blocks = int(num_blocks)
+        self.max_blocks_per_seq = int(max_blocks_per_seq)
+        h = _P()
+        if order is not None:
+            self._order = np.ascontiguousarray(order, dtype=np.int32)
+            optr = self._order.ctypes.data
+        else:
+            optr = None
+        _check(lib.kvc_pool_create(num_blocks, block_size, max_blocks_per_seq, optr,
+                                   ctypes.byref(h)), "kvc_pool_create")
+        self._h = h
+
+    def close(self) -> None:
+        if getattr(self, "_h", None):
+            _lib().kvc_pool_destroy(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def alloc(self) -> int:
+        s = ctypes.c_int32()
+        _check(_lib().kvc_alloc(self._h, ctypes.byref(s)), "kvc_alloc")
+        return s.value
+
+    def append(self, seqs: Sequence[int], n_tokens: int):
+        """Returns (slots int64[n_seqs*n_tokens], cow_src int32[n], cow_dst int32[n])."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = len(seqs)
+        slots = np.empty(max(1, n * n_tokens), dtype=np.int64)
+        src = np.empty(max(1, n), dtype=np.int32)
+        dst = np.empty(max(1, n), dtype=np.int32)
+        ncow = ctypes.c_int32()
+        _check(_lib().kvc_append(self._h, seqs.ctypes.data, n, n_tokens, slots.ctypes.data,
+                                 src.ctypes.data, dst.ctypes.data, max(1, n),
+                                 ctypes.byref(ncow)), "kvc_append")
+        k = ncow.value
+        return slots[:n * n_tokens], src[:k].copy(), dst[:k].copy()
+
+    def fork(self, parent: int) -> int:
+        c = ctypes.c_int32()
+        _check(_lib().kvc_fork(self._h, parent, ctypes.byref(c)), "kvc_fork")
+        return c.value
+
+    def free(self, seq: int) -> None:
+        _check(_lib().kvc_free(self._h, seq), "kvc_free")
+
+    def block_table(self, seqs: Sequence[int], out_tables=None, out_lens=None):
+        """Tables [n, max_blocks_per_seq] (-1 padded) and lengths [n], int32. Optional output
+        arrays (e.g. pinned host tensors' numpy views) are filled in place."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = len(seqs)
+        t = out_tables if out_tables is not None else np.empty((n, self.max_blocks_per_seq),
+                                                               dtype=np.int32)
+        ln = out_lens if out_lens is not None else np.empty(n, dtype=np.int32)
+        assert t.dtype == np.int32 and t.flags.c_contiguous and t.shape == (n, self.max_blocks_per_seq)
+        assert ln.dtype == np.int32 and ln.shape == (n,)
+        _check(_lib().kvc_block_table(self._h, seqs.ctypes.data, n, t.ctypes.data, ln.ctypes.data),
+               "kvc_block_table")
+        return t, ln
+
+    def stats(self) -> dict:
+        st = PoolStats()
+        _check(_lib().kvc_stats(self._h, ctypes.byref(st)), "kvc_stats")
+        return {f: getattr(st, f) for f, _ in PoolStats._fields_ if f != "reserved"}
+
+    def check(self) -> None:
+        _check(_lib().kvc_check(self._h), "kvc_check")
+
+
+# ---------------------------------------------------------------------------------------------
+# Device side (torch tensors on the current device; launches on the current torch stream)
+# ---------------------------------------------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return F32
+    if t.dtype == torch.float16:
+        return F16
+    if t.dtype == torch.uint8:
+        return E4M3
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _ptr(t) -> int:
+    if not t.is_cuda:
+        raise ValueError("tensor must live in device memory")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(stream) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+@dataclass
+class PagedLayer:
+    """One layer of a paged cache: pools [num_blocks, H, 16, D] (float32/float16, or uint8 holding
+    e4m3 codes with float32 scales [num_blocks] for K and V)."""
+    k_pool: object
+    v_pool: object
+    k_scale: object = None
+    v_scale: object = None
+
+    @staticmethod
+    def empty(num_blocks: int, heads: int, head_dim: int, dtype: str, device="cuda", fill=None):
+        torch = _torch()
+        td = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8}[dtype]
+        shape = (num_blocks, heads, BLOCK_SIZE, head_dim)
+        if dtype == "e4m3" and fill is not None:
+            fill = 0x7F if fill != fill else int(fill)     # NaN -> the e4m3 NaN code
+        if fill is None:
+            k = torch.zeros(shape, dtype=td, device=device)
+            v = torch.zeros(shape, dtype=td, device=device)
+        else:
+            k = torch.full(shape, fill, dtype=td, device=device)
+            v = torch.full(shape, fill, dtype=td, device=device)
+        ks = vs = None
+        if dtype == "e4m3":
+            ks = torch.zeros(num_blocks, dtype=torch.float32, device=device)
+            vs = torch.zeros(num_blocks, dtype=torch.float32, device=device)
+        return PagedLayer(k, v, ks, vs)
+
+    @property
+    def num_blocks(self) -> int:
+        return self.k_pool.shape[0]
+
+    @property
+    def heads(self) -> int:
+        return self.k_pool.shape[1]
+
+    @property
+    def head_dim(self) -> int:
+        return self.k_pool.shape[3]
+
+    def struct(self) -> _Layer:
+        if tuple(self.k_pool.shape) != tuple(self.v_pool.shape) or self.k_pool.dim() != 4 \
+                or self.k_pool.shape[2] != BLOCK_SIZE:
+            raise ValueError("pools must be [num_blocks, H, 16, D] and alike")
+        code = _dtype_code(self.k_pool)
+        s = _Layer(code, self.num_blocks, self.heads, self.head_dim, _ptr(self.k_pool),
+                   _ptr(self.v_pool), None, None)
+        if code == E4M3:
+            s.k_scale = _ptr(self.k_scale)
+            s.v_scale = _ptr(self.v_scale)
+        return s
+
+
+def workspace_bytes(B: int, H: int, D: int) -> int:
+    return int(_lib().kvc_decode_workspace_bytes(B, H, D))
+
+
+def _workspace(B, H, D, ws, device):
+    torch = _torch()
+    need = workspace_bytes(B, H, D)
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError(f"workspace too small: {ws.numel()} < {need}")
+    return ws
+
+
+def append_contig(k_cache, v_cache, pos, k_new, v_new, stream=None) -> None:
+    """K[b,h,pos[b]+t,:] = k_new[b,t,h,:] (k_cache [B,H,S_max,D], k_new [B,n,H,D], pos int32[B])."""
+    B, H, S, D = k_cache.shape
+    if k_new.shape[0] != B or k_new.shape[2] != H or k_new.shape[3] != D:
+        raise ValueError("k_new must be [B, n, H, D]")
+    if k_new.dtype != k_cache.dtype or v_new.dtype != v_cache.dtype:
+        raise ValueError("new K/V must have the cache dtype")
+    _check(_lib().kvc_append_contig(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), B, H, S,
+                                    D, _ptr(pos), k_new.shape[1], _ptr(k_new), _ptr(v_new),
+                                    _stream(stream)), "kvc_append_contig")
+
+
+def copy_blocks(layer: PagedLayer, src, dst, stream=None) -> None:
+    n = int(src.numel())
+    if n == 0:
+        return
+    st = layer.struct()
+    _check(_lib().kvc_copy_blocks(ctypes.byref(st), _ptr(src), _ptr(dst), n, _stream(stream)),
+           "kvc_copy_blocks")
+
+
+def write_paged(layer: PagedLayer, slots, k_new, v_new, stream=None) -> None:
+    """Store k_new/v_new [n, H, D] at int64 slots[n] (fp8 pools quantise per block)."""
+    n = int(slots.numel())
+    if n == 0:
+        return
+    if tuple(k_new.shape) != (n, layer.heads, layer.head_dim) or k_new.shape != v_new.shape:
+        raise ValueError("k_new/v_new must be [n, H, D]")
+    st = layer.struct()
+    _check(_lib().kvc_write_paged(ctypes.byref(st), _ptr(slots), n, _ptr(k_new), _ptr(v_new),
+                                  _dtype_code(k_new), _stream(stream)), "kvc_write_paged")
+
+
+def _out_for(q, out):
+    torch = _torch()
+    return torch.empty_like(q) if out is None else out
+
+
+def decode_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
+                          workspace=None, stream=None):
+    B, H, S, D = k_cache.shape
+    out = _out_for(q, out)
+    ws = _workspace(B, H, D, workspace, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(_lib().kvc_decode_partial_contig(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(ctx_lens),
+        B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        ws.numel(), _stream(stream)), "kvc_decode_partial_contig")
+    return out, ws
+
+
+def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
+                         out=None, workspace=None, stream=None):
+    B = q.shape[0]
+    out = _out_for(q, out)
+    ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(_lib().kvc_decode_partial_paged(
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        ws.numel(), _stream(stream)), "kvc_decode_partial_paged")
+    return out, ws
+
+
+def decode_merge(B, H, D, out, workspace, stream=None):
+    _check(_lib().kvc_decode_merge(B, H, D, _ptr(out), _dtype_code(out), _ptr(workspace),
+                                   workspace.numel(), _stream(stream)), "kvc_decode_merge")
+    return out
+
+
+def decode_attn_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
+                       workspace=None, stream=None):
+    """Single-query attention over a contiguous cache: q [B,H,D], caches [B,H,S_max,D],
+    ctx_lens int32[B] on the device. Returns out [B,H,D] (q's dtype unless `out` is given)."""
+    B, H, S, D = k_cache.shape
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError("q must be [B, H, D]")
+    out = _out_for(q, out)
+    ws = _workspace(B, H, D, workspace, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(_lib().kvc_decode_attn_contig(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(ctx_lens),
+        B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        ws.numel(), _stream(stream)), "kvc_decode_attn_contig")
+    return out
+
+
+def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
+                      out=None, workspace=None, stream=None):
+    """Single-query attention over a paged cache: q [B,H,D], block_tables int32 [B, max_blocks]
+    and ctx_lens int32[B] on the device. Returns out [B,H,D]."""
+    B = q.shape[0]
+    if tuple(q.shape) != (B, layer.heads, layer.head_dim):
+        raise ValueError("q must be [B, H, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    out = _out_for(q, out)
+    ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(_lib().kvc_decode_attn_paged(
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        ws.numel(), _stream(stream)), "kvc_decode_attn_paged")
+    return out

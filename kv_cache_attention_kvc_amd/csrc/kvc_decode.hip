@@ -1,0 +1,647 @@
+// Decode attention over a contiguous or paged KV cache, for gfx950 (64-lane wavefronts).
+//
+// out[b,h,:] = softmax(scale * q[b,h,:] . K[b,h,0:L_b,:]^T) . V[b,h,0:L_b,:]  -- one new query
+// per sequence against every cached position, the new token included ("LLM Inference
+// Acceleration -- KV Cache", section 3.1; "KV Cache Mechanism Explained", section 5.1). The
+// paged layout gathers each sequence's 16-token blocks through its block table ("KV Cache and
+// PagedAttention", section 3.2).
+//
+// Pass 1 (decode_partial_kernel). The work is the list of (sequence, head, block) triples in
+// (b, h, block) order: H * sum_b ceil(L_b/16) tiles of 16 positions. It is cut into P equal
+// contiguous chunks, one per wavefront, so every wavefront streams the same number of bytes
+// whatever the length mix. A wavefront walks its chunk tile by tile with the next tile's loads
+// in flight while it computes on the current one:
+//   * a token row (D elements) is read by LPT lanes with 16-byte loads, so one wave-wide load
+//     covers TPL = 64/LPT consecutive rows (1 KiB contiguous); a tile takes LOADS such loads;
+//   * each lane forms partial dot products over its 16 bytes of k; a butterfly of DPP adds
+//     inside each LPT-lane group gives every lane of the group the full score;
+//   * each group keeps its own online-softmax state (running max m, running sum l, and the
+//     unnormalised output for the lane's 16-byte column), so the loop has no cross-group
+//     traffic; the groups are combined once per (sequence, head) segment.
+// Scores are kept in log2 units (multiplied by scale*log2(e)) and exponentials use v_exp_f32.
+// A segment that covers a whole (sequence, head) is finished in place; a segment cut by a
+// chunk boundary leaves (m, l, o[D]) in one of the wavefront's two workspace records.
+//
+// Pass 2 (decode_merge_kernel) combines, for every (sequence, head) that was cut, the records
+// of the consecutive wavefronts that covered it, and writes zeros for empty sequences.
+#include <mutex>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+
+constexpr int kWgWaves = 4;
+constexpr int kWgThreads = kWave * kWgWaves;
+constexpr int kMaxWorkers = 8192;  // wavefronts of pass 1 at most (records in a workspace)
+constexpr int kMinChunk = 4;       // tiles per wavefront at least
+constexpr int kWavesPerCu = 16;    // pass-1 wavefronts per compute unit
+constexpr int kMaxBatch = 4096;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' never is NaN)
+
+struct WsLayout {
+  size_t pre_off, rec_off, total;
+};
+
+inline WsLayout ws_layout(int B, int D) {
+  WsLayout l;
+  l.pre_off = 256;
+  const size_t pre_bytes = ((static_cast<size_t>(B) + 1) * 4 + 255) & ~static_cast<size_t>(255);
+  l.rec_off = l.pre_off + pre_bytes;
+  l.total = l.rec_off + static_cast<size_t>(kMaxWorkers) * 2 * (D + 4) * sizeof(float);
+  return l;
+}
+
+struct DecodeArgs {
+  const void *q;
+  const char *k;
+  const char *v;
+  const float *k_scale;
+  const float *v_scale;
+  const int32_t *tables;
+  const int32_t *lens;
+  void *out;
+  int32_t *ws_hdr;
+  int32_t *ws_pre;
+  float *ws_rec;
+  int64_t seq_stride;  // contiguous: S_max
+  int32_t B, H, cap, mbps, num_blocks, P, cmin;
+  int32_t q_f16, out_f16;
+  float cl2;  // scale * log2(e)
+};
+
+// ---- wave helpers ----------------------------------------------------------------------
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of N lanes; every lane of a group gets the same bits.
+template <int N>
+__device__ __forceinline__ float group_sum(float x) {
+  x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]: lane ^ 1
+  x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of 8
+  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror: the other half of 16
+  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  return x;
+}
+
+__device__ __forceinline__ int32_t sread(const int32_t *p) {
+  return __builtin_amdgcn_readfirstlane(*p);
+}
+
+// Unpack the 16 bytes a lane loaded into EPL floats.
+template <int KV>
+__device__ __forceinline__ void unpack(const uint4 &r, float *f) {
+  if constexpr (KV == KVC_F32) {
+    f[0] = __uint_as_float(r.x);
+    f[1] = __uint_as_float(r.y);
+    f[2] = __uint_as_float(r.z);
+    f[3] = __uint_as_float(r.w);
+  } else if constexpr (KV == KVC_F16) {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i])));
+      f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+    }
+  } else {
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), false);
+      const auto hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(w[i]), true);
+      f[4 * i + 0] = lo[0];
+      f[4 * i + 1] = lo[1];
+      f[4 * i + 2] = hi[0];
+      f[4 * i + 3] = hi[1];
+    }
+  }
+}
+
+__device__ __forceinline__ float load_elem(const void *p, int64_t i, bool f16) {
+  if (f16) return static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]);
+  return reinterpret_cast<const float *>(p)[i];
+}
+
+__device__ __forceinline__ void store_elem(void *p, int64_t i, float x, bool f16) {
+  if (f16)
+    reinterpret_cast<_Float16 *>(p)[i] = static_cast<_Float16>(x);
+  else
+    reinterpret_cast<float *>(p)[i] = x;
+}
+
+// ---- per-workgroup prefix of block counts ------------------------------------------------
+// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences.
+__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *scan) {
+  const int tid = threadIdx.x;
+  const int per = (B + kWgThreads - 1) / kWgThreads;
+  const int lo = min(B, tid * per);
+  const int hi = min(B, lo + per);
+  int32_t sum = 0;
+  for (int i = lo; i < hi; ++i) {
+    const int32_t L = min(max(lens[i], 0), cap);
+    sum += (L + kBlock - 1) / kBlock;
+  }
+  scan[tid] = sum;
+  __syncthreads();
+  for (int off = 1; off < kWgThreads; off <<= 1) {
+    const int32_t add = tid >= off ? scan[tid - off] : 0;
+    __syncthreads();
+    scan[tid] += add;
+    __syncthreads();
+  }
+  int32_t run = scan[tid] - sum;
+  for (int i = lo; i < hi; ++i) {
+    pre[i] = run;
+    const int32_t L = min(max(lens[i], 0), cap);
+    run += (L + kBlock - 1) / kBlock;
+  }
+  if (tid == kWgThreads - 1) pre[B] = scan[tid];
+  __syncthreads();
+}
+
+// ---- one tile: loads ---------------------------------------------------------------------
+template <int KV, int D>
+struct TileRegs {
+  using G = Geo<KV, D>;
+  uint4 k[G::LOADS];
+  uint4 v[G::LOADS];
+  int32_t nt;      // valid rows (0 when the block id is out of range)
+  float ks, vs;    // fp8 block scales
+};
+
+template <bool PAGED, int KV, int D>
+__device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D> &t, int64_t bh,
+                                           int32_t h, int32_t j, int32_t phys, int32_t L,
+                                           int g, int c) {
+  using G = Geo<KV, D>;
+  const char *kt;
+  const char *vt;
+  bool valid = true;
+  if constexpr (PAGED) {
+    // addresses are formed from a clamped id, so nothing outside the pools is ever addressed
+    valid = static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
+    const int32_t sp = valid ? phys : 0;
+    const int64_t toff = (static_cast<int64_t>(sp) * a.H + h) * G::TILE;
+    kt = a.k + toff;
+    vt = a.v + toff;
+    if constexpr (KV == KVC_E4M3) {
+      t.ks = valid ? a.k_scale[sp] : 0.f;
+      t.vs = valid ? a.v_scale[sp] : 0.f;
+    }
+  } else {
+    const int64_t toff = (bh * a.seq_stride + static_cast<int64_t>(kBlock) * j) * G::ROW;
+    kt = a.k + toff;
+    vt = a.v + toff;
+  }
+  t.nt = valid ? min(kBlock, L - kBlock * j) : 0;
+  const int lane_off = g * G::ROW + c * 16;
+  if (t.nt == kBlock) {
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      t.k[i] = *reinterpret_cast<const uint4 *>(kt + lane_off + i * G::TPL * G::ROW);
+      t.v[i] = *reinterpret_cast<const uint4 *>(vt + lane_off + i * G::TPL * G::ROW);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      if (g + i * G::TPL < t.nt) {
+        t.k[i] = *reinterpret_cast<const uint4 *>(kt + lane_off + i * G::TPL * G::ROW);
+        t.v[i] = *reinterpret_cast<const uint4 *>(vt + lane_off + i * G::TPL * G::ROW);
+      } else {
+        t.k[i] = make_uint4(0, 0, 0, 0);
+        t.v[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+}
+
+// ---- one tile: online-softmax update of the group state ---------------------------------
+template <int KV, int D>
+__device__ __forceinline__ void consume_tile(const TileRegs<KV, D> &t, const float *qv, float cl2,
+                                             int g, float &m, float &l, float *acc) {
+  using G = Geo<KV, D>;
+  float s[G::LOADS];
+  const float sc = (KV == KVC_E4M3) ? cl2 * t.ks : cl2;
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    float kf[G::EPL];
+    unpack<KV>(t.k[i], kf);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) d = __builtin_fmaf(kf[e], qv[e], d);
+    d = group_sum<G::LPT>(d) * sc;
+    s[i] = (g + i * G::TPL < t.nt) ? d : -__builtin_inff();
+  }
+  float mb = s[0];
+#pragma unroll
+  for (int i = 1; i < G::LOADS; ++i) mb = fmaxf(mb, s[i]);
+  const float mn = fmaxf(m, mb);
+  const float alpha = __builtin_amdgcn_exp2f(m - mn);
+  float p[G::LOADS];
+  float psum = 0.f;
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    p[i] = __builtin_amdgcn_exp2f(s[i] - mn);
+    psum += p[i];
+  }
+  l = l * alpha + psum;
+  m = mn;
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) acc[e] *= alpha;
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    float vf[G::EPL];
+    unpack<KV>(t.v[i], vf);
+    const float pi = (KV == KVC_E4M3) ? p[i] * t.vs : p[i];
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[e] = __builtin_fmaf(pi, vf[e], acc[e]);
+  }
+}
+
+// ---- one (sequence, head) segment of a chunk --------------------------------------------
+template <bool PAGED, int KV, int D>
+__device__ __forceinline__ void run_segment(const DecodeArgs &a, int32_t b, int32_t h, int32_t j0,
+                                            int32_t n, int32_t w, bool cut_start, bool cut_end) {
+  using G = Geo<KV, D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G::LPT;
+  const int c = lane % G::LPT;
+  const int32_t L = min(max(__builtin_amdgcn_readfirstlane(a.lens[b]), 0), a.cap);
+  const int64_t bh = static_cast<int64_t>(b) * a.H + h;
+
+  float qv[G::EPL];
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) qv[e] = load_elem(a.q, bh * D + c * G::EPL + e, a.q_f16);
+
+  float m = kFloor, l = 0.f;
+  float acc[G::EPL];
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
+
+  // physical block ids of the next (up to) 64 tiles, one per lane
+  int32_t tbl = 0;
+  auto phys_of = [&](int32_t jj) -> int32_t {
+    if constexpr (PAGED) {
+      if ((jj & 63) == 0) {
+        const int32_t idx = jj + lane;
+        tbl = idx < n ? a.tables[static_cast<int64_t>(b) * a.mbps + j0 + idx] : -1;
+      }
+      return __builtin_amdgcn_readlane(tbl, jj & 63);
+    } else {
+      return 0;
+    }
+  };
+
+  TileRegs<KV, D> ta, tb;
+  fetch_tile<PAGED, KV, D>(a, ta, bh, h, j0, phys_of(0), L, g, c);
+  for (int32_t jj = 0; jj < n; jj += 2) {
+    if (jj + 1 < n) fetch_tile<PAGED, KV, D>(a, tb, bh, h, j0 + jj + 1, phys_of(jj + 1), L, g, c);
+    consume_tile<KV, D>(ta, qv, a.cl2, g, m, l, acc);
+    if (jj + 1 >= n) break;
+    if (jj + 2 < n) fetch_tile<PAGED, KV, D>(a, ta, bh, h, j0 + jj + 2, phys_of(jj + 2), L, g, c);
+    consume_tile<KV, D>(tb, qv, a.cl2, g, m, l, acc);
+  }
+
+  // combine the TPL groups of the wavefront (lanes sharing a column)
+#pragma unroll
+  for (int off = G::LPT; off < kWave; off <<= 1) {
+    const float mo = __shfl_xor(m, off);
+    const float lo = __shfl_xor(l, off);
+    const float M = fmaxf(m, mo);
+    const float fa = __builtin_amdgcn_exp2f(m - M);
+    const float fb = __builtin_amdgcn_exp2f(mo - M);
+    l = l * fa + lo * fb;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], off) * fb;
+    m = M;
+  }
+
+  if (g == 0) {
+    if (!cut_start && !cut_end) {
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e)
+        store_elem(a.out, bh * D + c * G::EPL + e, acc[e] * inv, a.out_f16);
+    } else {
+      const int slot = cut_start ? 0 : 1;
+      float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + slot) * (D + 4);
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) r[c * G::EPL + e] = acc[e];
+      if (c == 0) {
+        r[D] = m;
+        r[D + 1] = l;
+      }
+    }
+  }
+}
+
+template <bool PAGED, int KV, int D>
+__global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
+  extern __shared__ int32_t smem[];
+  int32_t *pre = smem;
+  int32_t *scan = smem + a.B + 1;
+  block_prefix(a.lens, a.B, a.cap, pre, scan);
+
+  const int32_t total = a.H * pre[a.B];
+  const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
+  if (blockIdx.x == 0) {
+    for (int i = threadIdx.x; i <= a.B; i += kWgThreads) a.ws_pre[i] = pre[i];
+    if (threadIdx.x == 0) {
+      a.ws_hdr[0] = a.P;
+      a.ws_hdr[1] = C;
+      a.ws_hdr[2] = total;
+      a.ws_hdr[3] = a.B;
+      a.ws_hdr[4] = a.H;
+      a.ws_hdr[5] = D;
+    }
+  }
+  const int32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWgWaves + (threadIdx.x >> 6));
+  const int64_t f0 = static_cast<int64_t>(w) * C;
+  if (f0 >= total) return;
+  const int32_t f1 = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
+  int32_t f = static_cast<int32_t>(f0);
+
+  // the sequence holding tile f: largest b in [0, B) with H*pre[b] <= f
+  int32_t lo = 0, hi = a.B - 1;
+  while (lo < hi) {
+    const int32_t mid = (lo + hi + 1) >> 1;
+    if (a.H * sread(pre + mid) <= f) lo = mid; else hi = mid - 1;
+  }
+  int32_t b = lo;
+  while (f < f1) {
+    while (a.H * sread(pre + b + 1) <= f) ++b;
+    const int32_t nb = sread(pre + b + 1) - sread(pre + b);
+    const int32_t base = a.H * sread(pre + b);
+    const int32_t rel = f - base;
+    const int32_t h = rel / nb;
+    const int32_t j0 = rel - h * nb;
+    const int32_t seg_end = base + (h + 1) * nb;
+    const int32_t e = min(f1, seg_end);
+    run_segment<PAGED, KV, D>(a, b, h, j0, e - f, w, j0 > 0, e < seg_end);
+    f = e;
+  }
+}
+
+struct MergeArgs {
+  void *out;
+  const int32_t *ws_hdr;
+  const int32_t *ws_pre;
+  const float *ws_rec;
+  int32_t B, H, D, out_f16;
+};
+
+__global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArgs a) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t bh = static_cast<int64_t>(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
+  if (bh >= static_cast<int64_t>(a.B) * a.H) return;
+  const int32_t b = static_cast<int32_t>(bh / a.H);
+  const int32_t h = static_cast<int32_t>(bh % a.H);
+  const int D = a.D;
+  const int32_t C = a.ws_hdr[1];
+  const int32_t pb = a.ws_pre[b];
+  const int32_t nb = a.ws_pre[b + 1] - pb;
+  if (nb == 0) {
+    for (int d = lane; d < D; d += kWave) store_elem(a.out, bh * D + d, 0.f, a.out_f16);
+    return;
+  }
+  if (C < 1 || nb < 0) return;  // no pass-1 record in this workspace
+  const int32_t start = a.H * pb + h * nb;
+  // worker indices are clamped into the record array whatever the workspace holds
+  const int32_t fw = min(max(start / C, 0), kMaxWorkers - 1);
+  const int32_t lw = min(max((start + nb - 1) / C, fw), kMaxWorkers - 1);
+  if (fw == lw) return;  // finished by pass 1
+  const int RS = D + 4;
+  auto rec = [&](int32_t wk) -> const float * {
+    return a.ws_rec + (static_cast<int64_t>(wk) * 2 + (wk == fw ? 1 : 0)) * RS;
+  };
+  float M = kFloor;
+  for (int32_t wk = fw; wk <= lw; ++wk) M = fmaxf(M, rec(wk)[D]);
+  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int32_t wk = fw; wk <= lw; ++wk) {
+    const float *r = rec(wk);
+    const float f = __builtin_amdgcn_exp2f(r[D] - M);
+    lsum += r[D + 1] * f;
+    if (lane < D) o0 += r[lane] * f;
+    if (lane + kWave < D) o1 += r[lane + kWave] * f;
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  if (lane < D) store_elem(a.out, bh * D + lane, o0 * inv, a.out_f16);
+  if (lane + kWave < D) store_elem(a.out, bh * D + lane + kWave, o1 * inv, a.out_f16);
+}
+
+// ---- host side ---------------------------------------------------------------------------
+int device_cu_count() {
+  static std::mutex mu;
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!cache[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
+using PartialKernel = void (*)(DecodeArgs);
+
+template <bool PAGED>
+PartialKernel pick_kernel(kvc_dtype kv, int D) {
+  if (D == 64) {
+    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 64>;
+    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 64>;
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 64>;
+  } else if (D == 128) {
+    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 128>;
+    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 128>;
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 128>;
+  }
+  return nullptr;
+}
+
+struct PartialPlan {
+  DecodeArgs a;
+  PartialKernel kern;
+  int grid;
+  size_t shmem;
+};
+
+// Shared validation and planning for both layouts.
+kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype kv_dtype,
+                        const int32_t *ctx_lens, int32_t B, int32_t H, int32_t D, int32_t cap,
+                        int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                        void *workspace, size_t ws_bytes, PartialPlan &pl) {
+  if (B < 0 || H < 1 || max_ctx < 0 || cap < 0) return KVC_E_INVALID;
+  if (B > kMaxBatch) return KVC_E_INVALID;
+  if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
+  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
+  if (!paged && kv_dtype == KVC_E4M3) return KVC_E_UNSUPPORTED;
+  if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
+  const int64_t tiles_cap = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
+  if (tiles_cap + kMaxWorkers >= INT32_MAX) return KVC_E_INVALID;
+  if (B == 0) {
+    pl.grid = 0;
+    return KVC_OK;
+  }
+  if (!q || !out || !ctx_lens || !workspace) return KVC_E_INVALID;
+  if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return KVC_E_INVALID;
+  const WsLayout wl = ws_layout(B, D);
+  if (ws_bytes < wl.total) return KVC_E_INVALID;
+
+  const int64_t tiles_hint =
+      static_cast<int64_t>(B) * H * ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
+  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * kWavesPerCu);
+  P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
+  P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
+
+  DecodeArgs &a = pl.a;
+  a = DecodeArgs{};
+  a.q = q;
+  a.lens = ctx_lens;
+  a.out = out;
+  char *ws = static_cast<char *>(workspace);
+  a.ws_hdr = reinterpret_cast<int32_t *>(ws);
+  a.ws_pre = reinterpret_cast<int32_t *>(ws + wl.pre_off);
+  a.ws_rec = reinterpret_cast<float *>(ws + wl.rec_off);
+  a.B = B;
+  a.H = H;
+  a.cap = cap;
+  a.P = static_cast<int32_t>(P);
+  a.cmin = kMinChunk;
+  a.q_f16 = q_dtype == KVC_F16;
+  a.out_f16 = out_dtype == KVC_F16;
+  a.cl2 = scale * kLog2e;
+  pl.kern = paged ? pick_kernel<true>(kv_dtype, D) : pick_kernel<false>(kv_dtype, D);
+  if (!pl.kern) return KVC_E_UNSUPPORTED;
+  pl.grid = static_cast<int>(P / kWgWaves);
+  pl.shmem = (static_cast<size_t>(B) + 1 + kWgThreads) * sizeof(int32_t);
+  return KVC_OK;
+}
+
+kvc_status launch_partial(const PartialPlan &pl, void *stream) {
+  if (pl.grid == 0) return KVC_OK;
+  hipLaunchKernelGGL(pl.kern, dim3(pl.grid), dim3(kWgThreads), pl.shmem,
+                     static_cast<hipStream_t>(stream), pl.a);
+  return launch_status();
+}
+
+}  // namespace kvc
+
+using namespace kvc;
+
+extern "C" {
+
+size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D) {
+  (void)H;
+  if (B < 0 || D < 1) return 0;
+  return ws_layout(B, D).total;
+}
+
+kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+                                     const void *v_cache, kvc_dtype kv_dtype,
+                                     const int32_t *ctx_lens, int32_t B, int32_t H, int32_t S_max,
+                                     int32_t D, int32_t max_ctx, float scale, void *out,
+                                     kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                     void *stream) {
+  if (S_max < 0) return KVC_E_INVALID;
+  if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
+  PartialPlan pl;
+  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, D, S_max, max_ctx,
+                               scale, out, out_dtype, workspace, ws_bytes, pl);
+  if (st != KVC_OK || pl.grid == 0) return st;
+  if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
+  pl.a.k = static_cast<const char *>(k_cache);
+  pl.a.v = static_cast<const char *>(v_cache);
+  pl.a.seq_stride = S_max;
+  return launch_partial(pl, stream);
+}
+
+kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
+                                    const kvc_paged_layer *layer, const int32_t *block_tables,
+                                    int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                    int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                    void *workspace, size_t ws_bytes, void *stream) {
+  if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
+    return KVC_E_INVALID;
+  if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
+  const kvc_dtype kv = layer->kv_dtype;
+  if (kv != KVC_F32 && kv != KVC_F16 && kv != KVC_E4M3) return KVC_E_UNSUPPORTED;
+  PartialPlan pl;
+  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads,
+                               layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, scale, out,
+                               out_dtype, workspace, ws_bytes, pl);
+  if (st != KVC_OK || pl.grid == 0) return st;
+  if (!block_tables || !layer->k_pool || !layer->v_pool || !aligned16(layer->k_pool) ||
+      !aligned16(layer->v_pool))
+    return KVC_E_INVALID;
+  if (kv == KVC_E4M3 && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
+  pl.a.k = static_cast<const char *>(layer->k_pool);
+  pl.a.v = static_cast<const char *>(layer->v_pool);
+  pl.a.k_scale = layer->k_scale;
+  pl.a.v_scale = layer->v_scale;
+  pl.a.tables = block_tables;
+  pl.a.mbps = max_blocks_per_seq;
+  pl.a.num_blocks = layer->num_blocks;
+  return launch_partial(pl, stream);
+}
+
+kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
+                            void *workspace, size_t ws_bytes, void *stream) {
+  if (B < 0 || H < 1 || B > kMaxBatch) return KVC_E_INVALID;
+  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
+  if (!is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
+  if (B == 0) return KVC_OK;
+  if (!out || !workspace || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return KVC_E_INVALID;
+  const WsLayout wl = ws_layout(B, D);
+  if (ws_bytes < wl.total) return KVC_E_INVALID;
+  MergeArgs a;
+  char *ws = static_cast<char *>(workspace);
+  a.out = out;
+  a.ws_hdr = reinterpret_cast<const int32_t *>(ws);
+  a.ws_pre = reinterpret_cast<const int32_t *>(ws + wl.pre_off);
+  a.ws_rec = reinterpret_cast<const float *>(ws + wl.rec_off);
+  a.B = B;
+  a.H = H;
+  a.D = D;
+  a.out_f16 = out_dtype == KVC_F16;
+  const int64_t pairs = static_cast<int64_t>(B) * H;
+  const int grid = static_cast<int>((pairs + kWgWaves - 1) / kWgWaves);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(grid), dim3(kWgThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
+kvc_status kvc_decode_attn_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+                                  const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                  int32_t B, int32_t H, int32_t S_max, int32_t D, int32_t max_ctx,
+                                  float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                  size_t ws_bytes, void *stream) {
+  kvc_status st = kvc_decode_partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, B,
+                                            H, S_max, D, max_ctx, scale, out, out_dtype,
+                                            workspace, ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_merge(B, H, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
+                                 const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                 const int32_t *ctx_lens, int32_t B, int32_t max_ctx, float scale,
+                                 void *out, kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream) {
+  kvc_status st = kvc_decode_partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq,
+                                           ctx_lens, B, max_ctx, scale, out, out_dtype, workspace,
+                                           ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
+                          ws_bytes, stream);
+}
+
+}  // extern "C"

@@ -56,8 +56,9 @@ class PagedCache:
     def __init__(self, num_blocks: int, H: int, D: int, dtype: str, fill=0.0):
         self.N, self.H, self.D, self.dtype = num_blocks, H, D, dtype
         if dtype == "e4m3":
-            self.K = np.zeros((num_blocks, H, BS, D), dtype=np.uint8)
-            self.V = np.zeros((num_blocks, H, BS, D), dtype=np.uint8)
+            code = 0x7F if (fill is not None and np.isnan(fill)) else 0   # NaN code poisons
+            self.K = np.full((num_blocks, H, BS, D), code, dtype=np.uint8)
+            self.V = np.full((num_blocks, H, BS, D), code, dtype=np.uint8)
             self.k_scale = np.zeros(num_blocks, dtype=np.float32)
             self.v_scale = np.zeros(num_blocks, dtype=np.float32)
         else:
