@@ -1,0 +1,334 @@
+"""Benchmark: decode attention over a paged (or contiguous) KV cache on one MI355X.
+
+One step = one decode step of the whole batch through every layer: host slot reservation
+(first fit / copy-on-write), block-table and length upload, then per layer the copy-on-write
+block copies, the new token's K/V write, decode attention pass 1 (split-context online
+softmax) and pass 2 (merge of split sequence-heads). Inputs are
+synthetic and already resident in device memory when timing starts; each step grows every
+sequence by one token.
+
+Prints one JSON line. `value` is the HBM throughput of the whole step in GB/s, counting the
+algorithmic bytes only (every cached K/V byte read once, block-table entries, q, out, the new
+K/V written). `roofline` is for the dominant kernel (attention pass 1), timed with HIP events
+recorded on the stream it is launched on. `cpu_baseline` is the CPU oracle timed on one layer.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+METRIC = "paged decode-attention HBM GB/s (% of peak) and decode tokens/s, 1 MI355X"
+PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+ELT = {"f32": 4, "f16": 2, "e4m3": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="llama13b-paged",
+                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig"])
+    ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after timing, run a plain 1 GiB device copy (torch) 3 times; its "
+                         "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
+    return ap.parse_args()
+
+
+class PagedBench:
+    """Paged workloads: LLaMA-13B shapes with drawn lengths, or fp8 long context."""
+
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev):
+        import torch
+
+        import kv_cache_attention_kvc_amd as kvc
+
+        self.kvc, self.torch, self.w, self.dev = kvc, torch, w, dev
+        self.L = layers
+        B, H, D = w.batch, w.heads, w.head_dim
+        self.B, self.H, self.D = B, H, D
+        if w.ctx:
+            lens = np.full(B, w.ctx, dtype=np.int64)
+        else:
+            lens = workloads.llama13b_lengths(w)
+        self.first_lens = lens                        # attended length at the first step
+        grow = steps + 1
+        nblk = int(sum(workloads.blocks_for(L + grow) for L in lens)) + B
+        self.mbps = workloads.blocks_for(int(lens.max()) + grow)
+        order = workloads.llama13b_pool_order(nblk, w.seed)
+        self.pool = kvc.Pool(nblk, self.mbps, order=order)
+        self.seqs = [self.pool.alloc() for _ in range(B)]
+        src = "f16"
+        self.layers = [kvc.PagedLayer.empty(nblk, H, D, w.kv_dtype, device=dev, fill=0.0)
+                       for _ in range(layers)]
+        # prefill: every sequence holds L_b - 1 tokens, written per layer in one call
+        slots = np.concatenate([self.pool.append([s], int(L) - 1)[0]
+                                for s, L in zip(self.seqs, lens)])
+        slots_d = torch.from_numpy(slots).to(dev)
+        for li, layer in enumerate(self.layers):
+            k = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li)
+            v = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li + 1)
+            kvc.write_paged(layer, slots_d, k, v)
+            del k, v
+        torch.cuda.synchronize()
+        # per-step inputs, resident in device memory: new K/V and q for every layer
+        self.knew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 1)
+        self.vnew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 2)
+        self.q = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 3)
+        self.out = torch.empty((layers, B, H, D), dtype=torch.float16, device=dev)
+        self.ws = kvc.new_workspace(B, H, D, device=dev)
+        # pinned host staging, a ring of buffers: a buffer is refilled only after the copy that
+        # last read it has executed (the host may run several steps ahead of the GPU)
+        self.ring = [(torch.empty((B, self.mbps), dtype=torch.int32, pin_memory=True),
+                      torch.empty(B, dtype=torch.int32, pin_memory=True),
+                      torch.empty(B, dtype=torch.int64, pin_memory=True),
+                      torch.cuda.Event()) for _ in range(4)]
+        self.ring_i = 0
+        self.tab_d = torch.empty((B, self.mbps), dtype=torch.int32, device=dev)
+        self.len_d = torch.empty(B, dtype=torch.int32, device=dev)
+        self.slot_d = torch.empty(B, dtype=torch.int64, device=dev)
+        self.cow_d = torch.empty((2, B), dtype=torch.int32, device=dev)
+        self.max_ctx = int(lens.max()) + grow
+        self.scale = float(np.float32(1.0 / math.sqrt(D)))
+        self.stream = torch.cuda.current_stream()
+        self.lens_now = lens.copy() - 1
+
+    def step(self, ev=None):
+        kvc, torch = self.kvc, self.torch
+        slots, src, dst = self.pool.append(self.seqs, 1)
+        tab_h, len_h, slot_h, done = self.ring[self.ring_i]
+        self.ring_i = (self.ring_i + 1) % len(self.ring)
+        done.synchronize()
+        self.pool.block_table(self.seqs, out_tables=tab_h.numpy(), out_lens=len_h.numpy())
+        slot_h.numpy()[:] = slots
+        self.tab_d.copy_(tab_h, non_blocking=True)
+        self.len_d.copy_(len_h, non_blocking=True)
+        self.slot_d.copy_(slot_h, non_blocking=True)
+        done.record(self.stream)
+        ncow = len(src)
+        if ncow:
+            self.cow_d[0, :ncow].copy_(torch.from_numpy(src))
+            self.cow_d[1, :ncow].copy_(torch.from_numpy(dst))
+        self.lens_now += 1
+        for li, layer in enumerate(self.layers):
+            if ncow:
+                kvc.copy_blocks(layer, self.cow_d[0, :ncow], self.cow_d[1, :ncow])
+            kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li, self.stream)
+            kvc.decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d, self.max_ctx,
+                                     scale=self.scale, out=self.out[li], workspace=self.ws)
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li + 1, self.stream)
+            kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
+
+    def bytes_step(self, lens):
+        """Algorithmic HBM bytes of one step over all layers, and of one pass-1 launch."""
+        elt = ELT[self.w.kv_dtype]
+        B, H, D = self.B, self.H, self.D
+        kv = int(lens.sum()) * H * D * 2 * elt
+        blocks = int(sum(workloads.blocks_for(L) for L in lens))
+        table = blocks * 4 + (blocks * 8 if self.w.kv_dtype == "e4m3" else 0) + B * 4
+        qo = B * H * D * (2 + 2)
+        append = B * H * D * 2 * elt + (B * 8 if self.w.kv_dtype == "e4m3" else 0)
+        pass1 = kv + table + qo
+        return (pass1 + append) * self.L, pass1
+
+    def oracle_layer(self, li):
+        """The CPU oracle's decode of one layer on the current state (for cpu_baseline and a
+        parity spot check): returns (seconds, output [B,H,D], bytes read)."""
+        from oracle.caches import PagedCache
+
+        layer = self.layers[li]
+        tables, lens = self.pool.block_table(self.seqs)
+        ref = PagedCache(layer.num_blocks, self.H, self.D, self.w.kv_dtype)
+        ref.K = layer.k_pool.cpu().numpy()
+        ref.V = layer.v_pool.cpu().numpy()
+        if self.w.kv_dtype == "e4m3":
+            ref.k_scale = layer.k_scale.cpu().numpy()
+            ref.v_scale = layer.v_scale.cpu().numpy()
+        q = self.q[li].float().cpu().numpy()
+        t0 = time.perf_counter()
+        out = ref.decode(q, tables, lens, self.scale)
+        dt = time.perf_counter() - t0
+        return dt, out, int(lens.sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
+
+
+class HipEvents:
+    """HIP timing events recorded on a stream, created with hipEventDisableSystemFence: a timing
+    event then skips the system-scope cache write-back and invalidate that default events do,
+    which would otherwise be timed too and would slow the kernels that follow."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n: int):
+        import ctypes
+
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            rc = self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE)
+            if rc != 0:
+                raise RuntimeError(f"hipEventCreateWithFlags failed: {rc}")
+            self.ev.append(e)
+
+    def record(self, i: int, stream) -> None:
+        rc = self.hip.hipEventRecord(self.ev[i], self.ct.c_void_p(stream.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed: {rc}")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = self.ct.c_float()
+        rc = self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j])
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {rc}")
+        return ms.value
+
+    def close(self) -> None:
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+        return max(n) if n else 1
+    except Exception:
+        return 1
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs "
+              "on a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = {"llama13b-paged": workloads.LLAMA13B_PAGED,
+         "fp8-longctx": workloads.LONGCTX_FP8}.get(args.workload)
+    if w is None:
+        print("workload not implemented in bench.py yet", file=sys.stderr)
+        sys.exit(2)
+    layers = args.layers or w.layers
+    K, W = args.steps, args.warmup
+    print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
+          file=sys.stderr, flush=True)
+    bench = PagedBench(w, K + W, layers, dev)
+    for _ in range(W):
+        bench.step()
+    torch.cuda.synchronize()
+    print("[bench] warm-up done", file=sys.stderr, flush=True)
+
+    evs = HipEvents(2 * layers * K)
+    total_bytes = 0
+    pass1_bytes = []
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        bench.step((evs, 2 * layers * s))
+        b_all, b_p1 = bench.bytes_step(bench.lens_now)
+        total_bytes += b_all
+        pass1_bytes.append(b_p1)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    elapsed = t1 - t0
+    p1_ms = np.array([[evs.elapsed_ms(2 * (layers * s + li), 2 * (layers * s + li) + 1)
+                       for li in range(layers)] for s in range(K)])  # [K, L]
+    evs.close()
+    p1_avg_s = float(p1_ms.mean()) / 1e3
+    p1_bytes_avg = float(np.mean(pass1_bytes))
+    achieved = p1_bytes_avg / p1_avg_s / 1e9
+    value = total_bytes / elapsed / 1e9
+    print(f"[bench] timed: {elapsed * 1e3 / K:.3f} ms/step, pass 1 {p1_avg_s * 1e6:.1f} us/launch",
+          file=sys.stderr, flush=True)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": W,
+        "ms_per_step": round(elapsed * 1e3 / K, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.kv_dtype,
+        "data": "synthetic: N(0,1) K/V/q, seeded; lengths and pool order seeded",
+        "config": {
+            "workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+            "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
+            "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
+            if not w.ctx else w.ctx,
+            "ctx_growth_per_step": 1,
+        },
+        "pct_of_peak": round(100 * value / PEAK_GBS, 2),
+        "tokens_per_s": round(w.batch * K / elapsed, 1),
+        "roofline": {
+            "kernel": "kvc::decode_partial_kernel<paged, f16, 128> (attention pass 1)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": None,
+            "avg_launch_us": round(p1_avg_s * 1e6, 2),
+            "algorithmic_bytes_per_launch": int(p1_bytes_avg),
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle on one layer", file=sys.stderr, flush=True)
+        dt, ref, nbytes = bench.oracle_layer(0)
+        got = bench.out[0].float().cpu().numpy()
+        line["cpu_baseline"] = {
+            "value": round(nbytes / dt / 1e9, 4),
+            "unit": "GB/s",
+            "cores": blas_threads(),
+            "kind": "oracle",
+            "sample": f"layer 0 of the last step: all {w.batch} sequences x {w.heads} heads, "
+                      f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
+                      f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers",
+        }
+        line["parity_layer0_max_abs_err"] = float(np.abs(got - ref).max())
+    if args.copy_calibration:
+        a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        line["copy_calibration_bytes"] = 1 << 30
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -196,25 +196,26 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
 /* ==================================================================================== *
  * Device side: decode attention.
  *
- * Pass 1 splits the work of all (sequence, head) pairs -- H * sum_b ceil(L_b/16) blocks of 16
+ * Pass 1 cuts the work of all (sequence, head) pairs -- H * sum_b ceil(L_b/16) tiles of 16
  * positions -- into equal contiguous chunks, one per wavefront of a grid sized to the GPU. Each
  * wavefront runs an online softmax (running max and running sum) over its chunk and either
  * writes the finished output row (when it saw the whole sequence-head) or a partial state
- * (max, sum, unnormalised output) to the workspace. Pass 2 combines the partial states of
- * every sequence-head that was split. Accumulation is fp32; scores are never rounded below
- * fp32 ("LLM Inference Acceleration -- KV Cache", section 3.1 takes the softmax in float).
+ * (max, sum, unnormalised output) to the workspace. Pass 2 combines the partial states of every
+ * sequence-head that was split and zeroes the rows of empty sequences. Accumulation is fp32;
+ * scores are never rounded below fp32 ("LLM Inference Acceleration -- KV Cache", section 3.1
+ * takes the softmax in float).
  *
  * Common arguments
  *   q:        [B][H][D] of q_dtype (KVC_F32 or KVC_F16)
  *   ctx_lens: device int32[B], L_b = positions attended by sequence b (its new token included);
  *             clamped to [0, capacity]; L_b = 0 gives a zero output row
  *   max_ctx:  host upper bound of every L_b (sizes the grid; need not be tight)
- *   scale:    multiplies q.k (normally 1/sqrt(D))
+ *   scale:    multiplies q.k (normally 1/sqrt(D)); finite
  *   out:      [B][H][D] of out_dtype (KVC_F32 or KVC_F16), rounded to nearest even
  *   workspace: device buffer of at least kvc_decode_workspace_bytes(B, H, D) bytes, 256-byte
- *             aligned, owned by the caller; its contents need no initialisation and are
- *             overwritten. Calls that overlap in time must use different workspaces.
- * Supported: D in {64, 128}; kv dtype f32/f16 (contiguous) and f32/f16/e4m3 (paged).
+ *             aligned, owned by the caller; no initialisation needed, contents overwritten.
+ *             Calls that may overlap in time need different workspaces.
+ * Supported: D in {64, 128}; B <= 4096; kv dtype f32/f16 (contiguous) and f32/f16/e4m3 (paged).
  * ==================================================================================== */
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D);
 

@@ -19,7 +19,7 @@ __all__ = [
     "KvcError", "load_library", "library_path", "Pool", "PagedLayer",
     "F32", "F16", "E4M3", "BLOCK_SIZE", "workspace_bytes",
     "append_contig", "copy_blocks", "write_paged", "decode_attn_contig", "decode_attn_paged",
-    "decode_partial_contig", "decode_partial_paged", "decode_merge", "EXPORTS",
+    "decode_partial_contig", "decode_partial_paged", "decode_merge", "new_workspace", "EXPORTS",
 ]
 
 F32, F16, E4M3 = 0, 1, 2
@@ -102,12 +102,12 @@ def load_library() -> ctypes.CDLL:
         "kvc_decode_attn_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P,
                                                   ctypes.c_size_t, _P]),
-        "kvc_decode_partial_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
-                                                     _I32, _I32, _I32, _I32, _I32, _F, _P,
-                                                     ctypes.c_int, _P, ctypes.c_size_t, _P]),
         "kvc_decode_attn_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P, _I32,
                                                  _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
                                                  ctypes.c_size_t, _P]),
+        "kvc_decode_partial_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
+                                                     _I32, _I32, _I32, _I32, _I32, _F, _P,
+                                                     ctypes.c_int, _P, ctypes.c_size_t, _P]),
         "kvc_decode_partial_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P,
                                                     _I32, _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
                                                     ctypes.c_size_t, _P]),
@@ -287,6 +287,12 @@ class PagedLayer:
         return self.k_pool.shape[3]
 
     def struct(self) -> _Layer:
+        key = (self.k_pool.data_ptr(), self.v_pool.data_ptr(),
+               None if self.k_scale is None else self.k_scale.data_ptr(),
+               None if self.v_scale is None else self.v_scale.data_ptr(), tuple(self.k_pool.shape))
+        cached = getattr(self, "_cached", None)
+        if cached is not None and cached[0] == key:
+            return cached[1]
         if tuple(self.k_pool.shape) != tuple(self.v_pool.shape) or self.k_pool.dim() != 4 \
                 or self.k_pool.shape[2] != BLOCK_SIZE:
             raise ValueError("pools must be [num_blocks, H, 16, D] and alike")
@@ -296,6 +302,7 @@ class PagedLayer:
         if code == E4M3:
             s.k_scale = _ptr(self.k_scale)
             s.v_scale = _ptr(self.v_scale)
+        self._cached = (key, s)
         return s
 
 
@@ -303,14 +310,14 @@ def workspace_bytes(B: int, H: int, D: int) -> int:
     return int(_lib().kvc_decode_workspace_bytes(B, H, D))
 
 
-def _workspace(B, H, D, ws, device):
+def new_workspace(B: int, H: int, D: int, device="cuda"):
+    """A decode workspace for batches of up to B sequences (no initialisation needed)."""
     torch = _torch()
-    need = workspace_bytes(B, H, D)
-    if ws is None:
-        ws = torch.empty(need, dtype=torch.uint8, device=device)
-    if ws.numel() * ws.element_size() < need:
-        raise ValueError(f"workspace too small: {ws.numel()} < {need}")
-    return ws
+    return torch.empty(workspace_bytes(B, H, D), dtype=torch.uint8, device=device)
+
+
+def _workspace(B, H, D, ws, device):
+    return new_workspace(B, H, D, device) if ws is None else ws   # libkvc checks the size
 
 
 def append_contig(k_cache, v_cache, pos, k_new, v_new, stream=None) -> None:
@@ -351,8 +358,12 @@ def _out_for(q, out):
     return torch.empty_like(q) if out is None else out
 
 
+
+
+
 def decode_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
                           workspace=None, stream=None):
+    """Pass 1 only (see decode_attn_contig); returns (out, workspace) for decode_merge."""
     B, H, S, D = k_cache.shape
     out = _out_for(q, out)
     ws = _workspace(B, H, D, workspace, q.device)
@@ -366,6 +377,7 @@ def decode_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, ou
 
 def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
                          out=None, workspace=None, stream=None):
+    """Pass 1 only (see decode_attn_paged); returns (out, workspace) for decode_merge."""
     B = q.shape[0]
     out = _out_for(q, out)
     ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
@@ -379,6 +391,7 @@ def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, 
 
 
 def decode_merge(B, H, D, out, workspace, stream=None):
+    """Pass 2: combine the split sequence-heads that pass 1 left in `workspace`."""
     _check(_lib().kvc_decode_merge(B, H, D, _ptr(out), _dtype_code(out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "kvc_decode_merge")
     return out

@@ -11,7 +11,8 @@
 // contiguous chunks, one per wavefront, so every wavefront streams the same number of bytes
 // whatever the length mix. A wavefront walks its chunk tile by tile with the next tile's loads
 // in flight while it computes on the current one:
-//   * a token row (D elements) is read by LPT lanes with 16-byte loads, so one wave-wide load
+//   * a token row (D elements) is read by LPT lanes with 16-byte non-temporal loads (the K/V
+//     stream is read once, so it is kept from displacing reusable lines), and one wave-wide load
 //     covers TPL = 64/LPT consecutive rows (1 KiB contiguous); a tile takes LOADS such loads;
 //   * each lane forms partial dot products over its 16 bytes of k; a butterfly of DPP adds
 //     inside each LPT-lane group gives every lane of the group the full score;
@@ -20,10 +21,13 @@
 //     traffic; the groups are combined once per (sequence, head) segment.
 // Scores are kept in log2 units (multiplied by scale*log2(e)) and exponentials use v_exp_f32.
 // A segment that covers a whole (sequence, head) is finished in place; a segment cut by a
-// chunk boundary leaves (m, l, o[D]) in one of the wavefront's two workspace records.
+// chunk boundary leaves (o[D], m, l) in one of the wavefront's two workspace records.
 //
-// Pass 2 (decode_merge_kernel) combines, for every (sequence, head) that was cut, the records
-// of the consecutive wavefronts that covered it, and writes zeros for empty sequences.
+// Pass 2 (decode_merge_kernel). One wavefront per (sequence, head): pairs that were cut combine
+// the records of the consecutive wavefronts that covered them, rescaling each by exp2 of its
+// max minus the overall max; rows of empty sequences are zeroed; other pairs were finished in
+// pass 1. Pass 1 leaves the chunk size and the per-sequence block prefix in the workspace, so
+// pass 2 needs no other input. Stream order makes pass 1's stores visible to pass 2.
 #include <mutex>
 
 #include "kvc_internal.h"
@@ -32,22 +36,25 @@ namespace kvc {
 
 constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
-constexpr int kMaxWorkers = 8192;  // wavefronts of pass 1 at most (records in a workspace)
+constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
-constexpr int kWavesPerCu = 16;    // pass-1 wavefronts per compute unit
+constexpr int kWavesPerCu = 8;     // pass-1 wavefronts per compute unit
 constexpr int kMaxBatch = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' never is NaN)
+constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' is never NaN)
 
+// Workspace: [header int32[64] | prefix int32[B+1] | records float[kMaxWorkers][2][D+4]], each
+// region 256-byte aligned. Header: chunk size C, and B, H, D of the pass-1 call.
 struct WsLayout {
   size_t pre_off, rec_off, total;
 };
 
+inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+
 inline WsLayout ws_layout(int B, int D) {
   WsLayout l;
   l.pre_off = 256;
-  const size_t pre_bytes = ((static_cast<size_t>(B) + 1) * 4 + 255) & ~static_cast<size_t>(255);
-  l.rec_off = l.pre_off + pre_bytes;
+  l.rec_off = l.pre_off + align256((static_cast<size_t>(B) + 1) * sizeof(int32_t));
   l.total = l.rec_off + static_cast<size_t>(kMaxWorkers) * 2 * (D + 4) * sizeof(float);
   return l;
 }
@@ -82,14 +89,22 @@ template <int N>
 __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0xB1>(x);  // quad_perm [1,0,3,2]: lane ^ 1
   x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]: lane ^ 2
-  if constexpr (N >= 8) x += dpp<0x141>(x);  // row_half_mirror: the other quad of 8
-  if constexpr (N >= 16) x += dpp<0x140>(x); // row_mirror: the other half of 16
+  if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror: the other quad of 8
+  if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other half of 16
   if constexpr (N >= 32) x += __shfl_xor(x, 16);
   return x;
 }
 
 __device__ __forceinline__ int32_t sread(const int32_t *p) {
   return __builtin_amdgcn_readfirstlane(*p);
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (non-temporal hint).
+__device__ __forceinline__ uint4 load_stream(const char *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Unpack the 16 bytes a lane loaded into EPL floats.
@@ -105,9 +120,11 @@ __device__ __forceinline__ void unpack(const uint4 &r, float *f) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i])));
-      f[2 * i + 1] = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
+      f[2 * i + 1] =
+          static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
     }
   } else {
+    // gfx950 converts OCP e4m3 in hardware (exact: every code is an fp32 value)
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -134,9 +151,13 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float x, bool f16
 }
 
 // ---- per-workgroup prefix of block counts ------------------------------------------------
-// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences.
-__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *scan) {
+// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences. Each thread
+// sums a run of consecutive sequences; runs are scanned with wave shuffles, then across the
+// four waves through LDS.
+__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *wsum) {
   const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = tid >> 6;
   const int per = (B + kWgThreads - 1) / kWgThreads;
   const int lo = min(B, tid * per);
   const int hi = min(B, lo + per);
@@ -145,21 +166,22 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
     const int32_t L = min(max(lens[i], 0), cap);
     sum += (L + kBlock - 1) / kBlock;
   }
-  scan[tid] = sum;
-  __syncthreads();
-  for (int off = 1; off < kWgThreads; off <<= 1) {
-    const int32_t add = tid >= off ? scan[tid - off] : 0;
-    __syncthreads();
-    scan[tid] += add;
-    __syncthreads();
+  int32_t inc = sum;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int32_t v = __shfl_up(inc, off);
+    if (lane >= off) inc += v;
   }
-  int32_t run = scan[tid] - sum;
+  if (lane == kWave - 1) wsum[wave] = inc;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) inc += wsum[w];
+  int32_t run = inc - sum;
   for (int i = lo; i < hi; ++i) {
     pre[i] = run;
     const int32_t L = min(max(lens[i], 0), cap);
     run += (L + kBlock - 1) / kBlock;
   }
-  if (tid == kWgThreads - 1) pre[B] = scan[tid];
+  if (tid == kWgThreads - 1) pre[B] = inc;
   __syncthreads();
 }
 
@@ -169,14 +191,14 @@ struct TileRegs {
   using G = Geo<KV, D>;
   uint4 k[G::LOADS];
   uint4 v[G::LOADS];
-  int32_t nt;      // valid rows (0 when the block id is out of range)
-  float ks, vs;    // fp8 block scales
+  int32_t nt;    // valid rows (0 when the block id is out of range)
+  float ks, vs;  // fp8 block scales
 };
 
 template <bool PAGED, int KV, int D>
 __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D> &t, int64_t bh,
-                                           int32_t h, int32_t j, int32_t phys, int32_t L,
-                                           int g, int c) {
+                                           int32_t h, int32_t j, int32_t phys, int32_t L, int g,
+                                           int c) {
   using G = Geo<KV, D>;
   const char *kt;
   const char *vt;
@@ -202,15 +224,15 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D> 
   if (t.nt == kBlock) {
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
-      t.k[i] = *reinterpret_cast<const uint4 *>(kt + lane_off + i * G::TPL * G::ROW);
-      t.v[i] = *reinterpret_cast<const uint4 *>(vt + lane_off + i * G::TPL * G::ROW);
+      t.k[i] = load_stream(kt + lane_off + i * G::TPL * G::ROW);
+      t.v[i] = load_stream(vt + lane_off + i * G::TPL * G::ROW);
     }
   } else {
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       if (g + i * G::TPL < t.nt) {
-        t.k[i] = *reinterpret_cast<const uint4 *>(kt + lane_off + i * G::TPL * G::ROW);
-        t.v[i] = *reinterpret_cast<const uint4 *>(vt + lane_off + i * G::TPL * G::ROW);
+        t.k[i] = load_stream(kt + lane_off + i * G::TPL * G::ROW);
+        t.v[i] = load_stream(vt + lane_off + i * G::TPL * G::ROW);
       } else {
         t.k[i] = make_uint4(0, 0, 0, 0);
         t.v[i] = make_uint4(0, 0, 0, 0);
@@ -319,23 +341,21 @@ __device__ __forceinline__ void run_segment(const DecodeArgs &a, int32_t b, int3
     for (int e = 0; e < G::EPL; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], off) * fb;
     m = M;
   }
-
-  if (g == 0) {
-    if (!cut_start && !cut_end) {
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
+  if (g != 0) return;
+  if (!cut_start && !cut_end) {
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
 #pragma unroll
-      for (int e = 0; e < G::EPL; ++e)
-        store_elem(a.out, bh * D + c * G::EPL + e, acc[e] * inv, a.out_f16);
-    } else {
-      const int slot = cut_start ? 0 : 1;
-      float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + slot) * (D + 4);
+    for (int e = 0; e < G::EPL; ++e)
+      store_elem(a.out, bh * D + c * G::EPL + e, acc[e] * inv, a.out_f16);
+    return;
+  }
+  // a cut segment: slot 0 if it began before this chunk, else slot 1
+  float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + (cut_start ? 0 : 1)) * (D + 4);
 #pragma unroll
-      for (int e = 0; e < G::EPL; ++e) r[c * G::EPL + e] = acc[e];
-      if (c == 0) {
-        r[D] = m;
-        r[D + 1] = l;
-      }
-    }
+  for (int e = 0; e < G::EPL; ++e) r[c * G::EPL + e] = acc[e];
+  if (c == 0) {
+    r[D] = m;
+    r[D + 1] = l;
   }
 }
 
@@ -343,20 +363,18 @@ template <bool PAGED, int KV, int D>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t *pre = smem;
-  int32_t *scan = smem + a.B + 1;
-  block_prefix(a.lens, a.B, a.cap, pre, scan);
+  int32_t *wsum = smem + a.B + 1;
+  block_prefix(a.lens, a.B, a.cap, pre, wsum);
 
   const int32_t total = a.H * pre[a.B];
   const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= a.B; i += kWgThreads) a.ws_pre[i] = pre[i];
     if (threadIdx.x == 0) {
-      a.ws_hdr[0] = a.P;
-      a.ws_hdr[1] = C;
-      a.ws_hdr[2] = total;
-      a.ws_hdr[3] = a.B;
-      a.ws_hdr[4] = a.H;
-      a.ws_hdr[5] = D;
+      a.ws_hdr[0] = C;
+      a.ws_hdr[1] = a.B;
+      a.ws_hdr[2] = a.H;
+      a.ws_hdr[3] = D;
     }
   }
   const int32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWgWaves + (threadIdx.x >> 6));
@@ -386,6 +404,7 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   }
 }
 
+// ---- pass 2 ------------------------------------------------------------------------------
 struct MergeArgs {
   void *out;
   const int32_t *ws_hdr;
@@ -394,6 +413,8 @@ struct MergeArgs {
   int32_t B, H, D, out_f16;
 };
 
+constexpr int kMaxParts = 16;  // parts whose loads are in flight together
+
 __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
@@ -401,7 +422,7 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
   const int32_t b = static_cast<int32_t>(bh / a.H);
   const int32_t h = static_cast<int32_t>(bh % a.H);
   const int D = a.D;
-  const int32_t C = a.ws_hdr[1];
+  const int32_t C = a.ws_hdr[0];
   const int32_t pb = a.ws_pre[b];
   const int32_t nb = a.ws_pre[b + 1] - pb;
   if (nb == 0) {
@@ -415,22 +436,46 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
   const int32_t lw = min(max((start + nb - 1) / C, fw), kMaxWorkers - 1);
   if (fw == lw) return;  // finished by pass 1
   const int RS = D + 4;
-  auto rec = [&](int32_t wk) -> const float * {
-    return a.ws_rec + (static_cast<int64_t>(wk) * 2 + (wk == fw ? 1 : 0)) * RS;
+  const int32_t nparts = lw - fw + 1;
+  auto rec = [&](int32_t i) -> const float * {  // part i of the pair: the first is in slot 1
+    return a.ws_rec + (static_cast<int64_t>(fw + i) * 2 + (i == 0 ? 1 : 0)) * RS;
   };
-  float M = kFloor;
-  for (int32_t wk = fw; wk <= lw; ++wk) M = fmaxf(M, rec(wk)[D]);
-  float lsum = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int32_t wk = fw; wk <= lw; ++wk) {
-    const float *r = rec(wk);
-    const float f = __builtin_amdgcn_exp2f(r[D] - M);
-    lsum += r[D + 1] * f;
-    if (lane < D) o0 += r[lane] * f;
-    if (lane + kWave < D) o1 += r[lane + kWave] * f;
+  // the loads of up to kMaxParts parts are issued before any is used
+  float M = kFloor, lsum = 0.f, o0 = 0.f, o1 = 0.f;
+  for (int32_t i0 = 0; i0 < nparts; i0 += kMaxParts) {
+    const int32_t n = min(nparts - i0, kMaxParts);
+    float mi[kMaxParts], li[kMaxParts], x0[kMaxParts], x1[kMaxParts];
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) {
+      mi[k] = kFloor;
+      li[k] = x0[k] = x1[k] = 0.f;
+      if (k < n) {
+        const float *r = rec(i0 + k);
+        mi[k] = r[D];
+        li[k] = r[D + 1];
+        x0[k] = r[lane];
+        if (D > kWave) x1[k] = r[lane + kWave];
+      }
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) Mn = fmaxf(Mn, mi[k]);
+    const float fo = __builtin_amdgcn_exp2f(M - Mn);
+    lsum *= fo;
+    o0 *= fo;
+    o1 *= fo;
+#pragma unroll
+    for (int k = 0; k < kMaxParts; ++k) {
+      const float f = k < n ? __builtin_amdgcn_exp2f(mi[k] - Mn) : 0.f;
+      lsum += li[k] * f;
+      o0 += x0[k] * f;
+      o1 += x1[k] * f;
+    }
+    M = Mn;
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  if (lane < D) store_elem(a.out, bh * D + lane, o0 * inv, a.out_f16);
-  if (lane + kWave < D) store_elem(a.out, bh * D + lane + kWave, o1 * inv, a.out_f16);
+  store_elem(a.out, bh * D + lane, o0 * inv, a.out_f16);
+  if (D > kWave) store_elem(a.out, bh * D + lane + kWave, o1 * inv, a.out_f16);
 }
 
 // ---- host side ---------------------------------------------------------------------------
@@ -442,7 +487,8 @@ int device_cu_count() {
   std::lock_guard<std::mutex> lock(mu);
   if (!cache[dev]) {
     int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
       n = 256;
     cache[dev] = n;
   }
@@ -483,7 +529,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
   if (!paged && kv_dtype == KVC_E4M3) return KVC_E_UNSUPPORTED;
   if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
-  const int64_t tiles_cap = static_cast<int64_t>(B) * H * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
+  const int64_t tiles_cap =
+      static_cast<int64_t>(B) * H * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
   if (tiles_cap + kMaxWorkers >= INT32_MAX) return KVC_E_INVALID;
   if (B == 0) {
     pl.grid = 0;
@@ -495,9 +542,10 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   const WsLayout wl = ws_layout(B, D);
   if (ws_bytes < wl.total) return KVC_E_INVALID;
 
-  const int64_t tiles_hint =
-      static_cast<int64_t>(B) * H * ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
-  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * kWavesPerCu);
+  const int64_t tiles_hint = static_cast<int64_t>(B) * H *
+                             ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
+  int64_t P = std::min<int64_t>(kMaxWorkers,
+                                static_cast<int64_t>(device_cu_count()) * kWavesPerCu);
   P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
   P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
 
@@ -521,7 +569,7 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   pl.kern = paged ? pick_kernel<true>(kv_dtype, D) : pick_kernel<false>(kv_dtype, D);
   if (!pl.kern) return KVC_E_UNSUPPORTED;
   pl.grid = static_cast<int>(P / kWgWaves);
-  pl.shmem = (static_cast<size_t>(B) + 1 + kWgThreads) * sizeof(int32_t);
+  pl.shmem = (static_cast<size_t>(B) + 1 + kWgWaves) * sizeof(int32_t);
   return KVC_OK;
 }
 
@@ -539,8 +587,7 @@ using namespace kvc;
 extern "C" {
 
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D) {
-  (void)H;
-  if (B < 0 || D < 1) return 0;
+  if (B < 0 || H < 1 || D < 1) return 0;
   return ws_layout(B, D).total;
 }
 

@@ -43,3 +43,11 @@ def max_err(got, want) -> float:
     assert got.shape == want.shape
     assert np.isfinite(got).all(), "non-finite output"
     return float(np.abs(got - want).max()) if got.size else 0.0
+
+
+def check(got, want, tol: float, what: str = "") -> float:
+    """Max-abs error of got vs want, asserted <= tol with a short message."""
+    err = max_err(got, want)
+    if not err <= tol:
+        raise AssertionError(f"{what}: max-abs error {err:.3e} > {tol:.1e}")
+    return err

@@ -13,7 +13,7 @@ from oracle.attention import cached_decode, decode_row
 from oracle.caches import ContigCache, PagedCache
 from oracle.codecs import e4m3_decode_table
 from oracle.pool import PoolModel
-from tests.gpu_util import TD, TOL, dev, kvc, max_err, note, scale_of, to_dev, torch
+from tests.gpu_util import TD, TOL, check, dev, kvc, max_err, note, scale_of, to_dev, torch
 
 pytestmark = pytest.mark.gpu
 
@@ -51,7 +51,7 @@ def test_contig_ragged(dtype, D, out_dtype):
     torch.cuda.synchronize()
     want = ref.decode(q, lens, scale_of(D))
     tol = TOL[dtype] if (out_dtype == "f32" or dtype == "f32") else TOL["f16"]
-    assert max_err(got.float().cpu().numpy(), want) <= tol
+    check(got.float().cpu().numpy(), want, tol)
     assert (got[0].float().abs().sum().item()) == 0.0    # L = 0 gives a zero row
 
 
@@ -71,7 +71,7 @@ def test_tiny_gpt_decode_every_step():
     P = w.extra["prefill"]
     kvc.append_contig(kc, vc, to_dev(np.zeros(1, np.int32), d), to_dev(K[:, :P], d),
                       to_dev(V[:, :P], d))
-    ws = torch.empty(kvc.workspace_bytes(1, H, D), dtype=torch.uint8, device=d)
+    ws = kvc.new_workspace(1, H, D, device=d)
     outs = []
     lens_d = torch.zeros(1, dtype=torch.int32, device=d)
     for t in range(P, T):
@@ -85,7 +85,7 @@ def test_tiny_gpt_decode_every_step():
     for h in range(H):
         want = cached_decode(Q[0, P:, h], K[0, P:, h], V[0, P:, h], w.scale,
                              prefix_K=K[0, :P, h], prefix_V=V[0, :P, h])
-        assert max_err(got[:, h], want) <= TOL["f32"]
+        check(got[:, h], want, TOL["f32"])
     np.testing.assert_array_equal(kc.cpu().numpy()[0], K[0].transpose(1, 0, 2))
 
 
@@ -142,17 +142,18 @@ def test_paged_ragged(dtype, D):
                                 scale=scale_of(D))
     torch.cuda.synchronize()
     want = ref.decode(q, tables, tl, scale_of(D))
-    err = max_err(got.float().cpu().numpy(), want)
-    assert err <= (TOL["f32"] if dtype == "f32" else TOL["f16"]), err
+    check(got.float().cpu().numpy(), want, TOL["f32"] if dtype == "f32" else TOL["f16"])
     if dtype == "e4m3":
-        # against the unquantised inputs as well
+        # against the unquantised inputs as well, where enough positions are averaged: one
+        # position alone reproduces a single dequantised row (e4m3 steps are 2^-4 relative)
         raw = PagedCache(layer.num_blocks, 3, D, "f32")
         for s, (k, v) in zip(seqs, data):
             t, L = pool.block_table([s])
             slots = [t[0][i // 16] * 16 + i % 16 for i in range(L[0])]
             raw.write(slots, k.astype(np.float32), v.astype(np.float32))
-        assert max_err(got.float().cpu().numpy(), raw.decode(q, tables, tl, scale_of(D))) \
-            <= TOL["e4m3"]
+        long_ = [i for i, L in enumerate(lens) if L >= 250]
+        unq = raw.decode(q, tables, tl, scale_of(D))
+        check(got.float().cpu().numpy()[long_], unq[long_], TOL["e4m3"])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
@@ -174,7 +175,7 @@ def test_paged_equals_contiguous_on_gpu(dtype):
     a = kvc.decode_attn_paged(q, layer, to_dev(tables, d), to_dev(tl, d), 200, out=out_f32)
     b = kvc.decode_attn_contig(q, kc, vc, to_dev(tl, d), 200,
                                out=torch.empty_like(out_f32)).cpu().numpy()
-    assert max_err(a.cpu().numpy(), b) <= 1e-6
+    check(a.cpu().numpy(), b, 1e-6)
 
 
 def test_e4m3_hardware_decode_matches_definition_for_every_code():
@@ -242,9 +243,10 @@ def test_fp8_writes_bit_exact_with_requantisation_and_block_reuse(src, D):
     seqs = [a, c]
     tables, tl = pool.block_table(seqs)
     q = workloads.normal(g, (2, H, D), "f16")
+    out = torch.empty((2, H, D), dtype=torch.float32, device=d)   # inputs reach ~7x unit scale
     got = kvc.decode_attn_paged(to_dev(q, d), layer, to_dev(tables, d), to_dev(tl, d), 100,
-                                scale=scale_of(D))
-    assert max_err(got.float().cpu().numpy(), ref.decode(q, tables, tl, scale_of(D))) <= 2e-3
+                                scale=scale_of(D), out=out)
+    check(got.cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)), 2e-3)
 
 
 @pytest.mark.parametrize("dtype", ["f16", "e4m3"])
@@ -270,7 +272,7 @@ def test_parallel_sampling_small_copy_on_write(dtype):
     seqs = [p] + [pool.fork(p) for _ in range(3)]
     for _ in range(3):
         model.fork(p)
-    ws = torch.empty(kvc.workspace_bytes(4, H, D), dtype=torch.uint8, device=d)
+    ws = kvc.new_workspace(4, H, D, device=d)
     n_copies = 0
     for step in range(30):
         slots, src_, dst_ = pool.append(seqs, 1)
@@ -289,8 +291,8 @@ def test_parallel_sampling_small_copy_on_write(dtype):
         got = kvc.decode_attn_paged(to_dev(q, d), layer, to_dev(tables, d), to_dev(tl, d),
                                     int(tl.max()), scale=scale_of(D), workspace=ws)
         if step in (0, 11, 29):
-            err = max_err(got.float().cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)))
-            assert err <= 2e-3, (step, err)
+            check(got.float().cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)), 2e-3,
+                  f"step {step}")
     assert n_copies == 3
     _compare_pools(layer, ref)
 
@@ -322,7 +324,7 @@ def test_edge_cases_clamped_lengths_bad_ids_and_empty_batch():
         keep = [t for t in range(tl[b]) if t3[b, t // 16] == tables[b, t // 16]]
         for h in range(H):
             want[b, h] = decode_row(q[b, h], K[h][keep], V[h][keep], scale)
-    assert max_err(got.float().cpu().numpy(), want) <= 2e-3
+    check(got.float().cpu().numpy(), want, 2e-3)
     # an underestimated max_ctx only changes the grid, not the result
     a = kvc.decode_attn_paged(to_dev(q, d), layer, to_dev(tables, d), to_dev(tl, d), 1)
     b_ = kvc.decode_attn_paged(to_dev(q, d), layer, to_dev(tables, d), to_dev(tl, d), 40)
@@ -351,3 +353,26 @@ def test_two_phase_api_equals_single_call():
     kvc.decode_merge(3, H, D, out, ws)
     torch.cuda.synchronize()
     assert torch.equal(a, out)
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace serves calls of different batch sizes in stream order, with results equal
+    to those of a fresh workspace."""
+    d = dev()
+    note("workspace reuse")
+    D, H = 128, 4
+    g, pool, model, seqs, layer, ref, data = _paged_setup(d, "f16", D, [300, 7, 1000, 64], H=H,
+                                                          seed=4)
+    tables, tl = pool.block_table(seqs)
+    tdv, tlv = to_dev(tables, d), to_dev(tl, d)
+    q = to_dev(workloads.normal(g, (4, H, D), "f16"), d)
+    ws = kvc.new_workspace(4, H, D, device=d)
+    ws.fill_(0xA5)   # arbitrary prior contents
+    for rep in range(3):
+        for B in (4, 2, 3):
+            a = kvc.decode_attn_paged(q[:B].contiguous(), layer, tdv[:B].contiguous(),
+                                      tlv[:B].contiguous(), 1000, workspace=ws)
+            b_ = kvc.decode_attn_paged(q[:B].contiguous(), layer, tdv[:B].contiguous(),
+                                       tlv[:B].contiguous(), 1000)
+            torch.cuda.synchronize()
+            assert torch.equal(a, b_), (rep, B)
