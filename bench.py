@@ -39,9 +39,12 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
-                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig"])
+                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
+                    help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv output) "
+                         "of this script with --copy-calibration, and print the traffic record")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (torch) 3 times; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -210,6 +213,90 @@ class HipEvents:
         self.ev = []
 
 
+class ContigBench:
+    """Contiguous [B, H, S_max, D] caches. LLaMA-7B shapes: every step appends one token per
+    sequence at position ctx-1 (overwriting, so each step attends exactly ctx positions) and
+    attends. Tiny char-GPT: a 16-token prefill, then each step appends at the next position and
+    attends (context 17 .. 256)."""
+
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev):
+        import torch
+
+        import kv_cache_attention_kvc_amd as kvc
+
+        self.kvc, self.torch, self.w, self.dev, self.L = kvc, torch, w, dev, layers
+        B, H, D, S = w.batch, w.heads, w.head_dim, w.s_max
+        self.B, self.H, self.D, self.S = B, H, D, S
+        self.growing = "prefill" in w.extra
+        pre = w.extra["prefill"] if self.growing else w.ctx - 1
+        if self.growing and pre + steps > S:
+            raise SystemExit(f"at most {S - pre} steps for {w.name}")
+        td = torch.float32 if w.kv_dtype == "f32" else torch.float16
+        self.kc, self.vc = [], []
+        zeros = torch.zeros(B, dtype=torch.int32, device=dev)
+        for li in range(layers):
+            k = torch.empty((B, H, S, D), dtype=td, device=dev)
+            v = torch.empty_like(k)
+            kn = workloads.torch_normal((B, pre, H, D), td, dev, w.seed * 1000 + 2 * li)
+            vn = workloads.torch_normal((B, pre, H, D), td, dev, w.seed * 1000 + 2 * li + 1)
+            kvc.append_contig(k, v, zeros, kn, vn)
+            del kn, vn
+            self.kc.append(k)
+            self.vc.append(v)
+        torch.cuda.synchronize()
+        self.knew = workloads.torch_normal((layers, B, 1, H, D), td, dev, w.seed * 7 + 1)
+        self.vnew = workloads.torch_normal((layers, B, 1, H, D), td, dev, w.seed * 7 + 2)
+        self.q = workloads.torch_normal((layers, B, H, D), td, dev, w.seed * 7 + 3)
+        self.out = torch.empty((layers, B, H, D), dtype=td, device=dev)
+        self.ws = kvc.new_workspace(B, H, D, device=dev)
+        self.pos = pre                      # next position written
+        self.pos_d = torch.full((B,), pre, dtype=torch.int32, device=dev)
+        self.len_d = torch.full((B,), pre + 1, dtype=torch.int32, device=dev)
+        self.scale = w.scale
+        self.stream = torch.cuda.current_stream()
+        self.lens_now = np.full(B, pre, dtype=np.int64)
+
+    def step(self, ev=None):
+        kvc = self.kvc
+        if self.growing:
+            self.pos_d.fill_(self.pos)
+            self.len_d.fill_(self.pos + 1)
+        self.lens_now[:] = self.pos + 1
+        for li in range(self.L):
+            kvc.append_contig(self.kc[li], self.vc[li], self.pos_d, self.knew[li], self.vnew[li])
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li, self.stream)
+            kvc.decode_partial_contig(self.q[li], self.kc[li], self.vc[li], self.len_d,
+                                      self.pos + 1, scale=self.scale, out=self.out[li],
+                                      workspace=self.ws)
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li + 1, self.stream)
+            kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
+        if self.growing:
+            self.pos += 1
+
+    def bytes_step(self, lens):
+        elt = ELT[self.w.kv_dtype]
+        B, H, D = self.B, self.H, self.D
+        kv = int(lens.sum()) * H * D * 2 * elt
+        qo = B * H * D * 2 * elt
+        pass1 = kv + qo + B * 4
+        return (pass1 + B * H * D * 2 * elt) * self.L, pass1
+
+    def oracle_layer(self, li):
+        from oracle.caches import ContigCache
+
+        ref = ContigCache(self.B, self.H, self.S, self.D, self.w.kv_dtype)
+        ref.K = self.kc[li].cpu().numpy()
+        ref.V = self.vc[li].cpu().numpy()
+        q = self.q[li].float().cpu().numpy()
+        lens = self.lens_now.copy()
+        t0 = time.perf_counter()
+        out = ref.decode(q, lens, self.scale)
+        dt = time.perf_counter() - t0
+        return dt, out, int(lens.sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -220,8 +307,79 @@ def blas_threads() -> int:
         return 1
 
 
+KERNEL_SRC = os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", "kvc_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_paged_f16_llama13b_traffic.txt")
+PASS1 = "decode_partial_kernel<true, 1, 128>"
+
+
+def source_hash() -> str:
+    import hashlib
+
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def pmc_summary(fetch_dir: str, write_dir: str, bench_log: str) -> dict:
+    """HBM bytes per pass-1 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
+    each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    import csv
+    import glob
+
+    def rows(d):
+        (f,) = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        return list(csv.DictReader(open(f)))
+
+    def per_kernel(rs, pred):
+        v = [float(r["Counter_Value"]) for r in rs if pred(r["Kernel_Name"])]
+        return sum(v) / len(v), len(v)
+
+    fr, wr = rows(fetch_dir), rows(write_dir)
+    cal = float(1 << 30)
+    # the calibration copies: the three largest copy dispatches at the end of the run
+    def copy_kib(rs):
+        v = sorted(float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]
+                   and int(r["Grid_Size"]) >= 65536)
+        return v[-1]
+    f_fac = cal / (copy_kib(fr) * 1024)
+    w_fac = cal / (copy_kib(wr) * 1024)
+    fk, nf = per_kernel(fr, lambda n: PASS1 in n)
+    wk, nw = per_kernel(wr, lambda n: PASS1 in n)
+    alg = src = None
+    for ln in open(bench_log):
+        if ln.startswith("{"):
+            rec = json.loads(ln)
+            alg = rec["roofline"]["algorithmic_bytes_per_launch"]
+            src = rec["roofline"]["kernel_source_sha256_16"]
+    fetch_b = fk * 1024 * f_fac
+    write_b = wk * 1024 * w_fac
+    return {"kernel": PASS1, "source_sha256_16": src, "dispatches": [nf, nw],
+            "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+            "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5),
+            "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+            "traffic_bytes": int(fetch_b + write_b),
+            "algorithmic_bytes_per_launch_same_run": alg,
+            "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4) if alg else None}
+
+
+def measured_traffic():
+    """Traffic per pass-1 launch from the committed counter summary, if it was taken on the
+    current kernel source (else None)."""
+    try:
+        for ln in open(TRAFFIC_FILE):
+            if ln.startswith("{"):
+                rec = json.loads(ln)
+                if rec.get("source_sha256_16") == source_hash():
+                    return rec["traffic_bytes"]
+    except OSError:
+        pass
+    return None
+
+
 def main():
     args = parse()
+    if args.pmc_summary:
+        print(json.dumps(pmc_summary(*args.pmc_summary)))
+        return
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs "
               "on a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
@@ -233,16 +391,15 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = {"llama13b-paged": workloads.LLAMA13B_PAGED,
-         "fp8-longctx": workloads.LONGCTX_FP8}.get(args.workload)
-    if w is None:
-        print("workload not implemented in bench.py yet", file=sys.stderr)
-        sys.exit(2)
+    w = {"llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
+         "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
+    if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
+        K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    bench = PagedBench(w, K + W, layers, dev)
+    bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev)
     for _ in range(W):
         bench.step()
     torch.cuda.synchronize()
@@ -288,21 +445,23 @@ def main():
             "workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
             "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
-            if not w.ctx else w.ctx,
-            "ctx_growth_per_step": 1,
+            if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
+            "ctx_growth_per_step": 0 if w is workloads.LLAMA7B_CONTIG else 1,
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(w.batch * K / elapsed, 1),
         "roofline": {
-            "kernel": "kvc::decode_partial_kernel<paged, f16, 128> (attention pass 1)",
+            "kernel": f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> "
+                      "(attention pass 1)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic() if w is workloads.LLAMA13B_PAGED else None,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
+            "kernel_source_sha256_16": source_hash(),
         },
     }
     if not args.no_cpu_baseline:

@@ -1,0 +1,236 @@
+"""HIP path vs the CPU oracle at the full workload sizes (one layer each), in the launch
+configuration the benchmark uses. Where the oracle cannot take the whole output in seconds it
+checks sampled (sequence, head) rows one by one; cache contents and block tables are compared
+bit for bit. The tiny char-GPT workload runs in full in test_gpu_parity.py."""
+import numpy as np
+import pytest
+
+import workloads
+from oracle.attention import decode_row
+from oracle.caches import PagedCache
+from oracle.codecs import e4m3_decode, fp8_write_token
+from oracle.pool import PoolModel
+from tests.gpu_util import TOL, check, dev, kvc, note, scale_of, torch
+
+pytestmark = pytest.mark.gpu
+
+
+def _sample_pairs(rng, B, H, n):
+    idx = rng.choice(B * H, size=n, replace=False)
+    return [(int(i) // H, int(i) % H) for i in idx]
+
+
+def test_llama7b_contiguous_full_layer():
+    """B=16, H=32, D=128, fp16, S_max=2048: prefill 2047 positions, append one, attend 2048."""
+    d = dev()
+    w = workloads.LLAMA7B_CONTIG
+    B, H, D, S = w.batch, w.heads, w.head_dim, w.s_max
+    note("llama7b contiguous full layer")
+    kc = torch.full((B, H, S, D), float("nan"), dtype=torch.float16, device=d)
+    vc = torch.full_like(kc, float("nan"))
+    kn = workloads.torch_normal((B, S, H, D), torch.float16, d, w.seed * 10 + 1)
+    vn = workloads.torch_normal((B, S, H, D), torch.float16, d, w.seed * 10 + 2)
+    zeros = torch.zeros(B, dtype=torch.int32, device=d)
+    kvc.append_contig(kc, vc, zeros, kn[:, :S - 1].contiguous(), vn[:, :S - 1].contiguous())
+    kvc.append_contig(kc, vc, torch.full((B,), S - 1, dtype=torch.int32, device=d),
+                      kn[:, S - 1:].contiguous(), vn[:, S - 1:].contiguous())
+    q = workloads.torch_normal((B, H, D), torch.float16, d, w.seed * 10 + 3)
+    lens = torch.full((B,), S, dtype=torch.int32, device=d)
+    out = kvc.decode_attn_contig(q, kc, vc, lens, S, scale=w.scale)
+    torch.cuda.synchronize()
+    # the cache holds exactly the appended values (bitwise), in [B, H, S, D] order
+    assert torch.equal(kc, kn.permute(0, 2, 1, 3)) and torch.equal(vc, vn.permute(0, 2, 1, 3))
+    rng = np.random.default_rng(0)
+    got = out.float().cpu().numpy()
+    qh = q.float().cpu().numpy()
+    for b, h in _sample_pairs(rng, B, H, 12):
+        want = decode_row(qh[b, h], kc[b, h].float().cpu().numpy(), vc[b, h].float().cpu().numpy(),
+                          w.scale)
+        check(got[b, h], want, TOL["f16"], f"b={b} h={h}")
+
+
+def _llama13b_state(d, w, layer_count=1):
+    lens = workloads.llama13b_lengths(w)
+    N = int(sum(workloads.blocks_for(L) for L in lens)) + w.batch
+    MB = workloads.blocks_for(int(lens.max())) + 1
+    order = workloads.llama13b_pool_order(N, w.seed)
+    pool = kvc.Pool(N, MB, order=order)
+    model = PoolModel(N, 16, MB, order=order)
+    seqs = [pool.alloc() for _ in range(w.batch)]
+    for _ in seqs:
+        model.alloc()
+    return lens, N, MB, pool, model, seqs
+
+
+def test_llama13b_paged_full_layer():
+    """B=32, H=40, D=128, fp16, lengths U[64, 2048], shuffled pool: prefill L_b - 1 tokens per
+    sequence, one decode step (append, write, attend); tables bit-exact against the pool model,
+    sampled rows against the oracle."""
+    d = dev()
+    w = workloads.LLAMA13B_PAGED
+    B, H, D = w.batch, w.heads, w.head_dim
+    note("llama13b paged full layer")
+    lens, N, MB, pool, model, seqs = _llama13b_state(d, w)
+    slots = np.concatenate([pool.append([s], int(L) - 1)[0] for s, L in zip(seqs, lens)])
+    mslots = sum((model.append([s], int(L) - 1)[0] for s, L in zip(seqs, lens)), [])
+    assert slots.tolist() == mslots
+    layer = kvc.PagedLayer.empty(N, H, D, "f16", device=d, fill=float("nan"))
+    k = workloads.torch_normal((len(slots), H, D), torch.float16, d, 31)
+    v = workloads.torch_normal((len(slots), H, D), torch.float16, d, 32)
+    kvc.write_paged(layer, torch.from_numpy(slots).to(d), k, v)
+    step, src, _ = pool.append(seqs, 1)
+    mstep, cow = model.append(seqs, 1)
+    assert step.tolist() == mstep and len(src) == 0 and cow == []
+    kn = workloads.torch_normal((B, H, D), torch.float16, d, 33)
+    vn = workloads.torch_normal((B, H, D), torch.float16, d, 34)
+    kvc.write_paged(layer, torch.from_numpy(step).to(d), kn, vn)
+    tables, tl = pool.block_table(seqs)
+    mt, ml = model.block_table(seqs)
+    assert tables.tolist() == mt and tl.tolist() == ml == lens.tolist()
+    q = workloads.torch_normal((B, H, D), torch.float16, d, 35)
+    out = kvc.decode_attn_paged(q, layer, torch.from_numpy(tables).to(d),
+                                torch.from_numpy(tl).to(d), int(lens.max()), scale=w.scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    qh = q.float().cpu().numpy()
+    kp = layer.k_pool.cpu().numpy()
+    vp = layer.v_pool.cpu().numpy()
+    rng = np.random.default_rng(1)
+    for b, h in _sample_pairs(rng, B, H, 16):
+        L = int(tl[b])
+        ids = [tables[b][t // 16] for t in range(L)]
+        Kb = np.stack([kp[ids[t], h, t % 16] for t in range(L)]).astype(np.float64)
+        Vb = np.stack([vp[ids[t], h, t % 16] for t in range(L)]).astype(np.float64)
+        check(got[b, h], decode_row(qh[b, h], Kb, Vb, w.scale), TOL["f16"], f"b={b} h={h}")
+    # the appended token of every sequence is where its slot says, bit for bit
+    knh = kn.cpu().numpy()
+    for b in range(B):
+        blk, off = divmod(int(step[b]), 16)
+        np.testing.assert_array_equal(kp[blk, :, off], knh[b])
+
+
+@pytest.mark.parametrize("prompt,copies", [(1024, 0), (1020, 7)])
+def test_parallel_sampling_full(prompt, copies):
+    """8 candidates share a prompt (refcount 8), then each appends 128 tokens with attention at
+    every step (H=40, D=128, fp16). Pools, tables and sampled steps against the oracle; block
+    counts against the pages' 2048-slot figure (and the copy-on-write variant's 135 blocks)."""
+    d = dev()
+    w = workloads.PARALLEL_SAMPLING
+    H, D, G = w.heads, w.head_dim, w.extra["generate"]
+    note(f"parallel sampling prompt={prompt}")
+    N, MB = 160, 80
+    g = workloads.rng(w.seed + prompt)
+    pool = kvc.Pool(N, MB)
+    model = PoolModel(N, 16, MB)
+    layer = kvc.PagedLayer.empty(N, H, D, "f16", device=d, fill=float("nan"))
+    ref = PagedCache(N, H, D, "f16", fill=np.nan)
+    p = pool.alloc()
+    model.alloc()
+    slots, _, _ = pool.append([p], prompt)
+    model.append([p], prompt)
+    k = workloads.normal(g, (prompt, H, D), "f16")
+    v = workloads.normal(g, (prompt, H, D), "f16")
+    kvc.write_paged(layer, torch.from_numpy(slots).to(d), torch.from_numpy(k).to(d),
+                    torch.from_numpy(v).to(d))
+    ref.write(slots, k, v)
+    seqs = [p] + [pool.fork(p) for _ in range(7)]
+    for _ in range(7):
+        model.fork(p)
+    ws = kvc.new_workspace(8, H, D, device=d)
+    n_copies = 0
+    for step in range(G):
+        slots, src, dst = pool.append(seqs, 1)
+        ms, cow = model.append(seqs, 1)
+        assert slots.tolist() == ms and list(zip(src.tolist(), dst.tolist())) == cow
+        n_copies += len(cow)
+        if len(cow):
+            kvc.copy_blocks(layer, torch.from_numpy(src).to(d), torch.from_numpy(dst).to(d))
+            ref.copy_blocks(cow)
+        k = workloads.normal(g, (8, H, D), "f16")
+        v = workloads.normal(g, (8, H, D), "f16")
+        kvc.write_paged(layer, torch.from_numpy(slots).to(d), torch.from_numpy(k).to(d),
+                        torch.from_numpy(v).to(d))
+        ref.write(slots, k, v)
+        tables, tl = pool.block_table(seqs)
+        q = workloads.normal(g, (8, H, D), "f16")
+        out = kvc.decode_attn_paged(torch.from_numpy(q).to(d), layer,
+                                    torch.from_numpy(tables).to(d), torch.from_numpy(tl).to(d),
+                                    prompt + G, scale=scale_of(D), workspace=ws)
+        if step in (0, 63, G - 1):
+            check(out.float().cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)), TOL["f16"],
+                  f"step {step}")
+    assert n_copies == copies
+    st = pool.stats()
+    assert st["used"] == (128 if prompt == 1024 else 135)
+    if prompt == 1024:
+        assert st["used"] * 16 == 2048 and st["tokens"] == 8 * (1024 + 128)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(layer.k_pool.cpu().numpy(), ref.K)
+    np.testing.assert_array_equal(layer.v_pool.cpu().numpy(), ref.V)
+
+
+def test_fp8_long_context_full_layer():
+    """B=64, H=32, D=128, e4m3 with per-block scales, context 4096: prefill 4095 tokens per
+    sequence through the fp8 writer, append one, attend. Codes and scales of sampled blocks
+    bit-exact against the oracle's writer; sampled rows against the oracle over the stored codes
+    (2e-3) and over the unquantised inputs (3e-2)."""
+    d = dev()
+    w = workloads.LONGCTX_FP8
+    B, H, D, T = w.batch, w.heads, w.head_dim, w.ctx
+    note("fp8 long context full layer")
+    nblk = workloads.blocks_for(T)
+    N = B * nblk
+    pool = kvc.Pool(N, nblk)
+    seqs = [pool.alloc() for _ in range(B)]
+    slots = pool.append(seqs, T - 1)[0]
+    layer = kvc.PagedLayer.empty(N, H, D, "e4m3", device=d, fill=float("nan"))
+    k = workloads.torch_normal((len(slots), H, D), torch.float16, d, 51)
+    v = workloads.torch_normal((len(slots), H, D), torch.float16, d, 52)
+    kvc.write_paged(layer, torch.from_numpy(slots).to(d), k, v)
+    step = pool.append(seqs, 1)[0]
+    kn = workloads.torch_normal((B, H, D), torch.float16, d, 53)
+    vn = workloads.torch_normal((B, H, D), torch.float16, d, 54)
+    kvc.write_paged(layer, torch.from_numpy(step).to(d), kn, vn)
+    tables, tl = pool.block_table(seqs)
+    assert (tl == T).all()
+    q = workloads.torch_normal((B, H, D), torch.float16, d, 55)
+    out = kvc.decode_attn_paged(q, layer, torch.from_numpy(tables).to(d),
+                                torch.from_numpy(tl).to(d), T, scale=w.scale)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    qh = q.float().cpu().numpy()
+    rng = np.random.default_rng(2)
+    # bit-exact writer check on sampled blocks (including each sampled sequence's last block)
+    kh_rows = {}
+    for b in rng.choice(B, size=3, replace=False):
+        for j in (0, int(rng.integers(1, nblk - 1)), nblk - 1):
+            blk = int(tables[b][j])
+            codes_k = np.zeros((H, 16, D), np.uint8)
+            codes_v = np.zeros((H, 16, D), np.uint8)
+            sk = sv = np.float32(0)
+            for t in range(16):
+                pos = j * 16 + t
+                if pos < T - 1:
+                    i = int(b) * (T - 1) + pos
+                    xk, xv = k[i].float().cpu().numpy(), v[i].float().cpu().numpy()
+                else:
+                    xk, xv = kn[b].float().cpu().numpy(), vn[b].float().cpu().numpy()
+                sk = fp8_write_token(codes_k, sk, t, xk)
+                sv = fp8_write_token(codes_v, sv, t, xv)
+            np.testing.assert_array_equal(layer.k_pool[blk].cpu().numpy(), codes_k)
+            np.testing.assert_array_equal(layer.v_pool[blk].cpu().numpy(), codes_v)
+            assert layer.k_scale[blk].item() == sk and layer.v_scale[blk].item() == sv
+    # sampled rows over the stored codes, and over the unquantised inputs
+    ks = layer.k_scale.cpu().numpy()
+    vs = layer.v_scale.cpu().numpy()
+    for b, h in _sample_pairs(rng, B, H, 6):
+        ids = tables[b][:nblk]
+        Kc = layer.k_pool[torch.from_numpy(ids.astype(np.int64)).to(d), h].cpu().numpy()  # [nblk,16,D]
+        Vc = layer.v_pool[torch.from_numpy(ids.astype(np.int64)).to(d), h].cpu().numpy()
+        Kq = (e4m3_decode(Kc) * ks[ids][:, None, None].astype(np.float64)).reshape(T, D)
+        Vq = (e4m3_decode(Vc) * vs[ids][:, None, None].astype(np.float64)).reshape(T, D)
+        check(got[b, h], decode_row(qh[b, h], Kq, Vq, w.scale), TOL["f16"], f"codes b={b} h={h}")
+        rows = slice(int(b) * (T - 1), int(b) * (T - 1) + T - 1)
+        Kr = np.concatenate([k[rows, h].float().cpu().numpy(), kn[b:b + 1, h].float().cpu().numpy()])
+        Vr = np.concatenate([v[rows, h].float().cpu().numpy(), vn[b:b + 1, h].float().cpu().numpy()])
+        check(got[b, h], decode_row(qh[b, h], Kr, Vr, w.scale), TOL["e4m3"], f"raw b={b} h={h}")
