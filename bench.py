@@ -309,7 +309,7 @@ def blas_threads() -> int:
 
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", "kvc_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_paged_f16_llama13b_traffic.txt")
-PASS1 = "decode_partial_kernel<true, 1, 128>"
+PASS1 = "decode_partial_kernel<true, 1, 128, true>"
 
 
 def source_hash() -> str:

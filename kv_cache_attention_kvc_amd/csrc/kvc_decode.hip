@@ -138,9 +138,67 @@ __device__ __forceinline__ void unpack(const uint4 &r, float *f) {
   }
 }
 
-__device__ __forceinline__ float load_elem(const void *p, int64_t i, bool f16) {
-  if (f16) return static_cast<float>(reinterpret_cast<const _Float16 *>(p)[i]);
-  return reinterpret_cast<const float *>(p)[i];
+__device__ __forceinline__ float half_lo(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w)));
+}
+__device__ __forceinline__ float half_hi(uint32_t w) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
+}
+
+// N consecutive q elements (fp16 or fp32) starting at element i, as floats, with 8- or 16-byte
+// vector loads and no branches (so the loads of a slice are all in flight together).
+template <bool QF16, int N>
+__device__ __forceinline__ void load_q(const void *p, int64_t i, float *x) {
+  if constexpr (QF16) {
+    const char *b = static_cast<const char *>(p) + i * 2;
+    if constexpr (N % 8 == 0) {
+#pragma unroll
+      for (int k = 0; k < N / 8; ++k) {
+        const uint4 r = reinterpret_cast<const uint4 *>(b)[k];
+        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          x[8 * k + 2 * u] = half_lo(w[u]);
+          x[8 * k + 2 * u + 1] = half_hi(w[u]);
+        }
+      }
+    } else {
+      static_assert(N == 4, "fp16 q slices are 4, 8 or 16 elements");
+      const uint2 r = *reinterpret_cast<const uint2 *>(b);
+      x[0] = half_lo(r.x);
+      x[1] = half_hi(r.x);
+      x[2] = half_lo(r.y);
+      x[3] = half_hi(r.y);
+    }
+  } else {
+    static_assert(N % 4 == 0, "fp32 q slices are a multiple of 4 elements");
+    const float4 *b = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+#pragma unroll
+    for (int k = 0; k < N / 4; ++k) {
+      const float4 r = b[k];
+      x[4 * k] = r.x;
+      x[4 * k + 1] = r.y;
+      x[4 * k + 2] = r.z;
+      x[4 * k + 3] = r.w;
+    }
+  }
+}
+
+// N consecutive output elements from floats, fp16 (round to nearest even) or fp32.
+template <int N>
+__device__ __forceinline__ void store_row(void *p, int64_t i, const float *x, float s, bool f16) {
+  if (f16) {
+    _Float16 h[N];
+#pragma unroll
+    for (int e = 0; e < N; ++e) h[e] = static_cast<_Float16>(x[e] * s);
+    _Float16 *d = static_cast<_Float16 *>(p) + i;
+#pragma unroll
+    for (int e = 0; e < N; ++e) d[e] = h[e];
+  } else {
+    float *d = static_cast<float *>(p) + i;
+#pragma unroll
+    for (int e = 0; e < N; ++e) d[e] = x[e] * s;
+  }
 }
 
 __device__ __forceinline__ void store_elem(void *p, int64_t i, float x, bool f16) {
@@ -284,51 +342,59 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D> &t, const flo
   }
 }
 
-// ---- one (sequence, head) segment of a chunk --------------------------------------------
-template <bool PAGED, int KV, int D>
-__device__ __forceinline__ void run_segment(const DecodeArgs &a, int32_t b, int32_t h, int32_t j0,
-                                            int32_t n, int32_t w, bool cut_start, bool cut_end) {
+// ---- the wavefront's chunk: segments and the tile pipeline --------------------------------
+// A segment is the part of one (sequence, head) pair that lies in the chunk: tiles j0 .. j0+n-1.
+struct Seg {
+  int32_t b, h, j0, n, L;
+  bool cut_start, cut_end;
+};
+
+// Next segment of the chunk starting at tile f (b is a cursor over sequences that only moves
+// forward). Returns false at the end of the chunk.
+__device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre, int32_t &f,
+                                         int32_t f1, int32_t &b, Seg &s) {
+  if (f >= f1) return false;
+  while (a.H * sread(pre + b + 1) <= f) ++b;
+  const int32_t nb = sread(pre + b + 1) - sread(pre + b);
+  const int32_t base = a.H * sread(pre + b);
+  const int32_t rel = f - base;
+  s.b = b;
+  s.h = rel / nb;
+  s.j0 = rel - s.h * nb;
+  const int32_t seg_end = base + (s.h + 1) * nb;
+  const int32_t e = min(f1, seg_end);
+  s.n = e - f;
+  s.cut_start = s.j0 > 0;
+  s.cut_end = e < seg_end;
+  s.L = min(max(a.lens[b], 0), a.cap);
+  f = e;
+  return true;
+}
+
+// Per-segment registers: the query slice of this lane's column and (paged) the physical block
+// ids of the segment's first 64 tiles, one per lane.
+template <int EPL>
+struct SegRegs {
+  Seg s;
+  float q[EPL];
+  int32_t win;
+};
+
+template <bool PAGED, bool QF16, int EPL>
+__device__ __forceinline__ void load_seg(const DecodeArgs &a, SegRegs<EPL> &r, int D, int c,
+                                         int lane) {
+  const int64_t bh = static_cast<int64_t>(r.s.b) * a.H + r.s.h;
+  load_q<QF16, EPL>(a.q, bh * D + c * EPL, r.q);
+  if constexpr (PAGED)
+    r.win = lane < r.s.n ? a.tables[static_cast<int64_t>(r.s.b) * a.mbps + r.s.j0 + lane] : -1;
+}
+
+// Finish a segment: combine the TPL lane groups, then either write the output row (the whole
+// pair was in this chunk) or leave a record (slot 0 if the pair began before the chunk, else 1).
+template <int KV, int D>
+__device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, int32_t w, int g,
+                                           int c, float m, float l, float *acc) {
   using G = Geo<KV, D>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int g = lane / G::LPT;
-  const int c = lane % G::LPT;
-  const int32_t L = min(max(__builtin_amdgcn_readfirstlane(a.lens[b]), 0), a.cap);
-  const int64_t bh = static_cast<int64_t>(b) * a.H + h;
-
-  float qv[G::EPL];
-#pragma unroll
-  for (int e = 0; e < G::EPL; ++e) qv[e] = load_elem(a.q, bh * D + c * G::EPL + e, a.q_f16);
-
-  float m = kFloor, l = 0.f;
-  float acc[G::EPL];
-#pragma unroll
-  for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
-
-  // physical block ids of the next (up to) 64 tiles, one per lane
-  int32_t tbl = 0;
-  auto phys_of = [&](int32_t jj) -> int32_t {
-    if constexpr (PAGED) {
-      if ((jj & 63) == 0) {
-        const int32_t idx = jj + lane;
-        tbl = idx < n ? a.tables[static_cast<int64_t>(b) * a.mbps + j0 + idx] : -1;
-      }
-      return __builtin_amdgcn_readlane(tbl, jj & 63);
-    } else {
-      return 0;
-    }
-  };
-
-  TileRegs<KV, D> ta, tb;
-  fetch_tile<PAGED, KV, D>(a, ta, bh, h, j0, phys_of(0), L, g, c);
-  for (int32_t jj = 0; jj < n; jj += 2) {
-    if (jj + 1 < n) fetch_tile<PAGED, KV, D>(a, tb, bh, h, j0 + jj + 1, phys_of(jj + 1), L, g, c);
-    consume_tile<KV, D>(ta, qv, a.cl2, g, m, l, acc);
-    if (jj + 1 >= n) break;
-    if (jj + 2 < n) fetch_tile<PAGED, KV, D>(a, ta, bh, h, j0 + jj + 2, phys_of(jj + 2), L, g, c);
-    consume_tile<KV, D>(tb, qv, a.cl2, g, m, l, acc);
-  }
-
-  // combine the TPL groups of the wavefront (lanes sharing a column)
 #pragma unroll
   for (int off = G::LPT; off < kWave; off <<= 1) {
     const float mo = __shfl_xor(m, off);
@@ -342,15 +408,12 @@ __device__ __forceinline__ void run_segment(const DecodeArgs &a, int32_t b, int3
     m = M;
   }
   if (g != 0) return;
-  if (!cut_start && !cut_end) {
-    const float inv = l > 0.f ? 1.0f / l : 0.f;
-#pragma unroll
-    for (int e = 0; e < G::EPL; ++e)
-      store_elem(a.out, bh * D + c * G::EPL + e, acc[e] * inv, a.out_f16);
+  const int64_t bh = static_cast<int64_t>(s.b) * a.H + s.h;
+  if (!s.cut_start && !s.cut_end) {
+    store_row<G::EPL>(a.out, bh * D + c * G::EPL, acc, l > 0.f ? 1.0f / l : 0.f, a.out_f16);
     return;
   }
-  // a cut segment: slot 0 if it began before this chunk, else slot 1
-  float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + (cut_start ? 0 : 1)) * (D + 4);
+  float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + (s.cut_start ? 0 : 1)) * (D + 4);
 #pragma unroll
   for (int e = 0; e < G::EPL; ++e) r[c * G::EPL + e] = acc[e];
   if (c == 0) {
@@ -359,7 +422,102 @@ __device__ __forceinline__ void run_segment(const DecodeArgs &a, int32_t b, int3
   }
 }
 
-template <bool PAGED, int KV, int D>
+// Walk the chunk [f0, f1) tile by tile as one pipeline: while tile t is consumed, tile t+1 is in
+// flight -- also across segment boundaries, whose q slice and block ids are loaded one segment
+// ahead -- so a new segment starts without a stall on its first loads.
+template <bool PAGED, int KV, int D, bool QF16>
+__device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre, int32_t f0,
+                                          int32_t f1, int32_t b0, int32_t w) {
+  using G = Geo<KV, D>;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int g = lane / G::LPT;
+  const int c = lane % G::LPT;
+  int32_t f = f0, bcur = b0;
+
+  SegRegs<G::EPL> cur, nxt;
+  next_seg(a, pre, f, f1, bcur, cur.s);  // f0 < f1, so there is a first segment
+  load_seg<PAGED, QF16, G::EPL>(a, cur, D, c, lane);
+  bool has_nxt = next_seg(a, pre, f, f1, bcur, nxt.s);
+  if (has_nxt) load_seg<PAGED, QF16, G::EPL>(a, nxt, D, c, lane);
+
+  // block ids of tiles wb .. wb+63 of the current segment are in cur.win; the next 64 are
+  // prefetched into `ahead` once half of the window has been used
+  int32_t wb = 0;
+  int32_t ahead = -1;
+  auto phys_cur = [&](int32_t k) -> int32_t {
+    if constexpr (PAGED) {
+      if (k - wb == 64) {
+        cur.win = ahead;
+        wb += 64;
+      }
+      if (k - wb == 32 && wb + 64 < cur.s.n) {
+        const int32_t idx = wb + 64 + lane;
+        ahead = idx < cur.s.n
+                    ? a.tables[static_cast<int64_t>(cur.s.b) * a.mbps + cur.s.j0 + idx]
+                    : -1;
+      }
+      return __builtin_amdgcn_readlane(cur.win, k - wb);
+    } else {
+      return 0;
+    }
+  };
+  auto phys_first = [&](const SegRegs<G::EPL> &r) -> int32_t {
+    if constexpr (PAGED) return __builtin_amdgcn_readlane(r.win, 0);
+    else return 0;
+  };
+  auto fetch = [&](TileRegs<KV, D> &t, const Seg &s, int32_t k, int32_t phys) {
+    const int64_t bh = static_cast<int64_t>(s.b) * a.H + s.h;
+    fetch_tile<PAGED, KV, D>(a, t, bh, s.h, s.j0 + k, phys, s.L, g, c);
+  };
+
+  float m = kFloor, l = 0.f;
+  float acc[G::EPL];
+#pragma unroll
+  for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
+
+  int32_t i = 0;  // index, within the current segment, of the tile being consumed
+  // one pipeline step: issue the next tile into `nb`, consume `cb`; false when the chunk is done
+  auto step = [&](TileRegs<KV, D> &cb, TileRegs<KV, D> &nb) -> bool {
+    const bool last = i + 1 == cur.s.n;
+    if (!last || has_nxt) {
+      // one load site for both cases (scalar selects pick the tile), so the compiler keeps a
+      // single set of loads in flight across the consume below
+      const int32_t ph = last ? phys_first(nxt) : phys_cur(i + 1);
+      Seg ns;
+      ns.b = last ? nxt.s.b : cur.s.b;
+      ns.h = last ? nxt.s.h : cur.s.h;
+      ns.j0 = last ? nxt.s.j0 : cur.s.j0;
+      ns.L = last ? nxt.s.L : cur.s.L;
+      fetch(nb, ns, last ? 0 : i + 1, ph);
+    }
+    consume_tile<KV, D>(cb, cur.q, a.cl2, g, m, l, acc);
+    if (!last) {
+      ++i;
+      return true;
+    }
+    finish_seg<KV, D>(a, cur.s, w, g, c, m, l, acc);
+    if (!has_nxt) return false;
+    cur = nxt;
+    i = 0;
+    wb = 0;
+    m = kFloor;
+    l = 0.f;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
+    has_nxt = next_seg(a, pre, f, f1, bcur, nxt.s);
+    if (has_nxt) load_seg<PAGED, QF16, G::EPL>(a, nxt, D, c, lane);
+    return true;
+  };
+
+  TileRegs<KV, D> ta, tb;
+  fetch(ta, cur.s, 0, phys_first(cur));
+  for (;;) {
+    if (!step(ta, tb)) break;
+    if (!step(tb, ta)) break;
+  }
+}
+
+template <bool PAGED, int KV, int D, bool QF16>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t *pre = smem;
@@ -383,25 +541,13 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   const int32_t f1 = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
   int32_t f = static_cast<int32_t>(f0);
 
-  // the sequence holding tile f: largest b in [0, B) with H*pre[b] <= f
+  // the sequence holding tile f0: largest b in [0, B) with H*pre[b] <= f0
   int32_t lo = 0, hi = a.B - 1;
   while (lo < hi) {
     const int32_t mid = (lo + hi + 1) >> 1;
     if (a.H * sread(pre + mid) <= f) lo = mid; else hi = mid - 1;
   }
-  int32_t b = lo;
-  while (f < f1) {
-    while (a.H * sread(pre + b + 1) <= f) ++b;
-    const int32_t nb = sread(pre + b + 1) - sread(pre + b);
-    const int32_t base = a.H * sread(pre + b);
-    const int32_t rel = f - base;
-    const int32_t h = rel / nb;
-    const int32_t j0 = rel - h * nb;
-    const int32_t seg_end = base + (h + 1) * nb;
-    const int32_t e = min(f1, seg_end);
-    run_segment<PAGED, KV, D>(a, b, h, j0, e - f, w, j0 > 0, e < seg_end);
-    f = e;
-  }
+  run_chunk<PAGED, KV, D, QF16>(a, pre, f, f1, lo, w);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -497,18 +643,23 @@ int device_cu_count() {
 
 using PartialKernel = void (*)(DecodeArgs);
 
-template <bool PAGED>
-PartialKernel pick_kernel(kvc_dtype kv, int D) {
+template <bool PAGED, bool QF16>
+PartialKernel pick_kernel_q(kvc_dtype kv, int D) {
   if (D == 64) {
-    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 64>;
-    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 64>;
-    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 64>;
+    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 64, QF16>;
+    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 64, QF16>;
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 64, QF16>;
   } else if (D == 128) {
-    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 128>;
-    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 128>;
-    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 128>;
+    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 128, QF16>;
+    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 128, QF16>;
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 128, QF16>;
   }
   return nullptr;
+}
+
+template <bool PAGED>
+PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16) {
+  return q_f16 ? pick_kernel_q<PAGED, true>(kv, D) : pick_kernel_q<PAGED, false>(kv, D);
 }
 
 struct PartialPlan {
@@ -566,7 +717,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   a.q_f16 = q_dtype == KVC_F16;
   a.out_f16 = out_dtype == KVC_F16;
   a.cl2 = scale * kLog2e;
-  pl.kern = paged ? pick_kernel<true>(kv_dtype, D) : pick_kernel<false>(kv_dtype, D);
+  pl.kern = paged ? pick_kernel<true>(kv_dtype, D, a.q_f16)
+                  : pick_kernel<false>(kv_dtype, D, a.q_f16);
   if (!pl.kern) return KVC_E_UNSUPPORTED;
   pl.grid = static_cast<int>(P / kWgWaves);
   pl.shmem = (static_cast<size_t>(B) + 1 + kWgWaves) * sizeof(int32_t);
