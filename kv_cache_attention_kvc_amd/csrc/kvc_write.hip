@@ -12,44 +12,49 @@ namespace kvc {
 constexpr int kThreads = 256;
 
 // ---- plain copies ------------------------------------------------------------------------
-// One workgroup per (sequence, token): H rows of D elements, moved as 16-byte chunks.
+// One thread per 16-byte chunk of every new (token, head) row, for K and for V: all loads of a
+// call are in flight at once.
 __global__ void __launch_bounds__(kThreads)
 append_contig_kernel(char *kc, char *vc, const char *kn, const char *vn, const int32_t *pos,
-                     int32_t H, int32_t S_max, int32_t n_tok, int32_t row_bytes) {
-  const int32_t b = blockIdx.x / n_tok;
-  const int32_t t = blockIdx.x % n_tok;
-  const int64_t p = static_cast<int64_t>(pos[b]) + t;
-  if (p < 0 || p >= S_max) return;
+                     int32_t B, int32_t H, int32_t S_max, int32_t n_tok, int32_t row_bytes) {
   const int32_t cpr = row_bytes / 16;  // 16-byte chunks per row
-  const int64_t src_tok = (static_cast<int64_t>(b) * n_tok + t) * H * row_bytes;
-  for (int32_t i = threadIdx.x; i < H * cpr; i += kThreads) {
-    const int32_t h = i / cpr;
-    const int32_t ch = i % cpr;
-    const int64_t dst = ((static_cast<int64_t>(b) * H + h) * S_max + p) * row_bytes + ch * 16;
-    const int64_t src = src_tok + static_cast<int64_t>(h) * row_bytes + ch * 16;
-    *reinterpret_cast<uint4 *>(kc + dst) = *reinterpret_cast<const uint4 *>(kn + src);
-    *reinterpret_cast<uint4 *>(vc + dst) = *reinterpret_cast<const uint4 *>(vn + src);
-  }
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (x >= static_cast<int64_t>(B) * n_tok * H * cpr) return;
+  const int32_t ch = static_cast<int32_t>(x % cpr);
+  const int64_t row = x / cpr;  // (b, t, h) in k_new order
+  const int32_t h = static_cast<int32_t>(row % H);
+  const int64_t bt = row / H;
+  const int32_t t = static_cast<int32_t>(bt % n_tok);
+  const int32_t b = static_cast<int32_t>(bt / n_tok);
+  const int64_t p = static_cast<int64_t>(pos[b]) + t;
+  const uint4 k = *reinterpret_cast<const uint4 *>(kn + row * row_bytes + ch * 16);
+  const uint4 v = *reinterpret_cast<const uint4 *>(vn + row * row_bytes + ch * 16);
+  if (p < 0 || p >= S_max) return;
+  const int64_t dst = ((static_cast<int64_t>(b) * H + h) * S_max + p) * row_bytes + ch * 16;
+  *reinterpret_cast<uint4 *>(kc + dst) = k;
+  *reinterpret_cast<uint4 *>(vc + dst) = v;
 }
 
-// One workgroup per token entry: pool[(blk*H + h)*16 + off][:] = new[i][h][:].
+// pool[(blk*H + h)*16 + off][:] = new[i][h][:], one thread per 16-byte chunk.
 __global__ void __launch_bounds__(kThreads)
 write_paged_kernel(char *kp, char *vp, const char *kn, const char *vn, const int64_t *slots,
-                   int32_t H, int32_t num_blocks, int32_t row_bytes) {
-  const int64_t i = blockIdx.x;
+                   int32_t n_tok, int32_t H, int32_t num_blocks, int32_t row_bytes) {
+  const int32_t cpr = row_bytes / 16;
+  const int64_t x = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x;
+  if (x >= static_cast<int64_t>(n_tok) * H * cpr) return;
+  const int32_t ch = static_cast<int32_t>(x % cpr);
+  const int64_t row = x / cpr;  // (i, h) in k_new order
+  const int32_t h = static_cast<int32_t>(row % H);
+  const int64_t i = row / H;
   const int64_t slot = slots[i];
+  const uint4 k = *reinterpret_cast<const uint4 *>(kn + row * row_bytes + ch * 16);
+  const uint4 v = *reinterpret_cast<const uint4 *>(vn + row * row_bytes + ch * 16);
   if (slot < 0 || slot >= static_cast<int64_t>(num_blocks) * kBlock) return;
   const int64_t blk = slot / kBlock;
   const int32_t off = static_cast<int32_t>(slot % kBlock);
-  const int32_t cpr = row_bytes / 16;
-  for (int32_t c = threadIdx.x; c < H * cpr; c += kThreads) {
-    const int32_t h = c / cpr;
-    const int32_t ch = c % cpr;
-    const int64_t dst = ((blk * H + h) * kBlock + off) * row_bytes + ch * 16;
-    const int64_t src = (i * H + h) * row_bytes + ch * 16;
-    *reinterpret_cast<uint4 *>(kp + dst) = *reinterpret_cast<const uint4 *>(kn + src);
-    *reinterpret_cast<uint4 *>(vp + dst) = *reinterpret_cast<const uint4 *>(vn + src);
-  }
+  const int64_t dst = ((blk * H + h) * kBlock + off) * row_bytes + ch * 16;
+  *reinterpret_cast<uint4 *>(kp + dst) = k;
+  *reinterpret_cast<uint4 *>(vp + dst) = v;
 }
 
 // One workgroup per copy pair: the whole block (all heads) of K and V, and the fp8 scales.
@@ -242,12 +247,14 @@ kvc_status kvc_append_contig(void *k_cache, void *v_cache, kvc_dtype dtype, int3
   if (!k_cache || !v_cache || !pos || !k_new || !v_new) return KVC_E_INVALID;
   if (!aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_new) || !aligned16(v_new))
     return KVC_E_INVALID;
-  const int64_t grid = static_cast<int64_t>(B) * n_tok;
+  const int32_t row_bytes = D * elt_bytes(dtype);
+  const int64_t threads = static_cast<int64_t>(B) * n_tok * H * (row_bytes / 16);
+  const int64_t grid = (threads + kThreads - 1) / kThreads;
   if (grid > INT32_MAX) return KVC_E_INVALID;
   hipLaunchKernelGGL(append_contig_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<char *>(k_cache),
                      static_cast<char *>(v_cache), static_cast<const char *>(k_new),
-                     static_cast<const char *>(v_new), pos, H, S_max, n_tok, D * elt_bytes(dtype));
+                     static_cast<const char *>(v_new), pos, B, H, S_max, n_tok, row_bytes);
   return launch_status();
 }
 
@@ -304,10 +311,14 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
     return launch_status();
   }
   if (new_dtype != layer->kv_dtype) return KVC_E_UNSUPPORTED;
-  hipLaunchKernelGGL(write_paged_kernel, dim3(n_tok), dim3(kThreads), 0, s,
+  const int32_t row_bytes = D * elt_bytes(layer->kv_dtype);
+  const int64_t threads = static_cast<int64_t>(n_tok) * H * (row_bytes / 16);
+  const int64_t grid = (threads + kThreads - 1) / kThreads;
+  if (grid > INT32_MAX) return KVC_E_INVALID;
+  hipLaunchKernelGGL(write_paged_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0, s,
                      static_cast<char *>(layer->k_pool), static_cast<char *>(layer->v_pool),
-                     static_cast<const char *>(k_new), static_cast<const char *>(v_new), slots, H,
-                     layer->num_blocks, D * elt_bytes(layer->kv_dtype));
+                     static_cast<const char *>(k_new), static_cast<const char *>(v_new), slots,
+                     n_tok, H, layer->num_blocks, row_bytes);
   return launch_status();
 }
 
