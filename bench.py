@@ -3,7 +3,10 @@
 One step = one decode step of the whole batch through every layer: host slot reservation
 (first fit / copy-on-write), block-table and length upload, then per layer the copy-on-write
 block copies, the new token's K/V write, decode attention pass 1 (split-context online
-softmax) and pass 2 (merge of split sequence-heads). Inputs are
+softmax) and pass 2 (merge of split sequence-heads). With `--append fused` (the default for
+f32/f16 caches) the new token's K/V is stored by pass 1 itself, which takes that row from the
+new K/V instead of reading it back; `--append separate` runs the cache writer first (always the
+case for e4m3 caches, whose block scale may change). Inputs are
 synthetic and already resident in device memory when timing starts; each step grows every
 sequence by one token.
 
@@ -41,6 +44,9 @@ def parse():
     ap.add_argument("--workload", default="llama13b-paged",
                     choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
+    ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
+                    help="store the new K/V inside attention pass 1 (fused) or with the cache "
+                         "writer first (separate); auto = fused unless the cache is e4m3")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv output) "
@@ -54,13 +60,14 @@ def parse():
 class PagedBench:
     """Paged workloads: LLaMA-13B shapes with drawn lengths, or fp8 long context."""
 
-    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev):
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
 
         import kv_cache_attention_kvc_amd as kvc
 
         self.kvc, self.torch, self.w, self.dev = kvc, torch, w, dev
         self.L = layers
+        self.fused = fused
         B, H, D = w.batch, w.heads, w.head_dim
         self.B, self.H, self.D = B, H, D
         if w.ctx:
@@ -129,17 +136,27 @@ class PagedBench:
         for li, layer in enumerate(self.layers):
             if ncow:
                 kvc.copy_blocks(layer, self.cow_d[0, :ncow], self.cow_d[1, :ncow])
-            kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
+            if not self.fused:
+                kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li, self.stream)
-            kvc.decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d, self.max_ctx,
-                                     scale=self.scale, out=self.out[li], workspace=self.ws)
+            if self.fused:
+                kvc.append_decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
+                                                self.knew[li], self.vnew[li], self.max_ctx,
+                                                scale=self.scale, out=self.out[li],
+                                                workspace=self.ws)
+            else:
+                kvc.decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d, self.max_ctx,
+                                         scale=self.scale, out=self.out[li], workspace=self.ws)
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li + 1, self.stream)
             kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
 
     def bytes_step(self, lens):
-        """Algorithmic HBM bytes of one step over all layers, and of one pass-1 launch."""
+        """Algorithmic HBM bytes of one step over all layers, and of one pass-1 launch: every
+        attended K/V row read once (the new one from the new-K/V buffer), the new rows written
+        once, block tables (and fp8 scales), lengths, q and out. The fused pass 1 also does the
+        write."""
         elt = ELT[self.w.kv_dtype]
         B, H, D = self.B, self.H, self.D
         kv = int(lens.sum()) * H * D * 2 * elt
@@ -147,8 +164,8 @@ class PagedBench:
         table = blocks * 4 + (blocks * 8 if self.w.kv_dtype == "e4m3" else 0) + B * 4
         qo = B * H * D * (2 + 2)
         append = B * H * D * 2 * elt + (B * 8 if self.w.kv_dtype == "e4m3" else 0)
-        pass1 = kv + table + qo
-        return (pass1 + append) * self.L, pass1
+        pass1 = kv + table + qo + (append if self.fused else 0)
+        return (kv + table + qo + append) * self.L, pass1
 
     def oracle_layer(self, li):
         """The CPU oracle's decode of one layer on the current state (for cpu_baseline and a
@@ -219,12 +236,13 @@ class ContigBench:
     attends. Tiny char-GPT: a 16-token prefill, then each step appends at the next position and
     attends (context 17 .. 256)."""
 
-    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev):
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
 
         import kv_cache_attention_kvc_amd as kvc
 
         self.kvc, self.torch, self.w, self.dev, self.L = kvc, torch, w, dev, layers
+        self.fused = fused
         B, H, D, S = w.batch, w.heads, w.head_dim, w.s_max
         self.B, self.H, self.D, self.S = B, H, D, S
         self.growing = "prefill" in w.extra
@@ -246,6 +264,8 @@ class ContigBench:
         torch.cuda.synchronize()
         self.knew = workloads.torch_normal((layers, B, 1, H, D), td, dev, w.seed * 7 + 1)
         self.vnew = workloads.torch_normal((layers, B, 1, H, D), td, dev, w.seed * 7 + 2)
+        self.knew3 = self.knew.view(layers, B, H, D)      # the same rows, [B, H, D] per layer
+        self.vnew3 = self.vnew.view(layers, B, H, D)
         self.q = workloads.torch_normal((layers, B, H, D), td, dev, w.seed * 7 + 3)
         self.out = torch.empty((layers, B, H, D), dtype=td, device=dev)
         self.ws = kvc.new_workspace(B, H, D, device=dev)
@@ -263,12 +283,20 @@ class ContigBench:
             self.len_d.fill_(self.pos + 1)
         self.lens_now[:] = self.pos + 1
         for li in range(self.L):
-            kvc.append_contig(self.kc[li], self.vc[li], self.pos_d, self.knew[li], self.vnew[li])
+            if not self.fused:
+                kvc.append_contig(self.kc[li], self.vc[li], self.pos_d, self.knew[li],
+                                  self.vnew[li])
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li, self.stream)
-            kvc.decode_partial_contig(self.q[li], self.kc[li], self.vc[li], self.len_d,
-                                      self.pos + 1, scale=self.scale, out=self.out[li],
-                                      workspace=self.ws)
+            if self.fused:
+                kvc.append_decode_partial_contig(self.q[li], self.kc[li], self.vc[li],
+                                                 self.len_d, self.knew3[li], self.vnew3[li],
+                                                 self.pos + 1, scale=self.scale,
+                                                 out=self.out[li], workspace=self.ws)
+            else:
+                kvc.decode_partial_contig(self.q[li], self.kc[li], self.vc[li], self.len_d,
+                                          self.pos + 1, scale=self.scale, out=self.out[li],
+                                          workspace=self.ws)
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li + 1, self.stream)
             kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
@@ -280,8 +308,9 @@ class ContigBench:
         B, H, D = self.B, self.H, self.D
         kv = int(lens.sum()) * H * D * 2 * elt
         qo = B * H * D * 2 * elt
-        pass1 = kv + qo + B * 4
-        return (pass1 + B * H * D * 2 * elt) * self.L, pass1
+        append = B * H * D * 2 * elt
+        pass1 = kv + qo + B * 4 + (append if self.fused else 0)
+        return (kv + qo + B * 4 + append) * self.L, pass1
 
     def oracle_layer(self, li):
         from oracle.caches import ContigCache
@@ -350,9 +379,10 @@ def pmc_summary(fetch_dir: str, write_dir: str, bench_log: str) -> dict:
             rec = json.loads(ln)
             alg = rec["roofline"]["algorithmic_bytes_per_launch"]
             src = rec["roofline"]["kernel_source_sha256_16"]
+            path = rec["config"]["append"]
     fetch_b = fk * 1024 * f_fac
     write_b = wk * 1024 * w_fac
-    return {"kernel": PASS1, "source_sha256_16": src, "dispatches": [nf, nw],
+    return {"kernel": PASS1, "source_sha256_16": src, "append": path, "dispatches": [nf, nw],
             "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
             "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5),
             "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
@@ -361,14 +391,14 @@ def pmc_summary(fetch_dir: str, write_dir: str, bench_log: str) -> dict:
             "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4) if alg else None}
 
 
-def measured_traffic():
+def measured_traffic(path: str):
     """Traffic per pass-1 launch from the committed counter summary, if it was taken on the
-    current kernel source (else None)."""
+    current kernel source with the same append path (else None)."""
     try:
         for ln in open(TRAFFIC_FILE):
             if ln.startswith("{"):
                 rec = json.loads(ln)
-                if rec.get("source_sha256_16") == source_hash():
+                if rec.get("source_sha256_16") == source_hash() and rec.get("append") == path:
                     return rec["traffic_bytes"]
     except OSError:
         pass
@@ -399,7 +429,12 @@ def main():
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev)
+    fused = args.append == "fused" or (args.append == "auto" and w.kv_dtype != "e4m3")
+    if fused and w.kv_dtype == "e4m3":
+        print("--append fused: e4m3 caches take the separate writer", file=sys.stderr)
+        sys.exit(2)
+    path = "fused" if fused else "separate"
+    bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev, fused)
     for _ in range(W):
         bench.step()
     torch.cuda.synchronize()
@@ -447,6 +482,7 @@ def main():
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
             if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
             "ctx_growth_per_step": 0 if w is workloads.LLAMA7B_CONTIG else 1,
+            "append": path,
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(w.batch * K / elapsed, 1),
@@ -458,7 +494,7 @@ def main():
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": measured_traffic() if w is workloads.LLAMA13B_PAGED else None,
+            "traffic": measured_traffic(path) if w is workloads.LLAMA13B_PAGED else None,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
             "kernel_source_sha256_16": source_hash(),

@@ -253,6 +253,49 @@ kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
                             void *workspace, size_t ws_bytes, void *stream);
 
+/* Append and attend in one pass ("LLM Inference Acceleration -- KV Cache", section 3.1: each
+ * decode step stores the new token's k/v in the cache and then attends over the whole cache,
+ * itself included). Same arguments and result as the matching kvc_decode_* call, plus
+ *   k_new, v_new: [B][H][D] of the cache's dtype (KVC_F32 or KVC_F16; e4m3 caches return
+ *                 KVC_E_UNSUPPORTED, their block scale needs kvc_write_paged), 16-byte aligned
+ * For every sequence with L_b >= 1 and every head, position L_b - 1 is the new token: its
+ * scores and values are taken from k_new/v_new, and the row is stored into the cache --
+ * contiguous: at [b][h][L_b-1]; paged: at offset (L_b-1) % 16 of block
+ * block_tables[b][(L_b-1) / 16] (skipped if that id is outside [0, num_blocks)). Output and
+ * cache contents equal those of kvc_write_paged / kvc_append_contig of the same rows followed
+ * by the plain decode call, bit for bit; one read of the cache is saved. Paged callers run
+ * kvc_append and kvc_block_table first, and kvc_copy_blocks for its copy-on-write pairs on the
+ * same stream before this call, so that the written block belongs to this sequence alone.
+ * k_cache and v_cache are written, so the contiguous variant takes them non-const. */
+kvc_status kvc_append_decode_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
+                                    void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                    const void *k_new, const void *v_new, int32_t B, int32_t H,
+                                    int32_t S_max, int32_t D, int32_t max_ctx, float scale,
+                                    void *out, kvc_dtype out_dtype, void *workspace,
+                                    size_t ws_bytes, void *stream);
+kvc_status kvc_append_decode_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *ctx_lens, const void *k_new, const void *v_new,
+                                   int32_t B, int32_t max_ctx, float scale, void *out,
+                                   kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                   void *stream);
+/* Pass 1 alone of the two calls above (the cache row is stored by pass 1); follow with
+ * kvc_decode_merge exactly as for kvc_decode_partial_*. */
+kvc_status kvc_append_decode_partial_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
+                                            void *v_cache, kvc_dtype kv_dtype,
+                                            const int32_t *ctx_lens, const void *k_new,
+                                            const void *v_new, int32_t B, int32_t H,
+                                            int32_t S_max, int32_t D, int32_t max_ctx, float scale,
+                                            void *out, kvc_dtype out_dtype, void *workspace,
+                                            size_t ws_bytes, void *stream);
+kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
+                                           const kvc_paged_layer *layer,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *ctx_lens, const void *k_new,
+                                           const void *v_new, int32_t B, int32_t max_ctx,
+                                           float scale, void *out, kvc_dtype out_dtype,
+                                           void *workspace, size_t ws_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,6 +20,8 @@ __all__ = [
     "F32", "F16", "E4M3", "BLOCK_SIZE", "workspace_bytes",
     "append_contig", "copy_blocks", "write_paged", "decode_attn_contig", "decode_attn_paged",
     "decode_partial_contig", "decode_partial_paged", "decode_merge", "new_workspace", "EXPORTS",
+    "append_decode_contig", "append_decode_paged", "append_decode_partial_contig",
+    "append_decode_partial_paged",
 ]
 
 F32, F16, E4M3 = 0, 1, 2
@@ -33,7 +35,8 @@ EXPORTS = [
     "kvc_fork", "kvc_free", "kvc_block_table", "kvc_stats", "kvc_check", "kvc_append_contig",
     "kvc_copy_blocks", "kvc_write_paged", "kvc_decode_workspace_bytes", "kvc_decode_attn_contig",
     "kvc_decode_attn_paged", "kvc_decode_partial_contig", "kvc_decode_partial_paged",
-    "kvc_decode_merge",
+    "kvc_decode_merge", "kvc_append_decode_contig", "kvc_append_decode_paged",
+    "kvc_append_decode_partial_contig", "kvc_append_decode_partial_paged",
 ]
 
 
@@ -114,6 +117,14 @@ def load_library() -> ctypes.CDLL:
         "kvc_decode_merge": (ctypes.c_int, [_I32, _I32, _I32, _P, ctypes.c_int, _P,
                                             ctypes.c_size_t, _P]),
     }
+    contig_append = [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32,
+                     _I32, _F, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]
+    paged_append = [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P, _I32, _P, _P, _P, _I32, _I32,
+                    _F, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]
+    for name in ("kvc_append_decode_contig", "kvc_append_decode_partial_contig"):
+        sig[name] = (ctypes.c_int, contig_append)
+    for name in ("kvc_append_decode_paged", "kvc_append_decode_partial_paged"):
+        sig[name] = (ctypes.c_int, paged_append)
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -432,3 +443,75 @@ def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, sca
         _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_attn_paged")
     return out
+
+
+def _check_new(k_new, v_new, B, H, D, dtype):
+    if tuple(k_new.shape) != (B, H, D) or tuple(v_new.shape) != (B, H, D):
+        raise ValueError("k_new/v_new must be [B, H, D]")
+    if k_new.dtype != dtype or v_new.dtype != dtype:
+        raise ValueError("k_new/v_new must have the cache dtype")
+
+
+def _append_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx, scale, out,
+                        workspace, stream):
+    B, H, S, D = k_cache.shape
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError("q must be [B, H, D]")
+    _check_new(k_new, v_new, B, H, D, k_cache.dtype)
+    out = _out_for(q, out)
+    ws = _workspace(B, H, D, workspace, q.device)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(ctx_lens), _ptr(k_new), _ptr(v_new), B, H, S, D, int(max_ctx), float(scale),
+        _ptr(out), _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def _append_paged_call(name, q, layer, block_tables, ctx_lens, k_new, v_new, max_ctx, scale, out,
+                       workspace, stream):
+    B = q.shape[0]
+    if tuple(q.shape) != (B, layer.heads, layer.head_dim):
+        raise ValueError("q must be [B, H, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    _check_new(k_new, v_new, B, layer.heads, layer.head_dim, layer.k_pool.dtype)
+    out = _out_for(q, out)
+    ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(ctx_lens), _ptr(k_new), _ptr(v_new), B, int(max_ctx), float(scale), _ptr(out),
+        _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def append_decode_contig(q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx, scale=None,
+                         out=None, workspace=None, stream=None):
+    """Store k_new/v_new [B,H,D] at position ctx_lens[b]-1 of the contiguous cache and attend
+    over positions [0, ctx_lens[b]) in the same pass. Returns out [B,H,D]."""
+    return _append_contig_call("kvc_append_decode_contig", q, k_cache, v_cache, ctx_lens, k_new,
+                               v_new, max_ctx, scale, out, workspace, stream)[0]
+
+
+def append_decode_partial_contig(q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx,
+                                 scale=None, out=None, workspace=None, stream=None):
+    """Pass 1 of append_decode_contig; returns (out, workspace) for decode_merge."""
+    return _append_contig_call("kvc_append_decode_partial_contig", q, k_cache, v_cache, ctx_lens,
+                               k_new, v_new, max_ctx, scale, out, workspace, stream)
+
+
+def append_decode_paged(q, layer: PagedLayer, block_tables, ctx_lens, k_new, v_new, max_ctx,
+                        scale=None, out=None, workspace=None, stream=None):
+    """Store k_new/v_new [B,H,D] at position ctx_lens[b]-1 of each sequence's blocks (after the
+    pool's append and its copy-on-write copies) and attend in the same pass. Returns out."""
+    return _append_paged_call("kvc_append_decode_paged", q, layer, block_tables, ctx_lens, k_new,
+                              v_new, max_ctx, scale, out, workspace, stream)[0]
+
+
+def append_decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, k_new, v_new,
+                                max_ctx, scale=None, out=None, workspace=None, stream=None):
+    """Pass 1 of append_decode_paged; returns (out, workspace) for decode_merge."""
+    return _append_paged_call("kvc_append_decode_partial_paged", q, layer, block_tables, ctx_lens,
+                              k_new, v_new, max_ctx, scale, out, workspace, stream)

@@ -67,6 +67,8 @@ struct DecodeArgs {
   const float *v_scale;
   const int32_t *tables;
   const int32_t *lens;
+  const char *k_new;  // append mode: the new token's K and V, [B][H][D]; else null
+  const char *v_new;
   void *out;
   int32_t *ws_hdr;
   int32_t *ws_pre;
@@ -97,6 +99,13 @@ __device__ __forceinline__ float group_sum(float x) {
 
 __device__ __forceinline__ int32_t sread(const int32_t *p) {
   return __builtin_amdgcn_readfirstlane(*p);
+}
+
+// Load of a wave-uniform address through the scalar cache (read-only data: block tables). Its
+// completion is counted apart from the vector loads, so waiting for it never waits for K/V.
+typedef const __attribute__((address_space(4))) int32_t const_i32;
+__device__ __forceinline__ int32_t sload(const int32_t *p) {
+  return *(const_i32 *)(p);
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -145,42 +154,47 @@ __device__ __forceinline__ float half_hi(uint32_t w) {
   return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w >> 16)));
 }
 
-// N consecutive q elements (fp16 or fp32) starting at element i, as floats, with 8- or 16-byte
-// vector loads and no branches (so the loads of a slice are all in flight together).
+// N consecutive q elements (fp16 or fp32) starting at element i, loaded as raw 32-bit words with
+// 8- or 16-byte vector loads and no branches (so the loads of a slice are all in flight together).
+// The words are converted only when the slice is used, so the load is never waited for early.
 template <bool QF16, int N>
-__device__ __forceinline__ void load_q(const void *p, int64_t i, float *x) {
-  if constexpr (QF16) {
-    const char *b = static_cast<const char *>(p) + i * 2;
-    if constexpr (N % 8 == 0) {
+struct QWords {
+  static constexpr int W = QF16 ? N / 2 : N;
+  uint32_t w[W];
+};
+
+template <bool QF16, int N>
+__device__ __forceinline__ void load_q_words(const void *p, int64_t i, QWords<QF16, N> &q) {
+  constexpr int W = QWords<QF16, N>::W;
+  const char *b = static_cast<const char *>(p) + i * (QF16 ? 2 : 4);
+  if constexpr (W % 4 == 0) {
 #pragma unroll
-      for (int k = 0; k < N / 8; ++k) {
-        const uint4 r = reinterpret_cast<const uint4 *>(b)[k];
-        const uint32_t w[4] = {r.x, r.y, r.z, r.w};
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          x[8 * k + 2 * u] = half_lo(w[u]);
-          x[8 * k + 2 * u + 1] = half_hi(w[u]);
-        }
-      }
-    } else {
-      static_assert(N == 4, "fp16 q slices are 4, 8 or 16 elements");
-      const uint2 r = *reinterpret_cast<const uint2 *>(b);
-      x[0] = half_lo(r.x);
-      x[1] = half_hi(r.x);
-      x[2] = half_lo(r.y);
-      x[3] = half_hi(r.y);
+    for (int k = 0; k < W / 4; ++k) {
+      const uint4 r = reinterpret_cast<const uint4 *>(b)[k];
+      q.w[4 * k] = r.x;
+      q.w[4 * k + 1] = r.y;
+      q.w[4 * k + 2] = r.z;
+      q.w[4 * k + 3] = r.w;
     }
   } else {
-    static_assert(N % 4 == 0, "fp32 q slices are a multiple of 4 elements");
-    const float4 *b = reinterpret_cast<const float4 *>(static_cast<const float *>(p) + i);
+    static_assert(W == 2, "q slices are 8 bytes or a multiple of 16");
+    const uint2 r = *reinterpret_cast<const uint2 *>(b);
+    q.w[0] = r.x;
+    q.w[1] = r.y;
+  }
+}
+
+template <bool QF16, int N>
+__device__ __forceinline__ void q_floats(const QWords<QF16, N> &q, float *x) {
+  if constexpr (QF16) {
 #pragma unroll
-    for (int k = 0; k < N / 4; ++k) {
-      const float4 r = b[k];
-      x[4 * k] = r.x;
-      x[4 * k + 1] = r.y;
-      x[4 * k + 2] = r.z;
-      x[4 * k + 3] = r.w;
+    for (int u = 0; u < N / 2; ++u) {
+      x[2 * u] = half_lo(q.w[u]);
+      x[2 * u + 1] = half_hi(q.w[u]);
     }
+  } else {
+#pragma unroll
+    for (int u = 0; u < N; ++u) x[u] = __uint_as_float(q.w[u]);
   }
 }
 
@@ -209,10 +223,11 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float x, bool f16
 }
 
 // ---- per-workgroup prefix of block counts ------------------------------------------------
-// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences. Each thread
-// sums a run of consecutive sequences; runs are scanned with wave shuffles, then across the
-// four waves through LDS.
-__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *wsum) {
+// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences, and
+// len[b] = clamp(L_b), all in LDS. Each thread sums a run of consecutive sequences; runs are
+// scanned with wave shuffles, then across the four waves through LDS.
+__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *len,
+                             int32_t *wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
@@ -237,6 +252,7 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
   for (int i = lo; i < hi; ++i) {
     pre[i] = run;
     const int32_t L = min(max(lens[i], 0), cap);
+    len[i] = L;
     run += (L + kBlock - 1) / kBlock;
   }
   if (tid == kWgThreads - 1) pre[B] = inc;
@@ -244,26 +260,37 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
 }
 
 // ---- one tile: loads ---------------------------------------------------------------------
-template <int KV, int D>
+// Every fetch issues the same loads -- the q slice of the tile's sequence-head, then LOADS
+// 16-byte loads of K and of V -- whatever the tile, so the compiler can count exactly how many
+// loads follow a tile's and wait for that tile alone when it is consumed.
+template <int KV, int D, bool QF16>
 struct TileRegs {
   using G = Geo<KV, D>;
+  QWords<QF16, G::EPL> q;
   uint4 k[G::LOADS];
   uint4 v[G::LOADS];
-  int32_t nt;    // valid rows (0 when the block id is out of range)
-  float ks, vs;  // fp8 block scales
+  int32_t nt;       // valid rows (0: the tile contributes nothing)
+  int32_t new_row;  // append mode: the row of the new token in this tile, else -1
+  const char *kt;   // the tile's K and V in the cache (where the new row is stored)
+  const char *vt;
+  float ks, vs;     // fp8 block scales
 };
 
-template <bool PAGED, int KV, int D>
-__device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D> &t, int64_t bh,
-                                           int32_t h, int32_t j, int32_t phys, int32_t L, int g,
-                                           int c) {
+// Tile j of sequence-head (b, h) = bh; phys is its block id (paged). live = false fetches a
+// stand-in with nt = 0 (the first row of block 0 / of the sequence-head), for the step after a
+// chunk's last tile.
+template <bool PAGED, int KV, int D, bool QF16>
+__device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, QF16> &t,
+                                           int64_t bh, int32_t h, int32_t j, int32_t phys,
+                                           int32_t L, bool live, int g, int c) {
   using G = Geo<KV, D>;
+  load_q_words<QF16, G::EPL>(a.q, bh * D + c * G::EPL, t.q);
   const char *kt;
   const char *vt;
-  bool valid = true;
+  bool valid = live;
   if constexpr (PAGED) {
     // addresses are formed from a clamped id, so nothing outside the pools is ever addressed
-    valid = static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
+    valid = valid && static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
     const int32_t sp = valid ? phys : 0;
     const int64_t toff = (static_cast<int64_t>(sp) * a.H + h) * G::TILE;
     kt = a.k + toff;
@@ -273,37 +300,79 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D> 
       t.vs = valid ? a.v_scale[sp] : 0.f;
     }
   } else {
-    const int64_t toff = (bh * a.seq_stride + static_cast<int64_t>(kBlock) * j) * G::ROW;
+    const int64_t toff = (bh * a.seq_stride + static_cast<int64_t>(kBlock) * (valid ? j : 0)) *
+                         G::ROW;
     kt = a.k + toff;
     vt = a.v + toff;
   }
   t.nt = valid ? min(kBlock, L - kBlock * j) : 0;
-  const int lane_off = g * G::ROW + c * 16;
-  if (t.nt == kBlock) {
+  t.kt = kt;
+  t.vt = vt;
+  // append mode: the tile holding position L-1 takes that row from k_new/v_new (the lanes of
+  // that row load from there instead of the cache) and stores it into the cache when consumed.
+  // That tile is the last of its sequence-head, so it always takes the general path below and
+  // the full-tile path carries no per-lane address choice.
+  t.new_row = (a.k_new && t.nt > 0 && j == (L - 1) / kBlock) ? (L - 1) % kBlock : -1;
+  if (t.nt == kBlock && t.new_row < 0) {
+    const int lane_off = g * G::ROW + c * 16;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
       t.k[i] = load_stream(kt + lane_off + i * G::TPL * G::ROW);
       t.v[i] = load_stream(vt + lane_off + i * G::TPL * G::ROW);
     }
   } else {
+    // rows past the end load the last valid row again (the same cache lines, so no extra
+    // traffic; with nt = 0, row 0): their scores are masked to -inf, so they weigh 0
+    const int64_t new_off = bh * G::ROW + c * 16;
+    const int last_row = max(t.nt, 1) - 1;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
-      if (g + i * G::TPL < t.nt) {
-        t.k[i] = load_stream(kt + lane_off + i * G::TPL * G::ROW);
-        t.v[i] = load_stream(vt + lane_off + i * G::TPL * G::ROW);
-      } else {
-        t.k[i] = make_uint4(0, 0, 0, 0);
-        t.v[i] = make_uint4(0, 0, 0, 0);
-      }
+      const int row = min(g + i * G::TPL, last_row);
+      const bool nw = row == t.new_row;
+      t.k[i] = load_stream(nw ? a.k_new + new_off : kt + row * G::ROW + c * 16);
+      t.v[i] = load_stream(nw ? a.v_new + new_off : vt + row * G::ROW + c * 16);
+    }
+  }
+}
+
+// Append mode: store the new token's row (already in registers) into the cache.
+template <int KV, int D, bool QF16>
+__device__ __forceinline__ void store_new_row(const TileRegs<KV, D, QF16> &t, int g, int c) {
+  using G = Geo<KV, D>;
+  if (t.new_row < 0) return;
+  const int lane_off = g * G::ROW + c * 16;
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    if (g + i * G::TPL == t.new_row) {
+      *reinterpret_cast<uint4 *>(const_cast<char *>(t.kt) + lane_off + i * G::TPL * G::ROW) =
+          t.k[i];
+      *reinterpret_cast<uint4 *>(const_cast<char *>(t.vt) + lane_off + i * G::TPL * G::ROW) =
+          t.v[i];
     }
   }
 }
 
 // ---- one tile: online-softmax update of the group state ---------------------------------
-template <int KV, int D>
-__device__ __forceinline__ void consume_tile(const TileRegs<KV, D> &t, const float *qv, float cl2,
-                                             int g, float &m, float &l, float *acc) {
+// Rows at or past nt get score -inf (weight 0); their V registers hold a valid row's data.
+// A tile with nt = 0 adds nothing (its registers may hold anything), but its registers are
+// still read (by an empty asm statement), so that no load into them stays outstanding into the
+// fetch that next reuses them: that fetch must not wait.
+template <int KV, int D, bool QF16>
+__device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16> &t, float cl2, int g,
+                                             float &m, float &l, float *acc) {
   using G = Geo<KV, D>;
+  if (t.nt <= 0) {
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      asm volatile("" ::"v"(t.k[i].x), "v"(t.k[i].y), "v"(t.k[i].z), "v"(t.k[i].w));
+      asm volatile("" ::"v"(t.v[i].x), "v"(t.v[i].y), "v"(t.v[i].z), "v"(t.v[i].w));
+    }
+#pragma unroll
+    for (int u = 0; u < QWords<QF16, G::EPL>::W; ++u) asm volatile("" ::"v"(t.q.w[u]));
+    return;
+  }
+  float qv[G::EPL];
+  q_floats<QF16, G::EPL>(t.q, qv);
   float s[G::LOADS];
   const float sc = (KV == KVC_E4M3) ? cl2 * t.ks : cl2;
 #pragma unroll
@@ -346,13 +415,15 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D> &t, const flo
 // A segment is the part of one (sequence, head) pair that lies in the chunk: tiles j0 .. j0+n-1.
 struct Seg {
   int32_t b, h, j0, n, L;
+  int32_t ph0, ph1;  // paged: block ids of the segment's first two tiles (-1 past the end)
   bool cut_start, cut_end;
 };
 
 // Next segment of the chunk starting at tile f (b is a cursor over sequences that only moves
 // forward). Returns false at the end of the chunk.
-__device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre, int32_t &f,
-                                         int32_t f1, int32_t &b, Seg &s) {
+__device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre,
+                                         const int32_t *len, int32_t &f, int32_t f1, int32_t &b,
+                                         Seg &s) {
   if (f >= f1) return false;
   while (a.H * sread(pre + b + 1) <= f) ++b;
   const int32_t nb = sread(pre + b + 1) - sread(pre + b);
@@ -366,28 +437,24 @@ __device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre
   s.n = e - f;
   s.cut_start = s.j0 > 0;
   s.cut_end = e < seg_end;
-  s.L = min(max(a.lens[b], 0), a.cap);
+  s.L = sread(len + b);
   f = e;
   return true;
 }
 
-// Per-segment registers: the query slice of this lane's column and (paged) the physical block
-// ids of the segment's first 64 tiles, one per lane.
-template <int EPL>
-struct SegRegs {
-  Seg s;
-  float q[EPL];
-  int32_t win;
-};
-
-template <bool PAGED, bool QF16, int EPL>
-__device__ __forceinline__ void load_seg(const DecodeArgs &a, SegRegs<EPL> &r, int D, int c,
-                                         int lane) {
-  const int64_t bh = static_cast<int64_t>(r.s.b) * a.H + r.s.h;
-  load_q<QF16, EPL>(a.q, bh * D + c * EPL, r.q);
-  if constexpr (PAGED)
-    r.win = lane < r.s.n ? a.tables[static_cast<int64_t>(r.s.b) * a.mbps + r.s.j0 + lane] : -1;
+// Block id of tile j of sequence b (scalar load).
+__device__ __forceinline__ int32_t block_id(const DecodeArgs &a, int32_t b, int32_t j) {
+  return sload(a.tables + static_cast<int64_t>(b) * a.mbps + j);
 }
+
+template <bool PAGED>
+__device__ __forceinline__ void seg_ids(const DecodeArgs &a, Seg &s) {
+  if constexpr (PAGED) {
+    s.ph0 = block_id(a, s.b, s.j0);
+    s.ph1 = s.n > 1 ? block_id(a, s.b, s.j0 + 1) : -1;
+  }
+}
+
 
 // Finish a segment: combine the TPL lane groups, then either write the output row (the whole
 // pair was in this chunk) or leave a record (slot 0 if the pair began before the chunk, else 1).
@@ -423,94 +490,74 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
 }
 
 // Walk the chunk [f0, f1) tile by tile as one pipeline: while tile t is consumed, tile t+1 is in
-// flight -- also across segment boundaries, whose q slice and block ids are loaded one segment
-// ahead -- so a new segment starts without a stall on its first loads.
+// flight, also across segment boundaries. Every step issues one fetch of the same shape (after
+// the chunk's last tile, a stand-in that is not consumed), so waiting for the tile about to be
+// consumed never waits for the one just issued. Paged block ids come through the scalar cache
+// one tile ahead of their use (a segment's first two when the segment is found).
 template <bool PAGED, int KV, int D, bool QF16>
-__device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre, int32_t f0,
-                                          int32_t f1, int32_t b0, int32_t w) {
+__device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre,
+                                          const int32_t *len, int32_t f0, int32_t f1, int32_t b0,
+                                          int32_t w) {
   using G = Geo<KV, D>;
+  using Tile = TileRegs<KV, D, QF16>;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane / G::LPT;
   const int c = lane % G::LPT;
   int32_t f = f0, bcur = b0;
 
-  SegRegs<G::EPL> cur, nxt;
-  next_seg(a, pre, f, f1, bcur, cur.s);  // f0 < f1, so there is a first segment
-  load_seg<PAGED, QF16, G::EPL>(a, cur, D, c, lane);
-  bool has_nxt = next_seg(a, pre, f, f1, bcur, nxt.s);
-  if (has_nxt) load_seg<PAGED, QF16, G::EPL>(a, nxt, D, c, lane);
-
-  // block ids of tiles wb .. wb+63 of the current segment are in cur.win; the next 64 are
-  // prefetched into `ahead` once half of the window has been used
-  int32_t wb = 0;
-  int32_t ahead = -1;
-  auto phys_cur = [&](int32_t k) -> int32_t {
-    if constexpr (PAGED) {
-      if (k - wb == 64) {
-        cur.win = ahead;
-        wb += 64;
-      }
-      if (k - wb == 32 && wb + 64 < cur.s.n) {
-        const int32_t idx = wb + 64 + lane;
-        ahead = idx < cur.s.n
-                    ? a.tables[static_cast<int64_t>(cur.s.b) * a.mbps + cur.s.j0 + idx]
-                    : -1;
-      }
-      return __builtin_amdgcn_readlane(cur.win, k - wb);
-    } else {
-      return 0;
-    }
-  };
-  auto phys_first = [&](const SegRegs<G::EPL> &r) -> int32_t {
-    if constexpr (PAGED) return __builtin_amdgcn_readlane(r.win, 0);
-    else return 0;
-  };
-  auto fetch = [&](TileRegs<KV, D> &t, const Seg &s, int32_t k, int32_t phys) {
-    const int64_t bh = static_cast<int64_t>(s.b) * a.H + s.h;
-    fetch_tile<PAGED, KV, D>(a, t, bh, s.h, s.j0 + k, phys, s.L, g, c);
-  };
+  Seg cur, nxt;
+  next_seg(a, pre, len, f, f1, bcur, cur);  // f0 < f1, so there is a first segment
+  seg_ids<PAGED>(a, cur);
+  bool has_nxt = next_seg(a, pre, len, f, f1, bcur, nxt);
+  if (has_nxt) seg_ids<PAGED>(a, nxt);
 
   float m = kFloor, l = 0.f;
   float acc[G::EPL];
 #pragma unroll
   for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
 
-  int32_t i = 0;  // index, within the current segment, of the tile being consumed
-  // one pipeline step: issue the next tile into `nb`, consume `cb`; false when the chunk is done
-  auto step = [&](TileRegs<KV, D> &cb, TileRegs<KV, D> &nb) -> bool {
-    const bool last = i + 1 == cur.s.n;
-    if (!last || has_nxt) {
-      // one load site for both cases (scalar selects pick the tile), so the compiler keeps a
-      // single set of loads in flight across the consume below
-      const int32_t ph = last ? phys_first(nxt) : phys_cur(i + 1);
-      Seg ns;
-      ns.b = last ? nxt.s.b : cur.s.b;
-      ns.h = last ? nxt.s.h : cur.s.h;
-      ns.j0 = last ? nxt.s.j0 : cur.s.j0;
-      ns.L = last ? nxt.s.L : cur.s.L;
-      fetch(nb, ns, last ? 0 : i + 1, ph);
+  int32_t i = 0;        // index, within the current segment, of the tile being consumed
+  int32_t ph_next = 0;  // paged: block id of tile i+1 of the current segment (-1 past its end)
+  if constexpr (PAGED) ph_next = cur.ph1;
+  // one pipeline step: issue the next fetch into `nb`, consume `cb`; false when the chunk is done
+  auto step = [&](Tile &cb, Tile &nb) -> bool {
+    const bool last = i + 1 == cur.n;
+    const bool to_nxt = last && has_nxt;
+    {
+      // one load site (scalar selects pick the tile): the next tile of this segment, the first
+      // of the next one, or after the chunk's end a stand-in
+      const int32_t ph = to_nxt ? nxt.ph0 : ph_next;
+      const int32_t b = to_nxt ? nxt.b : cur.b;
+      const int32_t h = to_nxt ? nxt.h : cur.h;
+      const int32_t j = to_nxt ? nxt.j0 : cur.j0 + i + 1;
+      const int32_t L = to_nxt ? nxt.L : cur.L;
+      fetch_tile<PAGED, KV, D, QF16>(a, nb, static_cast<int64_t>(b) * a.H + h, h, j, ph, L,
+                                     !last || has_nxt, g, c);
     }
-    consume_tile<KV, D>(cb, cur.q, a.cl2, g, m, l, acc);
+    if constexpr (PAGED) ph_next = i + 2 < cur.n ? block_id(a, cur.b, cur.j0 + i + 2) : -1;
+    consume_tile<KV, D, QF16>(cb, a.cl2, g, m, l, acc);
+    store_new_row<KV, D, QF16>(cb, g, c);
     if (!last) {
       ++i;
       return true;
     }
-    finish_seg<KV, D>(a, cur.s, w, g, c, m, l, acc);
+    finish_seg<KV, D>(a, cur, w, g, c, m, l, acc);
     if (!has_nxt) return false;
     cur = nxt;
     i = 0;
-    wb = 0;
+    if constexpr (PAGED) ph_next = cur.ph1;
     m = kFloor;
     l = 0.f;
 #pragma unroll
     for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
-    has_nxt = next_seg(a, pre, f, f1, bcur, nxt.s);
-    if (has_nxt) load_seg<PAGED, QF16, G::EPL>(a, nxt, D, c, lane);
+    has_nxt = next_seg(a, pre, len, f, f1, bcur, nxt);
+    if (has_nxt) seg_ids<PAGED>(a, nxt);
     return true;
   };
 
-  TileRegs<KV, D> ta, tb;
-  fetch(ta, cur.s, 0, phys_first(cur));
+  Tile ta, tb;
+  fetch_tile<PAGED, KV, D, QF16>(a, ta, static_cast<int64_t>(cur.b) * a.H + cur.h, cur.h, cur.j0,
+                                 PAGED ? cur.ph0 : 0, cur.L, true, g, c);
   for (;;) {
     if (!step(ta, tb)) break;
     if (!step(tb, ta)) break;
@@ -521,8 +568,9 @@ template <bool PAGED, int KV, int D, bool QF16>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t *pre = smem;
-  int32_t *wsum = smem + a.B + 1;
-  block_prefix(a.lens, a.B, a.cap, pre, wsum);
+  int32_t *len = smem + a.B + 1;
+  int32_t *wsum = len + a.B;
+  block_prefix(a.lens, a.B, a.cap, pre, len, wsum);
 
   const int32_t total = a.H * pre[a.B];
   const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
@@ -547,7 +595,7 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
     const int32_t mid = (lo + hi + 1) >> 1;
     if (a.H * sread(pre + mid) <= f) lo = mid; else hi = mid - 1;
   }
-  run_chunk<PAGED, KV, D, QF16>(a, pre, f, f1, lo, w);
+  run_chunk<PAGED, KV, D, QF16>(a, pre, len, f, f1, lo, w);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -721,7 +769,7 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
                   : pick_kernel<false>(kv_dtype, D, a.q_f16);
   if (!pl.kern) return KVC_E_UNSUPPORTED;
   pl.grid = static_cast<int>(P / kWgWaves);
-  pl.shmem = (static_cast<size_t>(B) + 1 + kWgWaves) * sizeof(int32_t);
+  pl.shmem = (2 * static_cast<size_t>(B) + 1 + kWgWaves) * sizeof(int32_t);
   return KVC_OK;
 }
 
@@ -736,6 +784,65 @@ kvc_status launch_partial(const PartialPlan &pl, void *stream) {
 
 using namespace kvc;
 
+// Pass 1 for both layouts; k_new/v_new non-null selects append mode.
+static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+                                 const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                 const void *k_new, const void *v_new, int32_t B, int32_t H,
+                                 int32_t S_max, int32_t D, int32_t max_ctx, float scale, void *out,
+                                 kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                 void *stream) {
+  if (S_max < 0) return KVC_E_INVALID;
+  if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
+  PartialPlan pl;
+  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, D, S_max, max_ctx,
+                               scale, out, out_dtype, workspace, ws_bytes, pl);
+  if (st != KVC_OK || pl.grid == 0) return st;
+  if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
+  if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVC_E_INVALID;
+  pl.a.k = static_cast<const char *>(k_cache);
+  pl.a.v = static_cast<const char *>(v_cache);
+  pl.a.k_new = static_cast<const char *>(k_new);
+  pl.a.v_new = static_cast<const char *>(v_new);
+  pl.a.seq_stride = S_max;
+  return launch_partial(pl, stream);
+}
+
+static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
+                                const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                const int32_t *ctx_lens, const void *k_new, const void *v_new,
+                                int32_t B, int32_t max_ctx, float scale, void *out,
+                                kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                void *stream) {
+  if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
+    return KVC_E_INVALID;
+  if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
+  const kvc_dtype kv = layer->kv_dtype;
+  if (kv != KVC_F32 && kv != KVC_F16 && kv != KVC_E4M3) return KVC_E_UNSUPPORTED;
+  if (k_new && kv == KVC_E4M3) return KVC_E_UNSUPPORTED;  // the block scale may change
+  PartialPlan pl;
+  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads,
+                               layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, scale, out,
+                               out_dtype, workspace, ws_bytes, pl);
+  if (st != KVC_OK || pl.grid == 0) return st;
+  if (!block_tables || !layer->k_pool || !layer->v_pool || !aligned16(layer->k_pool) ||
+      !aligned16(layer->v_pool))
+    return KVC_E_INVALID;
+  if (kv == KVC_E4M3 && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
+  if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVC_E_INVALID;
+  pl.a.k = static_cast<const char *>(layer->k_pool);
+  pl.a.v = static_cast<const char *>(layer->v_pool);
+  pl.a.k_scale = layer->k_scale;
+  pl.a.v_scale = layer->v_scale;
+  pl.a.tables = block_tables;
+  pl.a.mbps = max_blocks_per_seq;
+  pl.a.num_blocks = layer->num_blocks;
+  pl.a.k_new = static_cast<const char *>(k_new);
+  pl.a.v_new = static_cast<const char *>(v_new);
+  return launch_partial(pl, stream);
+}
+
 extern "C" {
 
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D) {
@@ -749,17 +856,8 @@ kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const voi
                                      int32_t D, int32_t max_ctx, float scale, void *out,
                                      kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                      void *stream) {
-  if (S_max < 0) return KVC_E_INVALID;
-  if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
-  PartialPlan pl;
-  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, D, S_max, max_ctx,
-                               scale, out, out_dtype, workspace, ws_bytes, pl);
-  if (st != KVC_OK || pl.grid == 0) return st;
-  if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
-  pl.a.k = static_cast<const char *>(k_cache);
-  pl.a.v = static_cast<const char *>(v_cache);
-  pl.a.seq_stride = S_max;
-  return launch_partial(pl, stream);
+  return partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B, H,
+                        S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
@@ -767,28 +865,32 @@ kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                     int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
                                     int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                                     void *workspace, size_t ws_bytes, void *stream) {
-  if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
-    return KVC_E_INVALID;
-  if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
-  const kvc_dtype kv = layer->kv_dtype;
-  if (kv != KVC_F32 && kv != KVC_F16 && kv != KVC_E4M3) return KVC_E_UNSUPPORTED;
-  PartialPlan pl;
-  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads,
-                               layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, scale, out,
-                               out_dtype, workspace, ws_bytes, pl);
-  if (st != KVC_OK || pl.grid == 0) return st;
-  if (!block_tables || !layer->k_pool || !layer->v_pool || !aligned16(layer->k_pool) ||
-      !aligned16(layer->v_pool))
-    return KVC_E_INVALID;
-  if (kv == KVC_E4M3 && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
-  pl.a.k = static_cast<const char *>(layer->k_pool);
-  pl.a.v = static_cast<const char *>(layer->v_pool);
-  pl.a.k_scale = layer->k_scale;
-  pl.a.v_scale = layer->v_scale;
-  pl.a.tables = block_tables;
-  pl.a.mbps = max_blocks_per_seq;
-  pl.a.num_blocks = layer->num_blocks;
-  return launch_partial(pl, stream);
+  return partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                       nullptr, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_partial_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
+                                            void *v_cache, kvc_dtype kv_dtype,
+                                            const int32_t *ctx_lens, const void *k_new,
+                                            const void *v_new, int32_t B, int32_t H,
+                                            int32_t S_max, int32_t D, int32_t max_ctx, float scale,
+                                            void *out, kvc_dtype out_dtype, void *workspace,
+                                            size_t ws_bytes, void *stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  return partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H,
+                        S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
+                                           const kvc_paged_layer *layer,
+                                           const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                           const int32_t *ctx_lens, const void *k_new,
+                                           const void *v_new, int32_t B, int32_t max_ctx,
+                                           float scale, void *out, kvc_dtype out_dtype,
+                                           void *workspace, size_t ws_bytes, void *stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  return partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new, v_new,
+                       B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
@@ -838,6 +940,35 @@ kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_pag
   kvc_status st = kvc_decode_partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq,
                                            ctx_lens, B, max_ctx, scale, out, out_dtype, workspace,
                                            ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
+                          ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
+                                    void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                    const void *k_new, const void *v_new, int32_t B, int32_t H,
+                                    int32_t S_max, int32_t D, int32_t max_ctx, float scale,
+                                    void *out, kvc_dtype out_dtype, void *workspace,
+                                    size_t ws_bytes, void *stream) {
+  kvc_status st = kvc_append_decode_partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype,
+                                                   ctx_lens, k_new, v_new, B, H, S_max, D,
+                                                   max_ctx, scale, out, out_dtype, workspace,
+                                                   ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_merge(B, H, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
+                                   const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                   const int32_t *ctx_lens, const void *k_new, const void *v_new,
+                                   int32_t B, int32_t max_ctx, float scale, void *out,
+                                   kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+  kvc_status st = kvc_append_decode_partial_paged(q, q_dtype, layer, block_tables,
+                                                  max_blocks_per_seq, ctx_lens, k_new, v_new, B,
+                                                  max_ctx, scale, out, out_dtype, workspace,
+                                                  ws_bytes, stream);
   if (st != KVC_OK) return st;
   return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
                           ws_bytes, stream);
