@@ -38,7 +38,7 @@ constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
-constexpr int kWavesPerCu = 8;     // pass-1 wavefronts per compute unit
+constexpr int kStage = 4;          // finished segments a wavefront holds in LDS before storing
 constexpr int kMaxBatch = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' is never NaN)
@@ -86,6 +86,28 @@ __device__ __forceinline__ float dpp(float x) {
       float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
 }
 
+// The value of x in this lane and in a partner lane OFF lanes away, as an unordered pair
+// {a, b} (so a symmetric combination of a and b is the same in both lanes). OFF = 32 and 16 use
+// the gfx950 lane-swap instructions (halves of the wave, neighbouring rows of 16); OFF = 8 and 4
+// rotate within a row of 16 (row_ror), which pairs lane i with lane i+OFF mod 16.
+template <int OFF>
+__device__ __forceinline__ void lane_pair(float x, float &a, float &b) {
+  const uint32_t u = __float_as_uint(x);
+  if constexpr (OFF == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else if constexpr (OFF == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    a = __uint_as_float(r[0]);
+    b = __uint_as_float(r[1]);
+  } else {
+    static_assert(OFF == 8 || OFF == 4, "lane distance 4, 8, 16 or 32");
+    a = x;
+    b = dpp<0x120 + OFF>(x);  // row_ror:OFF
+  }
+}
+
 // Sum over aligned groups of N lanes; every lane of a group gets the same bits.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
@@ -93,7 +115,11 @@ __device__ __forceinline__ float group_sum(float x) {
   x += dpp<0x4E>(x);  // quad_perm [2,3,0,1]: lane ^ 2
   if constexpr (N >= 8) x += dpp<0x141>(x);   // row_half_mirror: the other quad of 8
   if constexpr (N >= 16) x += dpp<0x140>(x);  // row_mirror: the other half of 16
-  if constexpr (N >= 32) x += __shfl_xor(x, 16);
+  if constexpr (N >= 32) {
+    float a, b;
+    lane_pair<16>(x, a, b);  // the neighbouring row
+    x = a + b;
+  }
   return x;
 }
 
@@ -421,23 +447,36 @@ struct Seg {
 
 // Next segment of the chunk starting at tile f (b is a cursor over sequences that only moves
 // forward). Returns false at the end of the chunk.
+// The sequence a chunk cursor is in: its index, first tile H*pre[b], tiles per head and length
+// (read from LDS once per sequence, not once per segment).
+struct SeqCur {
+  int32_t b, base, nb, L;
+};
+
+__device__ __forceinline__ void load_seq(const DecodeArgs &a, const int32_t *pre,
+                                         const int32_t *len, int32_t b, SeqCur &q) {
+  const int32_t p0 = sread(pre + b);
+  q.b = b;
+  q.base = a.H * p0;
+  q.nb = sread(pre + b + 1) - p0;
+  q.L = sread(len + b);
+}
+
 __device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre,
-                                         const int32_t *len, int32_t &f, int32_t f1, int32_t &b,
+                                         const int32_t *len, int32_t &f, int32_t f1, SeqCur &q,
                                          Seg &s) {
   if (f >= f1) return false;
-  while (a.H * sread(pre + b + 1) <= f) ++b;
-  const int32_t nb = sread(pre + b + 1) - sread(pre + b);
-  const int32_t base = a.H * sread(pre + b);
-  const int32_t rel = f - base;
-  s.b = b;
-  s.h = rel / nb;
-  s.j0 = rel - s.h * nb;
-  const int32_t seg_end = base + (s.h + 1) * nb;
+  while (f >= q.base + a.H * q.nb) load_seq(a, pre, len, q.b + 1, q);  // f < total: ends
+  const int32_t rel = f - q.base;
+  s.b = q.b;
+  s.h = rel / q.nb;
+  s.j0 = rel - s.h * q.nb;
+  const int32_t seg_end = q.base + (s.h + 1) * q.nb;
   const int32_t e = min(f1, seg_end);
   s.n = e - f;
   s.cut_start = s.j0 > 0;
   s.cut_end = e < seg_end;
-  s.L = sread(len + b);
+  s.L = q.L;
   f = e;
   return true;
 }
@@ -456,37 +495,93 @@ __device__ __forceinline__ void seg_ids(const DecodeArgs &a, Seg &s) {
 }
 
 
-// Finish a segment: combine the TPL lane groups, then either write the output row (the whole
-// pair was in this chunk) or leave a record (slot 0 if the pair began before the chunk, else 1).
+// One level of the combination of lane groups' states (running max m, sum l, output acc): each
+// lane merges its state with the one OFF lanes away. The merge is symmetric in the two states,
+// so after the levels for OFF = LPT, 2*LPT, ..., 32 lane group 0 holds the whole segment's.
+template <int OFF, int EPL>
+__device__ __forceinline__ void merge_lanes(float &m, float &l, float *acc) {
+  float ma, mb, la, lb;
+  lane_pair<OFF>(m, ma, mb);
+  lane_pair<OFF>(l, la, lb);
+  const float M = fmaxf(ma, mb);
+  const float fa = __builtin_amdgcn_exp2f(ma - M);
+  const float fb = __builtin_amdgcn_exp2f(mb - M);
+  l = la * fa + lb * fb;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) {
+    float xa, xb;
+    lane_pair<OFF>(acc[e], xa, xb);
+    acc[e] = xa * fa + xb * fb;
+  }
+  m = M;
+}
+
+// LDS of a pass-1 workgroup: pre[B+1], len[B], wsum[kWgWaves], then (16-byte aligned) the
+// stages of its wavefronts.
+__host__ __device__ inline int32_t stage_offset(int32_t B) { return (2 * B + 1 + kWgWaves + 3) & ~3; }
+
+// Finished segments wait in LDS until the wavefront's loads are done (or the stage is full), so
+// that no global store sits between a tile's loads and the wait for them: a wait for loads on
+// this GPU also waits for every store issued before it. An entry is D+4 floats: the combined
+// unnormalised output, then m, l and the destination (int bits: >= 0 the output row b*H+h;
+// < 0 the record slot -1-slot).
+struct Stage {
+  float *base;  // this wavefront's kStage entries
+  int32_t n;    // entries in use
+};
+
+// Store the staged entries: output rows normalised by 1/l (fp16 rounded to nearest even, or
+// fp32), records copied with their m and l. Every lane takes columns lane, lane+64, ...
+template <int D>
+__device__ __forceinline__ void flush_stage(const DecodeArgs &a, Stage &st) {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int lane = threadIdx.x & (kWave - 1);
+  for (int32_t k = 0; k < st.n; ++k) {
+    const float *e = st.base + k * (D + 4);
+    const int32_t dest = __float_as_int(e[D + 2]);
+    if (dest >= 0) {
+      const float l = e[D + 1];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+#pragma unroll
+      for (int d = lane; d < D; d += kWave)
+        store_elem(a.out, static_cast<int64_t>(dest) * D + d, e[d] * inv, a.out_f16);
+    } else {
+      float *r = a.ws_rec + static_cast<int64_t>(-1 - dest) * (D + 4);
+      for (int d = lane; d < D + 2; d += kWave) r[d] = e[d];
+    }
+  }
+  st.n = 0;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Finish a segment: combine the TPL lane groups, then stage either the output row (the whole
+// pair was in this chunk) or a record (slot 0 if the pair began before the chunk, else 1).
 template <int KV, int D>
 __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, int32_t w, int g,
-                                           int c, float m, float l, float *acc) {
+                                           int c, float m, float l, float *acc, Stage &st) {
   using G = Geo<KV, D>;
+  if constexpr (G::LPT <= 4) merge_lanes<4, G::EPL>(m, l, acc);
+  if constexpr (G::LPT <= 8) merge_lanes<8, G::EPL>(m, l, acc);
+  if constexpr (G::LPT <= 16) merge_lanes<16, G::EPL>(m, l, acc);
+  merge_lanes<32, G::EPL>(m, l, acc);
+  const int32_t dest = (!s.cut_start && !s.cut_end)
+                           ? s.b * a.H + s.h
+                           : -1 - (w * 2 + (s.cut_start ? 0 : 1));
+  float *e = st.base + st.n * (D + 4);
+  if (g == 0) {
 #pragma unroll
-  for (int off = G::LPT; off < kWave; off <<= 1) {
-    const float mo = __shfl_xor(m, off);
-    const float lo = __shfl_xor(l, off);
-    const float M = fmaxf(m, mo);
-    const float fa = __builtin_amdgcn_exp2f(m - M);
-    const float fb = __builtin_amdgcn_exp2f(mo - M);
-    l = l * fa + lo * fb;
-#pragma unroll
-    for (int e = 0; e < G::EPL; ++e) acc[e] = acc[e] * fa + __shfl_xor(acc[e], off) * fb;
-    m = M;
+    for (int k = 0; k < G::EPL; ++k) e[c * G::EPL + k] = acc[k];
+    if (c == 0) {
+      e[D] = m;
+      e[D + 1] = l;
+      e[D + 2] = __int_as_float(dest);
+    }
   }
-  if (g != 0) return;
-  const int64_t bh = static_cast<int64_t>(s.b) * a.H + s.h;
-  if (!s.cut_start && !s.cut_end) {
-    store_row<G::EPL>(a.out, bh * D + c * G::EPL, acc, l > 0.f ? 1.0f / l : 0.f, a.out_f16);
-    return;
-  }
-  float *r = a.ws_rec + (static_cast<int64_t>(w) * 2 + (s.cut_start ? 0 : 1)) * (D + 4);
-#pragma unroll
-  for (int e = 0; e < G::EPL; ++e) r[c * G::EPL + e] = acc[e];
-  if (c == 0) {
-    r[D] = m;
-    r[D + 1] = l;
-  }
+  if (++st.n == kStage) flush_stage<D>(a, st);
 }
 
 // Walk the chunk [f0, f1) tile by tile as one pipeline: while tile t is consumed, tile t+1 is in
@@ -497,18 +592,20 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
 template <bool PAGED, int KV, int D, bool QF16>
 __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre,
                                           const int32_t *len, int32_t f0, int32_t f1, int32_t b0,
-                                          int32_t w) {
+                                          int32_t w, Stage &st) {
   using G = Geo<KV, D>;
   using Tile = TileRegs<KV, D, QF16>;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane / G::LPT;
   const int c = lane % G::LPT;
-  int32_t f = f0, bcur = b0;
+  int32_t f = f0;
+  SeqCur sq;
+  load_seq(a, pre, len, b0, sq);
 
   Seg cur, nxt;
-  next_seg(a, pre, len, f, f1, bcur, cur);  // f0 < f1, so there is a first segment
+  next_seg(a, pre, len, f, f1, sq, cur);  // f0 < f1, so there is a first segment
   seg_ids<PAGED>(a, cur);
-  bool has_nxt = next_seg(a, pre, len, f, f1, bcur, nxt);
+  bool has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
   if (has_nxt) seg_ids<PAGED>(a, nxt);
 
   float m = kFloor, l = 0.f;
@@ -541,7 +638,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
       ++i;
       return true;
     }
-    finish_seg<KV, D>(a, cur, w, g, c, m, l, acc);
+    finish_seg<KV, D>(a, cur, w, g, c, m, l, acc, st);
     if (!has_nxt) return false;
     cur = nxt;
     i = 0;
@@ -550,7 +647,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
     l = 0.f;
 #pragma unroll
     for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
-    has_nxt = next_seg(a, pre, len, f, f1, bcur, nxt);
+    has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
     if (has_nxt) seg_ids<PAGED>(a, nxt);
     return true;
   };
@@ -562,6 +659,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
     if (!step(ta, tb)) break;
     if (!step(tb, ta)) break;
   }
+  flush_stage<D>(a, st);
 }
 
 template <bool PAGED, int KV, int D, bool QF16>
@@ -571,6 +669,10 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   int32_t *len = smem + a.B + 1;
   int32_t *wsum = len + a.B;
   block_prefix(a.lens, a.B, a.cap, pre, len, wsum);
+  Stage st;
+  st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
+            (threadIdx.x >> 6) * kStage * (D + 4);
+  st.n = 0;
 
   const int32_t total = a.H * pre[a.B];
   const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
@@ -589,13 +691,21 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   const int32_t f1 = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
   int32_t f = static_cast<int32_t>(f0);
 
-  // the sequence holding tile f0: largest b in [0, B) with H*pre[b] <= f0
-  int32_t lo = 0, hi = a.B - 1;
-  while (lo < hi) {
-    const int32_t mid = (lo + hi + 1) >> 1;
-    if (a.H * sread(pre + mid) <= f) lo = mid; else hi = mid - 1;
+  // the sequence holding tile f0: the largest b in [0, B) with H*pre[b] <= f0 (pre does not
+  // decrease and pre[0] = 0). Lanes test 64 evenly spaced candidates at once, then the 64 (or
+  // fewer) sequences from the last one that passed.
+  const int lane = threadIdx.x & (kWave - 1);
+  const int32_t S = (a.B + kWave - 1) / kWave;
+  const int32_t i0 = min(lane * S, a.B - 1);
+  const uint64_t m0 = __ballot(lane * S < a.B && a.H * pre[i0] <= f);
+  int32_t lo = (kWave - 1 - __clzll(static_cast<long long>(m0))) * S;
+  if (S > 1) {
+    const int32_t i1 = min(lo + lane, a.B - 1);
+    const uint64_t m1 = __ballot(lane < S && lo + lane < a.B && a.H * pre[i1] <= f);
+    lo += kWave - 1 - __clzll(static_cast<long long>(m1));
   }
-  run_chunk<PAGED, KV, D, QF16>(a, pre, len, f, f1, lo, w);
+  lo = __builtin_amdgcn_readfirstlane(lo);
+  run_chunk<PAGED, KV, D, QF16>(a, pre, len, f, f1, lo, w, st);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -717,6 +827,14 @@ struct PartialPlan {
   size_t shmem;
 };
 
+// Pass-1 wavefronts per compute unit: each wavefront has about one tile of loads in flight, so
+// small tiles (K+V of 16 positions) need more wavefronts to keep enough bytes in flight: 8 for
+// tiles of 8 KiB or more, 12 for 4 KiB, 16 for 2 KiB (register use allows each).
+inline int waves_per_cu(kvc_dtype kv, int D) {
+  const int tile = 2 * kBlock * D * static_cast<int>(elt_bytes(kv));
+  return tile >= 8192 ? 8 : tile >= 4096 ? 12 : 16;
+}
+
 // Shared validation and planning for both layouts.
 kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype kv_dtype,
                         const int32_t *ctx_lens, int32_t B, int32_t H, int32_t D, int32_t cap,
@@ -743,8 +861,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
 
   const int64_t tiles_hint = static_cast<int64_t>(B) * H *
                              ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
-  int64_t P = std::min<int64_t>(kMaxWorkers,
-                                static_cast<int64_t>(device_cu_count()) * kWavesPerCu);
+  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) *
+                                                 waves_per_cu(kv_dtype, D));
   P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
   P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
 
@@ -769,7 +887,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
                   : pick_kernel<false>(kv_dtype, D, a.q_f16);
   if (!pl.kern) return KVC_E_UNSUPPORTED;
   pl.grid = static_cast<int>(P / kWgWaves);
-  pl.shmem = (2 * static_cast<size_t>(B) + 1 + kWgWaves) * sizeof(int32_t);
+  pl.shmem = (static_cast<size_t>(stage_offset(B)) + static_cast<size_t>(kWgWaves) * kStage * (D + 4)) *
+             sizeof(int32_t);
   return KVC_OK;
 }
 
