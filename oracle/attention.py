@@ -6,6 +6,8 @@ Three independent paths:
   * decode_row       -- the definition for one query over L cached positions;
   * full_causal      -- recompute all rows with the causal mask, no cache;
   * cached_decode    -- the naive cached loop: concatenate the new k, v and attend the new q.
+and the head-sharing variant:
+  * grouped_decode   -- several query heads attend one shared key/value head (MQA / GQA).
 """
 from __future__ import annotations
 
@@ -84,3 +86,32 @@ def cached_decode(Qs, Ks, Vs, scale, prefix_K=None, prefix_V=None) -> np.ndarray
         V_cache = np.concatenate([V_cache, np.asarray(Vs[t:t + 1], dtype=np.float64)], axis=0)
         rows.append(decode_row(Qs[t], K_cache, V_cache, scale))
     return np.stack(rows) if rows else np.zeros((0, D))
+
+
+def kv_head_of(hq: int, q_heads: int, kv_heads: int) -> int:
+    """The key/value head that query head hq reads when q_heads query heads share kv_heads
+    key/value heads.
+
+    "LLM Inference Acceleration -- KV Cache", section 6.2: MHA has one key/value head per query
+    head; MQA gives all heads one shared key/value head, each head keeping its own query; GQA
+    splits the query heads into groups and each group shares one key/value head. The page does
+    not say which query heads form a group; the reading here is consecutive runs of
+    G = q_heads / kv_heads heads (query head hq belongs to group hq // G), which makes MHA the
+    case G = 1 and MQA the case kv_heads = 1.
+    """
+    if kv_heads < 1 or q_heads % kv_heads:
+        raise ValueError("the query heads must split evenly over the key/value heads")
+    return hq // (q_heads // kv_heads)
+
+
+def grouped_decode(q, K, V, scale) -> np.ndarray:
+    """Decode for one sequence with shared key/value heads.
+
+    q: [Hq, D]; K, V: [Hkv, L, D] with Hq a multiple of Hkv. Row hq of the result is
+    decode_row(q[hq], K[g], V[g]) for g = kv_head_of(hq, Hq, Hkv). Returns [Hq, D] fp64.
+    """
+    q = np.asarray(q)
+    Hq, Hkv = q.shape[0], K.shape[0]
+    return np.stack([decode_row(q[h], K[kv_head_of(h, Hq, Hkv)], V[kv_head_of(h, Hq, Hkv)], scale)
+                     for h in range(Hq)])
+

@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode_row
+from .attention import decode_row, grouped_decode
 from .codecs import e4m3_decode, fp8_write_token
 
 BS = 16
@@ -43,12 +43,14 @@ class ContigCache:
                     self.V[b, :, p, :] = v_new[b, t]
 
     def decode(self, q, lens, scale) -> np.ndarray:
-        """q: [B, H, D]; lens[b]: attended length (the new token included). Returns [B, H, D]."""
-        out = np.zeros((self.B, self.H, self.D))
+        """q: [B, Hq, D] with Hq a multiple of the cache's H (query heads sharing key/value heads
+        as in grouped_decode; Hq = H is plain multi-head attention); lens[b]: attended length
+        (the new token included). Returns [B, Hq, D]."""
+        Hq = q.shape[1]
+        out = np.zeros((self.B, Hq, self.D))
         for b in range(self.B):
             L = int(lens[b])
-            for h in range(self.H):
-                out[b, h] = decode_row(q[b, h], self.K[b, h, :L], self.V[b, h, :L], scale)
+            out[b] = grouped_decode(q[b], self.K[b, :, :L], self.V[b, :, :L], scale)
         return out
 
 
@@ -108,13 +110,18 @@ class PagedCache:
         return K, V
 
     def decode(self, q, tables, lens, scale, heads=None) -> np.ndarray:
-        """q: [B, H, D]; tables: [B, max_blocks]; lens[b]: attended length. Returns [B, H, D]
-        (only the listed heads are computed when `heads` is given; the rest stay 0)."""
-        B = len(lens)
-        out = np.zeros((B, self.H, self.D))
-        hs = range(self.H) if heads is None else heads
+        """q: [B, Hq, D] with Hq a multiple of the pool's H (query head hq reads key/value head
+        kv_head_of(hq, Hq, H), as in grouped_decode); tables: [B, max_blocks]; lens[b]: attended
+        length. Returns [B, Hq, D] (only the listed query heads are computed when `heads` is
+        given; the rest stay 0)."""
+        B, Hq = len(lens), q.shape[1]
+        G = Hq // self.H
+        if G * self.H != Hq:
+            raise ValueError("query heads must be a multiple of the pool's heads")
+        out = np.zeros((B, Hq, self.D))
+        hs = range(Hq) if heads is None else heads
         for b in range(B):
             K, V = self.gather(tables[b], int(lens[b]))
             for h in hs:
-                out[b, h] = decode_row(q[b, h], K[h], V[h], scale)
+                out[b, h] = decode_row(q[b, h], K[h // G], V[h // G], scale)
         return out

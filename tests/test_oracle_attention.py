@@ -139,3 +139,87 @@ def test_cached_loop_equals_full_recompute(T, D, start):
     np.testing.assert_allclose(cached, full, rtol=0, atol=1e-14)
     # full recompute over all n rows, then keep the last T: same rows
     np.testing.assert_allclose(full_causal(Q, K, V, 0.125)[start:], full, atol=1e-14)
+
+
+# ---- shared key/value heads (MQA / GQA), "LLM Inference Acceleration -- KV Cache" section 6.2 ----
+from oracle.attention import grouped_decode, kv_head_of  # noqa: E402
+
+
+def _rand(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+@pytest.mark.parametrize("Hq,Hkv", [(8, 8), (8, 2), (8, 1), (12, 4), (6, 3)])
+def test_grouped_decode_equals_multi_head_on_repeated_kv_heads(Hq, Hkv):
+    """Sharing a key/value head among G consecutive query heads is multi-head attention over a
+    cache whose heads are each repeated G times in place; repeating the whole head list G
+    times (a different grouping) must give a different answer unless G = 1 or Hkv = 1."""
+    L, D, G = 37, 16, Hq // Hkv
+    q, K, V = _rand((Hq, D), 1), _rand((Hkv, L, D), 2), _rand((Hkv, L, D), 3)
+    got = grouped_decode(q, K, V, 0.25)
+    Kr, Vr = np.repeat(K, G, axis=0), np.repeat(V, G, axis=0)
+    want = np.stack([decode_row(q[h], Kr[h], Vr[h], 0.25) for h in range(Hq)])
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-13)
+    Kt, Vt = np.tile(K, (G, 1, 1)), np.tile(V, (G, 1, 1))
+    other = np.stack([decode_row(q[h], Kt[h], Vt[h], 0.25) for h in range(Hq)])
+    if G > 1 and Hkv > 1:
+        assert np.abs(got - other).max() > 1e-3
+
+
+def test_mqa_every_query_head_reads_the_one_shared_head():
+    L, D, Hq = 50, 8, 5
+    q, K, V = _rand((Hq, D), 4), _rand((1, L, D), 5), _rand((1, L, D), 6)
+    got = grouped_decode(q, K, V, 0.5)
+    for h in range(Hq):
+        np.testing.assert_allclose(got[h], decode_row(q[h], K[0], V[0], 0.5), rtol=0, atol=0)
+    same = grouped_decode(np.repeat(q[:1], Hq, axis=0), K, V, 0.5)
+    assert (same == same[0]).all()
+
+
+def test_grouped_decode_equal_keys_average_their_values():
+    """Keys equal within each key/value head give uniform weights: every query head of a group
+    gets the mean of that group's value rows (closed form)."""
+    Hq, Hkv, L, D = 8, 2, 23, 4
+    K = np.repeat(_rand((Hkv, 1, D), 7), L, axis=1)
+    V = _rand((Hkv, L, D), 8)
+    got = grouped_decode(_rand((Hq, D), 9), K, V, 1.0)
+    for h in range(Hq):
+        np.testing.assert_allclose(got[h], V[h // 4].mean(axis=0), rtol=0, atol=1e-14)
+
+
+def test_kv_head_mapping_and_uneven_split():
+    assert [kv_head_of(h, 8, 2) for h in range(8)] == [0, 0, 0, 0, 1, 1, 1, 1]
+    assert [kv_head_of(h, 4, 4) for h in range(4)] == [0, 1, 2, 3]
+    assert {kv_head_of(h, 7, 1) for h in range(7)} == {0}
+    with pytest.raises(ValueError):
+        kv_head_of(0, 6, 4)
+
+
+def test_paged_and_contiguous_models_agree_with_shared_heads():
+    from oracle.caches import ContigCache, PagedCache
+    H, G, D, lens = 2, 3, 8, [5, 21, 0]
+    B, S = len(lens), 32
+    rng = np.random.default_rng(10)
+    contig = ContigCache(B, H, S, D, "f32")
+    paged = PagedCache(12, H, D, "f32")
+    tables = np.full((B, 2), -1, np.int64)
+    nxt = 11
+    for b, L in enumerate(lens):
+        k = rng.standard_normal((L, H, D)).astype(np.float32)
+        v = rng.standard_normal((L, H, D)).astype(np.float32)
+        pos = np.full(B, S, np.int32)
+        pos[b] = 0
+        kk = np.zeros((B, L, H, D), np.float32)
+        vv = np.zeros((B, L, H, D), np.float32)
+        kk[b], vv[b] = k, v
+        contig.append(pos, kk, vv)
+        slots = []
+        for t in range(L):
+            if t % 16 == 0:
+                tables[b, t // 16] = nxt
+                nxt -= 1
+            slots.append(tables[b, t // 16] * 16 + t % 16)
+        paged.write(slots, k, v)
+    q = rng.standard_normal((B, H * G, D))
+    np.testing.assert_allclose(paged.decode(q, tables, lens, 0.3), contig.decode(q, lens, 0.3),
+                               rtol=0, atol=1e-14)
