@@ -42,7 +42,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
-                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt"])
+                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
+                             "gqa8-paged"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
@@ -70,6 +71,8 @@ class PagedBench:
         self.fused = fused
         B, H, D = w.batch, w.heads, w.head_dim
         self.B, self.H, self.D = B, H, D
+        self.G = w.extra.get("group", 1)   # query heads per K/V head
+        Hq = H * self.G
         if w.ctx:
             lens = np.full(B, w.ctx, dtype=np.int64)
         else:
@@ -97,9 +100,9 @@ class PagedBench:
         # per-step inputs, resident in device memory: new K/V and q for every layer
         self.knew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 1)
         self.vnew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 2)
-        self.q = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 3)
-        self.out = torch.empty((layers, B, H, D), dtype=torch.float16, device=dev)
-        self.ws = kvc.new_workspace(B, H, D, device=dev)
+        self.q = workloads.torch_normal((layers, B, Hq, D), torch.float16, dev, w.seed * 7 + 3)
+        self.out = torch.empty((layers, B, Hq, D), dtype=torch.float16, device=dev)
+        self.ws = kvc.new_gqa_workspace(B, H, self.G, D, device=dev)
         # pinned host staging, a ring of buffers: a buffer is refilled only after the copy that
         # last read it has executed (the host may run several steps ahead of the GPU)
         self.ring = [(torch.empty((B, self.mbps), dtype=torch.int32, pin_memory=True),
@@ -145,12 +148,19 @@ class PagedBench:
                                                 self.knew[li], self.vnew[li], self.max_ctx,
                                                 scale=self.scale, out=self.out[li],
                                                 workspace=self.ws)
+            elif self.G > 1:
+                kvc.decode_gqa_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
+                                             self.max_ctx, scale=self.scale, out=self.out[li],
+                                             workspace=self.ws)
             else:
                 kvc.decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d, self.max_ctx,
                                          scale=self.scale, out=self.out[li], workspace=self.ws)
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li + 1, self.stream)
-            kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
+            if self.G > 1:
+                kvc.decode_gqa_merge(self.B, self.H, self.G, self.D, self.out[li], self.ws)
+            else:
+                kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
 
     def bytes_step(self, lens):
         """Algorithmic HBM bytes of one step over all layers, and of one pass-1 launch: every
@@ -162,7 +172,7 @@ class PagedBench:
         kv = int(lens.sum()) * H * D * 2 * elt
         blocks = int(sum(workloads.blocks_for(L) for L in lens))
         table = blocks * 4 + (blocks * 8 if self.w.kv_dtype == "e4m3" else 0) + B * 4
-        qo = B * H * D * (2 + 2)
+        qo = B * H * self.G * D * (2 + 2)
         append = B * H * D * 2 * elt + (B * 8 if self.w.kv_dtype == "e4m3" else 0)
         pass1 = kv + table + qo + (append if self.fused else 0)
         return (kv + table + qo + append) * self.L, pass1
@@ -422,16 +432,20 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = {"llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
-         "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT}[args.workload]
+         "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
+         "gqa8-paged": workloads.GQA8_PAGED}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    fused = args.append == "fused" or (args.append == "auto" and w.kv_dtype != "e4m3")
-    if fused and w.kv_dtype == "e4m3":
-        print("--append fused: e4m3 caches take the separate writer", file=sys.stderr)
+    grouped = w.extra.get("group", 1) > 1
+    fused = args.append == "fused" or (args.append == "auto" and w.kv_dtype != "e4m3"
+                                        and not grouped)
+    if fused and (w.kv_dtype == "e4m3" or grouped):
+        print("--append fused: e4m3 caches and shared K/V heads take the separate writer",
+              file=sys.stderr)
         sys.exit(2)
     path = "fused" if fused else "separate"
     bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev, fused)
@@ -477,7 +491,8 @@ def main():
         "dtype": w.kv_dtype,
         "data": "synthetic: N(0,1) K/V/q, seeded; lengths and pool order seeded",
         "config": {
-            "workload": w.name, "batch": w.batch, "heads": w.heads, "head_dim": w.head_dim,
+            "workload": w.name, "batch": w.batch, "heads": w.heads * w.extra.get("group", 1),
+            "kv_heads": w.heads, "head_dim": w.head_dim,
             "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
             if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
@@ -487,8 +502,8 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(w.batch * K / elapsed, 1),
         "roofline": {
-            "kernel": f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> "
-                      "(attention pass 1)",
+            "kernel": f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}, "
+                      f"{min(w.extra.get('group', 1), 8)} q heads per wavefront> (attention pass 1)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,

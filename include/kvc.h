@@ -296,6 +296,53 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                            float scale, void *out, kvc_dtype out_dtype,
                                            void *workspace, size_t ws_bytes, void *stream);
 
+/* ==================================================================================== *
+ * Shared key/value heads (MQA / GQA).
+ *
+ * "LLM Inference Acceleration -- KV Cache", section 6.2: with MQA all query heads share one
+ * key/value head; with GQA the query heads form groups and each group shares one key/value
+ * head. Here G consecutive query heads share each K/V head: query head hq (of H_kv * G) reads
+ * K/V head hq / G. G = 1 is multi-head attention (results equal kvc_decode_*, bit for bit);
+ * H_kv = 1 is MQA.
+ *
+ *   q, out:   [B][H_kv*G][D] (q_dtype, out_dtype as above)
+ *   caches:   as for kvc_decode_* with H_kv heads (contiguous [B][H_kv][S_max][D]; paged: the
+ *             layer's num_heads is H_kv)
+ *   workspace: at least kvc_gqa_workspace_bytes(B, H_kv, G, D) bytes, otherwise as above
+ *
+ * One wavefront serves up to 8 query heads of a group from each K/V tile it loads (the largest
+ * of 8, 4, 2 dividing G) when q is fp16 and the cache fp16 (or paged e4m3); then each K/V byte is
+ * read from HBM G/8 times or fewer (once for G <= 8). Other dtype combinations are supported
+ * with one query head per wavefront (each K/V byte read G times). No append variant. */
+size_t kvc_gqa_workspace_bytes(int32_t B, int32_t H_kv, int32_t G, int32_t D);
+
+kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
+                                 const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                 int32_t B, int32_t H_kv, int32_t S_max, int32_t D,
+                                 int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                 void *workspace, size_t ws_bytes, void *stream);
+kvc_status kvc_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                const kvc_paged_layer *layer, const int32_t *block_tables,
+                                int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                void *workspace, size_t ws_bytes, void *stream);
+/* The two passes of the calls above, as for kvc_decode_partial_* and kvc_decode_merge. */
+kvc_status kvc_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                         const void *k_cache, const void *v_cache,
+                                         kvc_dtype kv_dtype, const int32_t *ctx_lens, int32_t B,
+                                         int32_t H_kv, int32_t S_max, int32_t D, int32_t max_ctx,
+                                         float scale, void *out, kvc_dtype out_dtype,
+                                         void *workspace, size_t ws_bytes, void *stream);
+kvc_status kvc_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                        const kvc_paged_layer *layer, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                        int32_t B, int32_t max_ctx, float scale, void *out,
+                                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                        void *stream);
+kvc_status kvc_decode_gqa_merge(int32_t B, int32_t H_kv, int32_t G, int32_t D, void *out,
+                                kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                void *stream);
+
 #ifdef __cplusplus
 }
 #endif

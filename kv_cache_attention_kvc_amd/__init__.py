@@ -21,7 +21,9 @@ __all__ = [
     "append_contig", "copy_blocks", "write_paged", "decode_attn_contig", "decode_attn_paged",
     "decode_partial_contig", "decode_partial_paged", "decode_merge", "new_workspace", "EXPORTS",
     "append_decode_contig", "append_decode_paged", "append_decode_partial_contig",
-    "append_decode_partial_paged",
+    "append_decode_partial_paged", "gqa_workspace_bytes", "new_gqa_workspace",
+    "decode_gqa_contig", "decode_gqa_paged", "decode_gqa_partial_contig",
+    "decode_gqa_partial_paged", "decode_gqa_merge",
 ]
 
 F32, F16, E4M3 = 0, 1, 2
@@ -37,6 +39,8 @@ EXPORTS = [
     "kvc_decode_attn_paged", "kvc_decode_partial_contig", "kvc_decode_partial_paged",
     "kvc_decode_merge", "kvc_append_decode_contig", "kvc_append_decode_paged",
     "kvc_append_decode_partial_contig", "kvc_append_decode_partial_paged",
+    "kvc_gqa_workspace_bytes", "kvc_decode_gqa_contig", "kvc_decode_gqa_paged",
+    "kvc_decode_gqa_partial_contig", "kvc_decode_gqa_partial_paged", "kvc_decode_gqa_merge",
 ]
 
 
@@ -125,6 +129,17 @@ def load_library() -> ctypes.CDLL:
         sig[name] = (ctypes.c_int, contig_append)
     for name in ("kvc_append_decode_paged", "kvc_append_decode_partial_paged"):
         sig[name] = (ctypes.c_int, paged_append)
+    contig_gqa = [_P, ctypes.c_int, _I32, _P, _P, ctypes.c_int, _P, _I32, _I32, _I32, _I32, _I32,
+                  _F, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]
+    paged_gqa = [_P, ctypes.c_int, _I32, ctypes.POINTER(_Layer), _P, _I32, _P, _I32, _I32, _F, _P,
+                 ctypes.c_int, _P, ctypes.c_size_t, _P]
+    for name in ("kvc_decode_gqa_contig", "kvc_decode_gqa_partial_contig"):
+        sig[name] = (ctypes.c_int, contig_gqa)
+    for name in ("kvc_decode_gqa_paged", "kvc_decode_gqa_partial_paged"):
+        sig[name] = (ctypes.c_int, paged_gqa)
+    sig["kvc_gqa_workspace_bytes"] = (ctypes.c_size_t, [_I32, _I32, _I32, _I32])
+    sig["kvc_decode_gqa_merge"] = (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, ctypes.c_int, _P,
+                                                  ctypes.c_size_t, _P])
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
         fn.restype = res
@@ -515,3 +530,94 @@ def append_decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, k_
     """Pass 1 of append_decode_paged; returns (out, workspace) for decode_merge."""
     return _append_paged_call("kvc_append_decode_partial_paged", q, layer, block_tables, ctx_lens,
                               k_new, v_new, max_ctx, scale, out, workspace, stream)
+
+
+# ---- shared key/value heads (MQA / GQA) ----------------------------------------------------
+def gqa_workspace_bytes(B: int, H_kv: int, G: int, D: int) -> int:
+    return int(_lib().kvc_gqa_workspace_bytes(B, H_kv, G, D))
+
+
+def new_gqa_workspace(B: int, H_kv: int, G: int, D: int, device="cuda"):
+    """A workspace for grouped-query decode of up to B sequences (no initialisation needed)."""
+    torch = _torch()
+    return torch.empty(gqa_workspace_bytes(B, H_kv, G, D), dtype=torch.uint8, device=device)
+
+
+def _gqa_group(q, H_kv):
+    Hq = q.shape[1]
+    if Hq % H_kv:
+        raise ValueError("q heads must be a multiple of the cache's heads")
+    return Hq // H_kv
+
+
+def _gqa_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, scale, out, workspace, stream):
+    B, H, S, D = k_cache.shape
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    G = _gqa_group(q, H)
+    out = _out_for(q, out)
+    ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(ctx_lens), B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out),
+        _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def _gqa_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, scale, out, workspace,
+                    stream):
+    B = q.shape[0]
+    if q.dim() != 3 or q.shape[2] != layer.head_dim:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    G = _gqa_group(q, layer.heads)
+    out = _out_for(q, out)
+    ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
+          else workspace)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def decode_gqa_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
+                      workspace=None, stream=None):
+    """Grouped-query decode over a contiguous cache: q [B, H_kv*G, D], caches
+    [B, H_kv, S_max, D]; query head hq reads K/V head hq // G. Returns out [B, H_kv*G, D]."""
+    return _gqa_contig_call("kvc_decode_gqa_contig", q, k_cache, v_cache, ctx_lens, max_ctx,
+                            scale, out, workspace, stream)[0]
+
+
+def decode_gqa_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
+                              workspace=None, stream=None):
+    """Pass 1 of decode_gqa_contig; returns (out, workspace) for decode_gqa_merge."""
+    return _gqa_contig_call("kvc_decode_gqa_partial_contig", q, k_cache, v_cache, ctx_lens,
+                            max_ctx, scale, out, workspace, stream)
+
+
+def decode_gqa_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None, out=None,
+                     workspace=None, stream=None):
+    """Grouped-query decode over a paged cache whose layer holds the K/V heads. q is
+    [B, H_kv*G, D]. Returns out [B, H_kv*G, D]."""
+    return _gqa_paged_call("kvc_decode_gqa_paged", q, layer, block_tables, ctx_lens, max_ctx,
+                           scale, out, workspace, stream)[0]
+
+
+def decode_gqa_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
+                             out=None, workspace=None, stream=None):
+    """Pass 1 of decode_gqa_paged; returns (out, workspace) for decode_gqa_merge."""
+    return _gqa_paged_call("kvc_decode_gqa_partial_paged", q, layer, block_tables, ctx_lens,
+                           max_ctx, scale, out, workspace, stream)
+
+
+def decode_gqa_merge(B, H_kv, G, D, out, workspace, stream=None):
+    """Pass 2 of grouped-query decode."""
+    _check(_lib().kvc_decode_gqa_merge(B, H_kv, G, D, _ptr(out), _dtype_code(out),
+                                       _ptr(workspace), workspace.numel(), _stream(stream)),
+           "kvc_decode_gqa_merge")
+    return out

@@ -29,6 +29,7 @@
 // pass 1. Pass 1 leaves the chunk size and the per-sequence block prefix in the workspace, so
 // pass 2 needs no other input. Stream order makes pass 1's stores visible to pass 2.
 #include <mutex>
+#include <vector>
 
 #include "kvc_internal.h"
 
@@ -38,24 +39,27 @@ constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
-constexpr int kStage = 4;          // finished segments a wavefront holds in LDS before storing
+constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
+constexpr int kMaxGroup = 8;       // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' is never NaN)
 
-// Workspace: [header int32[64] | prefix int32[B+1] | records float[kMaxWorkers][2][D+4]], each
-// region 256-byte aligned. Header: chunk size C, and B, H, D of the pass-1 call.
+// Workspace: [header int32[64] | prefix int32[B+1] | records float[kMaxWorkers][2][GQ][D+4]],
+// each region 256-byte aligned. Header: chunk size C, and B, pairs per sequence, D, GQ of the
+// pass-1 call. GQ is the number of query heads a wavefront serves from one K/V head (1 for
+// multi-head attention).
 struct WsLayout {
   size_t pre_off, rec_off, total;
 };
 
 inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-inline WsLayout ws_layout(int B, int D) {
+inline WsLayout ws_layout(int B, int D, int GQ) {
   WsLayout l;
   l.pre_off = 256;
   l.rec_off = l.pre_off + align256((static_cast<size_t>(B) + 1) * sizeof(int32_t));
-  l.total = l.rec_off + static_cast<size_t>(kMaxWorkers) * 2 * (D + 4) * sizeof(float);
+  l.total = l.rec_off + static_cast<size_t>(kMaxWorkers) * 2 * GQ * (D + 4) * sizeof(float);
   return l;
 }
 
@@ -67,7 +71,7 @@ struct DecodeArgs {
   const float *v_scale;
   const int32_t *tables;
   const int32_t *lens;
-  const char *k_new;  // append mode: the new token's K and V, [B][H][D]; else null
+  const char *k_new;  // append mode: the new token's K and V, [B][H][D]; else null (H = K/V heads)
   const char *v_new;
   void *out;
   int32_t *ws_hdr;
@@ -75,6 +79,10 @@ struct DecodeArgs {
   float *ws_rec;
   int64_t seq_stride;  // contiguous: S_max
   int32_t B, H, cap, mbps, num_blocks, P, cmin;
+  // shared K/V heads: G query heads per K/V head (q and out have Hq = H*G heads per sequence);
+  // a pair is (sequence, K/V head, sub-group of GQ query heads), nsub = G/GQ pairs per K/V head
+  // and Hp = H*nsub pairs per sequence. Multi-head attention: G = nsub = 1, Hp = Hq = H.
+  int32_t G, nsub, Hp, Hq;
   int32_t q_f16, out_f16;
   float cl2;  // scale * log2(e)
 };
@@ -286,13 +294,12 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
 }
 
 // ---- one tile: loads ---------------------------------------------------------------------
-// Every fetch issues the same loads -- the q slice of the tile's sequence-head, then LOADS
-// 16-byte loads of K and of V -- whatever the tile, so the compiler can count exactly how many
-// loads follow a tile's and wait for that tile alone when it is consumed.
-template <int KV, int D, bool QF16>
+// Every fetch issues the same loads -- with one query head per wavefront the q slice of the
+// tile's head first, then LOADS 16-byte loads of K and of V -- whatever the tile.
+template <int KV, int D, bool QF16, int GQ>
 struct TileRegs {
   using G = Geo<KV, D>;
-  QWords<QF16, G::EPL> q;
+  QWords<QF16, G::EPL> q[1];  // GQ == 1: this tile's q slice (unused otherwise)
   uint4 k[G::LOADS];
   uint4 v[G::LOADS];
   int32_t nt;       // valid rows (0: the tile contributes nothing)
@@ -302,15 +309,16 @@ struct TileRegs {
   float ks, vs;     // fp8 block scales
 };
 
-// Tile j of sequence-head (b, h) = bh; phys is its block id (paged). live = false fetches a
-// stand-in with nt = 0 (the first row of block 0 / of the sequence-head), for the step after a
-// chunk's last tile.
-template <bool PAGED, int KV, int D, bool QF16>
-__device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, QF16> &t,
-                                           int64_t bh, int32_t h, int32_t j, int32_t phys,
-                                           int32_t L, bool live, int g, int c) {
+// Tile j of K/V head hkv of sequence b (bkv = b*H + hkv); phys is its block id (paged); qrow is
+// the row of q of the first query head the wavefront serves (loaded here when GQ == 1).
+// live = false fetches a stand-in with nt = 0 (the first row of block 0 / of the sequence-head),
+// for the step after a chunk's last tile.
+template <bool PAGED, int KV, int D, bool QF16, int GQ>
+__device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, QF16, GQ> &t,
+                                           int64_t bkv, int32_t hkv, int64_t qrow, int32_t j,
+                                           int32_t phys, int32_t L, bool live, int g, int c) {
   using G = Geo<KV, D>;
-  load_q_words<QF16, G::EPL>(a.q, bh * D + c * G::EPL, t.q);
+  if constexpr (GQ == 1) load_q_words<QF16, G::EPL>(a.q, qrow * D + c * G::EPL, t.q[0]);
   const char *kt;
   const char *vt;
   bool valid = live;
@@ -318,7 +326,7 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
     // addresses are formed from a clamped id, so nothing outside the pools is ever addressed
     valid = valid && static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
     const int32_t sp = valid ? phys : 0;
-    const int64_t toff = (static_cast<int64_t>(sp) * a.H + h) * G::TILE;
+    const int64_t toff = (static_cast<int64_t>(sp) * a.H + hkv) * G::TILE;
     kt = a.k + toff;
     vt = a.v + toff;
     if constexpr (KV == KVC_E4M3) {
@@ -326,7 +334,7 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
       t.vs = valid ? a.v_scale[sp] : 0.f;
     }
   } else {
-    const int64_t toff = (bh * a.seq_stride + static_cast<int64_t>(kBlock) * (valid ? j : 0)) *
+    const int64_t toff = (bkv * a.seq_stride + static_cast<int64_t>(kBlock) * (valid ? j : 0)) *
                          G::ROW;
     kt = a.k + toff;
     vt = a.v + toff;
@@ -349,7 +357,7 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
   } else {
     // rows past the end load the last valid row again (the same cache lines, so no extra
     // traffic; with nt = 0, row 0): their scores are masked to -inf, so they weigh 0
-    const int64_t new_off = bh * G::ROW + c * 16;
+    const int64_t new_off = bkv * G::ROW + c * 16;
     const int last_row = max(t.nt, 1) - 1;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
@@ -362,8 +370,8 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
 }
 
 // Append mode: store the new token's row (already in registers) into the cache.
-template <int KV, int D, bool QF16>
-__device__ __forceinline__ void store_new_row(const TileRegs<KV, D, QF16> &t, int g, int c) {
+template <int KV, int D, bool QF16, int GQ>
+__device__ __forceinline__ void store_new_row(const TileRegs<KV, D, QF16, GQ> &t, int g, int c) {
   using G = Geo<KV, D>;
   if (t.new_row < 0) return;
   const int lane_off = g * G::ROW + c * 16;
@@ -378,76 +386,102 @@ __device__ __forceinline__ void store_new_row(const TileRegs<KV, D, QF16> &t, in
   }
 }
 
+// Read every register of a tile that adds nothing (nt = 0) in an empty asm statement, so that
+// no load into them stays outstanding into the fetch that next reuses them.
+template <int KV, int D, bool QF16, int GQ>
+__device__ __forceinline__ void touch_tile(const TileRegs<KV, D, QF16, GQ> &t) {
+  using G = Geo<KV, D>;
+#pragma unroll
+  for (int i = 0; i < G::LOADS; ++i) {
+    asm volatile("" ::"v"(t.k[i].x), "v"(t.k[i].y), "v"(t.k[i].z), "v"(t.k[i].w));
+    asm volatile("" ::"v"(t.v[i].x), "v"(t.v[i].y), "v"(t.v[i].z), "v"(t.v[i].w));
+  }
+  if constexpr (GQ == 1) {
+#pragma unroll
+    for (int u = 0; u < QWords<QF16, G::EPL>::W; ++u) asm volatile("" ::"v"(t.q[0].w[u]));
+  }
+}
+
+// Partial dot product of this lane's 16 loaded bytes of one K row with its q slice.
+template <int KV, bool QF16, int EPL>
+__device__ __forceinline__ float dot_slice(const uint4 &kr, const QWords<QF16, EPL> &q) {
+  float kf[EPL], qv[EPL];
+  unpack<KV>(kr, kf);
+  q_floats<QF16, EPL>(q, qv);
+  float d = 0.f;
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) d = __builtin_fmaf(kf[e], qv[e], d);
+  return d;
+}
+
 // ---- one tile: online-softmax update of the group state ---------------------------------
 // Rows at or past nt get score -inf (weight 0); their V registers hold a valid row's data.
-// A tile with nt = 0 adds nothing (its registers may hold anything), but its registers are
-// still read (by an empty asm statement), so that no load into them stays outstanding into the
-// fetch that next reuses them: that fetch must not wait.
-template <int KV, int D, bool QF16>
-__device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16> &t, float cl2, int g,
-                                             float &m, float &l, float *acc) {
+// A tile with nt = 0 adds nothing. With GQ query heads per wavefront, each head r keeps its own
+// state (m[r], l[r], acc[r]) and reads the q slice qs[r]; the K and V registers are shared.
+template <int KV, int D, bool QF16, int GQ>
+__device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
+                                             const QWords<QF16, Geo<KV, D>::EPL> *qs, float cl2,
+                                             int g, float *m, float *l,
+                                             float (*acc)[Geo<KV, D>::EPL]) {
   using G = Geo<KV, D>;
   if (t.nt <= 0) {
-#pragma unroll
-    for (int i = 0; i < G::LOADS; ++i) {
-      asm volatile("" ::"v"(t.k[i].x), "v"(t.k[i].y), "v"(t.k[i].z), "v"(t.k[i].w));
-      asm volatile("" ::"v"(t.v[i].x), "v"(t.v[i].y), "v"(t.v[i].z), "v"(t.v[i].w));
-    }
-#pragma unroll
-    for (int u = 0; u < QWords<QF16, G::EPL>::W; ++u) asm volatile("" ::"v"(t.q.w[u]));
+    touch_tile(t);
     return;
   }
-  float qv[G::EPL];
-  q_floats<QF16, G::EPL>(t.q, qv);
-  float s[G::LOADS];
+  const QWords<QF16, G::EPL> *qq = GQ == 1 ? t.q : qs;
+  float s[GQ][G::LOADS];
   const float sc = (KV == KVC_E4M3) ? cl2 * t.ks : cl2;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
-    float kf[G::EPL];
-    unpack<KV>(t.k[i], kf);
-    float d = 0.f;
+    const bool ok = g + i * G::TPL < t.nt;
 #pragma unroll
-    for (int e = 0; e < G::EPL; ++e) d = __builtin_fmaf(kf[e], qv[e], d);
-    d = group_sum<G::LPT>(d) * sc;
-    s[i] = (g + i * G::TPL < t.nt) ? d : -__builtin_inff();
+    for (int r = 0; r < GQ; ++r) {
+      const float d = group_sum<G::LPT>(dot_slice<KV, QF16, G::EPL>(t.k[i], qq[r])) * sc;
+      s[r][i] = ok ? d : -__builtin_inff();
+    }
   }
-  float mb = s[0];
 #pragma unroll
-  for (int i = 1; i < G::LOADS; ++i) mb = fmaxf(mb, s[i]);
-  const float mn = fmaxf(m, mb);
-  const float alpha = __builtin_amdgcn_exp2f(m - mn);
-  float p[G::LOADS];
-  float psum = 0.f;
+  for (int r = 0; r < GQ; ++r) {
+    float mb = s[r][0];
 #pragma unroll
-  for (int i = 0; i < G::LOADS; ++i) {
-    p[i] = __builtin_amdgcn_exp2f(s[i] - mn);
-    psum += p[i];
+    for (int i = 1; i < G::LOADS; ++i) mb = fmaxf(mb, s[r][i]);
+    const float mn = fmaxf(m[r], mb);
+    const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);
+    float psum = 0.f;
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      s[r][i] = __builtin_amdgcn_exp2f(s[r][i] - mn);  // now the weight p
+      psum += s[r][i];
+    }
+    l[r] = l[r] * alpha + psum;
+    m[r] = mn;
+#pragma unroll
+    for (int e = 0; e < G::EPL; ++e) acc[r][e] *= alpha;
   }
-  l = l * alpha + psum;
-  m = mn;
-#pragma unroll
-  for (int e = 0; e < G::EPL; ++e) acc[e] *= alpha;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     float vf[G::EPL];
     unpack<KV>(t.v[i], vf);
-    const float pi = (KV == KVC_E4M3) ? p[i] * t.vs : p[i];
 #pragma unroll
-    for (int e = 0; e < G::EPL; ++e) acc[e] = __builtin_fmaf(pi, vf[e], acc[e]);
+    for (int r = 0; r < GQ; ++r) {
+      const float pi = (KV == KVC_E4M3) ? s[r][i] * t.vs : s[r][i];
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) acc[r][e] = __builtin_fmaf(pi, vf[e], acc[r][e]);
+    }
   }
 }
 
 // ---- the wavefront's chunk: segments and the tile pipeline --------------------------------
 // A segment is the part of one (sequence, head) pair that lies in the chunk: tiles j0 .. j0+n-1.
 struct Seg {
-  int32_t b, h, j0, n, L;
+  int32_t b, h, j0, n, L;  // h: the pair index in [0, Hp)
   int32_t ph0, ph1;  // paged: block ids of the segment's first two tiles (-1 past the end)
   bool cut_start, cut_end;
 };
 
 // Next segment of the chunk starting at tile f (b is a cursor over sequences that only moves
 // forward). Returns false at the end of the chunk.
-// The sequence a chunk cursor is in: its index, first tile H*pre[b], tiles per head and length
+// The sequence a chunk cursor is in: its index, first tile Hp*pre[b], tiles per pair and length
 // (read from LDS once per sequence, not once per segment).
 struct SeqCur {
   int32_t b, base, nb, L;
@@ -457,7 +491,7 @@ __device__ __forceinline__ void load_seq(const DecodeArgs &a, const int32_t *pre
                                          const int32_t *len, int32_t b, SeqCur &q) {
   const int32_t p0 = sread(pre + b);
   q.b = b;
-  q.base = a.H * p0;
+  q.base = a.Hp * p0;
   q.nb = sread(pre + b + 1) - p0;
   q.L = sread(len + b);
 }
@@ -466,7 +500,7 @@ __device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre
                                          const int32_t *len, int32_t &f, int32_t f1, SeqCur &q,
                                          Seg &s) {
   if (f >= f1) return false;
-  while (f >= q.base + a.H * q.nb) load_seq(a, pre, len, q.b + 1, q);  // f < total: ends
+  while (f >= q.base + a.Hp * q.nb) load_seq(a, pre, len, q.b + 1, q);  // f < total: ends
   const int32_t rel = f - q.base;
   s.b = q.b;
   s.h = rel / q.nb;
@@ -522,11 +556,11 @@ __host__ __device__ inline int32_t stage_offset(int32_t B) { return (2 * B + 1 +
 
 // Finished segments wait in LDS until the wavefront's loads are done (or the stage is full), so
 // that no global store sits between a tile's loads and the wait for them: a wait for loads on
-// this GPU also waits for every store issued before it. An entry is D+4 floats: the combined
-// unnormalised output, then m, l and the destination (int bits: >= 0 the output row b*H+h;
-// < 0 the record slot -1-slot).
+// this GPU also waits for every store issued before it. A row entry is D+4 floats: the combined
+// unnormalised output, then m, l and the destination (int bits: >= 0 the output row b*Hq+hq;
+// < 0 the record row -1-r).
 struct Stage {
-  float *base;  // this wavefront's kStage entries
+  float *base;  // this wavefront's kStageRows entries
   int32_t n;    // entries in use
 };
 
@@ -558,43 +592,51 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs &a, Stage &st) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Finish a segment: combine the TPL lane groups, then stage either the output row (the whole
-// pair was in this chunk) or a record (slot 0 if the pair began before the chunk, else 1).
-template <int KV, int D>
+// Finish a segment: for each of its GQ query heads combine the TPL lane groups, then stage
+// either the output row (the whole pair was in this chunk) or a record (slot 0 if the pair
+// began before the chunk, else 1; the record of head r is row (2w+slot)*GQ + r).
+template <int KV, int D, int GQ>
 __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, int32_t w, int g,
-                                           int c, float m, float l, float *acc, Stage &st) {
+                                           int c, float *m, float *l,
+                                           float (*acc)[Geo<KV, D>::EPL], Stage &st) {
   using G = Geo<KV, D>;
-  if constexpr (G::LPT <= 4) merge_lanes<4, G::EPL>(m, l, acc);
-  if constexpr (G::LPT <= 8) merge_lanes<8, G::EPL>(m, l, acc);
-  if constexpr (G::LPT <= 16) merge_lanes<16, G::EPL>(m, l, acc);
-  merge_lanes<32, G::EPL>(m, l, acc);
-  const int32_t dest = (!s.cut_start && !s.cut_end)
-                           ? s.b * a.H + s.h
-                           : -1 - (w * 2 + (s.cut_start ? 0 : 1));
-  float *e = st.base + st.n * (D + 4);
-  if (g == 0) {
+  if (st.n + GQ > kStageRows) flush_stage<D>(a, st);
+  const bool whole = !s.cut_start && !s.cut_end;
+  const int32_t out0 = s.b * a.Hq + s.h * GQ;
+  const int32_t rec0 = (w * 2 + (s.cut_start ? 0 : 1)) * GQ;
 #pragma unroll
-    for (int k = 0; k < G::EPL; ++k) e[c * G::EPL + k] = acc[k];
-    if (c == 0) {
-      e[D] = m;
-      e[D + 1] = l;
-      e[D + 2] = __int_as_float(dest);
+  for (int r = 0; r < GQ; ++r) {
+    if constexpr (G::LPT <= 4) merge_lanes<4, G::EPL>(m[r], l[r], acc[r]);
+    if constexpr (G::LPT <= 8) merge_lanes<8, G::EPL>(m[r], l[r], acc[r]);
+    if constexpr (G::LPT <= 16) merge_lanes<16, G::EPL>(m[r], l[r], acc[r]);
+    merge_lanes<32, G::EPL>(m[r], l[r], acc[r]);
+    const int32_t dest = whole ? out0 + r : -1 - (rec0 + r);
+    float *e = st.base + (st.n + r) * (D + 4);
+    if (g == 0) {
+#pragma unroll
+      for (int k = 0; k < G::EPL; ++k) e[c * G::EPL + k] = acc[r][k];
+      if (c == 0) {
+        e[D] = m[r];
+        e[D + 1] = l[r];
+        e[D + 2] = __int_as_float(dest);
+      }
     }
   }
-  if (++st.n == kStage) flush_stage<D>(a, st);
+  st.n += GQ;
 }
 
 // Walk the chunk [f0, f1) tile by tile as one pipeline: while tile t is consumed, tile t+1 is in
 // flight, also across segment boundaries. Every step issues one fetch of the same shape (after
-// the chunk's last tile, a stand-in that is not consumed), so waiting for the tile about to be
-// consumed never waits for the one just issued. Paged block ids come through the scalar cache
-// one tile ahead of their use (a segment's first two when the segment is found).
-template <bool PAGED, int KV, int D, bool QF16>
+// the chunk's last tile, a stand-in that is not consumed). Paged block ids come through the
+// scalar cache one tile ahead of their use (a segment's first two when the segment is found).
+// With GQ > 1 the q slices of the current segment's GQ heads stay in registers; they are loaded
+// when the segment becomes current, after the loads of its first tile.
+template <bool PAGED, int KV, int D, bool QF16, int GQ>
 __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre,
                                           const int32_t *len, int32_t f0, int32_t f1, int32_t b0,
                                           int32_t w, Stage &st) {
   using G = Geo<KV, D>;
-  using Tile = TileRegs<KV, D, QF16>;
+  using Tile = TileRegs<KV, D, QF16, GQ>;
   const int lane = threadIdx.x & (kWave - 1);
   const int g = lane / G::LPT;
   const int c = lane % G::LPT;
@@ -608,10 +650,35 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
   bool has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
   if (has_nxt) seg_ids<PAGED>(a, nxt);
 
-  float m = kFloor, l = 0.f;
-  float acc[G::EPL];
+  // K/V head and q row of a pair h of sequence b
+  auto bkv_of = [&](int32_t b, int32_t h) -> int64_t {
+    return static_cast<int64_t>(b) * a.H + h / a.nsub;
+  };
+  auto qrow_of = [&](int32_t b, int32_t h) -> int64_t {
+    return static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(h) * GQ;
+  };
+  QWords<QF16, G::EPL> qs[GQ];
+  auto load_qs = [&](const Seg &sg) {
+    if constexpr (GQ > 1) {
+      const int64_t q0 = qrow_of(sg.b, sg.h);
 #pragma unroll
-  for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
+      for (int r = 0; r < GQ; ++r)
+        load_q_words<QF16, G::EPL>(a.q, (q0 + r) * D + c * G::EPL, qs[r]);
+    }
+  };
+
+  float m[GQ], l[GQ];
+  float acc[GQ][G::EPL];
+  auto reset = [&]() {
+#pragma unroll
+    for (int r = 0; r < GQ; ++r) {
+      m[r] = kFloor;
+      l[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) acc[r][e] = 0.f;
+    }
+  };
+  reset();
 
   int32_t i = 0;        // index, within the current segment, of the tile being consumed
   int32_t ph_next = 0;  // paged: block id of tile i+1 of the current segment (-1 past its end)
@@ -628,33 +695,33 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
       const int32_t h = to_nxt ? nxt.h : cur.h;
       const int32_t j = to_nxt ? nxt.j0 : cur.j0 + i + 1;
       const int32_t L = to_nxt ? nxt.L : cur.L;
-      fetch_tile<PAGED, KV, D, QF16>(a, nb, static_cast<int64_t>(b) * a.H + h, h, j, ph, L,
-                                     !last || has_nxt, g, c);
+      fetch_tile<PAGED, KV, D, QF16, GQ>(a, nb, bkv_of(b, h), h / a.nsub, qrow_of(b, h), j, ph,
+                                         L, !last || has_nxt, g, c);
     }
     if constexpr (PAGED) ph_next = i + 2 < cur.n ? block_id(a, cur.b, cur.j0 + i + 2) : -1;
-    consume_tile<KV, D, QF16>(cb, a.cl2, g, m, l, acc);
-    store_new_row<KV, D, QF16>(cb, g, c);
+    consume_tile<KV, D, QF16, GQ>(cb, qs, a.cl2, g, m, l, acc);
+    store_new_row<KV, D, QF16, GQ>(cb, g, c);
     if (!last) {
       ++i;
       return true;
     }
-    finish_seg<KV, D>(a, cur, w, g, c, m, l, acc, st);
+    finish_seg<KV, D, GQ>(a, cur, w, g, c, m, l, acc, st);
     if (!has_nxt) return false;
     cur = nxt;
+    load_qs(cur);
     i = 0;
     if constexpr (PAGED) ph_next = cur.ph1;
-    m = kFloor;
-    l = 0.f;
-#pragma unroll
-    for (int e = 0; e < G::EPL; ++e) acc[e] = 0.f;
+    reset();
     has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
     if (has_nxt) seg_ids<PAGED>(a, nxt);
     return true;
   };
 
   Tile ta, tb;
-  fetch_tile<PAGED, KV, D, QF16>(a, ta, static_cast<int64_t>(cur.b) * a.H + cur.h, cur.h, cur.j0,
-                                 PAGED ? cur.ph0 : 0, cur.L, true, g, c);
+  fetch_tile<PAGED, KV, D, QF16, GQ>(a, ta, bkv_of(cur.b, cur.h), cur.h / a.nsub,
+                                     qrow_of(cur.b, cur.h), cur.j0, PAGED ? cur.ph0 : 0, cur.L,
+                                     true, g, c);
+  load_qs(cur);
   for (;;) {
     if (!step(ta, tb)) break;
     if (!step(tb, ta)) break;
@@ -662,7 +729,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
   flush_stage<D>(a, st);
 }
 
-template <bool PAGED, int KV, int D, bool QF16>
+template <bool PAGED, int KV, int D, bool QF16, int GQ>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
   int32_t *pre = smem;
@@ -671,18 +738,19 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   block_prefix(a.lens, a.B, a.cap, pre, len, wsum);
   Stage st;
   st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
-            (threadIdx.x >> 6) * kStage * (D + 4);
+            (threadIdx.x >> 6) * kStageRows * (D + 4);
   st.n = 0;
 
-  const int32_t total = a.H * pre[a.B];
+  const int32_t total = a.Hp * pre[a.B];
   const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= a.B; i += kWgThreads) a.ws_pre[i] = pre[i];
     if (threadIdx.x == 0) {
       a.ws_hdr[0] = C;
       a.ws_hdr[1] = a.B;
-      a.ws_hdr[2] = a.H;
+      a.ws_hdr[2] = a.Hp;
       a.ws_hdr[3] = D;
+      a.ws_hdr[4] = GQ;
     }
   }
   const int32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWgWaves + (threadIdx.x >> 6));
@@ -691,21 +759,21 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   const int32_t f1 = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
   int32_t f = static_cast<int32_t>(f0);
 
-  // the sequence holding tile f0: the largest b in [0, B) with H*pre[b] <= f0 (pre does not
+  // the sequence holding tile f0: the largest b in [0, B) with Hp*pre[b] <= f0 (pre does not
   // decrease and pre[0] = 0). Lanes test 64 evenly spaced candidates at once, then the 64 (or
   // fewer) sequences from the last one that passed.
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t S = (a.B + kWave - 1) / kWave;
   const int32_t i0 = min(lane * S, a.B - 1);
-  const uint64_t m0 = __ballot(lane * S < a.B && a.H * pre[i0] <= f);
+  const uint64_t m0 = __ballot(lane * S < a.B && a.Hp * pre[i0] <= f);
   int32_t lo = (kWave - 1 - __clzll(static_cast<long long>(m0))) * S;
   if (S > 1) {
     const int32_t i1 = min(lo + lane, a.B - 1);
-    const uint64_t m1 = __ballot(lane < S && lo + lane < a.B && a.H * pre[i1] <= f);
+    const uint64_t m1 = __ballot(lane < S && lo + lane < a.B && a.Hp * pre[i1] <= f);
     lo += kWave - 1 - __clzll(static_cast<long long>(m1));
   }
   lo = __builtin_amdgcn_readfirstlane(lo);
-  run_chunk<PAGED, KV, D, QF16>(a, pre, len, f, f1, lo, w, st);
+  run_chunk<PAGED, KV, D, QF16, GQ>(a, pre, len, f, f1, lo, w, st);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -714,27 +782,37 @@ struct MergeArgs {
   const int32_t *ws_hdr;
   const int32_t *ws_pre;
   const float *ws_rec;
-  int32_t B, H, D, out_f16;
+  int32_t B, H, G, D, out_f16;  // H: K/V heads; G: query heads per K/V head
 };
 
 constexpr int kMaxParts = 16;  // parts whose loads are in flight together
 
 __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
+  const int32_t Hq = a.H * a.G;
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
-  if (bh >= static_cast<int64_t>(a.B) * a.H) return;
-  const int32_t b = static_cast<int32_t>(bh / a.H);
-  const int32_t h = static_cast<int32_t>(bh % a.H);
+  if (bh >= static_cast<int64_t>(a.B) * Hq) return;
+  const int32_t b = static_cast<int32_t>(bh / Hq);
+  const int32_t hq = static_cast<int32_t>(bh % Hq);
   const int D = a.D;
   const int32_t C = a.ws_hdr[0];
+  // query heads pass 1 served per wavefront (1, 2, 4 or 8, dividing G); the pass-1 pair of this
+  // query head and its place among the pair's GQ heads
+  const int32_t GQ = a.ws_hdr[4];
+  const bool gq_ok = (GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8) && a.G % GQ == 0;
+  const int32_t gq = gq_ok ? GQ : 1;
+  const int32_t nsub = a.G / gq;
+  const int32_t rr = hq % a.G;
+  const int32_t h = (hq / a.G) * nsub + rr / gq;
+  const int32_t r = rr % gq;
   const int32_t pb = a.ws_pre[b];
   const int32_t nb = a.ws_pre[b + 1] - pb;
   if (nb == 0) {
     for (int d = lane; d < D; d += kWave) store_elem(a.out, bh * D + d, 0.f, a.out_f16);
     return;
   }
-  if (C < 1 || nb < 0) return;  // no pass-1 record in this workspace
-  const int32_t start = a.H * pb + h * nb;
+  if (C < 1 || nb < 0 || !gq_ok) return;  // no pass-1 record in this workspace
+  const int32_t start = a.H * nsub * pb + h * nb;
   // worker indices are clamped into the record array whatever the workspace holds
   const int32_t fw = min(max(start / C, 0), kMaxWorkers - 1);
   const int32_t lw = min(max((start + nb - 1) / C, fw), kMaxWorkers - 1);
@@ -742,7 +820,7 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
   const int RS = D + 4;
   const int32_t nparts = lw - fw + 1;
   auto rec = [&](int32_t i) -> const float * {  // part i of the pair: the first is in slot 1
-    return a.ws_rec + (static_cast<int64_t>(fw + i) * 2 + (i == 0 ? 1 : 0)) * RS;
+    return a.ws_rec + ((static_cast<int64_t>(fw + i) * 2 + (i == 0 ? 1 : 0)) * gq + r) * RS;
   };
   // the loads of up to kMaxParts parts are issued before any is used
   float M = kFloor, lsum = 0.f, o0 = 0.f, o1 = 0.f;
@@ -754,11 +832,11 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
       mi[k] = kFloor;
       li[k] = x0[k] = x1[k] = 0.f;
       if (k < n) {
-        const float *r = rec(i0 + k);
-        mi[k] = r[D];
-        li[k] = r[D + 1];
-        x0[k] = r[lane];
-        if (D > kWave) x1[k] = r[lane + kWave];
+        const float *p = rec(i0 + k);
+        mi[k] = p[D];
+        li[k] = p[D + 1];
+        x0[k] = p[lane];
+        if (D > kWave) x1[k] = p[lane + kWave];
       }
     }
     float Mn = M;
@@ -801,23 +879,58 @@ int device_cu_count() {
 
 using PartialKernel = void (*)(DecodeArgs);
 
-template <bool PAGED, bool QF16>
-PartialKernel pick_kernel_q(kvc_dtype kv, int D) {
-  if (D == 64) {
-    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 64, QF16>;
-    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 64, QF16>;
-    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 64, QF16>;
-  } else if (D == 128) {
-    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, 128, QF16>;
-    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, 128, QF16>;
-    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, 128, QF16>;
+// Query heads one wavefront serves from one K/V head: the largest of 8, 4, 2 dividing G for
+// fp16 queries over fp16 (or paged e4m3) caches, else 1 (then each query head is its own pair
+// and its K/V head is read once per query head).
+inline int group_width(int G, kvc_dtype kv, bool q_f16, bool paged) {
+  const bool shared = q_f16 && (kv == KVC_F16 || (paged && kv == KVC_E4M3));
+  if (!shared) return 1;
+  for (int w = kMaxGroup; w > 1; w >>= 1)
+    if (G % w == 0) return w;
+  return 1;
+}
+
+// Records are sized for the widest group G allows, whatever the dtypes.
+inline int ws_group(int G) {
+  for (int w = kMaxGroup; w > 1; w >>= 1)
+    if (G % w == 0) return w;
+  return 1;
+}
+
+template <bool PAGED, bool QF16, int D>
+PartialKernel pick_kernel_d(kvc_dtype kv, int GQ) {
+  if (GQ == 1) {
+    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, D, QF16, 1>;
+    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1>;
+    if constexpr (PAGED)
+      if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1>;
+    return nullptr;
+  }
+  if constexpr (QF16) {
+    if (kv == KVC_F16) {
+      if (GQ == 2) return decode_partial_kernel<PAGED, KVC_F16, D, true, 2>;
+      if (GQ == 4) return decode_partial_kernel<PAGED, KVC_F16, D, true, 4>;
+      if (GQ == 8) return decode_partial_kernel<PAGED, KVC_F16, D, true, 8>;
+    }
+    if constexpr (PAGED) {
+      if (kv == KVC_E4M3) {
+        if (GQ == 2) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 2>;
+        if (GQ == 4) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 4>;
+        if (GQ == 8) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 8>;
+      }
+    }
   }
   return nullptr;
 }
 
 template <bool PAGED>
-PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16) {
-  return q_f16 ? pick_kernel_q<PAGED, true>(kv, D) : pick_kernel_q<PAGED, false>(kv, D);
+PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, int GQ) {
+  if (D == 64)
+    return q_f16 ? pick_kernel_d<PAGED, true, 64>(kv, GQ) : pick_kernel_d<PAGED, false, 64>(kv, GQ);
+  if (D == 128)
+    return q_f16 ? pick_kernel_d<PAGED, true, 128>(kv, GQ)
+                 : pick_kernel_d<PAGED, false, 128>(kv, GQ);
+  return nullptr;
 }
 
 struct PartialPlan {
@@ -835,19 +948,46 @@ inline int waves_per_cu(kvc_dtype kv, int D) {
   return tile >= 8192 ? 8 : tile >= 4096 ? 12 : 16;
 }
 
+// Wavefronts of a pass-1 kernel that fit on one CU at once (from its register and LDS use),
+// cached per kernel and LDS size; 0 if the runtime cannot say.
+int resident_waves_per_cu(PartialKernel k, size_t shmem) {
+  struct Entry {
+    PartialKernel k;
+    size_t shmem;
+    int waves;
+  };
+  static std::mutex mu;
+  static std::vector<Entry> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  for (const Entry &e : cache)
+    if (e.k == k && e.shmem == shmem) return e.waves;
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, reinterpret_cast<const void *>(k),
+                                                   kWgThreads, shmem) != hipSuccess) {
+    blocks = 0;
+    (void)hipGetLastError();  // the failed query's error is not the caller's
+  }
+  if (cache.size() < 256) cache.push_back(Entry{k, shmem, blocks * kWgWaves});
+  return blocks * kWgWaves;
+}
+
 // Shared validation and planning for both layouts.
 kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype kv_dtype,
-                        const int32_t *ctx_lens, int32_t B, int32_t H, int32_t D, int32_t cap,
-                        int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                        const int32_t *ctx_lens, int32_t B, int32_t H, int32_t G, int32_t D,
+                        int32_t cap, int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                         void *workspace, size_t ws_bytes, PartialPlan &pl) {
-  if (B < 0 || H < 1 || max_ctx < 0 || cap < 0) return KVC_E_INVALID;
+  if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0) return KVC_E_INVALID;
+  if (static_cast<int64_t>(H) * G > (1 << 20)) return KVC_E_INVALID;
   if (B > kMaxBatch) return KVC_E_INVALID;
   if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
   if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
   if (!paged && kv_dtype == KVC_E4M3) return KVC_E_UNSUPPORTED;
   if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
+  const bool q_f16 = q_dtype == KVC_F16;
+  const int GQ = group_width(G, kv_dtype, q_f16, paged);
+  const int32_t Hp = H * (G / GQ);  // pairs per sequence
   const int64_t tiles_cap =
-      static_cast<int64_t>(B) * H * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
+      static_cast<int64_t>(B) * Hp * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
   if (tiles_cap + kMaxWorkers >= INT32_MAX) return KVC_E_INVALID;
   if (B == 0) {
     pl.grid = 0;
@@ -856,13 +996,22 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   if (!q || !out || !ctx_lens || !workspace) return KVC_E_INVALID;
   if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return KVC_E_INVALID;
-  const WsLayout wl = ws_layout(B, D);
+  const WsLayout wl = ws_layout(B, D, ws_group(G));
   if (ws_bytes < wl.total) return KVC_E_INVALID;
 
-  const int64_t tiles_hint = static_cast<int64_t>(B) * H *
+  const int64_t tiles_hint = static_cast<int64_t>(B) * Hp *
                              ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
-  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) *
-                                                 waves_per_cu(kv_dtype, D));
+  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, GQ)
+                             : pick_kernel<false>(kv_dtype, D, q_f16, GQ);
+  if (!kern) return KVC_E_UNSUPPORTED;
+  const size_t shmem = (static_cast<size_t>(stage_offset(B)) +
+                        static_cast<size_t>(kWgWaves) * kStageRows * (D + 4)) *
+                       sizeof(int32_t);
+  // one round of wavefronts: never more than fit on the GPU at once
+  int wpc = waves_per_cu(kv_dtype, D);
+  const int fit = resident_waves_per_cu(kern, shmem);
+  if (fit > 0) wpc = std::min(wpc, fit);
+  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
   P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
   P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
 
@@ -877,18 +1026,19 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   a.ws_rec = reinterpret_cast<float *>(ws + wl.rec_off);
   a.B = B;
   a.H = H;
+  a.G = G;
+  a.nsub = G / GQ;
+  a.Hp = Hp;
+  a.Hq = H * G;
   a.cap = cap;
   a.P = static_cast<int32_t>(P);
   a.cmin = kMinChunk;
-  a.q_f16 = q_dtype == KVC_F16;
+  a.q_f16 = q_f16;
   a.out_f16 = out_dtype == KVC_F16;
   a.cl2 = scale * kLog2e;
-  pl.kern = paged ? pick_kernel<true>(kv_dtype, D, a.q_f16)
-                  : pick_kernel<false>(kv_dtype, D, a.q_f16);
-  if (!pl.kern) return KVC_E_UNSUPPORTED;
+  pl.kern = kern;
   pl.grid = static_cast<int>(P / kWgWaves);
-  pl.shmem = (static_cast<size_t>(stage_offset(B)) + static_cast<size_t>(kWgWaves) * kStage * (D + 4)) *
-             sizeof(int32_t);
+  pl.shmem = shmem;
   return KVC_OK;
 }
 
@@ -903,8 +1053,9 @@ kvc_status launch_partial(const PartialPlan &pl, void *stream) {
 
 using namespace kvc;
 
-// Pass 1 for both layouts; k_new/v_new non-null selects append mode.
-static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
+// Pass 1 for both layouts. G query heads share each K/V head (q and out have H*G heads);
+// k_new/v_new non-null selects append mode (G = 1 only).
+static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
                                  const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
                                  const void *k_new, const void *v_new, int32_t B, int32_t H,
                                  int32_t S_max, int32_t D, int32_t max_ctx, float scale, void *out,
@@ -913,12 +1064,12 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, const void *k
   if (S_max < 0) return KVC_E_INVALID;
   if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
   PartialPlan pl;
-  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, D, S_max, max_ctx,
+  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, G, D, S_max, max_ctx,
                                scale, out, out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
   if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || G != 1)) return KVC_E_INVALID;
   pl.a.k = static_cast<const char *>(k_cache);
   pl.a.v = static_cast<const char *>(v_cache);
   pl.a.k_new = static_cast<const char *>(k_new);
@@ -927,12 +1078,12 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, const void *k
   return launch_partial(pl, stream);
 }
 
-static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
-                                const int32_t *block_tables, int32_t max_blocks_per_seq,
-                                const int32_t *ctx_lens, const void *k_new, const void *v_new,
-                                int32_t B, int32_t max_ctx, float scale, void *out,
-                                kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
-                                void *stream) {
+static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                const kvc_paged_layer *layer, const int32_t *block_tables,
+                                int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                const void *k_new, const void *v_new, int32_t B, int32_t max_ctx,
+                                float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                size_t ws_bytes, void *stream) {
   if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
     return KVC_E_INVALID;
   if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
@@ -940,7 +1091,7 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, const kvc_page
   if (kv != KVC_F32 && kv != KVC_F16 && kv != KVC_E4M3) return KVC_E_UNSUPPORTED;
   if (k_new && kv == KVC_E4M3) return KVC_E_UNSUPPORTED;  // the block scale may change
   PartialPlan pl;
-  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads,
+  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads, G,
                                layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, scale, out,
                                out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
@@ -949,7 +1100,7 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, const kvc_page
     return KVC_E_INVALID;
   if (kv == KVC_E4M3 && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new))) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || G != 1)) return KVC_E_INVALID;
   pl.a.k = static_cast<const char *>(layer->k_pool);
   pl.a.v = static_cast<const char *>(layer->v_pool);
   pl.a.k_scale = layer->k_scale;
@@ -962,11 +1113,45 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, const kvc_page
   return launch_partial(pl, stream);
 }
 
+static kvc_status merge(int32_t B, int32_t H, int32_t G, int32_t D, void *out, kvc_dtype out_dtype,
+                        void *workspace, size_t ws_bytes, void *stream) {
+  if (B < 0 || H < 1 || G < 1 || B > kMaxBatch) return KVC_E_INVALID;
+  if (static_cast<int64_t>(H) * G > (1 << 20)) return KVC_E_INVALID;
+  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
+  if (!is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
+  if (B == 0) return KVC_OK;
+  if (!out || !workspace || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return KVC_E_INVALID;
+  const WsLayout wl = ws_layout(B, D, ws_group(G));
+  if (ws_bytes < wl.total) return KVC_E_INVALID;
+  MergeArgs a;
+  char *ws = static_cast<char *>(workspace);
+  a.out = out;
+  a.ws_hdr = reinterpret_cast<const int32_t *>(ws);
+  a.ws_pre = reinterpret_cast<const int32_t *>(ws + wl.pre_off);
+  a.ws_rec = reinterpret_cast<const float *>(ws + wl.rec_off);
+  a.B = B;
+  a.H = H;
+  a.G = G;
+  a.D = D;
+  a.out_f16 = out_dtype == KVC_F16;
+  const int64_t rows = static_cast<int64_t>(B) * H * G;
+  const int grid = static_cast<int>((rows + kWgWaves - 1) / kWgWaves);
+  hipLaunchKernelGGL(decode_merge_kernel, dim3(grid), dim3(kWgThreads), 0,
+                     static_cast<hipStream_t>(stream), a);
+  return launch_status();
+}
+
 extern "C" {
 
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D) {
   if (B < 0 || H < 1 || D < 1) return 0;
-  return ws_layout(B, D).total;
+  return ws_layout(B, D, 1).total;
+}
+
+size_t kvc_gqa_workspace_bytes(int32_t B, int32_t H_kv, int32_t G, int32_t D) {
+  if (B < 0 || H_kv < 1 || G < 1 || D < 1) return 0;
+  return ws_layout(B, D, ws_group(G)).total;
 }
 
 kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
@@ -975,8 +1160,8 @@ kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const voi
                                      int32_t D, int32_t max_ctx, float scale, void *out,
                                      kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                      void *stream) {
-  return partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B, H,
-                        S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+  return partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
+                        H, S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
@@ -984,7 +1169,28 @@ kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                     int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
                                     int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                                     void *workspace, size_t ws_bytes, void *stream) {
-  return partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+  return partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                       nullptr, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                         const void *k_cache, const void *v_cache,
+                                         kvc_dtype kv_dtype, const int32_t *ctx_lens, int32_t B,
+                                         int32_t H_kv, int32_t S_max, int32_t D, int32_t max_ctx,
+                                         float scale, void *out, kvc_dtype out_dtype,
+                                         void *workspace, size_t ws_bytes, void *stream) {
+  return partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
+                        H_kv, S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes,
+                        stream);
+}
+
+kvc_status kvc_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                        const kvc_paged_layer *layer, const int32_t *block_tables,
+                                        int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                        int32_t B, int32_t max_ctx, float scale, void *out,
+                                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                        void *stream) {
+  return partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
                        nullptr, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
@@ -996,7 +1202,7 @@ kvc_status kvc_append_decode_partial_contig(const void *q, kvc_dtype q_dtype, vo
                                             void *out, kvc_dtype out_dtype, void *workspace,
                                             size_t ws_bytes, void *stream) {
   if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
-  return partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H,
+  return partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H,
                         S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
@@ -1008,35 +1214,19 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                            float scale, void *out, kvc_dtype out_dtype,
                                            void *workspace, size_t ws_bytes, void *stream) {
   if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
-  return partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new, v_new,
-                       B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+  return partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
+                       v_new, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
                             void *workspace, size_t ws_bytes, void *stream) {
-  if (B < 0 || H < 1 || B > kMaxBatch) return KVC_E_INVALID;
-  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
-  if (!is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
-  if (B == 0) return KVC_OK;
-  if (!out || !workspace || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return KVC_E_INVALID;
-  const WsLayout wl = ws_layout(B, D);
-  if (ws_bytes < wl.total) return KVC_E_INVALID;
-  MergeArgs a;
-  char *ws = static_cast<char *>(workspace);
-  a.out = out;
-  a.ws_hdr = reinterpret_cast<const int32_t *>(ws);
-  a.ws_pre = reinterpret_cast<const int32_t *>(ws + wl.pre_off);
-  a.ws_rec = reinterpret_cast<const float *>(ws + wl.rec_off);
-  a.B = B;
-  a.H = H;
-  a.D = D;
-  a.out_f16 = out_dtype == KVC_F16;
-  const int64_t pairs = static_cast<int64_t>(B) * H;
-  const int grid = static_cast<int>((pairs + kWgWaves - 1) / kWgWaves);
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(grid), dim3(kWgThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
-  return launch_status();
+  return merge(B, H, 1, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_gqa_merge(int32_t B, int32_t H_kv, int32_t G, int32_t D, void *out,
+                                kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                void *stream) {
+  return merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_attn_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
@@ -1062,6 +1252,31 @@ kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_pag
   if (st != KVC_OK) return st;
   return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
                           ws_bytes, stream);
+}
+
+kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
+                                 const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                 int32_t B, int32_t H_kv, int32_t S_max, int32_t D,
+                                 int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                 void *workspace, size_t ws_bytes, void *stream) {
+  kvc_status st = kvc_decode_gqa_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
+                                                ctx_lens, B, H_kv, S_max, D, max_ctx, scale, out,
+                                                out_dtype, workspace, ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                const kvc_paged_layer *layer, const int32_t *block_tables,
+                                int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
+                                void *workspace, size_t ws_bytes, void *stream) {
+  kvc_status st = kvc_decode_gqa_partial_paged(q, q_dtype, G, layer, block_tables,
+                                               max_blocks_per_seq, ctx_lens, B, max_ctx, scale,
+                                               out, out_dtype, workspace, ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
+                              ws_bytes, stream);
 }
 
 kvc_status kvc_append_decode_contig(const void *q, kvc_dtype q_dtype, void *k_cache,

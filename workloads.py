@@ -113,6 +113,14 @@ LONGCTX_FP8 = Workload(
 
 ALL = [TINY_GPT, LLAMA7B_CONTIG, LLAMA13B_PAGED, PARALLEL_SAMPLING, LONGCTX_FP8]
 
+# Shared K/V heads (grouped-query attention): 64 query heads over 8 K/V heads (G = 8), the
+# attention shape of a LLaMA-2-70B-class model, with the LLaMA-13B batch's length mix.
+# `heads` counts the K/V heads; the query heads are heads * extra["group"].
+GQA8_PAGED = Workload(
+    name="gqa-64q8kv-x128-f16-paged16-b32-ctxU64-2048", kind="paged", layers=80, batch=32,
+    heads=8, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=6, ctx_lo=64, ctx_hi=2048,
+    extra={"group": 8})
+
 
 def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
     """Attended lengths of the LLaMA-13B paged batch: uniform in [ctx_lo, ctx_hi]."""
