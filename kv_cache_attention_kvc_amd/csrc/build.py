@@ -1,7 +1,8 @@
 """Build libkvc.so for gfx950 with hipcc, in-tree (kv_cache_attention_kvc_amd/libkvc.so).
 
 Run as `python -m kv_cache_attention_kvc_amd.csrc.build` or call build(). Every HIP translation
-unit is compiled with the packed-fp32 target feature disabled (v_pk_*_f32 are never emitted).
+unit is compiled with the packed-fp32 target feature disabled (v_pk_*_f32 are never emitted), and
+MFMA accumulators are kept in VGPRs.
 """
 from __future__ import annotations
 
@@ -21,8 +22,11 @@ ARCH = "gfx950"
 
 SOURCES = ["kvc_pool.cpp", "kvc_decode.hip", "kvc_write.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", HERE]
+# The matrix-core decode accumulates in VGPRs (gfx950 MFMA takes C/D there): its softmax
+# rescale is VALU work on the accumulator, and AGPR accumulators would need copies both ways
+# plus a second register file's worth of space.
 HIP_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang",
-             "-packed-fp32-ops", "-x", "hip"]
+             "-packed-fp32-ops", "-mllvm", "-amdgpu-mfma-vgpr-form", "-x", "hip"]
 
 
 def _compile(src: str) -> str:

@@ -40,7 +40,7 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
-constexpr int kMaxGroup = 8;       // query heads one wavefront serves from one K/V head
+constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' is never NaN)
@@ -83,6 +83,8 @@ struct DecodeArgs {
   // a pair is (sequence, K/V head, sub-group of GQ query heads), nsub = G/GQ pairs per K/V head
   // and Hp = H*nsub pairs per sequence. Multi-head attention: G = nsub = 1, Hp = Hq = H.
   int32_t G, nsub, Hp, Hq;
+  int32_t gq;          // query heads per pair (G / nsub)
+  int32_t stage_rows;  // staged output rows per wavefront (LDS)
   int32_t q_f16, out_f16;
   float cl2;  // scale * log2(e)
 };
@@ -560,7 +562,7 @@ __host__ __device__ inline int32_t stage_offset(int32_t B) { return (2 * B + 1 +
 // unnormalised output, then m, l and the destination (int bits: >= 0 the output row b*Hq+hq;
 // < 0 the record row -1-r).
 struct Stage {
-  float *base;  // this wavefront's kStageRows entries
+  float *base;  // this wavefront's entries (DecodeArgs::stage_rows of them)
   int32_t n;    // entries in use
 };
 
@@ -625,21 +627,338 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
   st.n += GQ;
 }
 
+// ---- pass-1 cores ---------------------------------------------------------------------------
+// A core is how one wavefront loads a 16-position tile of one K/V head and folds it into the
+// softmax state of the query heads it serves. run_chunk below drives a core over a chunk.
+//   VecCore:  vector ALU; one query head per wavefront (multi-head attention), or two heads of a
+//             group that share the tile's K/V registers.
+//   MfmaCore: matrix cores; up to 16 query heads of a group against one K/V head.
+
+// Vector core: the tile code above, one (or two) query heads per wavefront.
+template <bool PAGED, int KV, int D, bool QF16, int GQ>
+struct VecCore {
+  using G = Geo<KV, D>;
+  using Tile = TileRegs<KV, D, QF16, GQ>;
+  static constexpr int kD = D;
+  struct State {
+    QWords<QF16, G::EPL> qs[GQ];  // GQ > 1: the segment's q slices
+    float m[GQ], l[GQ];
+    float acc[GQ][G::EPL];
+  };
+  int g, c;  // the lane's row within a wave-wide load, and its 16-byte column
+
+  __device__ explicit VecCore(int lane) : g(lane / G::LPT), c(lane % G::LPT) {}
+  __device__ int32_t gq(const DecodeArgs &) const { return GQ; }
+
+  __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t qrow,
+                        int32_t j, int32_t phys, int32_t L, bool live) const {
+    fetch_tile<PAGED, KV, D, QF16, GQ>(a, t, bkv, hkv, qrow, j, phys, L, live, g, c);
+  }
+  // A segment becomes current: its q slices (GQ > 1) and a fresh softmax state.
+  __device__ void begin(const DecodeArgs &a, int64_t qrow, State &s) const {
+    if constexpr (GQ > 1) {
+#pragma unroll
+      for (int r = 0; r < GQ; ++r)
+        load_q_words<QF16, G::EPL>(a.q, (qrow + r) * D + c * G::EPL, s.qs[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < GQ; ++r) {
+      s.m[r] = kFloor;
+      s.l[r] = 0.f;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) s.acc[r][e] = 0.f;
+    }
+  }
+  __device__ void consume(const DecodeArgs &a, const Tile &t, State &s) const {
+    consume_tile<KV, D, QF16, GQ>(t, s.qs, a.cl2, g, s.m, s.l, s.acc);
+    store_new_row<KV, D, QF16, GQ>(t, g, c);
+  }
+  __device__ void finish(const DecodeArgs &a, const Seg &sg, int32_t w, State &s,
+                         Stage &st) const {
+    finish_seg<KV, D, GQ>(a, sg, w, g, c, s.m, s.l, s.acc, st);
+  }
+};
+
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// Ordering point for LDS traffic between the lanes of one wavefront: the compiler keeps LDS
+// accesses on their side of it, and the LDS executes one wavefront's accesses in issue order.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Matrix-core core for grouped queries: the GQ (<= 16) query heads of a pair share every K/V
+// tile, so a tile is a 16-position x D block against a 16-column block of queries. Lanes are
+// (g, j) = (lane / 16, lane % 16).
+//   Scores: S^T = K . Q^T with v_mfma_f32_16x16x32_f16 (D/32 of them). Lane (g, j) holds K row
+//     j and q of head j (heads past GQ repeat the last one; their columns are never stored), 8
+//     dims per MFMA, the same dims in both. The result gives lane (g, j) the scores of positions
+//     4g..4g+3 for head j.
+//   Softmax: head j's weights are exp2(score - reference), the reference shared by the four
+//     lane groups. It is moved (and the output and sums rescaled) only when a tile's maximum
+//     passes it by more than a fixed headroom, so a tile normally costs no rescale; the weights
+//     stay below 2^15. Each lane keeps the partial sum of its own positions' weights.
+//   Output: O^T = V^T . P^T with v_mfma_f32_16x16x16_f16 per 16 output dims. The B operand is
+//     the weights exactly where the score MFMA left them (positions 4g..4g+3 of head j). The
+//     weights enter as two fp16 terms, p = hi + lo with hi = fp16(p) and lo = fp16(p - hi), so
+//     about 22 bits of each weight reach the fp32 accumulator. A needs V transposed (four
+//     positions of one dim per lane): the tile goes through LDS. It is loaded in the
+//     wave-contiguous layout, written as fp16 rows with 16-byte columns swizzled by row group,
+//     and read back one fp16 at a time; the swizzle puts the four lane groups of a read on
+//     distinct banks. Lane (g, j) accumulates dims 16*dc + 4g .. +3 of head j.
+//   e4m3: codes convert exactly to fp16 (v_cvt_scalef32_pk_f16_fp8 with scale 1). The K block
+//     scale multiplies the scores. O is held in units of a reference V scale; a tile's weights
+//     are multiplied by its block's scale over the reference (kept within [1/16, 16], else the
+//     reference moves to this block's scale and O is rescaled).
+template <bool PAGED, int KV, int D>
+struct MfmaCore {
+  static_assert(KV == KVC_F16 || KV == KVC_E4M3, "fp16 or e4m3 cache");
+  using G = Geo<KV, D>;            // wave-contiguous geometry (V loads)
+  static constexpr int kD = D;
+  static constexpr int KL = G::ROW / 64;  // K loads per lane per tile (16 bytes each)
+  static constexpr int NQK = D / 32;      // score MFMAs per tile
+  static constexpr int NDC = D / 16;      // 16-dim output blocks
+  static constexpr int kVbufBytes = kBlock * D * 2;
+  // Weight headroom (log2 units): weights are at most 2^kHi, times kRat for e4m3, below the
+  // fp16 maximum; a fresh reference gives the tile's top weight 2^kHead.
+  static constexpr float kHead = KV == KVC_E4M3 ? 3.f : 7.f;
+  static constexpr float kHi = KV == KVC_E4M3 ? 11.f : 15.f;
+  static constexpr float kRat = 16.f;
+  struct Tile {
+    uint4 k[KL];
+    uint4 v[G::LOADS];
+    int32_t nt;
+    float ks, vs;
+  };
+  struct State {
+    uint4 q[NQK];  // q operand, 8 fp16 dims per score MFMA
+    f32x4 o[NDC];
+    float m, l, vref;
+  };
+  int g, j;        // MFMA role
+  int gv, cv;      // wave-contiguous role: row gv + TPL*i, 16-byte column cv
+  _Float16 *vbuf;  // this wavefront's LDS tile, [16][D] fp16
+
+  __device__ MfmaCore(int lane, _Float16 *buf)
+      : g(lane >> 4), j(lane & 15), gv(lane / G::LPT), cv(lane % G::LPT), vbuf(buf) {}
+  __device__ int32_t gq(const DecodeArgs &a) const { return a.gq; }
+
+  // LDS column (8 fp16) of 16-byte column c of row t
+  static __device__ __forceinline__ int swz(int t, int c) { return c ^ (2 * ((t >> 2) & 3)); }
+
+  __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t,
+                        int32_t jt, int32_t phys, int32_t L, bool live) const {
+    const char *kt;
+    const char *vt;
+    bool valid = live;
+    if constexpr (PAGED) {
+      valid = valid && static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
+      const int32_t sp = valid ? phys : 0;
+      const int64_t toff = (static_cast<int64_t>(sp) * a.H + hkv) * G::TILE;
+      kt = a.k + toff;
+      vt = a.v + toff;
+      if constexpr (KV == KVC_E4M3) {
+        t.ks = valid ? a.k_scale[sp] : 0.f;
+        t.vs = valid ? a.v_scale[sp] : 0.f;
+      }
+    } else {
+      const int64_t toff = (bkv * a.seq_stride + static_cast<int64_t>(kBlock) * (valid ? jt : 0)) *
+                           G::ROW;
+      kt = a.k + toff;
+      vt = a.v + toff;
+    }
+    t.nt = valid ? min(kBlock, L - kBlock * jt) : 0;
+    // rows past the end read the last valid row (the same lines; their weights are 0, and their
+    // V values are finite, so 0 * v stays 0)
+    const int last = max(t.nt, 1) - 1;
+    const char *kr = kt + min(j, last) * G::ROW + g * 16;
+#pragma unroll
+    for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i)
+      t.v[i] = load_stream(vt + min(gv + i * G::TPL, last) * G::ROW + cv * 16);
+  }
+
+  // q operand of head j of the pair: 16-byte chunk of the fp16 q row for score MFMA n (the dims
+  // K load n / 2 half n % 2 covers for e4m3, K load n for fp16)
+  __device__ void begin(const DecodeArgs &a, int64_t qrow, State &s) const {
+    const char *qr = static_cast<const char *>(a.q) + (qrow + min(j, a.gq - 1)) * (D * 2);
+#pragma unroll
+    for (int n = 0; n < NQK; ++n) {
+      const int chunk = KV == KVC_F16 ? g + 4 * n : 2 * (g + 4 * (n >> 1)) + (n & 1);
+      s.q[n] = *reinterpret_cast<const uint4 *>(qr + chunk * 16);
+    }
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) s.o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    s.m = kFloor;
+    s.l = 0.f;
+    s.vref = 1.f;
+  }
+
+  static __device__ __forceinline__ f16x8 as_f16x8(const uint4 &u) {
+    return __builtin_bit_cast(f16x8, u);
+  }
+  // 8 e4m3 codes (two words) as fp16, exactly
+  static __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
+#define KVC_CVT8(w, hi) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, hi))
+    return __builtin_bit_cast(f16x8, make_uint4(KVC_CVT8(w0, false), KVC_CVT8(w0, true),
+                                                KVC_CVT8(w1, false), KVC_CVT8(w1, true)));
+#undef KVC_CVT8
+  }
+
+  __device__ void touch(const Tile &t) const {
+#pragma unroll
+    for (int c = 0; c < KL; ++c)
+      asm volatile("" ::"v"(t.k[c].x), "v"(t.k[c].y), "v"(t.k[c].z), "v"(t.k[c].w));
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i)
+      asm volatile("" ::"v"(t.v[i].x), "v"(t.v[i].y), "v"(t.v[i].z), "v"(t.v[i].w));
+  }
+
+  __device__ void consume(const DecodeArgs &a, const Tile &t, State &s) const {
+    if (t.nt <= 0) {
+      touch(t);
+      return;
+    }
+    // V rows into LDS as fp16
+#pragma unroll
+    for (int i = 0; i < G::LOADS; ++i) {
+      const int row = gv + i * G::TPL;
+      if constexpr (KV == KVC_F16) {
+        *reinterpret_cast<uint4 *>(vbuf + row * D + swz(row, cv) * 8) = t.v[i];
+      } else {
+        *reinterpret_cast<f16x8 *>(vbuf + row * D + swz(row, 2 * cv) * 8) =
+            fp8x8_to_f16(t.v[i].x, t.v[i].y);
+        *reinterpret_cast<f16x8 *>(vbuf + row * D + swz(row, 2 * cv + 1) * 8) =
+            fp8x8_to_f16(t.v[i].z, t.v[i].w);
+      }
+    }
+    // scores of positions 4g..4g+3 for head j
+    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int n = 0; n < NQK; ++n) {
+      f16x8 ka;
+      if constexpr (KV == KVC_F16) {
+        ka = as_f16x8(t.k[n]);
+      } else {
+        const uint4 &w = t.k[n >> 1];
+        ka = (n & 1) ? fp8x8_to_f16(w.z, w.w) : fp8x8_to_f16(w.x, w.y);
+      }
+      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, as_f16x8(s.q[n]), sacc, 0, 0, 0);
+    }
+    const float sc = KV == KVC_E4M3 ? a.cl2 * t.ks : a.cl2;
+    float x[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) x[e] = 4 * g + e < t.nt ? sacc[e] * sc : -__builtin_inff();
+    float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+    {
+      float u, v;
+      lane_pair<16>(mx, u, v);
+      mx = fmaxf(u, v);
+      lane_pair<32>(mx, u, v);
+      mx = fmaxf(u, v);
+    }
+    // The reference moves only when a score passes it by more than kHi (first tile included,
+    // since it starts at kFloor); then it is set kHead below the tile's maximum. e4m3: the ratio
+    // of this block's V scale to the reference scale must also stay within [1/kRat, kRat].
+    float ratio = 1.f;
+    bool rebase = false;
+    float vsn = 1.f;
+    if constexpr (KV == KVC_E4M3) {
+      // an all-zero block has scale 0 and zero codes: any scale represents it
+      vsn = t.vs != 0.f ? t.vs : 1.f;
+      ratio = vsn / s.vref;
+      rebase = !(ratio <= kRat && ratio >= 1.f / kRat);
+    }
+    const bool up = mx > s.m + kHi;
+    if (__ballot(up) != 0 || rebase) {
+      const float mnew = up ? mx - kHead : s.m;
+      float f = __builtin_amdgcn_exp2f(s.m - mnew);
+      s.l *= f;
+      if constexpr (KV == KVC_E4M3) {
+        f *= s.vref / vsn;
+        s.vref = vsn;
+        ratio = 1.f;
+      }
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc) s.o[dc] *= f;
+      s.m = mnew;
+    }
+    float p[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      p[e] = __builtin_amdgcn_exp2f(x[e] - s.m);
+      s.l += p[e];
+    }
+    f16x4 ph, pl;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float pv = KV == KVC_E4M3 ? p[e] * ratio : p[e];
+      ph[e] = static_cast<_Float16>(pv);
+      pl[e] = static_cast<_Float16>(pv - static_cast<float>(ph[e]));
+    }
+    wave_lds_sync();
+    // V^T: dims 16dc + j of positions 4g..4g+3
+    const _Float16 *vr = vbuf + (4 * g) * D + (j & 7);
+#pragma unroll
+    for (int dc = 0; dc < NDC; ++dc) {
+      const int col = (2 * dc + (j >> 3)) ^ (2 * g);
+      f16x4 va;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) va[e] = vr[e * D + col * 8];
+      s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, s.o[dc], 0, 0, 0);
+      s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, s.o[dc], 0, 0, 0);
+    }
+    wave_lds_sync();
+  }
+
+  // Finish a segment: head j's weight sum over the four lane groups, then stage its output row
+  // or record (as finish_seg does; the record of head r is row (2w + slot) * gq + r).
+  __device__ void finish(const DecodeArgs &a, const Seg &sg, int32_t w, State &s,
+                         Stage &st) const {
+    float u, v;
+    lane_pair<16>(s.l, u, v);
+    float l = u + v;
+    lane_pair<32>(l, u, v);
+    l = u + v;
+    const int32_t GQ = a.gq;
+    if (st.n + GQ > a.stage_rows) flush_stage<D>(a, st);
+    const bool whole = !sg.cut_start && !sg.cut_end;
+    const int32_t out0 = sg.b * a.Hq + sg.h * GQ;
+    const int32_t rec0 = (w * 2 + (sg.cut_start ? 0 : 1)) * GQ;
+    if (j < GQ) {
+      float *e = st.base + (st.n + j) * (D + 4);
+      const float vr = KV == KVC_E4M3 ? s.vref : 1.f;
+#pragma unroll
+      for (int dc = 0; dc < NDC; ++dc)
+        *reinterpret_cast<f32x4 *>(e + 16 * dc + 4 * g) = s.o[dc] * vr;
+      if (g == 0) {
+        e[D] = s.m;
+        e[D + 1] = l;
+        e[D + 2] = __int_as_float(whole ? out0 + j : -1 - (rec0 + j));
+      }
+    }
+    st.n += GQ;
+  }
+};
+
 // Walk the chunk [f0, f1) tile by tile as one pipeline: while tile t is consumed, tile t+1 is in
 // flight, also across segment boundaries. Every step issues one fetch of the same shape (after
 // the chunk's last tile, a stand-in that is not consumed). Paged block ids come through the
 // scalar cache one tile ahead of their use (a segment's first two when the segment is found).
-// With GQ > 1 the q slices of the current segment's GQ heads stay in registers; they are loaded
-// when the segment becomes current, after the loads of its first tile.
-template <bool PAGED, int KV, int D, bool QF16, int GQ>
+// A segment's per-segment registers (q of its heads when a wavefront serves several) are loaded
+// when it becomes current, after the loads of its first tile.
+template <bool PAGED, class Core>
 __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre,
                                           const int32_t *len, int32_t f0, int32_t f1, int32_t b0,
-                                          int32_t w, Stage &st) {
-  using G = Geo<KV, D>;
-  using Tile = TileRegs<KV, D, QF16, GQ>;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int g = lane / G::LPT;
-  const int c = lane % G::LPT;
+                                          int32_t w, Stage &st, const Core &core) {
+  using Tile = typename Core::Tile;
+  const int32_t GQ = core.gq(a);
   int32_t f = f0;
   SeqCur sq;
   load_seq(a, pre, len, b0, sq);
@@ -650,35 +969,14 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
   bool has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
   if (has_nxt) seg_ids<PAGED>(a, nxt);
 
-  // K/V head and q row of a pair h of sequence b
+  // K/V head and first q row of a pair h of sequence b
   auto bkv_of = [&](int32_t b, int32_t h) -> int64_t {
     return static_cast<int64_t>(b) * a.H + h / a.nsub;
   };
   auto qrow_of = [&](int32_t b, int32_t h) -> int64_t {
     return static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(h) * GQ;
   };
-  QWords<QF16, G::EPL> qs[GQ];
-  auto load_qs = [&](const Seg &sg) {
-    if constexpr (GQ > 1) {
-      const int64_t q0 = qrow_of(sg.b, sg.h);
-#pragma unroll
-      for (int r = 0; r < GQ; ++r)
-        load_q_words<QF16, G::EPL>(a.q, (q0 + r) * D + c * G::EPL, qs[r]);
-    }
-  };
-
-  float m[GQ], l[GQ];
-  float acc[GQ][G::EPL];
-  auto reset = [&]() {
-#pragma unroll
-    for (int r = 0; r < GQ; ++r) {
-      m[r] = kFloor;
-      l[r] = 0.f;
-#pragma unroll
-      for (int e = 0; e < G::EPL; ++e) acc[r][e] = 0.f;
-    }
-  };
-  reset();
+  typename Core::State s;
 
   int32_t i = 0;        // index, within the current segment, of the tile being consumed
   int32_t ph_next = 0;  // paged: block id of tile i+1 of the current segment (-1 past its end)
@@ -695,50 +993,50 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
       const int32_t h = to_nxt ? nxt.h : cur.h;
       const int32_t j = to_nxt ? nxt.j0 : cur.j0 + i + 1;
       const int32_t L = to_nxt ? nxt.L : cur.L;
-      fetch_tile<PAGED, KV, D, QF16, GQ>(a, nb, bkv_of(b, h), h / a.nsub, qrow_of(b, h), j, ph,
-                                         L, !last || has_nxt, g, c);
+      core.fetch(a, nb, bkv_of(b, h), h / a.nsub, qrow_of(b, h), j, ph, L, !last || has_nxt);
     }
     if constexpr (PAGED) ph_next = i + 2 < cur.n ? block_id(a, cur.b, cur.j0 + i + 2) : -1;
-    consume_tile<KV, D, QF16, GQ>(cb, qs, a.cl2, g, m, l, acc);
-    store_new_row<KV, D, QF16, GQ>(cb, g, c);
+    core.consume(a, cb, s);
     if (!last) {
       ++i;
       return true;
     }
-    finish_seg<KV, D, GQ>(a, cur, w, g, c, m, l, acc, st);
+    core.finish(a, cur, w, s, st);
     if (!has_nxt) return false;
     cur = nxt;
-    load_qs(cur);
+    core.begin(a, qrow_of(cur.b, cur.h), s);
     i = 0;
     if constexpr (PAGED) ph_next = cur.ph1;
-    reset();
     has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
     if (has_nxt) seg_ids<PAGED>(a, nxt);
     return true;
   };
 
   Tile ta, tb;
-  fetch_tile<PAGED, KV, D, QF16, GQ>(a, ta, bkv_of(cur.b, cur.h), cur.h / a.nsub,
-                                     qrow_of(cur.b, cur.h), cur.j0, PAGED ? cur.ph0 : 0, cur.L,
-                                     true, g, c);
-  load_qs(cur);
+  core.fetch(a, ta, bkv_of(cur.b, cur.h), cur.h / a.nsub, qrow_of(cur.b, cur.h), cur.j0,
+             PAGED ? cur.ph0 : 0, cur.L, true);
+  core.begin(a, qrow_of(cur.b, cur.h), s);
   for (;;) {
     if (!step(ta, tb)) break;
     if (!step(tb, ta)) break;
   }
-  flush_stage<D>(a, st);
+  flush_stage<Core::kD>(a, st);
 }
 
-template <bool PAGED, int KV, int D, bool QF16, int GQ>
-__global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
-  extern __shared__ int32_t smem[];
+// The body of both pass-1 kernels: block prefix, header, the wavefront's chunk, the walk. LDS:
+// pre, len, wsum, then a.stage_rows staged rows per wavefront, then (matrix cores) one fp16 V
+// tile per wavefront.
+template <bool PAGED, class Core, int D>
+__device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *smem, int32_t gq,
+                                               int32_t &f0_out, int32_t &f1_out, int32_t &b0_out,
+                                               int32_t &w_out) {
   int32_t *pre = smem;
   int32_t *len = smem + a.B + 1;
   int32_t *wsum = len + a.B;
   block_prefix(a.lens, a.B, a.cap, pre, len, wsum);
   Stage st;
   st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
-            (threadIdx.x >> 6) * kStageRows * (D + 4);
+            (threadIdx.x >> 6) * a.stage_rows * (D + 4);
   st.n = 0;
 
   const int32_t total = a.Hp * pre[a.B];
@@ -750,14 +1048,16 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
       a.ws_hdr[1] = a.B;
       a.ws_hdr[2] = a.Hp;
       a.ws_hdr[3] = D;
-      a.ws_hdr[4] = GQ;
+      a.ws_hdr[4] = gq;
     }
   }
   const int32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWgWaves + (threadIdx.x >> 6));
+  w_out = w;
   const int64_t f0 = static_cast<int64_t>(w) * C;
-  if (f0 >= total) return;
-  const int32_t f1 = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
-  int32_t f = static_cast<int32_t>(f0);
+  f0_out = static_cast<int32_t>(min(f0, static_cast<int64_t>(total)));
+  f1_out = static_cast<int32_t>(min(f0 + C, static_cast<int64_t>(total)));
+  if (f0 >= total) return st;
+  const int32_t f = static_cast<int32_t>(f0);
 
   // the sequence holding tile f0: the largest b in [0, B) with Hp*pre[b] <= f0 (pre does not
   // decrease and pre[0] = 0). Lanes test 64 evenly spaced candidates at once, then the 64 (or
@@ -772,8 +1072,34 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
     const uint64_t m1 = __ballot(lane < S && lo + lane < a.B && a.Hp * pre[i1] <= f);
     lo += kWave - 1 - __clzll(static_cast<long long>(m1));
   }
-  lo = __builtin_amdgcn_readfirstlane(lo);
-  run_chunk<PAGED, KV, D, QF16, GQ>(a, pre, len, f, f1, lo, w, st);
+  b0_out = __builtin_amdgcn_readfirstlane(lo);
+  return st;
+}
+
+template <bool PAGED, int KV, int D, bool QF16, int GQ>
+__global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
+  extern __shared__ int32_t smem[];
+  using Core = VecCore<PAGED, KV, D, QF16, GQ>;
+  int32_t f0, f1, b0, w;
+  Stage st = partial_setup<PAGED, Core, D>(a, smem, GQ, f0, f1, b0, w);
+  if (f0 >= f1) return;
+  const Core core(threadIdx.x & (kWave - 1));
+  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
+}
+
+template <bool PAGED, int KV, int D>
+__global__ void __launch_bounds__(kWgThreads) decode_partial_mfma_kernel(const DecodeArgs a) {
+  extern __shared__ int32_t smem[];
+  using Core = MfmaCore<PAGED, KV, D>;
+  int32_t f0, f1, b0, w;
+  Stage st = partial_setup<PAGED, Core, D>(a, smem, a.gq, f0, f1, b0, w);
+  if (f0 >= f1) return;
+  _Float16 *vbuf = reinterpret_cast<_Float16 *>(
+      reinterpret_cast<char *>(smem + stage_offset(a.B)) +
+      static_cast<size_t>(kWgWaves) * a.stage_rows * (D + 4) * sizeof(float) +
+      (threadIdx.x >> 6) * Core::kVbufBytes);
+  const Core core(threadIdx.x & (kWave - 1), vbuf);
+  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -796,10 +1122,10 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
   const int32_t hq = static_cast<int32_t>(bh % Hq);
   const int D = a.D;
   const int32_t C = a.ws_hdr[0];
-  // query heads pass 1 served per wavefront (1, 2, 4 or 8, dividing G); the pass-1 pair of this
+  // query heads pass 1 served per wavefront (1 to 16, dividing G); the pass-1 pair of this
   // query head and its place among the pair's GQ heads
   const int32_t GQ = a.ws_hdr[4];
-  const bool gq_ok = (GQ == 1 || GQ == 2 || GQ == 4 || GQ == 8) && a.G % GQ == 0;
+  const bool gq_ok = GQ >= 1 && GQ <= kMaxGroup && a.G % GQ == 0;
   const int32_t gq = gq_ok ? GQ : 1;
   const int32_t nsub = a.G / gq;
   const int32_t rr = hq % a.G;
@@ -879,57 +1205,59 @@ int device_cu_count() {
 
 using PartialKernel = void (*)(DecodeArgs);
 
-// Query heads one wavefront serves from one K/V head: the largest of 8, 4, 2 dividing G for
-// fp16 queries over fp16 (or paged e4m3) caches, else 1 (then each query head is its own pair
-// and its K/V head is read once per query head).
-inline int group_width(int G, kvc_dtype kv, bool q_f16, bool paged) {
-  const bool shared = q_f16 && (kv == KVC_F16 || (paged && kv == KVC_E4M3));
-  if (!shared) return 1;
-  for (int w = kMaxGroup; w > 1; w >>= 1)
+// How pass 1 serves G query heads per K/V head. With fp16 queries over an fp16 (or paged e4m3)
+// cache and G > 1, the matrix-core kernel serves gq heads per wavefront, the largest divisor of
+// G up to 16, and each K/V byte is read G/gq times (once for G <= 16). Otherwise each query head
+// is its own pair on the vector kernel and its K/V head is read once per query head.
+struct GroupPlan {
+  int gq;
+  bool mfma;
+};
+
+inline int largest_group_divisor(int G) {
+  for (int w = kMaxGroup; w > 1; --w)
     if (G % w == 0) return w;
   return 1;
+}
+
+inline GroupPlan group_plan(int G, kvc_dtype kv, bool q_f16, bool paged) {
+  const bool mfma_ok = q_f16 && (kv == KVC_F16 || (paged && kv == KVC_E4M3));
+  const int w = largest_group_divisor(G);
+  if (mfma_ok && w > 1) return {w, true};
+  return {1, false};
 }
 
 // Records are sized for the widest group G allows, whatever the dtypes.
-inline int ws_group(int G) {
-  for (int w = kMaxGroup; w > 1; w >>= 1)
-    if (G % w == 0) return w;
-  return 1;
-}
+inline int ws_group(int G) { return largest_group_divisor(G); }
 
 template <bool PAGED, bool QF16, int D>
-PartialKernel pick_kernel_d(kvc_dtype kv, int GQ) {
-  if (GQ == 1) {
-    if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, D, QF16, 1>;
-    if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1>;
-    if constexpr (PAGED)
-      if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1>;
-    return nullptr;
-  }
-  if constexpr (QF16) {
-    if (kv == KVC_F16) {
-      if (GQ == 2) return decode_partial_kernel<PAGED, KVC_F16, D, true, 2>;
-      if (GQ == 4) return decode_partial_kernel<PAGED, KVC_F16, D, true, 4>;
-      if (GQ == 8) return decode_partial_kernel<PAGED, KVC_F16, D, true, 8>;
-    }
-    if constexpr (PAGED) {
-      if (kv == KVC_E4M3) {
-        if (GQ == 2) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 2>;
-        if (GQ == 4) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 4>;
-        if (GQ == 8) return decode_partial_kernel<PAGED, KVC_E4M3, D, true, 8>;
-      }
-    }
-  }
+PartialKernel pick_vec_d(kvc_dtype kv) {
+  if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, D, QF16, 1>;
+  if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1>;
+  if constexpr (PAGED)
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1>;
+  return nullptr;
+}
+
+template <bool PAGED, int D>
+PartialKernel pick_mfma_d(kvc_dtype kv) {
+  if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D>;
+  if constexpr (PAGED)
+    if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D>;
   return nullptr;
 }
 
 template <bool PAGED>
-PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, int GQ) {
-  if (D == 64)
-    return q_f16 ? pick_kernel_d<PAGED, true, 64>(kv, GQ) : pick_kernel_d<PAGED, false, 64>(kv, GQ);
+PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, bool mfma) {
+  if (mfma) {
+    if (!q_f16) return nullptr;
+    if (D == 64) return pick_mfma_d<PAGED, 64>(kv);
+    if (D == 128) return pick_mfma_d<PAGED, 128>(kv);
+    return nullptr;
+  }
+  if (D == 64) return q_f16 ? pick_vec_d<PAGED, true, 64>(kv) : pick_vec_d<PAGED, false, 64>(kv);
   if (D == 128)
-    return q_f16 ? pick_kernel_d<PAGED, true, 128>(kv, GQ)
-                 : pick_kernel_d<PAGED, false, 128>(kv, GQ);
+    return q_f16 ? pick_vec_d<PAGED, true, 128>(kv) : pick_vec_d<PAGED, false, 128>(kv);
   return nullptr;
 }
 
@@ -984,7 +1312,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   if (!paged && kv_dtype == KVC_E4M3) return KVC_E_UNSUPPORTED;
   if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
   const bool q_f16 = q_dtype == KVC_F16;
-  const int GQ = group_width(G, kv_dtype, q_f16, paged);
+  const GroupPlan gp = group_plan(G, kv_dtype, q_f16, paged);
+  const int GQ = gp.gq;
   const int32_t Hp = H * (G / GQ);  // pairs per sequence
   const int64_t tiles_cap =
       static_cast<int64_t>(B) * Hp * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
@@ -1001,12 +1330,16 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
 
   const int64_t tiles_hint = static_cast<int64_t>(B) * Hp *
                              ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
-  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, GQ)
-                             : pick_kernel<false>(kv_dtype, D, q_f16, GQ);
+  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, gp.mfma)
+                             : pick_kernel<false>(kv_dtype, D, q_f16, gp.mfma);
   if (!kern) return KVC_E_UNSUPPORTED;
+  // staged rows per wavefront: a segment stages GQ rows at once; the matrix-core kernel also
+  // holds one fp16 V tile per wavefront
+  const int stage_rows = GQ <= kStageRows ? kStageRows : 2 * kStageRows;
   const size_t shmem = (static_cast<size_t>(stage_offset(B)) +
-                        static_cast<size_t>(kWgWaves) * kStageRows * (D + 4)) *
-                       sizeof(int32_t);
+                        static_cast<size_t>(kWgWaves) * stage_rows * (D + 4)) *
+                           sizeof(int32_t) +
+                       (gp.mfma ? static_cast<size_t>(kWgWaves) * kBlock * D * 2 : 0);
   // one round of wavefronts: never more than fit on the GPU at once
   int wpc = waves_per_cu(kv_dtype, D);
   const int fit = resident_waves_per_cu(kern, shmem);
@@ -1028,6 +1361,8 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   a.H = H;
   a.G = G;
   a.nsub = G / GQ;
+  a.gq = GQ;
+  a.stage_rows = stage_rows;
   a.Hp = Hp;
   a.Hq = H * G;
   a.cap = cap;
