@@ -336,6 +336,18 @@ class ContigBench:
         return dt, out, int(lens.sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
 
 
+def kernel_name(w: workloads.Workload) -> str:
+    """The pass-1 kernel the workload runs: the vector kernel for multi-head attention, the
+    matrix-core kernel (up to 16 query heads per wavefront, a divisor of the group) for shared
+    K/V heads with fp16 queries."""
+    G = w.extra.get("group", 1)
+    if G == 1:
+        return f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> (attention pass 1)"
+    gq = max(d for d in range(1, 17) if G % d == 0)
+    return (f"kvc::decode_partial_mfma_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> (attention "
+            f"pass 1 on the matrix cores, {gq} query heads per wavefront)")
+
+
 def blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
@@ -348,7 +360,7 @@ def blas_threads() -> int:
 
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", "kvc_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_paged_f16_llama13b_traffic.txt")
-PASS1 = "decode_partial_kernel<true, 1, 128, true>"
+PASS1 = "decode_partial_kernel<true, 1, 128, true, 1>"
 
 
 def source_hash() -> str:
@@ -502,8 +514,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(w.batch * K / elapsed, 1),
         "roofline": {
-            "kernel": f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}, "
-                      f"{min(w.extra.get('group', 1), 8)} q heads per wavefront> (attention pass 1)",
+            "kernel": kernel_name(w),
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBS,
