@@ -6,8 +6,10 @@ Three independent paths:
   * decode_row       -- the definition for one query over L cached positions;
   * full_causal      -- recompute all rows with the causal mask, no cache;
   * cached_decode    -- the naive cached loop: concatenate the new k, v and attend the new q.
-and the head-sharing variant:
-  * grouped_decode   -- several query heads attend one shared key/value head (MQA / GQA).
+and the variants:
+  * grouped_decode   -- several query heads attend one shared key/value head (MQA / GQA);
+  * window_decode    -- the query attends only the most recent `window` positions (rolling
+                        window), with rolling_cached_decode as the page's step-by-step procedure.
 """
 from __future__ import annotations
 
@@ -115,3 +117,42 @@ def grouped_decode(q, K, V, scale) -> np.ndarray:
     return np.stack([decode_row(q[h], K[kv_head_of(h, Hq, Hkv)], V[kv_head_of(h, Hq, Hkv)], scale)
                      for h in range(Hq)])
 
+
+def window_start(L: int, window: int) -> int:
+    """First position attended at attended length L (the new token included) under a rolling
+    window of `window` positions; window 0 means no window."""
+    if window < 0 or L < 0:
+        raise ValueError("window and length must be non-negative")
+    return max(0, L - window) if window else 0
+
+
+def window_decode(q, K, V, scale, window: int) -> np.ndarray:
+    """Decode under a rolling window: the new query attends only the most recent `window`
+    positions, its own included.
+
+    "KV Cache Mechanism Explained", section 8, item 2: the cache keeps a fixed-size window; when
+    it holds more than WINDOW_SIZE entries only the last WINDOW_SIZE are kept. The reading taken:
+    the trim follows each append and precedes the attention, so a query at length L attends
+    positions window_start(L, window) .. L-1. K, V: [L, D] hold every position 0 .. L-1.
+    """
+    s = window_start(np.asarray(K).shape[0], window)
+    return decode_row(q, np.asarray(K)[s:], np.asarray(V)[s:], scale)
+
+
+def rolling_cached_decode(Qs, Ks, Vs, scale, window: int) -> np.ndarray:
+    """The rolling cache of "KV Cache Mechanism Explained", section 8, item 2, step by step:
+    each step concatenates the new k, v onto the cache; if the cache then holds more than
+    `window` entries it keeps only the last `window`; the new query attends the whole cache.
+    window 0 never trims. Qs, Ks, Vs: [T, D]. Returns [T, D]."""
+    Qs = np.asarray(Qs, dtype=np.float64)
+    D = Qs.shape[1]
+    K_cache, V_cache = np.zeros((0, D)), np.zeros((0, D))
+    rows = []
+    for t in range(Qs.shape[0]):
+        K_cache = np.concatenate([K_cache, np.asarray(Ks[t:t + 1], dtype=np.float64)], axis=0)
+        V_cache = np.concatenate([V_cache, np.asarray(Vs[t:t + 1], dtype=np.float64)], axis=0)
+        if window and len(K_cache) > window:
+            K_cache = K_cache[-window:]
+            V_cache = V_cache[-window:]
+        rows.append(decode_row(Qs[t], K_cache, V_cache, scale))
+    return np.stack(rows) if rows else np.zeros((0, D))

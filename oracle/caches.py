@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode_row, grouped_decode
+from .attention import decode_row, grouped_decode, window_start
 from .codecs import e4m3_decode, fp8_write_token
 
 BS = 16
@@ -42,15 +42,17 @@ class ContigCache:
                     self.K[b, :, p, :] = k_new[b, t]
                     self.V[b, :, p, :] = v_new[b, t]
 
-    def decode(self, q, lens, scale) -> np.ndarray:
+    def decode(self, q, lens, scale, window: int = 0) -> np.ndarray:
         """q: [B, Hq, D] with Hq a multiple of the cache's H (query heads sharing key/value heads
         as in grouped_decode; Hq = H is plain multi-head attention); lens[b]: attended length
-        (the new token included). Returns [B, Hq, D]."""
+        (the new token included); window > 0: only positions window_start(lens[b], window) ..
+        lens[b]-1 are attended. Returns [B, Hq, D]."""
         Hq = q.shape[1]
         out = np.zeros((self.B, Hq, self.D))
         for b in range(self.B):
             L = int(lens[b])
-            out[b] = grouped_decode(q[b], self.K[b, :, :L], self.V[b, :, :L], scale)
+            s = window_start(L, window)
+            out[b] = grouped_decode(q[b], self.K[b, :, s:L], self.V[b, :, s:L], scale)
         return out
 
 
@@ -96,24 +98,28 @@ class PagedCache:
             return e4m3_decode(codes) * np.float64(s)
         return (self.K[blk] if pool == "k" else self.V[blk]).astype(np.float64)
 
-    def gather(self, table, L: int):
-        """K, V of one sequence, [H, L, D] fp64, read token by token through its block table."""
-        K = np.zeros((self.H, L, self.D))
-        V = np.zeros((self.H, L, self.D))
+    def gather(self, table, L: int, start: int = 0):
+        """K, V of positions start .. L-1 of one sequence, [H, L - start, D] fp64, read token by
+        token through its block table."""
+        K = np.zeros((self.H, L - start, self.D))
+        V = np.zeros((self.H, L - start, self.D))
         cache = {}
-        for t in range(L):
+        for t in range(start, L):
             blk, off = int(table[t // BS]), t % BS
+            if blk < 0:
+                raise ValueError(f"position {t} lies in a dropped block")
             if blk not in cache:
                 cache[blk] = (self.values("k", blk), self.values("v", blk))
-            K[:, t, :] = cache[blk][0][:, off, :]
-            V[:, t, :] = cache[blk][1][:, off, :]
+            K[:, t - start, :] = cache[blk][0][:, off, :]
+            V[:, t - start, :] = cache[blk][1][:, off, :]
         return K, V
 
-    def decode(self, q, tables, lens, scale, heads=None) -> np.ndarray:
+    def decode(self, q, tables, lens, scale, heads=None, window: int = 0) -> np.ndarray:
         """q: [B, Hq, D] with Hq a multiple of the pool's H (query head hq reads key/value head
         kv_head_of(hq, Hq, H), as in grouped_decode); tables: [B, max_blocks]; lens[b]: attended
-        length. Returns [B, Hq, D] (only the listed query heads are computed when `heads` is
-        given; the rest stay 0)."""
+        length; window > 0: only positions window_start(lens[b], window) .. lens[b]-1 are
+        attended (rolling window). Returns [B, Hq, D] (only the listed query heads are computed
+        when `heads` is given; the rest stay 0)."""
         B, Hq = len(lens), q.shape[1]
         G = Hq // self.H
         if G * self.H != Hq:
@@ -121,7 +127,7 @@ class PagedCache:
         out = np.zeros((B, Hq, self.D))
         hs = range(Hq) if heads is None else heads
         for b in range(B):
-            K, V = self.gather(tables[b], int(lens[b]))
+            K, V = self.gather(tables[b], int(lens[b]), window_start(int(lens[b]), window))
             for h in hs:
                 out[b, h] = decode_row(q[b, h], K[h // G], V[h // G], scale)
         return out

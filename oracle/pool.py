@@ -15,7 +15,11 @@ Acceleration -- KV Cache", section 6.1):
   * copy-on-write (section 3.3): writing into a block whose refcount > 1 first takes a fresh
     block, records a (src, dst) copy, drops one reference to src and repoints the table;
   * free: drop one reference per block; a block whose count reaches 0 is free again (its
-    contents are left as they are).
+    contents are left as they are);
+  * slide: the rolling window of "KV Cache Mechanism Explained", section 8, item 2, in paged
+    form: a block all of whose positions lie before the window is dropped from the sequence
+    (one reference released, its table entry set to -1). Positions stay absolute: the length
+    keeps counting every token appended, and dropped entries form a prefix of the table.
 
 Readings where the pages are silent: sequence ids are the lowest id not in use; appends for
 several sequences are applied in the order given, all tokens of one sequence before the next;
@@ -130,14 +134,39 @@ class PoolModel:
         child = self.alloc()
         self.seqs[child] = {"len": p["len"], "table": list(p["table"])}
         for b in p["table"]:
-            self.refcount[b] += 1
+            if b >= 0:
+                self.refcount[b] += 1
         return child
 
     def free(self, s: int) -> None:
         seq = self._need(s)
         for b in seq["table"]:
-            self.refcount[b] -= 1
+            if b >= 0:
+                self.refcount[b] -= 1
         del self.seqs[s]
+
+    def slide(self, seqs, window: int) -> int:
+        """Rolling window: for each listed sequence, drop every block whose 16 positions all lie
+        before the window's first position max(0, len - window), i.e. logical blocks
+        0 .. (len - window) // 16 - 1 still held. Each dropped entry releases one reference and
+        becomes -1. window 0 drops nothing. Returns the number of entries dropped."""
+        if window < 0:
+            raise PoolError(E_INVALID, "negative window")
+        for s in seqs:
+            self._need(s)
+        dropped = 0
+        if window == 0:
+            return 0
+        for s in seqs:
+            seq = self.seqs[s]
+            start = max(0, seq["len"] - window)
+            for i in range(start // self.block_size):
+                b = seq["table"][i]
+                if b >= 0:
+                    self.refcount[b] -= 1
+                    seq["table"][i] = -1
+                    dropped += 1
+        return dropped
 
     def block_table(self, seqs):
         """Per sequence: the table padded with -1 to max_blocks_per_seq, and the length."""
@@ -159,19 +188,25 @@ class PoolModel:
             "num_seqs": len(self.seqs),
             "cow_copies": self.cow_copies,
             "tokens": sum(s["len"] for s in self.seqs.values()),
-            "slots_logical": sum(len(s["table"]) * self.block_size for s in self.seqs.values()),
+            "slots_logical": sum(sum(1 for b in s["table"] if b >= 0) * self.block_size
+                                 for s in self.seqs.values()),
         }
 
     def check(self) -> None:
         """Raise PoolError(E_INVALID) unless every invariant holds: each block's refcount equals
         the number of table entries naming it; each table has exactly ceil(len/16) entries,
-        within the table capacity, in range and without repeats."""
+        within the table capacity, in range and without repeats, except a prefix of entries
+        dropped by slide (-1)."""
         refs = [0] * self.num_blocks
         for sid, s in self.seqs.items():
             t = s["table"]
             need = -(-s["len"] // self.block_size)
             if len(t) != need or len(t) > self.max_blocks_per_seq:
                 raise PoolError(E_INVALID, f"sequence {sid}: table size")
+            k = 0
+            while k < len(t) and t[k] == -1:
+                k += 1
+            t = t[k:]
             if len(set(t)) != len(t):
                 raise PoolError(E_INVALID, f"sequence {sid}: repeated block")
             for b in t:
