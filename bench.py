@@ -43,7 +43,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
                     choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
-                             "gqa8-paged"])
+                             "gqa8-paged", "llama13b-window"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
@@ -72,6 +72,7 @@ class PagedBench:
         B, H, D = w.batch, w.heads, w.head_dim
         self.B, self.H, self.D = B, H, D
         self.G = w.extra.get("group", 1)   # query heads per K/V head
+        self.W = w.extra.get("window", 0)  # rolling window (0: none)
         Hq = H * self.G
         if w.ctx:
             lens = np.full(B, w.ctx, dtype=np.int64)
@@ -90,6 +91,8 @@ class PagedBench:
         # prefill: every sequence holds L_b - 1 tokens, written per layer in one call
         slots = np.concatenate([self.pool.append([s], int(L) - 1)[0]
                                 for s, L in zip(self.seqs, lens)])
+        if self.W:
+            self.pool.slide(self.seqs, self.W)
         slots_d = torch.from_numpy(slots).to(dev)
         for li, layer in enumerate(self.layers):
             k = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li)
@@ -122,6 +125,8 @@ class PagedBench:
     def step(self, ev=None):
         kvc, torch = self.kvc, self.torch
         slots, src, dst = self.pool.append(self.seqs, 1)
+        if self.W:
+            self.pool.slide(self.seqs, self.W)
         tab_h, len_h, slot_h, done = self.ring[self.ring_i]
         self.ring_i = (self.ring_i + 1) % len(self.ring)
         done.synchronize()
@@ -148,6 +153,10 @@ class PagedBench:
                                                 self.knew[li], self.vnew[li], self.max_ctx,
                                                 scale=self.scale, out=self.out[li],
                                                 workspace=self.ws)
+            elif self.W:
+                kvc.decode_window_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
+                                                self.max_ctx, self.W, scale=self.scale,
+                                                out=self.out[li], workspace=self.ws)
             elif self.G > 1:
                 kvc.decode_gqa_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
                                              self.max_ctx, scale=self.scale, out=self.out[li],
@@ -157,7 +166,7 @@ class PagedBench:
                                          scale=self.scale, out=self.out[li], workspace=self.ws)
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li + 1, self.stream)
-            if self.G > 1:
+            if self.G > 1 or self.W:
                 kvc.decode_gqa_merge(self.B, self.H, self.G, self.D, self.out[li], self.ws)
             else:
                 kvc.decode_merge(self.B, self.H, self.D, self.out[li], self.ws)
@@ -165,12 +174,14 @@ class PagedBench:
     def bytes_step(self, lens):
         """Algorithmic HBM bytes of one step over all layers, and of one pass-1 launch: every
         attended K/V row read once (the new one from the new-K/V buffer), the new rows written
-        once, block tables (and fp8 scales), lengths, q and out. The fused pass 1 also does the
-        write."""
+        once, block tables (and fp8 scales) of the attended blocks, lengths, q and out. The fused
+        pass 1 also does the write. With a rolling window only the window's rows and blocks
+        count."""
         elt = ELT[self.w.kv_dtype]
         B, H, D = self.B, self.H, self.D
-        kv = int(lens.sum()) * H * D * 2 * elt
-        blocks = int(sum(workloads.blocks_for(L) for L in lens))
+        first = np.maximum(lens - self.W, 0) if self.W else np.zeros_like(lens)
+        kv = int((lens - first).sum()) * H * D * 2 * elt
+        blocks = int(sum(workloads.blocks_for(L) - int(f) // 16 for L, f in zip(lens, first)))
         table = blocks * 4 + (blocks * 8 if self.w.kv_dtype == "e4m3" else 0) + B * 4
         qo = B * H * self.G * D * (2 + 2)
         append = B * H * D * 2 * elt + (B * 8 if self.w.kv_dtype == "e4m3" else 0)
@@ -184,6 +195,7 @@ class PagedBench:
 
         layer = self.layers[li]
         tables, lens = self.pool.block_table(self.seqs)
+        first = np.maximum(lens - self.W, 0) if self.W else np.zeros_like(lens)
         ref = PagedCache(layer.num_blocks, self.H, self.D, self.w.kv_dtype)
         ref.K = layer.k_pool.cpu().numpy()
         ref.V = layer.v_pool.cpu().numpy()
@@ -192,9 +204,9 @@ class PagedBench:
             ref.v_scale = layer.v_scale.cpu().numpy()
         q = self.q[li].float().cpu().numpy()
         t0 = time.perf_counter()
-        out = ref.decode(q, tables, lens, self.scale)
+        out = ref.decode(q, tables, lens, self.scale, window=self.W)
         dt = time.perf_counter() - t0
-        return dt, out, int(lens.sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
+        return dt, out, int((lens - first).sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
 
 
 class HipEvents:
@@ -341,10 +353,12 @@ def kernel_name(w: workloads.Workload) -> str:
     matrix-core kernel (up to 16 query heads per wavefront, a divisor of the group) for shared
     K/V heads with fp16 queries."""
     G = w.extra.get("group", 1)
+    win = ", rolling window" if "window" in w.extra else ""
     if G == 1:
-        return f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> (attention pass 1)"
+        return (f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}{win}> "
+                "(attention pass 1)")
     gq = max(d for d in range(1, 17) if G % d == 0)
-    return (f"kvc::decode_partial_mfma_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}> (attention "
+    return (f"kvc::decode_partial_mfma_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}{win}> (attention "
             f"pass 1 on the matrix cores, {gq} query heads per wavefront)")
 
 
@@ -445,19 +459,19 @@ def main():
     torch.cuda.set_device(dev)
     w = {"llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
          "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
-         "gqa8-paged": workloads.GQA8_PAGED}[args.workload]
+         "gqa8-paged": workloads.GQA8_PAGED,
+         "llama13b-window": workloads.LLAMA13B_WINDOW}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    grouped = w.extra.get("group", 1) > 1
-    fused = args.append == "fused" or (args.append == "auto" and w.kv_dtype != "e4m3"
-                                        and not grouped)
-    if fused and (w.kv_dtype == "e4m3" or grouped):
-        print("--append fused: e4m3 caches and shared K/V heads take the separate writer",
-              file=sys.stderr)
+    separate = w.kv_dtype == "e4m3" or w.extra.get("group", 1) > 1 or "window" in w.extra
+    fused = args.append == "fused" or (args.append == "auto" and not separate)
+    if fused and separate:
+        print("--append fused: e4m3 caches, shared K/V heads and rolling windows take the "
+              "separate writer", file=sys.stderr)
         sys.exit(2)
     path = "fused" if fused else "separate"
     bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev, fused)
@@ -509,6 +523,7 @@ def main():
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
             if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
             "ctx_growth_per_step": 0 if w is workloads.LLAMA7B_CONTIG else 1,
+            "window": w.extra.get("window", 0),
             "append": path,
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),

@@ -86,7 +86,7 @@ typedef struct kvc_pool_stats {
   int32_t reserved;
   int64_t cow_copies;    /* copy-on-write copies emitted since creation */
   int64_t tokens;        /* sum of live sequence lengths (shared prefixes counted per sequence) */
-  int64_t slots_logical; /* sum over live sequences of 16 x table entries */
+  int64_t slots_logical; /* sum over live sequences of 16 x table entries (dropped ones not counted) */
 } kvc_pool_stats;
 
 /* Create a pool. block_size must be KVC_BLOCK_SIZE. order: host int32[num_blocks], a
@@ -117,15 +117,29 @@ kvc_status kvc_append(kvc_pool *pool, const int32_t *seqs, int32_t n_seqs, int32
                       int32_t cow_cap, int32_t *n_cow_out);
 
 /* New sequence sharing all of parent's blocks: same length, same table, one more reference on
- * every block (parallel sampling, section 5.1). *child_out receives its id. */
+ * every block it holds (parallel sampling, section 5.1). *child_out receives its id. */
 kvc_status kvc_fork(kvc_pool *pool, int32_t parent, int32_t *child_out);
 
-/* End a sequence: one reference fewer on each of its blocks; blocks reaching 0 become free
+/* End a sequence: one reference fewer on each block it holds; blocks reaching 0 become free
  * (their device contents are left as they are). */
 kvc_status kvc_free(kvc_pool *pool, int32_t seq);
 
+/* Rolling window in paged form ("KV Cache Mechanism Explained", section 8, item 2: keep only the
+ * most recent WINDOW_SIZE tokens). For each listed sequence of length L, every block whose 16
+ * positions all lie before max(0, L - window) is dropped: one reference released (a block that
+ * reaches 0 is free) and its table entry set to -1. The length keeps counting every token, so
+ * positions stay absolute and the table still needs ceil(L/16) <= max_blocks_per_seq entries;
+ * dropped entries form a prefix of the table. Decode such a sequence with the window entry
+ * points and the same window (they never read dropped entries).
+ *   seqs:          host int32[n_seqs]
+ *   window:        >= 0; 0 drops nothing
+ *   n_dropped_out: host, may be NULL; receives the number of entries dropped
+ * Errors: KVC_E_NOSEQ, KVC_E_INVALID (nothing changes). */
+kvc_status kvc_slide(kvc_pool *pool, const int32_t *seqs, int32_t n_seqs, int32_t window,
+                     int32_t *n_dropped_out);
+
 /* Block tables and lengths of the listed sequences.
- *   tables_out: host int32[n_seqs][max_blocks_per_seq], unused entries set to -1
+ *   tables_out: host int32[n_seqs][max_blocks_per_seq], unused (and dropped) entries are -1
  *   lens_out:   host int32[n_seqs] (may be NULL) */
 kvc_status kvc_block_table(const kvc_pool *pool, const int32_t *seqs, int32_t n_seqs,
                            int32_t *tables_out, int32_t *lens_out);
@@ -134,7 +148,8 @@ kvc_status kvc_stats(const kvc_pool *pool, kvc_pool_stats *out);
 
 /* Check the pool's invariants ("KV Cache and PagedAttention", section 6.2: leaks show up as
  * wrong reference counts): every refcount equals the number of table entries naming the block,
- * every table has exactly ceil(len/16) entries, within capacity, in range, without repeats.
+ * every table has exactly ceil(len/16) entries, within capacity, in range, without repeats,
+ * except a prefix of entries dropped by kvc_slide (-1).
  * Returns KVC_OK or KVC_E_INVALID. */
 kvc_status kvc_check(const kvc_pool *pool);
 
@@ -310,10 +325,11 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
  *             layer's num_heads is H_kv)
  *   workspace: at least kvc_gqa_workspace_bytes(B, H_kv, G, D) bytes, otherwise as above
  *
- * One wavefront serves up to 8 query heads of a group from each K/V tile it loads (the largest
- * of 8, 4, 2 dividing G) when q is fp16 and the cache fp16 (or paged e4m3); then each K/V byte is
- * read from HBM G/8 times or fewer (once for G <= 8). Other dtype combinations are supported
- * with one query head per wavefront (each K/V byte read G times). No append variant. */
+ * With an fp16 q over an fp16 cache (or a paged e4m3 one) and G > 1, one wavefront serves gq
+ * query heads of a group from each K/V tile it loads, on the matrix cores, gq being the largest
+ * divisor of G up to 16; each K/V byte is then read from HBM G/gq times (once for G <= 16).
+ * Other dtype combinations run one query head per wavefront (each K/V byte read G times).
+ * No append variant. */
 size_t kvc_gqa_workspace_bytes(int32_t B, int32_t H_kv, int32_t G, int32_t D);
 
 kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
@@ -342,6 +358,50 @@ kvc_status kvc_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_
 kvc_status kvc_decode_gqa_merge(int32_t B, int32_t H_kv, int32_t G, int32_t D, void *out,
                                 kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                 void *stream);
+
+/* ==================================================================================== *
+ * Rolling window ("KV Cache Mechanism Explained", section 8, item 2: the cache keeps only the
+ * most recent WINDOW_SIZE tokens).
+ *
+ * Sequence b attends positions max(0, L_b - window) .. L_b - 1 (the new token included), with
+ * L_b = ctx_lens[b] clamped to the capacity as above; window >= 1 (KVC_E_INVALID otherwise). G
+ * query heads share each K/V head exactly as for kvc_decode_gqa_* (G = 1: multi-head). All
+ * other arguments, layouts and errors are those of kvc_decode_gqa_*; the workspace is sized by
+ * kvc_gqa_workspace_bytes(B, H_kv, G, D).
+ *   Paged: positions keep their absolute logical blocks (block b // 16 of the table); entries
+ *     before block max(0, L_b - window) / 16 are never read, so a pool slid with kvc_slide and
+ *     the same window decodes correctly.
+ *   Contiguous: a window over the full-length cache [B][H_kv][S_max][D]. A cache that holds only
+ *     the window can instead be a ring of W = S_max slots (position p stored at slot p % W,
+ *     kvc_append_contig) decoded by kvc_decode_gqa_contig with ctx_lens min(L_b, W): attention
+ *     does not depend on the order of positions. */
+kvc_status kvc_decode_window_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                    const void *k_cache, const void *v_cache, kvc_dtype kv_dtype,
+                                    const int32_t *ctx_lens, int32_t B, int32_t H_kv,
+                                    int32_t S_max, int32_t D, int32_t max_ctx, int32_t window,
+                                    float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                    size_t ws_bytes, void *stream);
+kvc_status kvc_decode_window_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                   const kvc_paged_layer *layer, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                   int32_t max_ctx, int32_t window, float scale, void *out,
+                                   kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                   void *stream);
+/* Pass 1 alone of the two calls above; follow with kvc_decode_gqa_merge. */
+kvc_status kvc_decode_window_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                            const void *k_cache, const void *v_cache,
+                                            kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                            int32_t B, int32_t H_kv, int32_t S_max, int32_t D,
+                                            int32_t max_ctx, int32_t window, float scale,
+                                            void *out, kvc_dtype out_dtype, void *workspace,
+                                            size_t ws_bytes, void *stream);
+kvc_status kvc_decode_window_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                           const kvc_paged_layer *layer,
+                                           const int32_t *block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                           int32_t B, int32_t max_ctx, int32_t window,
+                                           float scale, void *out, kvc_dtype out_dtype,
+                                           void *workspace, size_t ws_bytes, void *stream);
 
 #ifdef __cplusplus
 }

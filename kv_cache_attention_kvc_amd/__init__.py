@@ -23,7 +23,8 @@ __all__ = [
     "append_decode_contig", "append_decode_paged", "append_decode_partial_contig",
     "append_decode_partial_paged", "gqa_workspace_bytes", "new_gqa_workspace",
     "decode_gqa_contig", "decode_gqa_paged", "decode_gqa_partial_contig",
-    "decode_gqa_partial_paged", "decode_gqa_merge",
+    "decode_gqa_partial_paged", "decode_gqa_merge", "decode_window_contig", "decode_window_paged",
+    "decode_window_partial_contig", "decode_window_partial_paged",
 ]
 
 F32, F16, E4M3 = 0, 1, 2
@@ -34,13 +35,16 @@ _STATUS = {0: "KVC_OK", -1: "KVC_E_INVALID", -2: "KVC_E_OOM", -3: "KVC_E_NOSEQ",
 # every symbol include/kvc.h declares
 EXPORTS = [
     "kvc_status_str", "kvc_pool_create", "kvc_pool_destroy", "kvc_alloc", "kvc_append",
-    "kvc_fork", "kvc_free", "kvc_block_table", "kvc_stats", "kvc_check", "kvc_append_contig",
+    "kvc_fork", "kvc_free", "kvc_slide", "kvc_block_table", "kvc_stats", "kvc_check",
+    "kvc_append_contig",
     "kvc_copy_blocks", "kvc_write_paged", "kvc_decode_workspace_bytes", "kvc_decode_attn_contig",
     "kvc_decode_attn_paged", "kvc_decode_partial_contig", "kvc_decode_partial_paged",
     "kvc_decode_merge", "kvc_append_decode_contig", "kvc_append_decode_paged",
     "kvc_append_decode_partial_contig", "kvc_append_decode_partial_paged",
     "kvc_gqa_workspace_bytes", "kvc_decode_gqa_contig", "kvc_decode_gqa_paged",
     "kvc_decode_gqa_partial_contig", "kvc_decode_gqa_partial_paged", "kvc_decode_gqa_merge",
+    "kvc_decode_window_contig", "kvc_decode_window_paged", "kvc_decode_window_partial_contig",
+    "kvc_decode_window_partial_paged",
 ]
 
 
@@ -97,6 +101,7 @@ def load_library() -> ctypes.CDLL:
         "kvc_append": (ctypes.c_int, [_P, _P, _I32, _I32, _P, _P, _P, _I32, _PI32]),
         "kvc_fork": (ctypes.c_int, [_P, _I32, _PI32]),
         "kvc_free": (ctypes.c_int, [_P, _I32]),
+        "kvc_slide": (ctypes.c_int, [_P, _P, _I32, _I32, _PI32]),
         "kvc_block_table": (ctypes.c_int, [_P, _P, _I32, _P, _P]),
         "kvc_stats": (ctypes.c_int, [_P, ctypes.POINTER(PoolStats)]),
         "kvc_check": (ctypes.c_int, [_P]),
@@ -138,6 +143,12 @@ def load_library() -> ctypes.CDLL:
     for name in ("kvc_decode_gqa_paged", "kvc_decode_gqa_partial_paged"):
         sig[name] = (ctypes.c_int, paged_gqa)
     sig["kvc_gqa_workspace_bytes"] = (ctypes.c_size_t, [_I32, _I32, _I32, _I32])
+    contig_win = contig_gqa[:12] + [_I32] + contig_gqa[12:]   # window after max_ctx
+    paged_win = paged_gqa[:9] + [_I32] + paged_gqa[9:]
+    for name in ("kvc_decode_window_contig", "kvc_decode_window_partial_contig"):
+        sig[name] = (ctypes.c_int, contig_win)
+    for name in ("kvc_decode_window_paged", "kvc_decode_window_partial_paged"):
+        sig[name] = (ctypes.c_int, paged_win)
     sig["kvc_decode_gqa_merge"] = (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, ctypes.c_int, _P,
                                                   ctypes.c_size_t, _P])
     for name, (res, args) in sig.items():
@@ -161,7 +172,8 @@ def _check(status: int, where: str) -> None:
 # Host block pool
 # ---------------------------------------------------------------------------------------------
 class Pool:
-    """Host-side block pool: first fit, refcounts, fork, copy-on-write (libkvc C++)."""
+    """Host-side block pool: first fit, refcounts, fork, copy-on-write, rolling-window slide
+    (libkvc C++)."""
 
     def __init__(self, num_blocks: int, max_blocks_per_seq: int, order=None,
                  block_size: int = BLOCK_SIZE):
@@ -215,6 +227,15 @@ class Pool:
 
     def free(self, seq: int) -> None:
         _check(_lib().kvc_free(self._h, seq), "kvc_free")
+
+    def slide(self, seqs: Sequence[int], window: int) -> int:
+        """Rolling window: drop from each sequence the blocks wholly before its last `window`
+        positions (table entries become -1). Returns the number of entries dropped."""
+        seqs = np.ascontiguousarray(seqs, dtype=np.int32)
+        n = ctypes.c_int32()
+        _check(_lib().kvc_slide(self._h, seqs.ctypes.data, len(seqs), int(window),
+                                ctypes.byref(n)), "kvc_slide")
+        return n.value
 
     def block_table(self, seqs: Sequence[int], out_tables=None, out_lens=None):
         """Tables [n, max_blocks_per_seq] (-1 padded) and lengths [n], int32. Optional output
@@ -621,3 +642,70 @@ def decode_gqa_merge(B, H_kv, G, D, out, workspace, stream=None):
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "kvc_decode_gqa_merge")
     return out
+
+
+# ---- rolling window --------------------------------------------------------------------------
+def _window_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, window, scale, out,
+                        workspace, stream):
+    B, H, S, D = k_cache.shape
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    G = _gqa_group(q, H)
+    out = _out_for(q, out)
+    ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(ctx_lens), B, H, S, D, int(max_ctx), int(window), float(scale), _ptr(out),
+        _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def _window_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, window, scale, out,
+                       workspace, stream):
+    B = q.shape[0]
+    if q.dim() != 3 or q.shape[2] != layer.head_dim:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    G = _gqa_group(q, layer.heads)
+    out = _out_for(q, out)
+    ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
+          else workspace)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(ctx_lens), B, int(max_ctx), int(window), float(scale), _ptr(out), _dtype_code(out),
+        _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def decode_window_contig(q, k_cache, v_cache, ctx_lens, max_ctx, window, scale=None, out=None,
+                         workspace=None, stream=None):
+    """Rolling-window decode over a contiguous cache [B, H_kv, S_max, D]: sequence b attends its
+    last `window` positions. q [B, H_kv*G, D] (G = 1: multi-head). Returns out."""
+    return _window_contig_call("kvc_decode_window_contig", q, k_cache, v_cache, ctx_lens, max_ctx,
+                               window, scale, out, workspace, stream)[0]
+
+
+def decode_window_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, window, scale=None,
+                                 out=None, workspace=None, stream=None):
+    """Pass 1 of decode_window_contig; returns (out, workspace) for decode_gqa_merge."""
+    return _window_contig_call("kvc_decode_window_partial_contig", q, k_cache, v_cache, ctx_lens,
+                               max_ctx, window, scale, out, workspace, stream)
+
+
+def decode_window_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, window, scale=None,
+                        out=None, workspace=None, stream=None):
+    """Rolling-window decode over a paged cache (tables may hold entries dropped by
+    Pool.slide with the same window). q [B, H_kv*G, D]. Returns out."""
+    return _window_paged_call("kvc_decode_window_paged", q, layer, block_tables, ctx_lens, max_ctx,
+                              window, scale, out, workspace, stream)[0]
+
+
+def decode_window_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, window,
+                                scale=None, out=None, workspace=None, stream=None):
+    """Pass 1 of decode_window_paged; returns (out, workspace) for decode_gqa_merge."""
+    return _window_paged_call("kvc_decode_window_partial_paged", q, layer, block_tables, ctx_lens,
+                              max_ctx, window, scale, out, workspace, stream)

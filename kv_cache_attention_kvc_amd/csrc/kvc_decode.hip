@@ -84,6 +84,7 @@ struct DecodeArgs {
   // and Hp = H*nsub pairs per sequence. Multi-head attention: G = nsub = 1, Hp = Hq = H.
   int32_t G, nsub, Hp, Hq;
   int32_t gq;          // query heads per pair (G / nsub)
+  int32_t window;      // rolling window: attend positions max(0, L - window) .. L-1 (0: none)
   int32_t stage_rows;  // staged output rows per wavefront (LDS)
   int32_t q_f16, out_f16;
   float cl2;  // scale * log2(e)
@@ -259,11 +260,20 @@ __device__ __forceinline__ void store_elem(void *p, int64_t i, float x, bool f16
 }
 
 // ---- per-workgroup prefix of block counts ------------------------------------------------
-// pre[b] = sum_{b' < b} ceil(clamp(L_b')/16), pre[B] = total blocks over sequences, and
-// len[b] = clamp(L_b), all in LDS. Each thread sums a run of consecutive sequences; runs are
-// scanned with wave shuffles, then across the four waves through LDS.
-__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, int32_t *len,
-                             int32_t *wsum) {
+// First logical block a sequence of length L attends under a rolling window (0 without one).
+template <bool WIN>
+__device__ __forceinline__ int32_t window_block(int32_t L, int32_t window) {
+  if constexpr (WIN) return max(0, L - window) / kBlock;
+  return 0;
+}
+
+// pre[b] = sum_{b' < b} nblk(b'), pre[B] = total blocks over sequences, and len[b] = clamp(L_b),
+// all in LDS; nblk(b) = ceil(clamp(L_b)/16), less the blocks wholly before a rolling window.
+// Each thread sums a run of consecutive sequences; runs are scanned with wave shuffles, then
+// across the four waves through LDS.
+template <bool WIN>
+__device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t window, int32_t *pre,
+                             int32_t *len, int32_t *wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = tid >> 6;
@@ -273,7 +283,7 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
   int32_t sum = 0;
   for (int i = lo; i < hi; ++i) {
     const int32_t L = min(max(lens[i], 0), cap);
-    sum += (L + kBlock - 1) / kBlock;
+    sum += (L + kBlock - 1) / kBlock - window_block<WIN>(L, window);
   }
   int32_t inc = sum;
 #pragma unroll
@@ -289,7 +299,7 @@ __device__ void block_prefix(const int32_t *lens, int B, int cap, int32_t *pre, 
     pre[i] = run;
     const int32_t L = min(max(lens[i], 0), cap);
     len[i] = L;
-    run += (L + kBlock - 1) / kBlock;
+    run += (L + kBlock - 1) / kBlock - window_block<WIN>(L, window);
   }
   if (tid == kWgThreads - 1) pre[B] = inc;
   __syncthreads();
@@ -305,17 +315,18 @@ struct TileRegs {
   uint4 k[G::LOADS];
   uint4 v[G::LOADS];
   int32_t nt;       // valid rows (0: the tile contributes nothing)
+  int32_t lo;       // rolling window: rows below lo lie before the window (first tile only)
   int32_t new_row;  // append mode: the row of the new token in this tile, else -1
   const char *kt;   // the tile's K and V in the cache (where the new row is stored)
   const char *vt;
   float ks, vs;     // fp8 block scales
 };
 
-// Tile j of K/V head hkv of sequence b (bkv = b*H + hkv); phys is its block id (paged); qrow is
-// the row of q of the first query head the wavefront serves (loaded here when GQ == 1).
-// live = false fetches a stand-in with nt = 0 (the first row of block 0 / of the sequence-head),
-// for the step after a chunk's last tile.
-template <bool PAGED, int KV, int D, bool QF16, int GQ>
+// Tile j (logical block j) of K/V head hkv of sequence b (bkv = b*H + hkv); phys is its block id
+// (paged); qrow is the row of q of the first query head the wavefront serves (loaded here when
+// GQ == 1). live = false fetches a stand-in with nt = 0 (the first row of block 0 / of the
+// sequence-head), for the step after a chunk's last tile.
+template <bool PAGED, int KV, int D, bool QF16, int GQ, bool WIN>
 __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, QF16, GQ> &t,
                                            int64_t bkv, int32_t hkv, int64_t qrow, int32_t j,
                                            int32_t phys, int32_t L, bool live, int g, int c) {
@@ -342,6 +353,8 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
     vt = a.v + toff;
   }
   t.nt = valid ? min(kBlock, L - kBlock * j) : 0;
+  // rolling window: positions before max(0, L - window) are not attended
+  t.lo = WIN ? min(max(max(0, L - a.window) - kBlock * j, 0), kBlock) : 0;
   t.kt = kt;
   t.vt = vt;
   // append mode: the tile holding position L-1 takes that row from k_new/v_new (the lanes of
@@ -349,7 +362,7 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
   // That tile is the last of its sequence-head, so it always takes the general path below and
   // the full-tile path carries no per-lane address choice.
   t.new_row = (a.k_new && t.nt > 0 && j == (L - 1) / kBlock) ? (L - 1) % kBlock : -1;
-  if (t.nt == kBlock && t.new_row < 0) {
+  if (t.nt == kBlock && t.new_row < 0 && (!WIN || t.lo == 0)) {
     const int lane_off = g * G::ROW + c * 16;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
@@ -358,12 +371,13 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
     }
   } else {
     // rows past the end load the last valid row again (the same cache lines, so no extra
-    // traffic; with nt = 0, row 0): their scores are masked to -inf, so they weigh 0
+    // traffic; with nt = 0, row 0), rows before a window's start its first row: their scores
+    // are masked to -inf, so they weigh 0
     const int64_t new_off = bkv * G::ROW + c * 16;
     const int last_row = max(t.nt, 1) - 1;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
-      const int row = min(g + i * G::TPL, last_row);
+      const int row = min(WIN ? max(g + i * G::TPL, t.lo) : g + i * G::TPL, last_row);
       const bool nw = row == t.new_row;
       t.k[i] = load_stream(nw ? a.k_new + new_off : kt + row * G::ROW + c * 16);
       t.v[i] = load_stream(nw ? a.v_new + new_off : vt + row * G::ROW + c * 16);
@@ -417,10 +431,11 @@ __device__ __forceinline__ float dot_slice(const uint4 &kr, const QWords<QF16, E
 }
 
 // ---- one tile: online-softmax update of the group state ---------------------------------
-// Rows at or past nt get score -inf (weight 0); their V registers hold a valid row's data.
-// A tile with nt = 0 adds nothing. With GQ query heads per wavefront, each head r keeps its own
-// state (m[r], l[r], acc[r]) and reads the q slice qs[r]; the K and V registers are shared.
-template <int KV, int D, bool QF16, int GQ>
+// Rows at or past nt (and below lo) get score -inf (weight 0); their V registers hold a valid
+// row's data. A tile with nt = 0 adds nothing. With GQ query heads per wavefront, each head r
+// keeps its own state (m[r], l[r], acc[r]) and reads the q slice qs[r]; the K and V registers
+// are shared.
+template <int KV, int D, bool QF16, int GQ, bool WIN>
 __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
                                              const QWords<QF16, Geo<KV, D>::EPL> *qs, float cl2,
                                              int g, float *m, float *l,
@@ -435,7 +450,7 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
   const float sc = (KV == KVC_E4M3) ? cl2 * t.ks : cl2;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
-    const bool ok = g + i * G::TPL < t.nt;
+    const bool ok = g + i * G::TPL < t.nt && (!WIN || g + i * G::TPL >= t.lo);
 #pragma unroll
     for (int r = 0; r < GQ; ++r) {
       const float d = group_sum<G::LPT>(dot_slice<KV, QF16, G::EPL>(t.k[i], qq[r])) * sc;
@@ -476,7 +491,7 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
 // ---- the wavefront's chunk: segments and the tile pipeline --------------------------------
 // A segment is the part of one (sequence, head) pair that lies in the chunk: tiles j0 .. j0+n-1.
 struct Seg {
-  int32_t b, h, j0, n, L;  // h: the pair index in [0, Hp)
+  int32_t b, h, j0, n, L;  // h: the pair index in [0, Hp); j0: logical block of the first tile
   int32_t ph0, ph1;  // paged: block ids of the segment's first two tiles (-1 past the end)
   bool cut_start, cut_end;
 };
@@ -487,8 +502,10 @@ struct Seg {
 // (read from LDS once per sequence, not once per segment).
 struct SeqCur {
   int32_t b, base, nb, L;
+  int32_t jb;  // first logical block the sequence attends (rolling window; else 0)
 };
 
+template <bool WIN>
 __device__ __forceinline__ void load_seq(const DecodeArgs &a, const int32_t *pre,
                                          const int32_t *len, int32_t b, SeqCur &q) {
   const int32_t p0 = sread(pre + b);
@@ -496,13 +513,15 @@ __device__ __forceinline__ void load_seq(const DecodeArgs &a, const int32_t *pre
   q.base = a.Hp * p0;
   q.nb = sread(pre + b + 1) - p0;
   q.L = sread(len + b);
+  q.jb = window_block<WIN>(q.L, a.window);
 }
 
+template <bool WIN>
 __device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre,
                                          const int32_t *len, int32_t &f, int32_t f1, SeqCur &q,
                                          Seg &s) {
   if (f >= f1) return false;
-  while (f >= q.base + a.Hp * q.nb) load_seq(a, pre, len, q.b + 1, q);  // f < total: ends
+  while (f >= q.base + a.Hp * q.nb) load_seq<WIN>(a, pre, len, q.b + 1, q);  // f < total: ends
   const int32_t rel = f - q.base;
   s.b = q.b;
   s.h = rel / q.nb;
@@ -513,6 +532,7 @@ __device__ __forceinline__ bool next_seg(const DecodeArgs &a, const int32_t *pre
   s.cut_start = s.j0 > 0;
   s.cut_end = e < seg_end;
   s.L = q.L;
+  if constexpr (WIN) s.j0 += q.jb;  // from here on j0 is the logical block of the first tile
   f = e;
   return true;
 }
@@ -635,11 +655,12 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
 //   MfmaCore: matrix cores; up to 16 query heads of a group against one K/V head.
 
 // Vector core: the tile code above, one (or two) query heads per wavefront.
-template <bool PAGED, int KV, int D, bool QF16, int GQ>
+template <bool PAGED, int KV, int D, bool QF16, int GQ, bool WIN>
 struct VecCore {
   using G = Geo<KV, D>;
   using Tile = TileRegs<KV, D, QF16, GQ>;
   static constexpr int kD = D;
+  static constexpr bool kWin = WIN;
   struct State {
     QWords<QF16, G::EPL> qs[GQ];  // GQ > 1: the segment's q slices
     float m[GQ], l[GQ];
@@ -652,7 +673,7 @@ struct VecCore {
 
   __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t qrow,
                         int32_t j, int32_t phys, int32_t L, bool live) const {
-    fetch_tile<PAGED, KV, D, QF16, GQ>(a, t, bkv, hkv, qrow, j, phys, L, live, g, c);
+    fetch_tile<PAGED, KV, D, QF16, GQ, WIN>(a, t, bkv, hkv, qrow, j, phys, L, live, g, c);
   }
   // A segment becomes current: its q slices (GQ > 1) and a fresh softmax state.
   __device__ void begin(const DecodeArgs &a, int64_t qrow, State &s) const {
@@ -670,7 +691,7 @@ struct VecCore {
     }
   }
   __device__ void consume(const DecodeArgs &a, const Tile &t, State &s) const {
-    consume_tile<KV, D, QF16, GQ>(t, s.qs, a.cl2, g, s.m, s.l, s.acc);
+    consume_tile<KV, D, QF16, GQ, WIN>(t, s.qs, a.cl2, g, s.m, s.l, s.acc);
     store_new_row<KV, D, QF16, GQ>(t, g, c);
   }
   __device__ void finish(const DecodeArgs &a, const Seg &sg, int32_t w, State &s,
@@ -714,11 +735,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 //     scale multiplies the scores. O is held in units of a reference V scale; a tile's weights
 //     are multiplied by its block's scale over the reference (kept within [1/16, 16], else the
 //     reference moves to this block's scale and O is rescaled).
-template <bool PAGED, int KV, int D>
+template <bool PAGED, int KV, int D, bool WIN>
 struct MfmaCore {
   static_assert(KV == KVC_F16 || KV == KVC_E4M3, "fp16 or e4m3 cache");
   using G = Geo<KV, D>;            // wave-contiguous geometry (V loads)
   static constexpr int kD = D;
+  static constexpr bool kWin = WIN;
   static constexpr int KL = G::ROW / 64;  // K loads per lane per tile (16 bytes each)
   static constexpr int NQK = D / 32;      // score MFMAs per tile
   static constexpr int NDC = D / 16;      // 16-dim output blocks
@@ -732,6 +754,7 @@ struct MfmaCore {
     uint4 k[KL];
     uint4 v[G::LOADS];
     int32_t nt;
+    int32_t lo;  // rolling window: rows below lo lie before the window
     float ks, vs;
   };
   struct State {
@@ -772,15 +795,17 @@ struct MfmaCore {
       vt = a.v + toff;
     }
     t.nt = valid ? min(kBlock, L - kBlock * jt) : 0;
-    // rows past the end read the last valid row (the same lines; their weights are 0, and their
-    // V values are finite, so 0 * v stays 0)
+    t.lo = WIN ? min(max(max(0, L - a.window) - kBlock * jt, 0), kBlock) : 0;
+    // rows past the end read the last valid row (the same lines), rows before a window's start
+    // its first row: their weights are 0, and their V values are finite, so 0 * v stays 0
     const int last = max(t.nt, 1) - 1;
-    const char *kr = kt + min(j, last) * G::ROW + g * 16;
+    auto row_of = [&](int r) { return min(WIN ? max(r, t.lo) : r, last); };
+    const char *kr = kt + row_of(j) * G::ROW + g * 16;
 #pragma unroll
     for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i)
-      t.v[i] = load_stream(vt + min(gv + i * G::TPL, last) * G::ROW + cv * 16);
+      t.v[i] = load_stream(vt + row_of(gv + i * G::TPL) * G::ROW + cv * 16);
   }
 
   // q operand of head j of the pair: 16-byte chunk of the fp16 q row for score MFMA n (the dims
@@ -854,7 +879,8 @@ struct MfmaCore {
     const float sc = KV == KVC_E4M3 ? a.cl2 * t.ks : a.cl2;
     float x[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) x[e] = 4 * g + e < t.nt ? sacc[e] * sc : -__builtin_inff();
+    for (int e = 0; e < 4; ++e)
+      x[e] = 4 * g + e < t.nt && (!WIN || 4 * g + e >= t.lo) ? sacc[e] * sc : -__builtin_inff();
     float mx = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
     {
       float u, v;
@@ -960,13 +986,14 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
   using Tile = typename Core::Tile;
   const int32_t GQ = core.gq(a);
   int32_t f = f0;
+  constexpr bool WIN = Core::kWin;
   SeqCur sq;
-  load_seq(a, pre, len, b0, sq);
+  load_seq<WIN>(a, pre, len, b0, sq);
 
   Seg cur, nxt;
-  next_seg(a, pre, len, f, f1, sq, cur);  // f0 < f1, so there is a first segment
+  next_seg<WIN>(a, pre, len, f, f1, sq, cur);  // f0 < f1, so there is a first segment
   seg_ids<PAGED>(a, cur);
-  bool has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
+  bool has_nxt = next_seg<WIN>(a, pre, len, f, f1, sq, nxt);
   if (has_nxt) seg_ids<PAGED>(a, nxt);
 
   // K/V head and first q row of a pair h of sequence b
@@ -1007,7 +1034,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
     core.begin(a, qrow_of(cur.b, cur.h), s);
     i = 0;
     if constexpr (PAGED) ph_next = cur.ph1;
-    has_nxt = next_seg(a, pre, len, f, f1, sq, nxt);
+    has_nxt = next_seg<WIN>(a, pre, len, f, f1, sq, nxt);
     if (has_nxt) seg_ids<PAGED>(a, nxt);
     return true;
   };
@@ -1033,7 +1060,7 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   int32_t *pre = smem;
   int32_t *len = smem + a.B + 1;
   int32_t *wsum = len + a.B;
-  block_prefix(a.lens, a.B, a.cap, pre, len, wsum);
+  block_prefix<Core::kWin>(a.lens, a.B, a.cap, a.window, pre, len, wsum);
   Stage st;
   st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
             (threadIdx.x >> 6) * a.stage_rows * (D + 4);
@@ -1076,10 +1103,10 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   return st;
 }
 
-template <bool PAGED, int KV, int D, bool QF16, int GQ>
+template <bool PAGED, int KV, int D, bool QF16, int GQ, bool WIN>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
-  using Core = VecCore<PAGED, KV, D, QF16, GQ>;
+  using Core = VecCore<PAGED, KV, D, QF16, GQ, WIN>;
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, GQ, f0, f1, b0, w);
   if (f0 >= f1) return;
@@ -1087,10 +1114,10 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
 }
 
-template <bool PAGED, int KV, int D>
+template <bool PAGED, int KV, int D, bool WIN>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_mfma_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
-  using Core = MfmaCore<PAGED, KV, D>;
+  using Core = MfmaCore<PAGED, KV, D, WIN>;
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, a.gq, f0, f1, b0, w);
   if (f0 >= f1) return;
@@ -1230,35 +1257,42 @@ inline GroupPlan group_plan(int G, kvc_dtype kv, bool q_f16, bool paged) {
 // Records are sized for the widest group G allows, whatever the dtypes.
 inline int ws_group(int G) { return largest_group_divisor(G); }
 
-template <bool PAGED, bool QF16, int D>
+template <bool PAGED, bool QF16, int D, bool WIN>
 PartialKernel pick_vec_d(kvc_dtype kv) {
-  if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, D, QF16, 1>;
-  if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1>;
+  if (kv == KVC_F32) return decode_partial_kernel<PAGED, KVC_F32, D, QF16, 1, WIN>;
+  if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1, WIN>;
   if constexpr (PAGED)
-    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1>;
+    if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1, WIN>;
   return nullptr;
 }
 
-template <bool PAGED, int D>
+template <bool PAGED, int D, bool WIN>
 PartialKernel pick_mfma_d(kvc_dtype kv) {
-  if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D>;
+  if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D, WIN>;
   if constexpr (PAGED)
-    if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D>;
+    if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D, WIN>;
+  return nullptr;
+}
+
+template <bool PAGED, bool WIN>
+PartialKernel pick_kernel_w(kvc_dtype kv, int D, bool q_f16, bool mfma) {
+  if (mfma) {
+    if (!q_f16) return nullptr;
+    if (D == 64) return pick_mfma_d<PAGED, 64, WIN>(kv);
+    if (D == 128) return pick_mfma_d<PAGED, 128, WIN>(kv);
+    return nullptr;
+  }
+  if (D == 64)
+    return q_f16 ? pick_vec_d<PAGED, true, 64, WIN>(kv) : pick_vec_d<PAGED, false, 64, WIN>(kv);
+  if (D == 128)
+    return q_f16 ? pick_vec_d<PAGED, true, 128, WIN>(kv) : pick_vec_d<PAGED, false, 128, WIN>(kv);
   return nullptr;
 }
 
 template <bool PAGED>
-PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, bool mfma) {
-  if (mfma) {
-    if (!q_f16) return nullptr;
-    if (D == 64) return pick_mfma_d<PAGED, 64>(kv);
-    if (D == 128) return pick_mfma_d<PAGED, 128>(kv);
-    return nullptr;
-  }
-  if (D == 64) return q_f16 ? pick_vec_d<PAGED, true, 64>(kv) : pick_vec_d<PAGED, false, 64>(kv);
-  if (D == 128)
-    return q_f16 ? pick_vec_d<PAGED, true, 128>(kv) : pick_vec_d<PAGED, false, 128>(kv);
-  return nullptr;
+PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, bool mfma, bool window) {
+  return window ? pick_kernel_w<PAGED, true>(kv, D, q_f16, mfma)
+                : pick_kernel_w<PAGED, false>(kv, D, q_f16, mfma);
 }
 
 struct PartialPlan {
@@ -1302,9 +1336,9 @@ int resident_waves_per_cu(PartialKernel k, size_t shmem) {
 // Shared validation and planning for both layouts.
 kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype kv_dtype,
                         const int32_t *ctx_lens, int32_t B, int32_t H, int32_t G, int32_t D,
-                        int32_t cap, int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
-                        void *workspace, size_t ws_bytes, PartialPlan &pl) {
-  if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0) return KVC_E_INVALID;
+                        int32_t cap, int32_t max_ctx, int32_t window, float scale, void *out,
+                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes, PartialPlan &pl) {
+  if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0 || window < 0) return KVC_E_INVALID;
   if (static_cast<int64_t>(H) * G > (1 << 20)) return KVC_E_INVALID;
   if (B > kMaxBatch) return KVC_E_INVALID;
   if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
@@ -1328,10 +1362,13 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   const WsLayout wl = ws_layout(B, D, ws_group(G));
   if (ws_bytes < wl.total) return KVC_E_INVALID;
 
-  const int64_t tiles_hint = static_cast<int64_t>(B) * Hp *
-                             ((static_cast<int64_t>(std::min(max_ctx, cap)) + kBlock - 1) / kBlock);
-  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, gp.mfma)
-                             : pick_kernel<false>(kv_dtype, D, q_f16, gp.mfma);
+  // a window covers at most window + 15 positions' blocks
+  const int64_t span = window > 0 ? std::min<int64_t>(std::min(max_ctx, cap),
+                                                      static_cast<int64_t>(window) + kBlock - 1)
+                                  : std::min(max_ctx, cap);
+  const int64_t tiles_hint = static_cast<int64_t>(B) * Hp * ((span + kBlock - 1) / kBlock);
+  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, gp.mfma, window > 0)
+                             : pick_kernel<false>(kv_dtype, D, q_f16, gp.mfma, window > 0);
   if (!kern) return KVC_E_UNSUPPORTED;
   // staged rows per wavefront: a segment stages GQ rows at once; the matrix-core kernel also
   // holds one fp16 V tile per wavefront
@@ -1362,6 +1399,7 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   a.G = G;
   a.nsub = G / GQ;
   a.gq = GQ;
+  a.window = window;
   a.stage_rows = stage_rows;
   a.Hp = Hp;
   a.Hq = H * G;
@@ -1389,18 +1427,19 @@ kvc_status launch_partial(const PartialPlan &pl, void *stream) {
 using namespace kvc;
 
 // Pass 1 for both layouts. G query heads share each K/V head (q and out have H*G heads);
-// k_new/v_new non-null selects append mode (G = 1 only).
+// k_new/v_new non-null selects append mode (G = 1 only); window > 0 attends only the last
+// `window` positions of each sequence.
 static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
                                  const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
                                  const void *k_new, const void *v_new, int32_t B, int32_t H,
-                                 int32_t S_max, int32_t D, int32_t max_ctx, float scale, void *out,
-                                 kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
-                                 void *stream) {
+                                 int32_t S_max, int32_t D, int32_t max_ctx, int32_t window,
+                                 float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                 size_t ws_bytes, void *stream) {
   if (S_max < 0) return KVC_E_INVALID;
   if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
   PartialPlan pl;
   kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, G, D, S_max, max_ctx,
-                               scale, out, out_dtype, workspace, ws_bytes, pl);
+                               window, scale, out, out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
   if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
@@ -1417,8 +1456,8 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
                                 const kvc_paged_layer *layer, const int32_t *block_tables,
                                 int32_t max_blocks_per_seq, const int32_t *ctx_lens,
                                 const void *k_new, const void *v_new, int32_t B, int32_t max_ctx,
-                                float scale, void *out, kvc_dtype out_dtype, void *workspace,
-                                size_t ws_bytes, void *stream) {
+                                int32_t window, float scale, void *out, kvc_dtype out_dtype,
+                                void *workspace, size_t ws_bytes, void *stream) {
   if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
     return KVC_E_INVALID;
   if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
@@ -1427,8 +1466,8 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
   if (k_new && kv == KVC_E4M3) return KVC_E_UNSUPPORTED;  // the block scale may change
   PartialPlan pl;
   kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads, G,
-                               layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, scale, out,
-                               out_dtype, workspace, ws_bytes, pl);
+                               layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, window, scale,
+                               out, out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
   if (!block_tables || !layer->k_pool || !layer->v_pool || !aligned16(layer->k_pool) ||
       !aligned16(layer->v_pool))
@@ -1496,7 +1535,8 @@ kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const voi
                                      kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                      void *stream) {
   return partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
-                        H, S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+                        H, S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes,
+                        stream);
 }
 
 kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
@@ -1505,7 +1545,7 @@ kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                     int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                                     void *workspace, size_t ws_bytes, void *stream) {
   return partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
-                       nullptr, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+                       nullptr, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1515,7 +1555,7 @@ kvc_status kvc_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32
                                          float scale, void *out, kvc_dtype out_dtype,
                                          void *workspace, size_t ws_bytes, void *stream) {
   return partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
-                        H_kv, S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes,
+                        H_kv, S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes,
                         stream);
 }
 
@@ -1526,7 +1566,7 @@ kvc_status kvc_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_
                                         kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                         void *stream) {
   return partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
-                       nullptr, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+                       nullptr, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_append_decode_partial_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
@@ -1538,7 +1578,7 @@ kvc_status kvc_append_decode_partial_contig(const void *q, kvc_dtype q_dtype, vo
                                             size_t ws_bytes, void *stream) {
   if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
   return partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H,
-                        S_max, D, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+                        S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
@@ -1550,7 +1590,7 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
                                            void *workspace, size_t ws_bytes, void *stream) {
   if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
   return partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
-                       v_new, B, max_ctx, scale, out, out_dtype, workspace, ws_bytes, stream);
+                       v_new, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
@@ -1609,6 +1649,61 @@ kvc_status kvc_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
   kvc_status st = kvc_decode_gqa_partial_paged(q, q_dtype, G, layer, block_tables,
                                                max_blocks_per_seq, ctx_lens, B, max_ctx, scale,
                                                out, out_dtype, workspace, ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
+                              ws_bytes, stream);
+}
+
+kvc_status kvc_decode_window_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                            const void *k_cache, const void *v_cache,
+                                            kvc_dtype kv_dtype, const int32_t *ctx_lens,
+                                            int32_t B, int32_t H_kv, int32_t S_max, int32_t D,
+                                            int32_t max_ctx, int32_t window, float scale,
+                                            void *out, kvc_dtype out_dtype, void *workspace,
+                                            size_t ws_bytes, void *stream) {
+  if (window < 1) return KVC_E_INVALID;
+  return partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
+                        H_kv, S_max, D, max_ctx, window, scale, out, out_dtype, workspace,
+                        ws_bytes, stream);
+}
+
+kvc_status kvc_decode_window_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                           const kvc_paged_layer *layer,
+                                           const int32_t *block_tables,
+                                           int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                           int32_t B, int32_t max_ctx, int32_t window,
+                                           float scale, void *out, kvc_dtype out_dtype,
+                                           void *workspace, size_t ws_bytes, void *stream) {
+  if (window < 1) return KVC_E_INVALID;
+  return partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                       nullptr, B, max_ctx, window, scale, out, out_dtype, workspace, ws_bytes,
+                       stream);
+}
+
+kvc_status kvc_decode_window_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                    const void *k_cache, const void *v_cache, kvc_dtype kv_dtype,
+                                    const int32_t *ctx_lens, int32_t B, int32_t H_kv,
+                                    int32_t S_max, int32_t D, int32_t max_ctx, int32_t window,
+                                    float scale, void *out, kvc_dtype out_dtype, void *workspace,
+                                    size_t ws_bytes, void *stream) {
+  kvc_status st = kvc_decode_window_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
+                                                   ctx_lens, B, H_kv, S_max, D, max_ctx, window,
+                                                   scale, out, out_dtype, workspace, ws_bytes,
+                                                   stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_window_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                   const kvc_paged_layer *layer, const int32_t *block_tables,
+                                   int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
+                                   int32_t max_ctx, int32_t window, float scale, void *out,
+                                   kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                   void *stream) {
+  kvc_status st = kvc_decode_window_partial_paged(q, q_dtype, G, layer, block_tables,
+                                                  max_blocks_per_seq, ctx_lens, B, max_ctx, window,
+                                                  scale, out, out_dtype, workspace, ws_bytes,
+                                                  stream);
   if (st != KVC_OK) return st;
   return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
                               ws_bytes, stream);

@@ -1,5 +1,7 @@
 // Host-side block pool of the paged KV cache: first-fit allocation, reference counts, fork and
-// copy-on-write ("KV Cache and PagedAttention", sections 2.1, 2.2, 3.1, 3.3 and 5.1).
+// copy-on-write ("KV Cache and PagedAttention", sections 2.1, 2.2, 3.1, 3.3 and 5.1), and the
+// rolling window in paged form ("KV Cache Mechanism Explained", section 8, item 2): blocks wholly
+// before a sequence's window are dropped from its table (entry -1), a prefix of the table.
 //
 // Host memory only; no HIP calls. Free blocks are kept in a bitmap indexed by position in the
 // pool's search order, so first fit is "lowest set bit at or after a hint". Every mutating call
@@ -227,7 +229,7 @@ kvc_status kvc_fork(kvc_pool *pool, int32_t parent, int32_t *child_out) {
   if (!pool || !child_out) return KVC_E_INVALID;
   if (!pool->is_live(parent)) return KVC_E_NOSEQ;
   for (int32_t b : pool->seqs[parent].table)
-    if (pool->refcount[b] == INT32_MAX) return KVC_E_INVALID;
+    if (b >= 0 && pool->refcount[b] == INT32_MAX) return KVC_E_INVALID;
   try {
     std::vector<int32_t> table = pool->seqs[parent].table;  // copy before any change
     const int32_t len = pool->seqs[parent].len;
@@ -236,7 +238,8 @@ kvc_status kvc_fork(kvc_pool *pool, int32_t parent, int32_t *child_out) {
     c.live = true;
     c.len = len;
     c.table.swap(table);
-    for (int32_t b : c.table) pool->set_refcount(b, pool->refcount[b] + 1);
+    for (int32_t b : c.table)
+      if (b >= 0) pool->set_refcount(b, pool->refcount[b] + 1);
     pool->live_count++;
     *child_out = id;
   } catch (const std::bad_alloc &) {
@@ -254,11 +257,38 @@ kvc_status kvc_free(kvc_pool *pool, int32_t seq) {
     return KVC_E_OOM;
   }
   Seq &s = pool->seqs[seq];
-  for (int32_t b : s.table) pool->set_refcount(b, pool->refcount[b] - 1);
+  for (int32_t b : s.table)
+    if (b >= 0) pool->set_refcount(b, pool->refcount[b] - 1);
   s.live = false;
   s.len = 0;
   std::vector<int32_t>().swap(s.table);
   pool->live_count--;
+  return KVC_OK;
+}
+
+kvc_status kvc_slide(kvc_pool *pool, const int32_t *seqs, int32_t n_seqs, int32_t window,
+                     int32_t *n_dropped_out) {
+  if (!pool || n_seqs < 0 || window < 0) return KVC_E_INVALID;
+  if (n_seqs > 0 && !seqs) return KVC_E_INVALID;
+  for (int32_t i = 0; i < n_seqs; ++i)
+    if (!pool->is_live(seqs[i])) return KVC_E_NOSEQ;
+  int32_t dropped = 0;
+  if (window > 0) {
+    for (int32_t i = 0; i < n_seqs; ++i) {
+      Seq &s = pool->seqs[seqs[i]];
+      const int32_t start = std::max(0, s.len - window);
+      const int32_t n = std::min<int32_t>(start / KVC_BLOCK_SIZE,
+                                          static_cast<int32_t>(s.table.size()));
+      for (int32_t j = 0; j < n; ++j) {
+        const int32_t b = s.table[j];
+        if (b < 0) continue;
+        pool->set_refcount(b, pool->refcount[b] - 1);
+        s.table[j] = -1;
+        ++dropped;
+      }
+    }
+  }
+  if (n_dropped_out) *n_dropped_out = dropped;
   return KVC_OK;
 }
 
@@ -294,7 +324,8 @@ kvc_status kvc_stats(const kvc_pool *pool, kvc_pool_stats *out) {
   for (const Seq &s : pool->seqs) {
     if (!s.live) continue;
     st.tokens += s.len;
-    st.slots_logical += static_cast<int64_t>(s.table.size()) * KVC_BLOCK_SIZE;
+    for (int32_t b : s.table)
+      if (b >= 0) st.slots_logical += KVC_BLOCK_SIZE;
   }
   *out = st;
   return KVC_OK;
@@ -317,7 +348,10 @@ kvc_status kvc_check(const kvc_pool *pool) {
       if (s.len < 0 || static_cast<int64_t>(s.table.size()) != need ||
           need > pool->max_blocks)
         return KVC_E_INVALID;
-      for (int32_t b : s.table) {
+      size_t k = 0;  // entries dropped by a rolling window form a prefix
+      while (k < s.table.size() && s.table[k] == -1) ++k;
+      for (size_t j = k; j < s.table.size(); ++j) {
+        const int32_t b = s.table[j];
         if (b < 0 || b >= pool->num_blocks) return KVC_E_INVALID;
         if (seen[b] == static_cast<int32_t>(sid)) return KVC_E_INVALID;
         seen[b] = static_cast<int32_t>(sid);

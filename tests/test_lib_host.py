@@ -86,6 +86,11 @@ class Mirror:
             assert rc == rp
             if rc[0] == "ok":
                 self.live.remove(s)
+        elif kind == "slide":
+            seqs, w = arg
+            seqs = [self.live[i % len(self.live)] for i in seqs] if self.live else [0]
+            rc, rp = self._both(lambda: self.c.slide(seqs, w), lambda: self.p.slide(seqs, w))
+            assert rc == rp
         self.compare()
 
     def compare(self):
@@ -104,7 +109,8 @@ class Mirror:
 
 OPS = ([("alloc", None)] + [("append", ([0], n)) for n in (1, 15, 17)]
        + [("append", ([0, 1], 1)), ("append", ([1, 0], 9))]
-       + [("fork", 0), ("fork", 1), ("free", 0), ("free", 1)])
+       + [("fork", 0), ("fork", 1), ("free", 0), ("free", 1)]
+       + [("slide", ([0], 3)), ("slide", ([1, 0], 17))])
 
 
 def test_pool_matches_model_on_every_short_op_sequence():
@@ -122,7 +128,7 @@ def test_pool_matches_model_on_random_long_sequences(seed):
     order = rng.permutation(nblk) if seed % 2 else None
     m = Mirror(nblk, int(rng.integers(1, 6)), order=order)
     for _ in range(150):
-        k = rng.integers(0, 10)
+        k = rng.integers(0, 11)
         if k < 2:
             m.op("alloc", None)
         elif k < 6:
@@ -130,8 +136,11 @@ def test_pool_matches_model_on_random_long_sequences(seed):
             m.op("append", (list(rng.integers(0, 8, nseq)), int(rng.integers(0, 24))))
         elif k < 8:
             m.op("fork", int(rng.integers(0, 8)))
-        else:
+        elif k < 9:
             m.op("free", int(rng.integers(0, 8)))
+        else:
+            nseq = int(rng.integers(1, 4))
+            m.op("slide", (list(rng.integers(0, 8, nseq)), int(rng.integers(0, 40))))
 
 
 def test_pool_argument_errors(lib):

@@ -122,6 +122,15 @@ GQA8_PAGED = Workload(
     extra={"group": 8})
 
 
+# Rolling window (KV Cache Mechanism Explained, section 8, item 2): LLaMA-13B shapes at a 2048
+# context with the cache window held to the last 1024 tokens (the page pairs a window cache with
+# LLaMA-13B at context 2048 and gives no window size).
+LLAMA13B_WINDOW = Workload(
+    name="llama13b-40x40x128-f16-paged16-b32-ctx2048-window1024", kind="paged", layers=40,
+    batch=32, heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=7, ctx=2048,
+    extra={"window": 1024})
+
+
 def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
     """Attended lengths of the LLaMA-13B paged batch: uniform in [ctx_lo, ctx_hi]."""
     g = rng(w.seed if seed is None else seed)
