@@ -18,7 +18,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from .attention import decode_row, grouped_decode, window_start
+from .attention import decode_row, full_causal, grouped_decode, kv_head_of, window_start
 from .codecs import e4m3_decode, fp8_write_token
 
 BS = 16
@@ -54,6 +54,16 @@ class ContigCache:
             s = window_start(L, window)
             out[b] = grouped_decode(q[b], self.K[b, :, s:L], self.V[b, :, s:L], scale)
         return out
+
+    def prefill(self, q, q_start, lens, scale) -> np.ndarray:
+        """Attention of a chunk of new tokens per sequence, their K/V already in the cache.
+
+        q: [total, Hq, D]; sequence b's chunk is rows q_start[b] .. q_start[b+1]-1, the last
+        n_b = q_start[b+1] - q_start[b] of its lens[b] positions. Row i attends positions
+        0 .. lens[b] - n_b + i (the causal mask of full_causal with start_pos lens[b] - n_b).
+        Query head hq reads key/value head kv_head_of(hq, Hq, H). Returns [total, Hq, D]."""
+        return _prefill(q, q_start, lens, scale, self.H,
+                        lambda b, L: (self.K[b, :, :L], self.V[b, :, :L]))
 
 
 class PagedCache:
@@ -114,6 +124,11 @@ class PagedCache:
             V[:, t - start, :] = cache[blk][1][:, off, :]
         return K, V
 
+    def prefill(self, q, q_start, tables, lens, scale) -> np.ndarray:
+        """As ContigCache.prefill, the positions read through the block tables."""
+        return _prefill(q, q_start, lens, scale, self.H,
+                        lambda b, L: self.gather(tables[b], L))
+
     def decode(self, q, tables, lens, scale, heads=None, window: int = 0) -> np.ndarray:
         """q: [B, Hq, D] with Hq a multiple of the pool's H (query head hq reads key/value head
         kv_head_of(hq, Hq, H), as in grouped_decode); tables: [B, max_blocks]; lens[b]: attended
@@ -131,3 +146,22 @@ class PagedCache:
             for h in hs:
                 out[b, h] = decode_row(q[b, h], K[h // G], V[h // G], scale)
         return out
+
+
+def _prefill(q, q_start, lens, scale, H, kv_of) -> np.ndarray:
+    """Chunked prefill through a cache model: for each sequence, full_causal over its chunk
+    ("LLM Inference Acceleration -- KV Cache", section 3.1: the chunk's K/V are written at
+    start_pos, then rows attend positions 0 .. start_pos + i under triu(-inf, start_pos + 1))."""
+    q = np.asarray(q)
+    Hq = q.shape[1]
+    out = np.zeros(q.shape, dtype=np.float64)
+    for b in range(len(lens)):
+        r0, r1 = int(q_start[b]), int(q_start[b + 1])
+        n, L = r1 - r0, int(lens[b])
+        if n == 0:
+            continue
+        K, V = kv_of(b, L)
+        for hq in range(Hq):
+            g = kv_head_of(hq, Hq, H)
+            out[r0:r1, hq] = full_causal(q[r0:r1, hq], K[g], V[g], scale, start_pos=L - n)
+    return out

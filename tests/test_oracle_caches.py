@@ -127,3 +127,44 @@ def test_paged_fp8_write_is_token_sequential_and_decodes_codes_times_scale():
     assert pc.k_scale[1] == s and pc.v_scale[1] == s
     K, V = pc.gather([1, 0], 20)
     np.testing.assert_array_equal(K[:, :16], (e4m3_decode(codes) * np.float64(s)))
+
+
+# ---- chunked prefill through the cache models -----------------------------------------------
+def test_prefill_rows_equal_decode_at_each_length_and_paged_equals_contig():
+    """Row i of a prefill chunk is the decode of the same query at length start + i + 1 (the
+    cached path reaches the recompute result, "LLM Inference Acceleration -- KV Cache", section
+    2.2); the paged and contiguous models agree bit for bit; grouped heads read kv_head_of."""
+    from oracle.pool import PoolModel
+    rng = np.random.default_rng(21)
+    H, G, D = 2, 2, 8
+    lens = [1, 17, 40, 5]
+    chunk = [1, 9, 40, 0]
+    q_start = np.concatenate([[0], np.cumsum(chunk)])
+    S = max(lens)
+    contig = ContigCache(len(lens), H, S, D, "f32", fill=np.nan)
+    pool = PoolModel(16, 16, 4, order=rng.permutation(16))
+    paged = PagedCache(16, H, D, "f32", fill=np.nan)
+    seqs = [pool.alloc() for _ in lens]
+    for b, (s, L) in enumerate(zip(seqs, lens)):
+        k = rng.standard_normal((1, L, H, D)).astype(np.float32)
+        v = rng.standard_normal((1, L, H, D)).astype(np.float32)
+        pos = np.full(len(lens), S, np.int32)
+        pos[b] = 0
+        kk = np.zeros((len(lens), L, H, D), np.float32)
+        vv = np.zeros_like(kk)
+        kk[b], vv[b] = k[0], v[0]
+        contig.append(pos, kk, vv)
+        slots, _ = pool.append([s], L)
+        paged.write(slots, k[0], v[0])
+    tables, tl = pool.block_table(seqs)
+    q = rng.standard_normal((int(q_start[-1]), H * G, D)).astype(np.float32)
+    a = contig.prefill(q, q_start, lens, 0.3)
+    bp = paged.prefill(q, q_start, tables, tl, 0.3)
+    np.testing.assert_array_equal(a, bp)
+    for b, L in enumerate(lens):
+        n = chunk[b]
+        for i in range(n):
+            row = int(q_start[b]) + i
+            dec = contig.decode(q[row][None].repeat(len(lens), 0), [L - n + i + 1] * len(lens),
+                                0.3)[b]
+            np.testing.assert_allclose(a[row], dec, rtol=0, atol=1e-14)
