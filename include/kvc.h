@@ -403,6 +403,38 @@ kvc_status kvc_decode_window_partial_paged(const void *q, kvc_dtype q_dtype, int
                                            float scale, void *out, kvc_dtype out_dtype,
                                            void *workspace, size_t ws_bytes, void *stream);
 
+/* ==================================================================================== *
+ * Chunked prefill: several new tokens per sequence attend with the causal mask ("LLM Inference
+ * Acceleration -- KV Cache", section 3.1: a forward pass over seqlen > 1 tokens at start_pos uses
+ * triu(-inf, start_pos + 1); "KV Cache and PagedAttention", section 5.3: FlashAttention tiles
+ * within blocks, PagedAttention between blocks).
+ *
+ * Sequence b's chunk is rows q_start[b] .. q_start[b+1]-1 of q and out: its last
+ * n_b = q_start[b+1] - q_start[b] positions, whose K/V are already in the cache (written with
+ * kvc_append_contig / kvc_write_paged). L_b = ctx_lens[b] counts every position, the chunk
+ * included. Row i of the chunk (position L_b - n_b + i) attends positions 0 .. L_b - n_b + i.
+ * G query heads share each K/V head as for kvc_decode_gqa_* (G = 1: multi-head).
+ *   q, out:    [total_q][H_kv*G][D] (q fp16; out fp16, rounded to nearest even, or fp32)
+ *   q_start:   device int32[B+1], non-decreasing, q_start[B] <= total_q
+ *   ctx_lens:  device int32[B], clamped to [0, capacity]; a chunk longer than L_b keeps its first
+ *              L_b rows (the rest of out is not written)
+ *   caches:    fp16 only, as for kvc_decode_* (contiguous [B][H_kv][S_max][D]; paged layer with
+ *              H_kv heads and the block tables of the sequences)
+ * D = 64 or 128. No workspace. Each workgroup of 4 wavefronts computes 64 query rows to the end
+ * (two HBM passes over K/V per 64 rows at most: no split across workgroups, no merge).
+ * Errors: KVC_E_UNSUPPORTED (dtypes, D), KVC_E_INVALID (shapes, alignment, B > 4096); block ids
+ * outside the pool skip their block. */
+kvc_status kvc_prefill_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
+                              const void *v_cache, kvc_dtype kv_dtype, const int32_t *q_start,
+                              const int32_t *ctx_lens, int32_t B, int32_t H_kv, int32_t S_max,
+                              int32_t D, int32_t total_q, float scale, void *out,
+                              kvc_dtype out_dtype, void *stream);
+kvc_status kvc_prefill_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                             const kvc_paged_layer *layer, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *q_start,
+                             const int32_t *ctx_lens, int32_t B, int32_t total_q, float scale,
+                             void *out, kvc_dtype out_dtype, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,7 +24,8 @@ __all__ = [
     "append_decode_partial_paged", "gqa_workspace_bytes", "new_gqa_workspace",
     "decode_gqa_contig", "decode_gqa_paged", "decode_gqa_partial_contig",
     "decode_gqa_partial_paged", "decode_gqa_merge", "decode_window_contig", "decode_window_paged",
-    "decode_window_partial_contig", "decode_window_partial_paged",
+    "decode_window_partial_contig", "decode_window_partial_paged", "prefill_contig",
+    "prefill_paged",
 ]
 
 F32, F16, E4M3 = 0, 1, 2
@@ -44,7 +45,7 @@ EXPORTS = [
     "kvc_gqa_workspace_bytes", "kvc_decode_gqa_contig", "kvc_decode_gqa_paged",
     "kvc_decode_gqa_partial_contig", "kvc_decode_gqa_partial_paged", "kvc_decode_gqa_merge",
     "kvc_decode_window_contig", "kvc_decode_window_paged", "kvc_decode_window_partial_contig",
-    "kvc_decode_window_partial_paged",
+    "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
 ]
 
 
@@ -149,6 +150,12 @@ def load_library() -> ctypes.CDLL:
         sig[name] = (ctypes.c_int, contig_win)
     for name in ("kvc_decode_window_paged", "kvc_decode_window_partial_paged"):
         sig[name] = (ctypes.c_int, paged_win)
+    sig["kvc_prefill_contig"] = (ctypes.c_int, [_P, ctypes.c_int, _I32, _P, _P, ctypes.c_int, _P,
+                                                _P, _I32, _I32, _I32, _I32, _I32, _F, _P,
+                                                ctypes.c_int, _P])
+    sig["kvc_prefill_paged"] = (ctypes.c_int, [_P, ctypes.c_int, _I32, ctypes.POINTER(_Layer), _P,
+                                               _I32, _P, _P, _I32, _I32, _F, _P, ctypes.c_int,
+                                               _P])
     sig["kvc_decode_gqa_merge"] = (ctypes.c_int, [_I32, _I32, _I32, _I32, _P, ctypes.c_int, _P,
                                                   ctypes.c_size_t, _P])
     for name, (res, args) in sig.items():
@@ -403,8 +410,6 @@ def write_paged(layer: PagedLayer, slots, k_new, v_new, stream=None) -> None:
 def _out_for(q, out):
     torch = _torch()
     return torch.empty_like(q) if out is None else out
-
-
 
 
 
@@ -709,3 +714,40 @@ def decode_window_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, ma
     """Pass 1 of decode_window_paged; returns (out, workspace) for decode_gqa_merge."""
     return _window_paged_call("kvc_decode_window_partial_paged", q, layer, block_tables, ctx_lens,
                               max_ctx, window, scale, out, workspace, stream)
+
+
+# ---- chunked prefill ---------------------------------------------------------------------------
+def prefill_contig(q, k_cache, v_cache, q_start, ctx_lens, scale=None, out=None, stream=None):
+    """Causal attention of a chunk of new tokens per sequence over a contiguous cache
+    [B, H_kv, S_max, D] that already holds them. q [total, H_kv*G, D] fp16; sequence b's rows
+    are q_start[b] .. q_start[b+1]-1 (device int32 [B+1]), its last positions of ctx_lens[b]."""
+    B, H, S, D = k_cache.shape
+    if q.dim() != 3 or q.shape[2] != D:
+        raise ValueError("q must be [total, H_kv*G, D]")
+    G = _gqa_group(q, H)
+    out = _out_for(q, out)
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(_lib().kvc_prefill_contig(
+        _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr(q_start), _ptr(ctx_lens), B, H, S, D, q.shape[0], float(scale), _ptr(out),
+        _dtype_code(out), _stream(stream)), "kvc_prefill_contig")
+    return out
+
+
+def prefill_paged(q, layer: PagedLayer, block_tables, q_start, ctx_lens, scale=None, out=None,
+                  stream=None):
+    """As prefill_contig over a paged layer through the sequences' block tables [B, max_blocks]."""
+    if q.dim() != 3 or q.shape[2] != layer.head_dim:
+        raise ValueError("q must be [total, H_kv*G, D]")
+    if block_tables.dim() != 2:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    B = block_tables.shape[0]
+    G = _gqa_group(q, layer.heads)
+    out = _out_for(q, out)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(_lib().kvc_prefill_paged(
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
+        _ptr(q_start), _ptr(ctx_lens), B, q.shape[0], float(scale), _ptr(out), _dtype_code(out),
+        _stream(stream)), "kvc_prefill_paged")
+    return out

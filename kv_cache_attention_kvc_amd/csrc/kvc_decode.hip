@@ -32,6 +32,7 @@
 #include <vector>
 
 #include "kvc_internal.h"
+#include "kvc_wave.h"
 
 namespace kvc {
 
@@ -42,8 +43,6 @@ constexpr int kMinChunk = 4;       // tiles per wavefront at least
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
 constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kFloor = -3.0e38f;  // initial running max (finite, so m - m' is never NaN)
 
 // Workspace: [header int32[64] | prefix int32[B+1] | records float[kMaxWorkers][2][GQ][D+4]],
 // each region 256-byte aligned. Header: chunk size C, and B, pairs per sequence, D, GQ of the
@@ -90,35 +89,6 @@ struct DecodeArgs {
   float cl2;  // scale * log2(e)
 };
 
-// ---- wave helpers ----------------------------------------------------------------------
-template <int CTRL>
-__device__ __forceinline__ float dpp(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-
-// The value of x in this lane and in a partner lane OFF lanes away, as an unordered pair
-// {a, b} (so a symmetric combination of a and b is the same in both lanes). OFF = 32 and 16 use
-// the gfx950 lane-swap instructions (halves of the wave, neighbouring rows of 16); OFF = 8 and 4
-// rotate within a row of 16 (row_ror), which pairs lane i with lane i+OFF mod 16.
-template <int OFF>
-__device__ __forceinline__ void lane_pair(float x, float &a, float &b) {
-  const uint32_t u = __float_as_uint(x);
-  if constexpr (OFF == 32) {
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-  } else if constexpr (OFF == 16) {
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    a = __uint_as_float(r[0]);
-    b = __uint_as_float(r[1]);
-  } else {
-    static_assert(OFF == 8 || OFF == 4, "lane distance 4, 8, 16 or 32");
-    a = x;
-    b = dpp<0x120 + OFF>(x);  // row_ror:OFF
-  }
-}
-
 // Sum over aligned groups of N lanes; every lane of a group gets the same bits.
 template <int N>
 __device__ __forceinline__ float group_sum(float x) {
@@ -143,14 +113,6 @@ __device__ __forceinline__ int32_t sread(const int32_t *p) {
 typedef const __attribute__((address_space(4))) int32_t const_i32;
 __device__ __forceinline__ int32_t sload(const int32_t *p) {
   return *(const_i32 *)(p);
-}
-
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-// 16-byte streaming load (non-temporal hint).
-__device__ __forceinline__ uint4 load_stream(const char *p) {
-  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
 // Unpack the 16 bytes a lane loaded into EPL floats.
@@ -700,18 +662,6 @@ struct VecCore {
   }
 };
 
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-// Ordering point for LDS traffic between the lanes of one wavefront: the compiler keeps LDS
-// accesses on their side of it, and the LDS executes one wavefront's accesses in issue order.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
 // Matrix-core core for grouped queries: the GQ (<= 16) query heads of a pair share every K/V
 // tile, so a tile is a 16-position x D block against a 16-column block of queries. Lanes are
 // (g, j) = (lane / 16, lane % 16).
@@ -822,18 +772,6 @@ struct MfmaCore {
     s.m = kFloor;
     s.l = 0.f;
     s.vref = 1.f;
-  }
-
-  static __device__ __forceinline__ f16x8 as_f16x8(const uint4 &u) {
-    return __builtin_bit_cast(f16x8, u);
-  }
-  // 8 e4m3 codes (two words) as fp16, exactly
-  static __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
-#define KVC_CVT8(w, hi) \
-  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w), 1.0f, hi))
-    return __builtin_bit_cast(f16x8, make_uint4(KVC_CVT8(w0, false), KVC_CVT8(w0, true),
-                                                KVC_CVT8(w1, false), KVC_CVT8(w1, true)));
-#undef KVC_CVT8
   }
 
   __device__ void touch(const Tile &t) const {

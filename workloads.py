@@ -131,6 +131,14 @@ LLAMA13B_WINDOW = Workload(
     extra={"window": 1024})
 
 
+# Prefill (the chunked multi-query attention on either side of decode): LLaMA-7B head shapes,
+# four 2048-token prompts each prefilled whole (causal attention over the prompt), 32 layers.
+LLAMA7B_PREFILL = Workload(
+    name="llama7b-32x32x128-f16-paged16-prefill-b4x2048", kind="paged", layers=32, batch=4,
+    heads=32, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=8, ctx=2048,
+    extra={"prefill": 2048})
+
+
 def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
     """Attended lengths of the LLaMA-13B paged batch: uniform in [ctx_lo, ctx_hi]."""
     g = rng(w.seed if seed is None else seed)
