@@ -33,6 +33,7 @@ import workloads  # noqa: E402
 
 METRIC = "paged decode-attention HBM GB/s (% of peak) and decode tokens/s, 1 MI355X"
 PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
+PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak, AMD's published figure
 ELT = {"f32": 4, "f16": 2, "e4m3": 1}
 
 
@@ -43,7 +44,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
                     choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
-                             "gqa8-paged", "llama13b-window"])
+                             "gqa8-paged", "llama13b-window", "llama7b-prefill"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
@@ -188,6 +189,9 @@ class PagedBench:
         pass1 = kv + table + qo + (append if self.fused else 0)
         return (kv + table + qo + append) * self.L, pass1
 
+    def gpu_sample(self):
+        return self.out[0]
+
     def oracle_layer(self, li):
         """The CPU oracle's decode of one layer on the current state (for cpu_baseline and a
         parity spot check): returns (seconds, output [B,H,D], bytes read)."""
@@ -207,6 +211,87 @@ class PagedBench:
         out = ref.decode(q, tables, lens, self.scale, window=self.W)
         dt = time.perf_counter() - t0
         return dt, out, int((lens - first).sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
+
+
+class PrefillBench:
+    """Prefill: every sequence's whole prompt enters at once. One step = per layer, the prompt's
+    K/V written into the paged cache, then causal attention of every prompt row (matrix cores).
+    The same slots are rewritten each step."""
+
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
+        import torch
+
+        import kv_cache_attention_kvc_amd as kvc
+
+        self.kvc, self.torch, self.w, self.dev, self.L = kvc, torch, w, dev, layers
+        B, H, D, T = w.batch, w.heads, w.head_dim, w.extra["prompt"]
+        self.B, self.H, self.D, self.T = B, H, D, T
+        N = B * workloads.blocks_for(T)
+        self.pool = kvc.Pool(N, workloads.blocks_for(T), order=workloads.llama13b_pool_order(N, w.seed))
+        self.seqs = [self.pool.alloc() for _ in range(B)]
+        slots = np.concatenate([self.pool.append([s], T)[0] for s in self.seqs])
+        self.slots = torch.from_numpy(slots).to(dev)
+        tables, lens = self.pool.block_table(self.seqs)
+        self.tab_d = torch.from_numpy(tables).to(dev)
+        self.len_d = torch.from_numpy(lens).to(dev)
+        self.qs_d = torch.from_numpy(np.arange(B + 1, dtype=np.int32) * T).to(dev)
+        self.layers = [kvc.PagedLayer.empty(N, H, D, w.kv_dtype, device=dev)
+                       for _ in range(layers)]
+        self.k = [workloads.torch_normal((B * T, H, D), torch.float16, dev, w.seed * 1000 + 3 * li)
+                  for li in range(layers)]
+        self.v = [workloads.torch_normal((B * T, H, D), torch.float16, dev, w.seed * 1000 + 3 * li + 1)
+                  for li in range(layers)]
+        self.q = [workloads.torch_normal((B * T, H, D), torch.float16, dev, w.seed * 1000 + 3 * li + 2)
+                  for li in range(layers)]
+        self.out = torch.empty((B * T, H, D), dtype=torch.float16, device=dev)
+        self.scale = w.scale
+        self.stream = torch.cuda.current_stream()
+        self.first_lens = lens.astype(np.int64)
+        self.lens_now = lens.astype(np.int64)
+
+    def step(self, ev=None):
+        kvc = self.kvc
+        for li, layer in enumerate(self.layers):
+            kvc.write_paged(layer, self.slots, self.k[li], self.v[li])
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li, self.stream)
+            kvc.prefill_paged(self.q[li], layer, self.tab_d, self.qs_d, self.len_d,
+                              scale=self.scale, out=self.out)
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li + 1, self.stream)
+
+    def flops_launch(self) -> float:
+        """Useful flops of one prefill launch: row i of a prompt attends i + 1 positions, with
+        2*D flops each for the score and for the weighted value sum."""
+        T = self.T
+        return self.B * self.H * (T * (T + 1) / 2) * 4 * self.D
+
+    def bytes_step(self, lens):
+        """Algorithmic HBM bytes: the K/V written and read once, q read, out written."""
+        elt = ELT[self.w.kv_dtype]
+        rows = self.B * self.T * self.H * self.D
+        kv = rows * 2 * elt
+        pass1 = kv + rows * 2 * 2 + self.B * workloads.blocks_for(self.T) * 4
+        return (pass1 + kv) * self.L, pass1
+
+    def gpu_sample(self):
+        """The GPU rows oracle_layer computes: the first prompt of the last layer."""
+        return self.out[:self.T]
+
+    def oracle_layer(self, li):
+        """The CPU oracle's prefill of the first prompt of the last layer (a bounded sample; its
+        output is still in the output buffer)."""
+        from oracle.attention import full_causal
+
+        li = self.L - 1
+        k = self.k[li][:self.T].float().cpu().numpy()
+        v = self.v[li][:self.T].float().cpu().numpy()
+        q = self.q[li][:self.T].float().cpu().numpy()
+        t0 = time.perf_counter()
+        ref = np.stack([full_causal(q[:, h], k[:, h], v[:, h], self.scale) for h in range(self.H)],
+                       axis=1)
+        dt = time.perf_counter() - t0
+        return dt, ref, self.T * self.H * self.D * 2 * ELT[self.w.kv_dtype]
 
 
 class HipEvents:
@@ -334,6 +419,9 @@ class ContigBench:
         pass1 = kv + qo + B * 4 + (append if self.fused else 0)
         return (kv + qo + B * 4 + append) * self.L, pass1
 
+    def gpu_sample(self):
+        return self.out[0]
+
     def oracle_layer(self, li):
         from oracle.caches import ContigCache
 
@@ -354,6 +442,8 @@ def kernel_name(w: workloads.Workload) -> str:
     K/V heads with fp16 queries."""
     G = w.extra.get("group", 1)
     win = ", rolling window" if "window" in w.extra else ""
+    if w is workloads.LLAMA7B_PREFILL:
+        return f"kvc::prefill_kernel<{w.kind}, {w.head_dim}> (causal prefill on the matrix cores)"
     if G == 1:
         return (f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}{win}> "
                 "(attention pass 1)")
@@ -460,21 +550,25 @@ def main():
     w = {"llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
          "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
          "gqa8-paged": workloads.GQA8_PAGED,
-         "llama13b-window": workloads.LLAMA13B_WINDOW}[args.workload]
+         "llama13b-window": workloads.LLAMA13B_WINDOW,
+         "llama7b-prefill": workloads.LLAMA7B_PREFILL}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    separate = w.kv_dtype == "e4m3" or w.extra.get("group", 1) > 1 or "window" in w.extra
+    separate = (w.kv_dtype == "e4m3" or w.extra.get("group", 1) > 1 or "window" in w.extra
+                or w is workloads.LLAMA7B_PREFILL)
     fused = args.append == "fused" or (args.append == "auto" and not separate)
     if fused and separate:
         print("--append fused: e4m3 caches, shared K/V heads and rolling windows take the "
               "separate writer", file=sys.stderr)
         sys.exit(2)
     path = "fused" if fused else "separate"
-    bench = (PagedBench if w.kind == "paged" else ContigBench)(w, K + W, layers, dev, fused)
+    prefill = w is workloads.LLAMA7B_PREFILL
+    cls = PrefillBench if prefill else (PagedBench if w.kind == "paged" else ContigBench)
+    bench = cls(w, K + W, layers, dev, fused)
     for _ in range(W):
         bench.step()
     torch.cuda.synchronize()
@@ -500,6 +594,18 @@ def main():
     p1_bytes_avg = float(np.mean(pass1_bytes))
     achieved = p1_bytes_avg / p1_avg_s / 1e9
     value = total_bytes / elapsed / 1e9
+    if prefill:
+        # compute-bound: the roofline is the matrix cores' fp16 peak over the useful flops
+        roof = {"bound": "mfma", "achieved": round(bench.flops_launch() / p1_avg_s / 1e12, 1),
+                "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(bench.flops_launch() / p1_avg_s / 1e12 / PEAK_F16_TFLOPS, 4),
+                "traffic": None, "flops_per_launch": bench.flops_launch()}
+        tokens = w.batch * bench.T * K
+    else:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4),
+                "traffic": measured_traffic(path) if w is workloads.LLAMA13B_PAGED else None}
+        tokens = w.batch * K
     print(f"[bench] timed: {elapsed * 1e3 / K:.3f} ms/step, pass 1 {p1_avg_s * 1e6:.1f} us/launch",
           file=sys.stderr, flush=True)
 
@@ -522,20 +628,16 @@ def main():
             "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
             if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
-            "ctx_growth_per_step": 0 if w is workloads.LLAMA7B_CONTIG else 1,
+            "ctx_growth_per_step": 0 if w in (workloads.LLAMA7B_CONTIG,
+                                              workloads.LLAMA7B_PREFILL) else 1,
             "window": w.extra.get("window", 0),
             "append": path,
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
-        "tokens_per_s": round(w.batch * K / elapsed, 1),
+        "tokens_per_s": round(tokens / elapsed, 1),
         "roofline": {
             "kernel": kernel_name(w),
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": PEAK_GBS,
-            "unit": "GB/s",
-            "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": measured_traffic(path) if w is workloads.LLAMA13B_PAGED else None,
+            **roof,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
             "kernel_source_sha256_16": source_hash(),
@@ -544,15 +646,18 @@ def main():
     if not args.no_cpu_baseline:
         print("[bench] CPU oracle on one layer", file=sys.stderr, flush=True)
         dt, ref, nbytes = bench.oracle_layer(0)
-        got = bench.out[0].float().cpu().numpy()
+        got = bench.gpu_sample().float().cpu().numpy()
         line["cpu_baseline"] = {
             "value": round(nbytes / dt / 1e9, 4),
             "unit": "GB/s",
             "cores": blas_threads(),
             "kind": "oracle",
-            "sample": f"layer 0 of the last step: all {w.batch} sequences x {w.heads} heads, "
-                      f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
-                      f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers",
+            "sample": (f"the first prompt of the last layer: {bench.T} rows x {w.heads} heads, "
+                       f"causal; {dt:.2f} s; {bench.T / (dt * layers):.3f} prefill tokens/s over "
+                       f"{layers} layers") if prefill else
+                      (f"layer 0 of the last step: all {w.batch} sequences x {w.heads} heads, "
+                       f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
+                       f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers"),
         }
         line["parity_layer0_max_abs_err"] = float(np.abs(got - ref).max())
     if args.copy_calibration:

@@ -136,7 +136,7 @@ LLAMA13B_WINDOW = Workload(
 LLAMA7B_PREFILL = Workload(
     name="llama7b-32x32x128-f16-paged16-prefill-b4x2048", kind="paged", layers=32, batch=4,
     heads=32, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=8, ctx=2048,
-    extra={"prefill": 2048})
+    extra={"prompt": 2048})
 
 
 def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
