@@ -11,15 +11,15 @@ positions [0, len_b] (section 3.1: write at start_pos, read up to start_pos + se
 PagedCache: K and V pools [num_blocks, H, 16, D] per layer; token t of a sequence lives in
 physical block table[t // 16] at in-block slot t % 16 ("KV Cache and PagedAttention", section
 2.1 and section 3.2: gather the sequence's blocks through its block table). Writes go to slots
-(physical_block * 16 + offset). Copy-on-write copies whole blocks (section 3.3). An fp8 pool keeps
-uint8 e4m3 codes plus one fp32 scale per block for K and one for V (codecs module).
+(physical_block * 16 + offset). Copy-on-write copies whole blocks (section 3.3). An fp8 (int8) pool
+keeps uint8 e4m3 (int8) codes plus one fp32 scale per block for K and one for V (codecs module).
 """
 from __future__ import annotations
 
 import numpy as np
 
 from .attention import decode_row, full_causal, grouped_decode, kv_head_of, window_start
-from .codecs import e4m3_decode, fp8_write_token
+from .codecs import e4m3_decode, fp8_write_token, i8_decode, i8_write_token
 
 BS = 16
 _NP = {"f32": np.float32, "f16": np.float16}
@@ -75,6 +75,13 @@ class PagedCache:
             self.V = np.full((num_blocks, H, BS, D), code, dtype=np.uint8)
             self.k_scale = np.zeros(num_blocks, dtype=np.float32)
             self.v_scale = np.zeros(num_blocks, dtype=np.float32)
+        elif dtype == "i8":
+            # int8 has no NaN; the never-written code -128 marks unused slots
+            code = -128 if (fill is not None and np.isnan(fill)) else 0
+            self.K = np.full((num_blocks, H, BS, D), code, dtype=np.int8)
+            self.V = np.full((num_blocks, H, BS, D), code, dtype=np.int8)
+            self.k_scale = np.zeros(num_blocks, dtype=np.float32)
+            self.v_scale = np.zeros(num_blocks, dtype=np.float32)
         else:
             self.K = np.full((num_blocks, H, BS, D), fill, dtype=_NP[dtype])
             self.V = np.full((num_blocks, H, BS, D), fill, dtype=_NP[dtype])
@@ -96,16 +103,20 @@ class PagedCache:
             if self.dtype == "e4m3":
                 self.k_scale[blk] = fp8_write_token(self.K[blk], self.k_scale[blk], off, k_new[i])
                 self.v_scale[blk] = fp8_write_token(self.V[blk], self.v_scale[blk], off, v_new[i])
+            elif self.dtype == "i8":
+                self.k_scale[blk] = i8_write_token(self.K[blk], self.k_scale[blk], off, k_new[i])
+                self.v_scale[blk] = i8_write_token(self.V[blk], self.v_scale[blk], off, v_new[i])
             else:
                 self.K[blk, :, off, :] = k_new[i]
                 self.V[blk, :, off, :] = v_new[i]
 
     def values(self, pool: str, blk: int) -> np.ndarray:
         """Stored values of one block, [H, 16, D] fp64."""
-        if self.dtype == "e4m3":
+        if self.dtype in ("e4m3", "i8"):
             codes = self.K[blk] if pool == "k" else self.V[blk]
             s = self.k_scale[blk] if pool == "k" else self.v_scale[blk]
-            return e4m3_decode(codes) * np.float64(s)
+            dec = e4m3_decode if self.dtype == "e4m3" else i8_decode
+            return dec(codes) * np.float64(s)
         return (self.K[blk] if pool == "k" else self.V[blk]).astype(np.float64)
 
     def gather(self, table, L: int, start: int = 0):

@@ -1,4 +1,5 @@
-"""Number formats of the cache: fp16 and OCP fp8-e4m3, and the per-block fp8 write rule.
+"""Number formats of the cache: fp16, OCP fp8-e4m3 and symmetric int8, and the per-block write
+rule of the two 8-bit formats.
 
 TEST INFRASTRUCTURE ONLY (see oracle/__init__.py).
 
@@ -20,6 +21,12 @@ rule below is the reading taken for a per-block fp32 scale:
     scale becomes s_new; then the token is stored as enc(fp32(x / scale)). While the scale is 0
     (every value written so far is +-0) a value is stored as a signed zero code.
   * The stored value of a code c in a block with scale s is dec(c) * s.
+
+The int8 cache ("KV Cache Mechanism Explained", section 8, item 3 names FP8/INT8 for the
+history tokens with a scaling factor max|x| / 127; "KV Cache and PagedAttention", section 7.2,
+8-bit quantisation of blocks) follows the same rule with the int8 limit: codes are two's-
+complement int8 in [-127, 127] (-128 is never written), enc(y) = y rounded to the nearest
+integer, ties to even, saturated to +-127 (NaN -> 0); s_new = fp32(max|x| / 127); dec(c) = c.
 """
 from __future__ import annotations
 
@@ -112,4 +119,50 @@ def fp8_write_token(codes: np.ndarray, scale, off: int, x) -> np.float32:
             codes[:, :off, :] = _enc_scaled(y, s_new)
         s = s_new
     codes[:, off, :] = _enc_scaled(x32, s)
+    return np.float32(s)
+
+
+# ---- int8 --------------------------------------------------------------------------------
+I8_MAX = 127.0
+
+
+def i8_decode(codes) -> np.ndarray:
+    return np.asarray(codes, dtype=np.int8).astype(np.float64)
+
+
+def i8_encode(y) -> np.ndarray:
+    """Nearest integer to each value of y (ties to the even integer), saturated to +-127; NaN
+    gives 0. Written out from the definition: take floor, compare the remainder with 1/2."""
+    y = np.asarray(y, dtype=np.float64)
+    nan = np.isnan(y)
+    a = np.clip(np.where(nan, 0.0, y), -I8_MAX, I8_MAX)
+    f = np.floor(a)
+    r = a - f
+    up = (r > 0.5) | ((r == 0.5) & (np.mod(f, 2.0) == 1.0))
+    return (f + up).astype(np.int8)
+
+
+def _i8_enc_scaled(y32: np.ndarray, s: np.float32) -> np.ndarray:
+    if s == 0:
+        return np.zeros(y32.shape, dtype=np.int8)
+    return i8_encode((y32 / np.float32(s)).astype(np.float32))
+
+
+def i8_write_token(codes: np.ndarray, scale, off: int, x) -> np.float32:
+    """Write one token into an int8 block: the fp8 rule with the int8 limit 127.
+
+    codes: int8 [H, block_size, D] of one physical block (modified in place); scale: the block's
+    current fp32 scale; off: in-block slot; x: [H, D] values exact in fp32. Returns the new
+    scale."""
+    x32 = np.asarray(x, dtype=np.float32)
+    s = np.float32(0.0) if off == 0 else np.float32(scale)
+    amax = np.float32(np.max(np.abs(x32))) if x32.size else np.float32(0.0)
+    s_new = np.float32(amax / np.float32(I8_MAX))
+    if s_new > s:
+        if off > 0:
+            old = np.float32(s)
+            y = (i8_decode(codes[:, :off, :]).astype(np.float32) * old).astype(np.float32)
+            codes[:, :off, :] = _i8_enc_scaled(y, s_new)
+        s = s_new
+    codes[:, off, :] = _i8_enc_scaled(x32, s)
     return np.float32(s)

@@ -129,6 +129,26 @@ def test_paged_fp8_write_is_token_sequential_and_decodes_codes_times_scale():
     np.testing.assert_array_equal(K[:, :16], (e4m3_decode(codes) * np.float64(s)))
 
 
+
+def test_paged_i8_write_is_token_sequential_and_decodes_codes_times_scale():
+    from oracle.codecs import i8_decode, i8_write_token
+    rng = np.random.default_rng(25)
+    H, D = 2, 8
+    pc = PagedCache(3, H, D, "i8", fill=np.nan)
+    assert (pc.K == -128).all()              # unused slots hold the never-written code
+    x = rng.standard_normal((20, H, D)).astype(np.float16)
+    slots = list(range(16, 32)) + [0, 1, 2, 3]
+    pc.write(slots, x, x)
+    codes = np.zeros((H, 16, D), dtype=np.int8)
+    s = np.float32(0)
+    for t in range(16):
+        s = i8_write_token(codes, s, t, x[t])
+    np.testing.assert_array_equal(pc.K[1], codes)
+    assert pc.k_scale[1] == s and pc.v_scale[1] == s
+    K, V = pc.gather([1, 0], 20)
+    np.testing.assert_array_equal(K[:, :16], i8_decode(codes) * np.float64(s))
+
+
 # ---- chunked prefill through the cache models -----------------------------------------------
 def test_prefill_rows_equal_decode_at_each_length_and_paged_equals_contig():
     """Row i of a prefill chunk is the decode of the same query at length start + i + 1 (the

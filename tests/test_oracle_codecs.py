@@ -171,3 +171,78 @@ def test_fp8_token_sequential_error_vs_unquantised(seed):
     assert err.max() < 0.5 and err.mean() < 0.05
     # the scale is the block maximum over all written tokens / 448
     assert s == np.float32(np.float32(np.abs(xs).max()) / np.float32(448))
+
+
+# ---- int8 ----------------------------------------------------------------------------------
+from oracle.codecs import I8_MAX, i8_decode, i8_encode, i8_write_token  # noqa: E402
+
+
+def test_i8_encode_matches_numpy_rint_and_saturates():
+    """Nearest integer, ties to even, is what NumPy's rint does (a library routine); values are
+    checked on a fine grid with every half-integer in range, plus saturation and NaN."""
+    y = np.concatenate([np.arange(-140.0, 140.0, 0.25), np.arange(-130.5, 131.0, 1.0),
+                        np.random.default_rng(3).standard_normal(2000) * 60])
+    want = np.clip(np.rint(y), -127, 127).astype(np.int8)
+    np.testing.assert_array_equal(i8_encode(y), want)
+    assert i8_encode(np.array([0.5, 1.5, 2.5, -0.5, -1.5, -2.5])).tolist() == [0, 2, 2, 0, -2, -2]
+    assert i8_encode(np.array([127.5, 1e9, np.inf, -127.5, -np.inf, np.nan])).tolist() == \
+        [127, 127, 127, -127, -127, 0]
+    np.testing.assert_array_equal(i8_decode(np.arange(-128, 128, dtype=np.int8)),
+                                  np.arange(-128.0, 128.0))
+
+
+def test_i8_first_token_scale_extreme_code_and_error_bound():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((3, 8)).astype(np.float32)
+    codes = np.zeros((3, 16, 8), dtype=np.int8)
+    s = i8_write_token(codes, 0.0, 0, x)
+    assert s == np.float32(np.float32(np.abs(x).max()) / np.float32(I8_MAX))
+    i = np.unravel_index(np.abs(x).argmax(), x.shape)
+    assert abs(int(codes[i[0], 0, i[1]])) == 127
+    vals = i8_decode(codes[:, 0, :]) * np.float64(s)
+    assert np.all(np.abs(vals - x) <= 0.5 * s * (1 + 1e-6))
+    # the quantiser is round(x / s) with torch's rounding (a library routine), ties to even
+    q = torch.round(torch.from_numpy(x) / torch.tensor(s, dtype=torch.float32))
+    np.testing.assert_array_equal(codes[:, 0, :], q.clamp(-127, 127).to(torch.int8).numpy())
+
+
+def test_i8_growing_scale_requantises_and_slot_zero_restarts():
+    rng = np.random.default_rng(22)
+    codes = np.zeros((2, 16, 8), dtype=np.int8)
+    x0 = rng.standard_normal((2, 8)).astype(np.float32)
+    s0 = i8_write_token(codes, 0.0, 0, x0)
+    c0 = codes[:, 0, :].copy()
+    s_same = i8_write_token(codes, s0, 1, x0 * np.float32(0.5))      # smaller: untouched
+    assert s_same == s0
+    np.testing.assert_array_equal(codes[:, 0, :], c0)
+    x2 = rng.standard_normal((2, 8)).astype(np.float32) * 9
+    s2 = i8_write_token(codes, s0, 2, x2)
+    assert s2 == np.float32(np.float32(np.abs(x2).max()) / np.float32(127)) and s2 > s0
+    deq = torch.from_numpy(c0).to(torch.float32) * float(s0)
+    ref = torch.round(deq / float(s2)).clamp(-127, 127).to(torch.int8).numpy()
+    np.testing.assert_array_equal(codes[:, 0, :], ref)
+    # slot 0 ignores a stale scale; an all-zero first token keeps scale 0 and zero codes
+    s3 = i8_write_token(codes, s2, 0, x0)
+    assert s3 == s0
+    z = np.zeros((2, 16, 8), dtype=np.int8)
+    assert i8_write_token(z, 0.0, 0, np.zeros((2, 8), np.float32)) == 0.0 and not z.any()
+
+
+def test_i8_token_sequential_error_vs_unquantised():
+    rng = np.random.default_rng(23)
+    H, D = 4, 32
+    xs = rng.standard_normal((16, H, D)).astype(np.float16).astype(np.float32)
+    codes = np.zeros((H, 16, D), dtype=np.int8)
+    s = 0.0
+    scales = []
+    for t in range(16):
+        s = i8_write_token(codes, s, t, xs[t])
+        scales.append(float(s))
+    vals = i8_decode(codes) * np.float64(s)
+    err = np.abs(vals - xs.transpose(1, 0, 2))          # [H, 16, D]
+    # token t was rounded once at its own scale and once more at every larger scale that came
+    # after it: each rounding moves it by at most half a step of that scale
+    for t in range(16):
+        bound = 0.5 * sum(sorted(set(scales[t:])))
+        assert err[:, t, :].max() <= bound * (1 + 1e-6), t
+    assert s == np.float32(np.float32(np.abs(xs).max()) / np.float32(127))
