@@ -6,7 +6,7 @@ block copies, the new token's K/V write, decode attention pass 1 (split-context 
 softmax) and pass 2 (merge of split sequence-heads). With `--append fused` (the default for
 f32/f16 caches) the new token's K/V is stored by pass 1 itself, which takes that row from the
 new K/V instead of reading it back; `--append separate` runs the cache writer first (always the
-case for e4m3 caches, whose block scale may change). Inputs are
+case for 8-bit (e4m3, int8) caches, whose block scale may change). Inputs are
 synthetic and already resident in device memory when timing starts; each step grows every
 sequence by one token.
 
@@ -34,7 +34,7 @@ import workloads  # noqa: E402
 METRIC = "paged decode-attention HBM GB/s (% of peak) and decode tokens/s, 1 MI355X"
 PEAK_GBS = 8000.0  # MI355X HBM3E, AMD's published figure
 PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak, AMD's published figure
-ELT = {"f32": 4, "f16": 2, "e4m3": 1}
+ELT = {"f32": 4, "f16": 2, "e4m3": 1, "i8": 1}
 
 
 def parse():
@@ -44,11 +44,11 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
                     choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
-                             "gqa8-paged", "llama13b-window", "llama7b-prefill"])
+                             "gqa8-paged", "llama13b-window", "llama7b-prefill", "i8-longctx"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
-                         "writer first (separate); auto = fused unless the cache is e4m3")
+                         "writer first (separate); auto = fused unless the cache is 8-bit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv output) "
@@ -183,9 +183,10 @@ class PagedBench:
         first = np.maximum(lens - self.W, 0) if self.W else np.zeros_like(lens)
         kv = int((lens - first).sum()) * H * D * 2 * elt
         blocks = int(sum(workloads.blocks_for(L) - int(f) // 16 for L, f in zip(lens, first)))
-        table = blocks * 4 + (blocks * 8 if self.w.kv_dtype == "e4m3" else 0) + B * 4
+        q8 = self.w.kv_dtype in ("e4m3", "i8")
+        table = blocks * 4 + (blocks * 8 if q8 else 0) + B * 4
         qo = B * H * self.G * D * (2 + 2)
-        append = B * H * D * 2 * elt + (B * 8 if self.w.kv_dtype == "e4m3" else 0)
+        append = B * H * D * 2 * elt + (B * 8 if q8 else 0)
         pass1 = kv + table + qo + (append if self.fused else 0)
         return (kv + table + qo + append) * self.L, pass1
 
@@ -203,7 +204,7 @@ class PagedBench:
         ref = PagedCache(layer.num_blocks, self.H, self.D, self.w.kv_dtype)
         ref.K = layer.k_pool.cpu().numpy()
         ref.V = layer.v_pool.cpu().numpy()
-        if self.w.kv_dtype == "e4m3":
+        if self.w.kv_dtype in ("e4m3", "i8"):
             ref.k_scale = layer.k_scale.cpu().numpy()
             ref.v_scale = layer.v_scale.cpu().numpy()
         q = self.q[li].float().cpu().numpy()
@@ -551,18 +552,19 @@ def main():
          "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
          "gqa8-paged": workloads.GQA8_PAGED,
          "llama13b-window": workloads.LLAMA13B_WINDOW,
-         "llama7b-prefill": workloads.LLAMA7B_PREFILL}[args.workload]
+         "llama7b-prefill": workloads.LLAMA7B_PREFILL,
+         "i8-longctx": workloads.LONGCTX_I8}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    separate = (w.kv_dtype == "e4m3" or w.extra.get("group", 1) > 1 or "window" in w.extra
-                or w is workloads.LLAMA7B_PREFILL)
+    separate = (w.kv_dtype in ("e4m3", "i8") or w.extra.get("group", 1) > 1
+                or "window" in w.extra or w is workloads.LLAMA7B_PREFILL)
     fused = args.append == "fused" or (args.append == "auto" and not separate)
     if fused and separate:
-        print("--append fused: e4m3 caches, shared K/V heads and rolling windows take the "
+        print("--append fused: 8-bit caches, shared K/V heads and rolling windows take the "
               "separate writer", file=sys.stderr)
         sys.exit(2)
     path = "fused" if fused else "separate"

@@ -52,7 +52,8 @@ typedef enum kvc_status {
 typedef enum kvc_dtype {
   KVC_F32 = 0,  /* IEEE binary32 */
   KVC_F16 = 1,  /* IEEE binary16 */
-  KVC_E4M3 = 2  /* OCP fp8 e4m3 ("fn": bias 7, max 448, no inf, 0x7F/0xFF NaN); cache only */
+  KVC_E4M3 = 2, /* OCP fp8 e4m3 ("fn": bias 7, max 448, no inf, 0x7F/0xFF NaN); cache only */
+  KVC_I8 = 3    /* two's-complement int8 codes in [-127, 127] with a scale; cache only */
 } kvc_dtype;
 
 #define KVC_BLOCK_SIZE 16
@@ -160,8 +161,8 @@ kvc_status kvc_check(const kvc_pool *pool);
 /* One layer of a paged cache (device pointers owned by the caller).
  *   k_pool, v_pool: [num_blocks][num_heads][16][head_dim] elements of kv_dtype
  *   k_scale, v_scale: float[num_blocks], one fp32 scale per block for K and for V, covering all
- *                     heads of the block (KVC_E4M3 only; NULL otherwise). The stored value of
- *                     code c in block p is e4m3(c) * scale[p]. */
+ *                     heads of the block (KVC_E4M3 and KVC_I8 only; NULL otherwise). The stored
+ *                     value of code c in block p is e4m3(c) * scale[p], or c * scale[p]. */
 typedef struct kvc_paged_layer {
   kvc_dtype kv_dtype;
   int32_t num_blocks;
@@ -203,6 +204,11 @@ kvc_status kvc_copy_blocks(const kvc_paged_layer *layer, const int32_t *src, con
  *     to nearest even and saturated to +-448 (signed zero while the scale is 0). ("KV Cache
  *     Mechanism Explained", section 8, item 3: fp8 e4m3 cache with a scaling factor.) All
  *     entries that target one block must be adjacent in `slots`; inputs must be finite.
+ *   int8 pools ("KV Cache Mechanism Explained", section 8, item 3 names FP8/INT8 with a scaling
+ *     factor max|x| / 127; "KV Cache and PagedAttention", section 7.2, 8-bit quantisation of
+ *     blocks): the same rule with the int8 limit, s_new = fp32(max|x| / 127), codes
+ *     rint(fp32(y / scale)) saturated to +-127 (never -128), ties to even, zero while the scale
+ *     is 0.
  * Entries with a slot outside [0, 16*num_blocks) are skipped. */
 kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, int32_t n_tok,
                            const void *k_new, const void *v_new, kvc_dtype new_dtype,
@@ -230,7 +236,8 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
  *   workspace: device buffer of at least kvc_decode_workspace_bytes(B, H, D) bytes, 256-byte
  *             aligned, owned by the caller; no initialisation needed, contents overwritten.
  *             Calls that may overlap in time need different workspaces.
- * Supported: D in {64, 128}; B <= 4096; kv dtype f32/f16 (contiguous) and f32/f16/e4m3 (paged).
+ * Supported: D in {64, 128}; B <= 4096; kv dtype f32/f16 (contiguous) and f32/f16/e4m3/int8
+ * (paged; 8-bit codes are dequantised in-kernel with their block scales).
  * ==================================================================================== */
 size_t kvc_decode_workspace_bytes(int32_t B, int32_t H, int32_t D);
 

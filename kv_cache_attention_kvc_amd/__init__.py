@@ -17,7 +17,7 @@ import numpy as np
 
 __all__ = [
     "KvcError", "load_library", "library_path", "Pool", "PagedLayer",
-    "F32", "F16", "E4M3", "BLOCK_SIZE", "workspace_bytes",
+    "F32", "F16", "E4M3", "I8", "BLOCK_SIZE", "workspace_bytes",
     "append_contig", "copy_blocks", "write_paged", "decode_attn_contig", "decode_attn_paged",
     "decode_partial_contig", "decode_partial_paged", "decode_merge", "new_workspace", "EXPORTS",
     "append_decode_contig", "append_decode_paged", "append_decode_partial_contig",
@@ -28,7 +28,7 @@ __all__ = [
     "prefill_paged",
 ]
 
-F32, F16, E4M3 = 0, 1, 2
+F32, F16, E4M3, I8 = 0, 1, 2, 3
 BLOCK_SIZE = 16
 _STATUS = {0: "KVC_OK", -1: "KVC_E_INVALID", -2: "KVC_E_OOM", -3: "KVC_E_NOSEQ",
            -4: "KVC_E_CAPACITY", -5: "KVC_E_UNSUPPORTED", -6: "KVC_E_HIP"}
@@ -283,6 +283,8 @@ def _dtype_code(t) -> int:
         return F16
     if t.dtype == torch.uint8:
         return E4M3
+    if t.dtype == torch.int8:
+        return I8
     raise TypeError(f"unsupported dtype {t.dtype}")
 
 
@@ -303,7 +305,7 @@ def _stream(stream) -> int:
 @dataclass
 class PagedLayer:
     """One layer of a paged cache: pools [num_blocks, H, 16, D] (float32/float16, or uint8 holding
-    e4m3 codes with float32 scales [num_blocks] for K and V)."""
+    e4m3 codes / int8 codes, with float32 scales [num_blocks] for K and V)."""
     k_pool: object
     v_pool: object
     k_scale: object = None
@@ -312,10 +314,13 @@ class PagedLayer:
     @staticmethod
     def empty(num_blocks: int, heads: int, head_dim: int, dtype: str, device="cuda", fill=None):
         torch = _torch()
-        td = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8}[dtype]
+        td = {"f32": torch.float32, "f16": torch.float16, "e4m3": torch.uint8,
+              "i8": torch.int8}[dtype]
         shape = (num_blocks, heads, BLOCK_SIZE, head_dim)
         if dtype == "e4m3" and fill is not None:
             fill = 0x7F if fill != fill else int(fill)     # NaN -> the e4m3 NaN code
+        if dtype == "i8" and fill is not None:
+            fill = -128 if fill != fill else int(fill)     # NaN -> the never-written int8 code
         if fill is None:
             k = torch.zeros(shape, dtype=td, device=device)
             v = torch.zeros(shape, dtype=td, device=device)
@@ -323,7 +328,7 @@ class PagedLayer:
             k = torch.full(shape, fill, dtype=td, device=device)
             v = torch.full(shape, fill, dtype=td, device=device)
         ks = vs = None
-        if dtype == "e4m3":
+        if dtype in ("e4m3", "i8"):
             ks = torch.zeros(num_blocks, dtype=torch.float32, device=device)
             vs = torch.zeros(num_blocks, dtype=torch.float32, device=device)
         return PagedLayer(k, v, ks, vs)
@@ -353,7 +358,7 @@ class PagedLayer:
         code = _dtype_code(self.k_pool)
         s = _Layer(code, self.num_blocks, self.heads, self.head_dim, _ptr(self.k_pool),
                    _ptr(self.v_pool), None, None)
-        if code == E4M3:
+        if code in (E4M3, I8):
             s.k_scale = _ptr(self.k_scale)
             s.v_scale = _ptr(self.v_scale)
         self._cached = (key, s)

@@ -131,6 +131,18 @@ __device__ __forceinline__ void unpack(const uint4 &r, float *f) {
       f[2 * i + 1] =
           static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(w[i] >> 16)));
     }
+  } else if constexpr (KV == KVC_I8) {
+    // exact through fp16 (see i8x4_to_f16); the fp16 values feed mixed-precision FMAs
+    const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f16x2 lo, hi;
+      i8x4_to_f16(w[i], lo, hi);
+      f[4 * i + 0] = static_cast<float>(lo[0]);
+      f[4 * i + 1] = static_cast<float>(lo[1]);
+      f[4 * i + 2] = static_cast<float>(hi[0]);
+      f[4 * i + 3] = static_cast<float>(hi[1]);
+    }
   } else {
     // gfx950 converts OCP e4m3 in hardware (exact: every code is an fp32 value)
     const uint32_t w[4] = {r.x, r.y, r.z, r.w};
@@ -304,7 +316,7 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
     const int64_t toff = (static_cast<int64_t>(sp) * a.H + hkv) * G::TILE;
     kt = a.k + toff;
     vt = a.v + toff;
-    if constexpr (KV == KVC_E4M3) {
+    if constexpr (is_q8(KV)) {
       t.ks = valid ? a.k_scale[sp] : 0.f;
       t.vs = valid ? a.v_scale[sp] : 0.f;
     }
@@ -409,7 +421,7 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
   }
   const QWords<QF16, G::EPL> *qq = GQ == 1 ? t.q : qs;
   float s[GQ][G::LOADS];
-  const float sc = (KV == KVC_E4M3) ? cl2 * t.ks : cl2;
+  const float sc = is_q8(KV) ? cl2 * t.ks : cl2;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
     const bool ok = g + i * G::TPL < t.nt && (!WIN || g + i * G::TPL >= t.lo);
@@ -443,7 +455,7 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
     unpack<KV>(t.v[i], vf);
 #pragma unroll
     for (int r = 0; r < GQ; ++r) {
-      const float pi = (KV == KVC_E4M3) ? s[r][i] * t.vs : s[r][i];
+      const float pi = is_q8(KV) ? s[r][i] * t.vs : s[r][i];
 #pragma unroll
       for (int e = 0; e < G::EPL; ++e) acc[r][e] = __builtin_fmaf(pi, vf[e], acc[r][e]);
     }
@@ -681,13 +693,14 @@ struct VecCore {
 //     wave-contiguous layout, written as fp16 rows with 16-byte columns swizzled by row group,
 //     and read back one fp16 at a time; the swizzle puts the four lane groups of a read on
 //     distinct banks. Lane (g, j) accumulates dims 16*dc + 4g .. +3 of head j.
-//   e4m3: codes convert exactly to fp16 (v_cvt_scalef32_pk_f16_fp8 with scale 1). The K block
+//   8-bit caches: e4m3 codes convert exactly to fp16 (v_cvt_scalef32_pk_f16_fp8 with scale 1),
+//     int8 codes too (through a biased fp16 exponent, i8x8_to_f16). The K block
 //     scale multiplies the scores. O is held in units of a reference V scale; a tile's weights
 //     are multiplied by its block's scale over the reference (kept within [1/16, 16], else the
 //     reference moves to this block's scale and O is rescaled).
 template <bool PAGED, int KV, int D, bool WIN>
 struct MfmaCore {
-  static_assert(KV == KVC_F16 || KV == KVC_E4M3, "fp16 or e4m3 cache");
+  static_assert(KV == KVC_F16 || is_q8(KV), "fp16 or 8-bit cache");
   using G = Geo<KV, D>;            // wave-contiguous geometry (V loads)
   static constexpr int kD = D;
   static constexpr bool kWin = WIN;
@@ -695,10 +708,10 @@ struct MfmaCore {
   static constexpr int NQK = D / 32;      // score MFMAs per tile
   static constexpr int NDC = D / 16;      // 16-dim output blocks
   static constexpr int kVbufBytes = kBlock * D * 2;
-  // Weight headroom (log2 units): weights are at most 2^kHi, times kRat for e4m3, below the
+  // Weight headroom (log2 units): weights are at most 2^kHi, times kRat for 8-bit caches, below the
   // fp16 maximum; a fresh reference gives the tile's top weight 2^kHead.
-  static constexpr float kHead = KV == KVC_E4M3 ? 3.f : 7.f;
-  static constexpr float kHi = KV == KVC_E4M3 ? 11.f : 15.f;
+  static constexpr float kHead = is_q8(KV) ? 3.f : 7.f;
+  static constexpr float kHi = is_q8(KV) ? 11.f : 15.f;
   static constexpr float kRat = 16.f;
   struct Tile {
     uint4 k[KL];
@@ -734,7 +747,7 @@ struct MfmaCore {
       const int64_t toff = (static_cast<int64_t>(sp) * a.H + hkv) * G::TILE;
       kt = a.k + toff;
       vt = a.v + toff;
-      if constexpr (KV == KVC_E4M3) {
+      if constexpr (is_q8(KV)) {
         t.ks = valid ? a.k_scale[sp] : 0.f;
         t.vs = valid ? a.v_scale[sp] : 0.f;
       }
@@ -759,7 +772,7 @@ struct MfmaCore {
   }
 
   // q operand of head j of the pair: 16-byte chunk of the fp16 q row for score MFMA n (the dims
-  // K load n / 2 half n % 2 covers for e4m3, K load n for fp16)
+  // K load n / 2 half n % 2 covers for 8-bit caches, K load n for fp16)
   __device__ void begin(const DecodeArgs &a, int64_t qrow, State &s) const {
     const char *qr = static_cast<const char *>(a.q) + (qrow + min(j, a.gq - 1)) * (D * 2);
 #pragma unroll
@@ -772,6 +785,12 @@ struct MfmaCore {
     s.m = kFloor;
     s.l = 0.f;
     s.vref = 1.f;
+  }
+
+  // 8 codes of the cache's 8-bit format as fp16, exactly
+  static __device__ __forceinline__ f16x8 q8x8_to_f16(uint32_t w0, uint32_t w1) {
+    if constexpr (KV == KVC_I8) return i8x8_to_f16(w0, w1);
+    return fp8x8_to_f16(w0, w1);
   }
 
   __device__ void touch(const Tile &t) const {
@@ -796,9 +815,9 @@ struct MfmaCore {
         *reinterpret_cast<uint4 *>(vbuf + row * D + swz(row, cv) * 8) = t.v[i];
       } else {
         *reinterpret_cast<f16x8 *>(vbuf + row * D + swz(row, 2 * cv) * 8) =
-            fp8x8_to_f16(t.v[i].x, t.v[i].y);
+            q8x8_to_f16(t.v[i].x, t.v[i].y);
         *reinterpret_cast<f16x8 *>(vbuf + row * D + swz(row, 2 * cv + 1) * 8) =
-            fp8x8_to_f16(t.v[i].z, t.v[i].w);
+            q8x8_to_f16(t.v[i].z, t.v[i].w);
       }
     }
     // scores of positions 4g..4g+3 for head j
@@ -810,11 +829,11 @@ struct MfmaCore {
         ka = as_f16x8(t.k[n]);
       } else {
         const uint4 &w = t.k[n >> 1];
-        ka = (n & 1) ? fp8x8_to_f16(w.z, w.w) : fp8x8_to_f16(w.x, w.y);
+        ka = (n & 1) ? q8x8_to_f16(w.z, w.w) : q8x8_to_f16(w.x, w.y);
       }
       sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, as_f16x8(s.q[n]), sacc, 0, 0, 0);
     }
-    const float sc = KV == KVC_E4M3 ? a.cl2 * t.ks : a.cl2;
+    const float sc = is_q8(KV) ? a.cl2 * t.ks : a.cl2;
     float x[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
@@ -828,12 +847,12 @@ struct MfmaCore {
       mx = fmaxf(u, v);
     }
     // The reference moves only when a score passes it by more than kHi (first tile included,
-    // since it starts at kFloor); then it is set kHead below the tile's maximum. e4m3: the ratio
+    // since it starts at kFloor); then it is set kHead below the tile's maximum. 8-bit: the ratio
     // of this block's V scale to the reference scale must also stay within [1/kRat, kRat].
     float ratio = 1.f;
     bool rebase = false;
     float vsn = 1.f;
-    if constexpr (KV == KVC_E4M3) {
+    if constexpr (is_q8(KV)) {
       // an all-zero block has scale 0 and zero codes: any scale represents it
       vsn = t.vs != 0.f ? t.vs : 1.f;
       ratio = vsn / s.vref;
@@ -844,7 +863,7 @@ struct MfmaCore {
       const float mnew = up ? mx - kHead : s.m;
       float f = __builtin_amdgcn_exp2f(s.m - mnew);
       s.l *= f;
-      if constexpr (KV == KVC_E4M3) {
+      if constexpr (is_q8(KV)) {
         f *= s.vref / vsn;
         s.vref = vsn;
         ratio = 1.f;
@@ -862,7 +881,7 @@ struct MfmaCore {
     f16x4 ph, pl;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float pv = KV == KVC_E4M3 ? p[e] * ratio : p[e];
+      const float pv = is_q8(KV) ? p[e] * ratio : p[e];
       ph[e] = static_cast<_Float16>(pv);
       pl[e] = static_cast<_Float16>(pv - static_cast<float>(ph[e]));
     }
@@ -897,7 +916,7 @@ struct MfmaCore {
     const int32_t rec0 = (w * 2 + (sg.cut_start ? 0 : 1)) * GQ;
     if (j < GQ) {
       float *e = st.base + (st.n + j) * (D + 4);
-      const float vr = KV == KVC_E4M3 ? s.vref : 1.f;
+      const float vr = is_q8(KV) ? s.vref : 1.f;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
         *reinterpret_cast<f32x4 *>(e + 16 * dc + 4 * g) = s.o[dc] * vr;
@@ -1170,7 +1189,7 @@ int device_cu_count() {
 
 using PartialKernel = void (*)(DecodeArgs);
 
-// How pass 1 serves G query heads per K/V head. With fp16 queries over an fp16 (or paged e4m3)
+// How pass 1 serves G query heads per K/V head. With fp16 queries over an fp16 (or paged 8-bit)
 // cache and G > 1, the matrix-core kernel serves gq heads per wavefront, the largest divisor of
 // G up to 16, and each K/V byte is read G/gq times (once for G <= 16). Otherwise each query head
 // is its own pair on the vector kernel and its K/V head is read once per query head.
@@ -1186,7 +1205,7 @@ inline int largest_group_divisor(int G) {
 }
 
 inline GroupPlan group_plan(int G, kvc_dtype kv, bool q_f16, bool paged) {
-  const bool mfma_ok = q_f16 && (kv == KVC_F16 || (paged && kv == KVC_E4M3));
+  const bool mfma_ok = q_f16 && (kv == KVC_F16 || (paged && is_q8(kv)));
   const int w = largest_group_divisor(G);
   if (mfma_ok && w > 1) return {w, true};
   return {1, false};
@@ -1201,6 +1220,8 @@ PartialKernel pick_vec_d(kvc_dtype kv) {
   if (kv == KVC_F16) return decode_partial_kernel<PAGED, KVC_F16, D, QF16, 1, WIN>;
   if constexpr (PAGED)
     if (kv == KVC_E4M3) return decode_partial_kernel<PAGED, KVC_E4M3, D, QF16, 1, WIN>;
+  if constexpr (PAGED)
+    if (kv == KVC_I8) return decode_partial_kernel<PAGED, KVC_I8, D, QF16, 1, WIN>;
   return nullptr;
 }
 
@@ -1209,6 +1230,8 @@ PartialKernel pick_mfma_d(kvc_dtype kv) {
   if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D, WIN>;
   if constexpr (PAGED)
     if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D, WIN>;
+  if constexpr (PAGED)
+    if (kv == KVC_I8) return decode_partial_mfma_kernel<PAGED, KVC_I8, D, WIN>;
   return nullptr;
 }
 
@@ -1281,7 +1304,7 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
   if (B > kMaxBatch) return KVC_E_INVALID;
   if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
   if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
-  if (!paged && kv_dtype == KVC_E4M3) return KVC_E_UNSUPPORTED;
+  if (!paged && is_q8(kv_dtype)) return KVC_E_UNSUPPORTED;
   if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
   const bool q_f16 = q_dtype == KVC_F16;
   const GroupPlan gp = group_plan(G, kv_dtype, q_f16, paged);
@@ -1400,8 +1423,8 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
     return KVC_E_INVALID;
   if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
   const kvc_dtype kv = layer->kv_dtype;
-  if (kv != KVC_F32 && kv != KVC_F16 && kv != KVC_E4M3) return KVC_E_UNSUPPORTED;
-  if (k_new && kv == KVC_E4M3) return KVC_E_UNSUPPORTED;  // the block scale may change
+  if (kv != KVC_F32 && kv != KVC_F16 && !is_q8(kv)) return KVC_E_UNSUPPORTED;
+  if (k_new && is_q8(kv)) return KVC_E_UNSUPPORTED;  // the block scale may change
   PartialPlan pl;
   kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads, G,
                                layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, window, scale,
@@ -1410,7 +1433,7 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
   if (!block_tables || !layer->k_pool || !layer->v_pool || !aligned16(layer->k_pool) ||
       !aligned16(layer->v_pool))
     return KVC_E_INVALID;
-  if (kv == KVC_E4M3 && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
+  if (is_q8(kv) && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
   if (k_new && (!aligned16(k_new) || !aligned16(v_new) || G != 1)) return KVC_E_INVALID;
   pl.a.k = static_cast<const char *>(layer->k_pool);

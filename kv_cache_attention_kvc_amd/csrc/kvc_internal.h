@@ -20,6 +20,9 @@ inline int elt_bytes(kvc_dtype t) { return t == KVC_F32 ? 4 : (t == KVC_F16 ? 2 
 
 inline bool is_f32_or_f16(kvc_dtype t) { return t == KVC_F32 || t == KVC_F16; }
 
+// 8-bit codes with one fp32 scale per block for K and one for V (e4m3 or int8).
+constexpr bool is_q8(int t) { return t == KVC_E4M3 || t == KVC_I8; }
+
 inline kvc_status launch_status() {
   return hipGetLastError() == hipSuccess ? KVC_OK : KVC_E_HIP;
 }

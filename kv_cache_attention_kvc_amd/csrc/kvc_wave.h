@@ -1,6 +1,7 @@
 // Wave-level device helpers shared by the HIP translation units of libkvc (not part of the
 // ABI): cross-lane exchanges, streaming loads, fp16 vector types for the matrix cores, exact
-// e4m3-to-fp16 conversion, and the LDS ordering point between lanes of one wavefront.
+// e4m3-to-fp16 and int8-to-fp16 conversions, and the LDS ordering point between lanes of one
+// wavefront.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -71,6 +72,27 @@ __device__ __forceinline__ f16x8 fp8x8_to_f16(uint32_t w0, uint32_t w1) {
   return __builtin_bit_cast(f16x8, make_uint4(KVC_CVT8(w0, false), KVC_CVT8(w0, true),
                                               KVC_CVT8(w1, false), KVC_CVT8(w1, true)));
 #undef KVC_CVT8
+}
+
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+// 4 int8 codes (one word, lowest byte first) as two fp16 pairs, exactly. Each byte b is biased
+// to u = b ^ 0x80 = b + 128 and placed under the fp16 exponent of 1024 (bits 0x6400 | u, the
+// value 1024 + u, exact since fp16 steps by 1 in [1024, 2048)); subtracting 1152 leaves b.
+// v_perm_b32 picks bytes of {S0, S1} (selector 0-3: S1's bytes, 4-7: S0's).
+__device__ __forceinline__ void i8x4_to_f16(uint32_t w, f16x2 &lo, f16x2 &hi) {
+  const uint32_t x = w ^ 0x80808080u;
+  const f16x2 bias = {static_cast<_Float16>(1152.0f), static_cast<_Float16>(1152.0f)};
+  lo = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04010400u)) - bias;
+  hi = __builtin_bit_cast(f16x2, __builtin_amdgcn_perm(0x64646464u, x, 0x04030402u)) - bias;
+}
+
+// 8 int8 codes (two words) as fp16, exactly.
+__device__ __forceinline__ f16x8 i8x8_to_f16(uint32_t w0, uint32_t w1) {
+  f16x2 a, b, c, d;
+  i8x4_to_f16(w0, a, b);
+  i8x4_to_f16(w1, c, d);
+  return f16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 }  // namespace kvc

@@ -1,10 +1,11 @@
-// Cache writes for gfx950: contiguous append, paged scatter, fp8-e4m3 per-block quantised
-// writes, and copy-on-write block copies.
+// Cache writes for gfx950: contiguous append, paged scatter, 8-bit (fp8-e4m3 or int8) per-block
+// quantised writes, and copy-on-write block copies.
 //
 // The new token's K/V are stored before attention reads the cache ("LLM Inference Acceleration
 // -- KV Cache", section 3.1). Paged writes go to slot = block*16 + offset chosen by the host pool
-// ("KV Cache and PagedAttention", sections 3.1 and 3.3). fp8 pools hold OCP e4m3 codes with one
-// fp32 scale per block for K and one for V ("KV Cache Mechanism Explained", section 8, item 3).
+// ("KV Cache and PagedAttention", sections 3.1 and 3.3). 8-bit pools hold OCP e4m3 or int8 codes
+// with one fp32 scale per block for K and one for V ("KV Cache Mechanism Explained", section 8,
+// item 3: FP8/INT8 history with a scaling factor; "KV Cache and PagedAttention", section 7.2).
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -109,9 +110,40 @@ __device__ __forceinline__ float e4m3_decode(uint32_t c) {
   return __uint_as_float(__float_as_uint(mag) | ((c & 0x80u) << 24));
 }
 
+// int8: nearest integer of q (ties to even, v_rndne), saturated to +-127; NaN -> 0.
+__device__ __forceinline__ uint32_t i8_encode(float q) {
+  if (!(q == q)) return 0u;
+  const float r = __builtin_rintf(fminf(fmaxf(q, -127.0f), 127.0f));
+  return static_cast<uint32_t>(static_cast<int32_t>(r)) & 0xFFu;
+}
+
+__device__ __forceinline__ float i8_decode(uint32_t c) {
+  return static_cast<float>(static_cast<int8_t>(static_cast<uint8_t>(c)));
+}
+
+// The two 8-bit formats: code limit, encode (of an fp32 value already divided by the scale),
+// exact decode, and the code of a value stored while the scale is 0.
+template <int FMT>
+struct Q8 {
+  static constexpr float kMax = FMT == KVC_E4M3 ? 448.0f : 127.0f;
+  static __device__ __forceinline__ uint32_t enc(float q) {
+    if constexpr (FMT == KVC_E4M3) return e4m3_encode(q);
+    return i8_encode(q);
+  }
+  static __device__ __forceinline__ float dec(uint32_t c) {
+    if constexpr (FMT == KVC_E4M3) return e4m3_decode(c);
+    return i8_decode(c);
+  }
+  static __device__ __forceinline__ uint32_t zero(float x) {
+    if constexpr (FMT == KVC_E4M3) return (__float_as_uint(x) >> 24) & 0x80u;  // signed zero
+    return 0u;
+  }
+};
+
+template <int FMT>
 __device__ __forceinline__ uint32_t enc_scaled(float x, float s) {
-  if (s == 0.f) return (__float_as_uint(x) >> 24) & 0x80u;  // signed zero code
-  return e4m3_encode(x / s);
+  if (s == 0.f) return Q8<FMT>::zero(x);
+  return Q8<FMT>::enc(x / s);
 }
 
 __device__ __forceinline__ float block_max(float v, float *red) {
@@ -142,6 +174,7 @@ __device__ __forceinline__ void load4(const void *p, int64_t idx, float *x) {
   }
 }
 
+template <int FMT>
 __device__ __forceinline__ void requant_rows(uint8_t *pool, int64_t row0, int32_t D, int32_t d,
                                              int32_t off, float old_s, float new_s) {
   for (int t = 0; t < off; ++t) {
@@ -150,8 +183,8 @@ __device__ __forceinline__ void requant_rows(uint8_t *pool, int64_t row0, int32_
     uint32_t nw = 0;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const float y = e4m3_decode((old >> (8 * u)) & 0xFFu) * old_s;
-      nw |= enc_scaled(y, new_s) << (8 * u);
+      const float y = Q8<FMT>::dec((old >> (8 * u)) & 0xFFu) * old_s;
+      nw |= enc_scaled<FMT>(y, new_s) << (8 * u);
     }
     *w = nw;
   }
@@ -160,9 +193,10 @@ __device__ __forceinline__ void requant_rows(uint8_t *pool, int64_t row0, int32_
 // One workgroup per run of adjacent entries that target the same block; tokens of the run are
 // applied in order. Each thread owns the same 4 consecutive elements of every (head, slot) row
 // of the block, for all 16 slots, so requantisation only reads bytes the same thread wrote.
-template <bool SRC_F16>
+// FMT: KVC_E4M3 or KVC_I8.
+template <bool SRC_F16, int FMT>
 __global__ void __launch_bounds__(kThreads)
-write_paged_fp8_kernel(uint8_t *kp, uint8_t *vp, float *ks, float *vs, const void *kn,
+write_paged_q8_kernel(uint8_t *kp, uint8_t *vp, float *ks, float *vs, const void *kn,
                        const void *vn, const int64_t *slots, int32_t n_tok, int32_t H, int32_t D,
                        int32_t num_blocks) {
   __shared__ float red[2][kThreads / 64];
@@ -198,8 +232,8 @@ write_paged_fp8_kernel(uint8_t *kp, uint8_t *vp, float *ks, float *vs, const voi
     }
     mk = block_max(mk, red[0]);
     mv = block_max(mv, red[1]);
-    const float nk = mk / 448.0f;
-    const float nv = mv / 448.0f;
+    const float nk = mk / Q8<FMT>::kMax;
+    const float nv = mv / Q8<FMT>::kMax;
     const bool gk = nk > sk;
     const bool gv = nv > sv;
     const float ck = gk ? nk : sk;
@@ -208,16 +242,16 @@ write_paged_fp8_kernel(uint8_t *kp, uint8_t *vp, float *ks, float *vs, const voi
       const int32_t h = e0 / D;
       const int32_t d = e0 % D;
       const int64_t row0 = (blk * H + h) * kBlock;  // slot-0 row of this head in the block
-      if (gk && off > 0) requant_rows(kp, row0, D, d, off, sk, nk);
-      if (gv && off > 0) requant_rows(vp, row0, D, d, off, sv, nv);
+      if (gk && off > 0) requant_rows<FMT>(kp, row0, D, d, off, sk, nk);
+      if (gv && off > 0) requant_rows<FMT>(vp, row0, D, d, off, sv, nv);
       float a[4], b[4];
       load4<SRC_F16>(kn, base + e0, a);
       load4<SRC_F16>(vn, base + e0, b);
       uint32_t wk = 0, wv = 0;
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
-        wk |= enc_scaled(a[u], ck) << (8 * u);
-        wv |= enc_scaled(b[u], cv) << (8 * u);
+        wk |= enc_scaled<FMT>(a[u], ck) << (8 * u);
+        wv |= enc_scaled<FMT>(b[u], cv) << (8 * u);
       }
       *reinterpret_cast<uint32_t *>(kp + (row0 + off) * D + d) = wk;
       *reinterpret_cast<uint32_t *>(vp + (row0 + off) * D + d) = wv;
@@ -261,11 +295,11 @@ kvc_status kvc_append_contig(void *k_cache, void *v_cache, kvc_dtype dtype, int3
 static kvc_status check_layer(const kvc_paged_layer *L) {
   if (!L || L->num_blocks < 1 || L->num_heads < 1) return KVC_E_INVALID;
   if (L->head_dim != 64 && L->head_dim != 128) return KVC_E_UNSUPPORTED;
-  if (L->kv_dtype != KVC_F32 && L->kv_dtype != KVC_F16 && L->kv_dtype != KVC_E4M3)
+  if (L->kv_dtype != KVC_F32 && L->kv_dtype != KVC_F16 && !is_q8(L->kv_dtype))
     return KVC_E_UNSUPPORTED;
   if (!L->k_pool || !L->v_pool || !aligned16(L->k_pool) || !aligned16(L->v_pool))
     return KVC_E_INVALID;
-  if (L->kv_dtype == KVC_E4M3 && (!L->k_scale || !L->v_scale)) return KVC_E_INVALID;
+  if (is_q8(L->kv_dtype) && (!L->k_scale || !L->v_scale)) return KVC_E_INVALID;
   return KVC_OK;
 }
 
@@ -278,7 +312,7 @@ kvc_status kvc_copy_blocks(const kvc_paged_layer *layer, const int32_t *src, con
   if (!src || !dst) return KVC_E_INVALID;
   const int64_t block_bytes = static_cast<int64_t>(layer->num_heads) * kBlock * layer->head_dim *
                               elt_bytes(layer->kv_dtype);
-  const bool fp8 = layer->kv_dtype == KVC_E4M3;
+  const bool fp8 = is_q8(layer->kv_dtype);
   hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<char *>(layer->k_pool),
                      static_cast<char *>(layer->v_pool), fp8 ? layer->k_scale : nullptr,
@@ -296,18 +330,16 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
   if (!slots || !k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return KVC_E_INVALID;
   const int32_t H = layer->num_heads, D = layer->head_dim;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (layer->kv_dtype == KVC_E4M3) {
+  if (is_q8(layer->kv_dtype)) {
     if (!is_f32_or_f16(new_dtype)) return KVC_E_UNSUPPORTED;
     auto *kp = static_cast<uint8_t *>(layer->k_pool);
     auto *vp = static_cast<uint8_t *>(layer->v_pool);
-    if (new_dtype == KVC_F16)
-      hipLaunchKernelGGL(write_paged_fp8_kernel<true>, dim3(n_tok), dim3(kThreads), 0, s, kp, vp,
-                         layer->k_scale, layer->v_scale, k_new, v_new, slots, n_tok, H, D,
-                         layer->num_blocks);
-    else
-      hipLaunchKernelGGL(write_paged_fp8_kernel<false>, dim3(n_tok), dim3(kThreads), 0, s, kp, vp,
-                         layer->k_scale, layer->v_scale, k_new, v_new, slots, n_tok, H, D,
-                         layer->num_blocks);
+    const bool f16 = new_dtype == KVC_F16;
+    auto kern = layer->kv_dtype == KVC_E4M3
+                    ? (f16 ? write_paged_q8_kernel<true, KVC_E4M3> : write_paged_q8_kernel<false, KVC_E4M3>)
+                    : (f16 ? write_paged_q8_kernel<true, KVC_I8> : write_paged_q8_kernel<false, KVC_I8>);
+    hipLaunchKernelGGL(kern, dim3(n_tok), dim3(kThreads), 0, s, kp, vp, layer->k_scale,
+                       layer->v_scale, k_new, v_new, slots, n_tok, H, D, layer->num_blocks);
     return launch_status();
   }
   if (new_dtype != layer->kv_dtype) return KVC_E_UNSUPPORTED;

@@ -22,6 +22,7 @@ LENS = [1, 15, 16, 17, 250, 513, 0, 64]
     ("f16", 128, 2, 2), ("f16", 128, 2, 4), ("f16", 128, 2, 8), ("f16", 128, 1, 8),
     ("f16", 64, 2, 4), ("f16", 64, 3, 8), ("f16", 128, 2, 16), ("f16", 128, 2, 6),
     ("e4m3", 128, 2, 4), ("e4m3", 128, 2, 8), ("e4m3", 64, 2, 2),
+    ("i8", 128, 2, 8), ("i8", 64, 2, 4),
     ("f32", 128, 2, 4), ("f32", 64, 1, 3)])
 def test_paged_gqa_against_oracle(dtype, D, H, G):
     d = dev()

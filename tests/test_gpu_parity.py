@@ -103,7 +103,7 @@ def _paged_setup(d, dtype, D, lens, H=3, seed=0, extra_blocks=5, new_dtype=None)
         model.alloc()
     layer = kvc.PagedLayer.empty(N, H, D, dtype, device=d, fill=float("nan"))
     ref = PagedCache(N, H, D, dtype, fill=np.nan)
-    src_dtype = new_dtype or ("f16" if dtype == "e4m3" else dtype)
+    src_dtype = new_dtype or ("f16" if dtype in ("e4m3", "i8") else dtype)
     data = []
     for s, L in zip(seqs, lens):
         slots, src, _ = pool.append([s], L)
@@ -128,7 +128,7 @@ def _compare_pools(layer, ref):
 
 
 @pytest.mark.parametrize("dtype,D", [("f32", 64), ("f32", 128), ("f16", 64), ("f16", 128),
-                                     ("e4m3", 64), ("e4m3", 128)])
+                                     ("e4m3", 64), ("e4m3", 128), ("i8", 64), ("i8", 128)])
 def test_paged_ragged(dtype, D):
     d = dev()
     note(f"paged ragged {dtype} D={D}")
@@ -143,7 +143,7 @@ def test_paged_ragged(dtype, D):
     torch.cuda.synchronize()
     want = ref.decode(q, tables, tl, scale_of(D))
     check(got.float().cpu().numpy(), want, TOL["f32"] if dtype == "f32" else TOL["f16"])
-    if dtype == "e4m3":
+    if dtype in ("e4m3", "i8"):
         # against the unquantised inputs as well, where enough positions are averaged: one
         # position alone reproduces a single dequantised row (e4m3 steps are 2^-4 relative)
         raw = PagedCache(layer.num_blocks, 3, D, "f32")
@@ -153,7 +153,7 @@ def test_paged_ragged(dtype, D):
             raw.write(slots, k.astype(np.float32), v.astype(np.float32))
         long_ = [i for i, L in enumerate(lens) if L >= 250]
         unq = raw.decode(q, tables, tl, scale_of(D))
-        check(got.float().cpu().numpy()[long_], unq[long_], TOL["e4m3"])
+        check(got.float().cpu().numpy()[long_], unq[long_], TOL[dtype])
 
 
 @pytest.mark.parametrize("dtype", ["f32", "f16"])
@@ -200,19 +200,43 @@ def test_e4m3_hardware_decode_matches_definition_for_every_code():
     np.testing.assert_array_equal(got, want)
 
 
+@pytest.mark.parametrize("G", [1, 4])
+def test_i8_decode_matches_definition_for_every_code(G):
+    """L = 1 and V scale 1: the output row is exactly the int8 V codes, all 256 of them, on the
+    vector kernel (G = 1) and on the matrix cores (G = 4, codes through fp16)."""
+    d = dev()
+    note(f"int8 code table through attention G={G}")
+    D, H = 128, 1
+    layer = kvc.PagedLayer.empty(2, H, D, "i8", device=d)
+    codes = np.arange(-128, 128, dtype=np.int8)
+    layer.v_pool[0, 0, 0] = to_dev(codes[:128], d)
+    layer.v_pool[1, 0, 0] = to_dev(codes[128:], d)
+    layer.k_scale.fill_(1.0)
+    layer.v_scale.fill_(1.0)
+    tables = to_dev(np.array([[0], [1]], np.int32), d)
+    lens = to_dev(np.array([1, 1], np.int32), d)
+    q = torch.ones((2, H * G, D), dtype=torch.float16, device=d)
+    out = torch.empty((2, H * G, D), dtype=torch.float32, device=d)
+    kvc.decode_gqa_paged(q, layer, tables, lens, 1, out=out)
+    got = out.cpu().numpy()
+    for r in range(G):
+        np.testing.assert_array_equal(got[:, r].reshape(256), codes.astype(np.float64))
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
 @pytest.mark.parametrize("src", ["f16", "f32"])
 @pytest.mark.parametrize("D", [64, 128])
-def test_fp8_writes_bit_exact_with_requantisation_and_block_reuse(src, D):
+def test_q8_writes_bit_exact_with_requantisation_and_block_reuse(fmt, src, D):
     """Token-by-token appends of growing magnitude force scale growth and requantisation; a freed
-    block is reused (stale scale must be ignored at slot 0)."""
+    block is reused (stale scale must be ignored at slot 0). e4m3 and int8 pools."""
     d = dev()
-    note(f"fp8 writes src={src} D={D}")
+    note(f"8-bit writes {fmt} src={src} D={D}")
     H, N, MB = 5, 12, 6
     g = workloads.rng(77 + D)
     pool = kvc.Pool(N, MB)
     model = PoolModel(N, 16, MB)
-    layer = kvc.PagedLayer.empty(N, H, D, "e4m3", device=d)
-    ref = PagedCache(N, H, D, "e4m3")
+    layer = kvc.PagedLayer.empty(N, H, D, fmt, device=d)
+    ref = PagedCache(N, H, D, fmt)
     a, b = pool.alloc(), pool.alloc()
     model.alloc(), model.alloc()
 
@@ -249,7 +273,7 @@ def test_fp8_writes_bit_exact_with_requantisation_and_block_reuse(src, D):
     check(got.cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)), 2e-3)
 
 
-@pytest.mark.parametrize("dtype", ["f16", "e4m3"])
+@pytest.mark.parametrize("dtype", ["f16", "e4m3", "i8"])
 def test_parallel_sampling_small_copy_on_write(dtype):
     """A 20-token prompt (partial last block) shared by 4 candidates; each appends 30 tokens with
     attention at every step; pools and outputs against the oracle."""

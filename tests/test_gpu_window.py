@@ -26,7 +26,8 @@ LENS = [1, 15, 16, 17, 250, 513, 0, 64, 1000]
     ("f32", 128, 2, 1, 16, True), ("f32", 64, 1, 1, 300, False),
     ("e4m3", 128, 2, 1, 33, True), ("e4m3", 64, 2, 1, 1000, True),
     ("f16", 128, 2, 4, 100, True), ("f16", 64, 2, 8, 47, False), ("f16", 128, 1, 16, 5, True),
-    ("e4m3", 128, 2, 8, 250, True), ("f32", 128, 2, 2, 64, True)])
+    ("e4m3", 128, 2, 8, 250, True), ("f32", 128, 2, 2, 64, True),
+    ("i8", 128, 2, 1, 100, True), ("i8", 128, 2, 8, 33, True)])
 def test_paged_window_against_oracle(dtype, D, H, G, W, slide):
     d = dev()
     note(f"window paged {dtype} D={D} H_kv={H} G={G} W={W} slide={slide}")

@@ -169,21 +169,26 @@ def test_parallel_sampling_full(prompt, copies):
     np.testing.assert_array_equal(layer.v_pool.cpu().numpy(), ref.V)
 
 
-def test_fp8_long_context_full_layer():
-    """B=64, H=32, D=128, e4m3 with per-block scales, context 4096: prefill 4095 tokens per
-    sequence through the fp8 writer, append one, attend. Codes and scales of sampled blocks
-    bit-exact against the oracle's writer; sampled rows against the oracle over the stored codes
-    (2e-3) and over the unquantised inputs (3e-2)."""
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+def test_q8_long_context_full_layer(fmt):
+    """B=64, H=32, D=128, 8-bit codes (e4m3 or int8) with per-block scales, context 4096:
+    prefill 4095 tokens per sequence through the 8-bit writer, append one, attend. Codes and
+    scales of sampled blocks bit-exact against the oracle's writer; sampled rows against the
+    oracle over the stored codes (2e-3) and over the unquantised inputs (3e-2)."""
+    from oracle.codecs import i8_decode, i8_write_token
     d = dev()
-    w = workloads.LONGCTX_FP8
+    w = workloads.LONGCTX_FP8 if fmt == "e4m3" else workloads.LONGCTX_I8
+    write_token = fp8_write_token if fmt == "e4m3" else i8_write_token
+    decode = e4m3_decode if fmt == "e4m3" else i8_decode
+    npdt = np.uint8 if fmt == "e4m3" else np.int8
     B, H, D, T = w.batch, w.heads, w.head_dim, w.ctx
-    note("fp8 long context full layer")
+    note(f"{fmt} long context full layer")
     nblk = workloads.blocks_for(T)
     N = B * nblk
     pool = kvc.Pool(N, nblk)
     seqs = [pool.alloc() for _ in range(B)]
     slots = pool.append(seqs, T - 1)[0]
-    layer = kvc.PagedLayer.empty(N, H, D, "e4m3", device=d, fill=float("nan"))
+    layer = kvc.PagedLayer.empty(N, H, D, fmt, device=d, fill=float("nan"))
     k = workloads.torch_normal((len(slots), H, D), torch.float16, d, 51)
     v = workloads.torch_normal((len(slots), H, D), torch.float16, d, 52)
     kvc.write_paged(layer, torch.from_numpy(slots).to(d), k, v)
@@ -205,8 +210,8 @@ def test_fp8_long_context_full_layer():
     for b in rng.choice(B, size=3, replace=False):
         for j in (0, int(rng.integers(1, nblk - 1)), nblk - 1):
             blk = int(tables[b][j])
-            codes_k = np.zeros((H, 16, D), np.uint8)
-            codes_v = np.zeros((H, 16, D), np.uint8)
+            codes_k = np.zeros((H, 16, D), npdt)
+            codes_v = np.zeros((H, 16, D), npdt)
             sk = sv = np.float32(0)
             for t in range(16):
                 pos = j * 16 + t
@@ -215,8 +220,8 @@ def test_fp8_long_context_full_layer():
                     xk, xv = k[i].float().cpu().numpy(), v[i].float().cpu().numpy()
                 else:
                     xk, xv = kn[b].float().cpu().numpy(), vn[b].float().cpu().numpy()
-                sk = fp8_write_token(codes_k, sk, t, xk)
-                sv = fp8_write_token(codes_v, sv, t, xv)
+                sk = write_token(codes_k, sk, t, xk)
+                sv = write_token(codes_v, sv, t, xv)
             np.testing.assert_array_equal(layer.k_pool[blk].cpu().numpy(), codes_k)
             np.testing.assert_array_equal(layer.v_pool[blk].cpu().numpy(), codes_v)
             assert layer.k_scale[blk].item() == sk and layer.v_scale[blk].item() == sv
@@ -227,10 +232,10 @@ def test_fp8_long_context_full_layer():
         ids = tables[b][:nblk]
         Kc = layer.k_pool[torch.from_numpy(ids.astype(np.int64)).to(d), h].cpu().numpy()  # [nblk,16,D]
         Vc = layer.v_pool[torch.from_numpy(ids.astype(np.int64)).to(d), h].cpu().numpy()
-        Kq = (e4m3_decode(Kc) * ks[ids][:, None, None].astype(np.float64)).reshape(T, D)
-        Vq = (e4m3_decode(Vc) * vs[ids][:, None, None].astype(np.float64)).reshape(T, D)
+        Kq = (decode(Kc) * ks[ids][:, None, None].astype(np.float64)).reshape(T, D)
+        Vq = (decode(Vc) * vs[ids][:, None, None].astype(np.float64)).reshape(T, D)
         check(got[b, h], decode_row(qh[b, h], Kq, Vq, w.scale), TOL["f16"], f"codes b={b} h={h}")
         rows = slice(int(b) * (T - 1), int(b) * (T - 1) + T - 1)
         Kr = np.concatenate([k[rows, h].float().cpu().numpy(), kn[b:b + 1, h].float().cpu().numpy()])
         Vr = np.concatenate([v[rows, h].float().cpu().numpy(), vn[b:b + 1, h].float().cpu().numpy()])
-        check(got[b, h], decode_row(qh[b, h], Kr, Vr, w.scale), TOL["e4m3"], f"raw b={b} h={h}")
+        check(got[b, h], decode_row(qh[b, h], Kr, Vr, w.scale), TOL[fmt], f"raw b={b} h={h}")

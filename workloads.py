@@ -113,6 +113,12 @@ LONGCTX_FP8 = Workload(
 
 ALL = [TINY_GPT, LLAMA7B_CONTIG, LLAMA13B_PAGED, PARALLEL_SAMPLING, LONGCTX_FP8]
 
+# The int8 cache (KV Cache Mechanism Explained, section 8, item 3 names FP8/INT8 for the cached
+# history): the fp8 long-context shapes with int8 codes and per-block scales.
+LONGCTX_I8 = Workload(
+    name="llama7b-32x32x128-i8-paged16-b64-ctx4096", kind="paged", layers=32, batch=64,
+    heads=32, head_dim=128, kv_dtype="i8", q_dtype="f16", seed=9, ctx=4096)
+
 # Shared K/V heads (grouped-query attention): 64 query heads over 8 K/V heads (G = 8), the
 # attention shape of a LLaMA-2-70B-class model, with the LLaMA-13B batch's length mix.
 # `heads` counts the K/V heads; the query heads are heads * extra["group"].
