@@ -1,7 +1,9 @@
 // Randomised operation sequences against the host block pool's C ABI, for sanitizer builds.
 // After every call the pool's invariants must hold (kvc_check), statistics must be consistent,
-// and a call that fails must leave every live sequence's table and length unchanged.
+// a call that fails must leave every live sequence's table and length unchanged, and a rolling-
+// window slide may only drop blocks that lie wholly before the window.
 // Usage: pool_fuzz <seeds> <ops-per-seed>; exit status 0 on success.
+#include <algorithm>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -54,7 +56,7 @@ bool run(uint64_t seed, int ops) {
   std::vector<int32_t> src, dst, t0, l0, t1, l1;
   for (int op = 0; op < ops; ++op) {
     if (!snapshot(p, live, mb, t0, l0)) FAIL("snapshot");
-    const int kind = live.empty() ? 0 : r.below(10);
+    const int kind = live.empty() ? 0 : r.below(11);
     kvc_status st = KVC_OK;
     if (kind < 2) {
       int32_t s = -1;
@@ -80,10 +82,28 @@ bool run(uint64_t seed, int ops) {
       int32_t c = -1;
       st = kvc_fork(p, live[r.below(static_cast<int>(live.size()))], &c);
       if (st == KVC_OK) live.push_back(c);
-    } else {
+    } else if (kind < 10) {
       const int idx = r.below(static_cast<int>(live.size()));
       st = kvc_free(p, live[idx]);
       if (st == KVC_OK) live.erase(live.begin() + idx);
+    } else {
+      // rolling window: a slide drops only leading blocks, never a position inside the window
+      const int32_t n = 1 + r.below(3);
+      std::vector<int32_t> seqs(n);
+      for (auto &s : seqs) s = live[r.below(static_cast<int>(live.size()))];
+      const int32_t window = r.below(60);
+      int32_t dropped = -1;
+      st = kvc_slide(p, seqs.data(), n, window, &dropped);
+      if (st != KVC_OK || dropped < 0) FAIL("seed %llu op %d: slide", (unsigned long long)seed, op);
+      if (!snapshot(p, live, mb, t1, l1)) FAIL("snapshot");
+      for (size_t i = 0; i < live.size(); ++i)
+        for (int32_t j = 0; j < mb; ++j) {
+          const int32_t before = t0[i * mb + j], after = t1[i * mb + j];
+          const int32_t start = window ? std::max(0, l1[i] - window) : 0;
+          if (after != before && (after != -1 || (j + 1) * KVC_BLOCK_SIZE > start))
+            FAIL("seed %llu op %d: slide changed a block inside the window",
+                 (unsigned long long)seed, op);
+        }
     }
     if (kvc_check(p) != KVC_OK) FAIL("seed %llu op %d: invariants broken", (unsigned long long)seed, op);
     kvc_pool_stats stt{};
