@@ -24,6 +24,8 @@
 // LDS layouts: K rows keep their 16-byte columns XOR-swizzled by the row index (the 16 rows a
 // read instruction takes land on distinct banks); V rows are swizzled by row group as in decode.
 #include <algorithm>
+#include <cmath>
+#include <type_traits>
 
 #include "kvc_internal.h"
 #include "kvc_wave.h"
@@ -32,11 +34,16 @@ namespace kvc {
 
 constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
-constexpr int kPfRows = 16 * kPfWaves;  // query rows per workgroup
+constexpr int kWaveRows = 32;                   // query rows per wavefront
+constexpr int kPfRows = kWaveRows * kPfWaves;  // query rows per workgroup
+constexpr int kStep = 2 * kBlock;               // keys per step (two cache blocks)
 constexpr int kMaxSeqs = 4096;
 // weight headroom (log2 units): weights stay below 2^kHi, so both fp16 terms stay finite
 constexpr float kHead = 7.f;
 constexpr float kHi = 15.f;
+
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 struct PrefillArgs {
   const char *q;  // fp16 [total][Hq][D]
@@ -48,9 +55,11 @@ struct PrefillArgs {
   void *out;               // [total][Hq][D]
   int64_t seq_stride;      // contiguous: S_max
   int32_t B, H, G, Hq, cap, mbps, num_blocks, total;
-  int32_t gh;  // query heads per workgroup (1, 2 or 4); positions per workgroup = 64 / gh
+  int32_t gh;  // query heads per workgroup (1, 2 or 4); positions per workgroup = 128 / gh
+  int32_t gx, gy;  // workgroups per head group (an upper bound) and head groups
   int32_t out_f16;
-  float cl2;   // scale * log2(e)
+  int32_t neg_q;  // the scale is negative: scores are taken with -q and |scale|
+  float cl2;      // |scale| * log2(e) (> 0)
 };
 
 // Row range [r0, r0 + n) of sequence b's chunk, clamped so that it lies inside [0, total) and
@@ -97,22 +106,58 @@ static __device__ void tile_prefix(const PrefillArgs &a, int32_t pt, int32_t *pr
   __syncthreads();
 }
 
+// gfx950 transposing LDS read: in each group of 16 lanes, lane 4i + e receives element e of the
+// 4 fp16 that lanes i, i + 4, i + 8 and i + 12 address.
+static __device__ __forceinline__ f16x4 lds_read_tr(const char *p) {
+  return __builtin_bit_cast(
+      f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                 (__attribute__((address_space(3))) i16x4 *)(p)));
+}
+
+// The weights p0, p1 as fp16 pairs: hi = (p0, p1) rounded to nearest, lo = the rounding errors
+// p - hi rounded to nearest. v_fma_mix takes hi's half as fp16 and computes fma(hi, -1, p) in
+// fp32, which is p - hi exactly, then rounds once to fp16 into the low or the high half.
+static __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi,
+                                                  uint32_t &lo) {
+  const f16x2 h = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
+  hi = __builtin_bit_cast(uint32_t, h);
+  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(p0));
+  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
+      : "+v"(lo)
+      : "v"(hi), "v"(p1));
+}
+
 template <bool PAGED, int D>
 __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a) {
-  constexpr int ROW = D * 2;         // bytes of one fp16 row
-  constexpr int NCH = D / 8;         // 16-byte columns per row
-  constexpr int BLK = kBlock * ROW;  // bytes of one block of K (or V)
-  constexpr int NQK = D / 32;        // score MFMAs per block
-  constexpr int NDC = D / 16;        // 16-dim output blocks
+  constexpr int ROW = D * 2;            // bytes of one fp16 row
+  constexpr int NCH = D / 8;            // 16-byte columns per row
+  constexpr int BLK = kBlock * ROW;     // bytes of one cache block of one head
+  // LDS rows are padded so that the rows one read instruction takes fall on distinct banks:
+  // K reads take 16 rows of 16 bytes, the V transposing reads 4 rows of 64 bytes.
+  constexpr int KROW = ROW + 16;
+  constexpr int VROW = ROW + 64;
+  constexpr int VOFF = kStep * KROW;
+  constexpr int BUF = kStep * (KROW + VROW);  // one step's K and V
+  constexpr int NQK = D / 16;           // score MFMAs per step (16 dims each)
+  constexpr int NDQ = D / 32;           // 32-dim output blocks
+  constexpr int LPT = kStep * NCH / kPfThreads;  // 16-byte pieces of K (and of V) per thread
+  static_assert(LPT >= 1 && kStep * NCH % kPfThreads == 0, "head dim");
   extern __shared__ int32_t smem[];
   int32_t *pre = smem;
   int32_t *wsum = smem + a.B + 1;
   char *kv_lds = reinterpret_cast<char *>(smem) + ((a.B + 1 + kPfWaves + 3) / 4) * 16;
-  // kv_lds: [2 buffers][K block | V block]
+  // kv_lds: [2 buffers][K rows (KROW bytes) | V rows (VROW bytes)], kStep rows each
 
+  // Workgroup L runs on XCD L % 8 (round-robin dispatch). Each XCD takes a contiguous range of
+  // (head group, tile) pairs, tiles fastest, so the workgroups that read one K/V head share that
+  // XCD's L2.
+  const uint32_t per = gridDim.x / 8;
+  const uint32_t lin = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (lin >= static_cast<uint32_t>(a.gx) * static_cast<uint32_t>(a.gy)) return;
+  const int32_t x = static_cast<int32_t>(lin % a.gx);
+  const int32_t hgroup = static_cast<int32_t>(lin / a.gx);
   const int32_t pt = kPfRows / a.gh;
   tile_prefix(a, pt, pre, wsum);
-  const int32_t x = blockIdx.x;
   if (x >= pre[a.B]) return;
   // the sequence of workgroup x: the largest b with pre[b] <= x
   int32_t lo = 0, hi = a.B - 1;
@@ -129,147 +174,232 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
   const int32_t base_pos = ch.L - ch.n;           // position of chunk row 0
 
   const int32_t nsub = a.G / a.gh;
-  const int32_t hk = blockIdx.y / nsub;
-  const int32_t hq0 = hk * a.G + (blockIdx.y % nsub) * a.gh;
+  const int32_t hk = hgroup / nsub;
+  const int32_t hq0 = hk * a.G + (hgroup % nsub) * a.gh;
 
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int w = tid >> 6;
-  const int g = lane >> 4;
-  const int j = lane & 15;
+  const int h = lane >> 5;   // half of the wavefront
+  const int j = lane & 31;   // query row of the wavefront (and K row / output dim in the MFMAs)
   const int32_t hq = hq0 + w % a.gh;
-  const int32_t rw0 = rt0 + 16 * (w / a.gh);      // the wavefront's first row
-  const int32_t nrow = max(0, min(16, rt1 - rw0));
-  const int32_t wave_last = base_pos + rw0 + nrow - 1;  // its last row's position
-  const int32_t last_pos = base_pos + rt1 - 1;          // the workgroup's
-  const int32_t nkb = last_pos / kBlock + 1;
+  const int32_t rw0 = rt0 + kWaveRows * (w / a.gh);  // the wavefront's first row
+  const int32_t nrow = max(0, min(kWaveRows, rt1 - rw0));
+  const int32_t wave_first = base_pos + rw0;         // its first and last rows' positions
+  const int32_t wave_last = wave_first + nrow - 1;
+  const int32_t last_pos = base_pos + rt1 - 1;       // the workgroup's last position
+  const int32_t nstep = last_pos / kStep + 1;
 
-  // q operand: row j of the wavefront (rows past its end repeat its last row; a wavefront with
-  // no rows reads the workgroup's first row and stores nothing), 8 dims per MFMA
+  // q operand of the score MFMAs: row j of the wavefront (rows past its end repeat its last row;
+  // a wavefront with no rows reads the workgroup's first row and stores nothing), dims
+  // 16c + 8h .. 16c + 8h + 7 for MFMA c; sign flipped for a negative scale
   const int32_t my_rel = nrow > 0 ? rw0 + min(j, nrow - 1) : rt0;
   uint4 qv[NQK];
   {
     const char *qr = a.q + (static_cast<int64_t>(ch.r0 + my_rel) * a.Hq + hq) * ROW;
+    const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) qv[c] = *reinterpret_cast<const uint4 *>(qr + (g + 4 * c) * 16);
+    for (int c = 0; c < NQK; ++c) {
+      uint4 t = *reinterpret_cast<const uint4 *>(qr + (2 * c + h) * 16);
+      t.x ^= flip;
+      t.y ^= flip;
+      t.z ^= flip;
+      t.w ^= flip;
+      qv[c] = t;
+    }
   }
   const int32_t my_pos = base_pos + my_rel;
 
-  // block loads: thread t < 16*NCH takes 16-byte column t % NCH of key row t / NCH
-  const bool loader = tid < kBlock * NCH;
-  const int kr = tid / NCH;
-  const int kc = tid % NCH;
+  // Step loads: piece i of thread t is 16-byte column (t + i * threads) % NCH of step row
+  // (t + i * threads) / NCH, of K and of V. Rows past the sequence's end read its last row, and a
+  // second block past the end reads the first block's rows (finite; those keys are masked). A
+  // block whose table entry lies outside the pool is stored as zeros and its keys are masked.
+  const int32_t L = ch.L;
   const int64_t kv_head_off = PAGED ? static_cast<int64_t>(hk) * BLK
                                     : (static_cast<int64_t>(b) * a.H + hk) * a.seq_stride * ROW;
-  auto load_block = [&](int32_t kb, uint4 &kreg, uint4 &vreg) -> bool {
-    // rows past the sequence's end read its last row (finite; those keys are masked)
-    const int32_t row = min(kb * kBlock + kr, ch.L - 1);
-    int64_t off;
-    bool ok = true;
+  const int32_t *trow = PAGED ? a.tables + static_cast<int64_t>(b) * a.mbps : nullptr;
+  uint4 kr[LPT], vr[LPT];
+  // loads step s (32 s <= L - 1, so its first block holds positions); returns bit i set when
+  // block i holds positions but is not in the pool
+  auto load_step = [&](int32_t s) -> int {
+    const int32_t nv0 = min(kBlock, L - s * kStep);
+    const int32_t nv1 = min(kBlock, L - s * kStep - kBlock);
+    int64_t base0, base1;
+    int bad = 0;
     if constexpr (PAGED) {
-      const int32_t phys = __builtin_amdgcn_readfirstlane(a.tables[static_cast<int64_t>(b) * a.mbps + kb]);
-      ok = static_cast<uint32_t>(phys) < static_cast<uint32_t>(a.num_blocks);
-      const int32_t sp = ok ? phys : 0;
-      off = static_cast<int64_t>(sp) * a.H * BLK + kv_head_off + (row - kb * kBlock) * ROW;
+      const int32_t p0 = trow[2 * s];
+      const int32_t p1 = nv1 > 0 ? trow[2 * s + 1] : p0;
+      const bool in0 = static_cast<uint32_t>(p0) < static_cast<uint32_t>(a.num_blocks);
+      const bool in1 = static_cast<uint32_t>(p1) < static_cast<uint32_t>(a.num_blocks);
+      bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
+      base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
+      base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
     } else {
-      off = kv_head_off + static_cast<int64_t>(row) * ROW;
+      base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
+      base1 = nv1 > 0 ? base0 + BLK : base0;
     }
-    if (loader) {
-      kreg = load_stream(a.k + off + kc * 16);
-      vreg = load_stream(a.v + off + kc * 16);
-    }
-    return ok;
-  };
-  auto store_block = [&](int buf, const uint4 &kreg, const uint4 &vreg) {
-    if (!loader) return;
-    char *kb_lds = kv_lds + buf * 2 * BLK;
-    char *vb_lds = kb_lds + BLK;
-    *reinterpret_cast<uint4 *>(kb_lds + kr * ROW + ((kc ^ (kr & (NCH - 1))) * 16)) = kreg;
-    *reinterpret_cast<uint4 *>(vb_lds + kr * ROW + ((kc ^ (2 * ((kr >> 2) & 3))) * 16)) = vreg;
-  };
-
-  f32x4 o[NDC];
+    const int32_t lim0 = nv0 - 1;
+    const int32_t lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) o[dc] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m = kFloor, l = 0.f;
+    for (int i = 0; i < LPT; ++i) {
+      const int p = tid + i * kPfThreads;
+      const int row = p / NCH;
+      const bool sb = (row >> 4) != 0;  // block of the step
+      const int32_t r = min(row & 15, sb ? lim1 : lim0);
+      const int64_t off = (sb ? base1 : base0) + r * ROW + (p % NCH) * 16;
+      kr[i] = *reinterpret_cast<const uint4 *>(a.k + off);
+      vr[i] = *reinterpret_cast<const uint4 *>(a.v + off);
+    }
+    return bad;
+  };
+  auto store_step = [&](char *buf, int bad) {
+    if (bad != 0) {
+#pragma unroll
+      for (int i = 0; i < LPT; ++i) {
+        const int sb = ((tid + i * kPfThreads) / NCH) >> 4;
+        if ((bad >> sb) & 1) kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int p = tid + i * kPfThreads;
+      const int row = p / NCH, col = p % NCH;
+      *reinterpret_cast<uint4 *>(buf + row * KROW + col * 16) = kr[i];
+      *reinterpret_cast<uint4 *>(buf + VOFF + row * VROW + col * 16) = vr[i];
+    }
+  };
 
-  uint4 kreg = make_uint4(0, 0, 0, 0), vreg = make_uint4(0, 0, 0, 0);
-  bool ok_cur = load_block(0, kreg, vreg);
-  for (int32_t kb = 0; kb < nkb; ++kb) {
-    store_block(kb & 1, kreg, vreg);
-    const bool ok = ok_cur;
-    if (kb + 1 < nkb) ok_cur = load_block(kb + 1, kreg, vreg);
-    __syncthreads();
-    // a wavefront whose rows all precede this block, or a block id outside the pool: skip
-    if (nrow == 0 || kb * kBlock > wave_last || !ok) continue;
-    const char *kb_lds = kv_lds + (kb & 1) * 2 * BLK;
-    const _Float16 *vb_lds = reinterpret_cast<const _Float16 *>(kb_lds + BLK);
-    f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
+  // Score MFMA: the A operand row j is key perm(j), perm swapping bits 2 and 3, so that lane
+  // (h, j)'s 16 scores (element v: A row 8(v/4) + 4h + v%4) are keys 16(v/8) + 8h + v%8 of query
+  // row j: two runs of 8 consecutive keys, one per cache block.
+  const int kperm = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+  const int k_lds = kperm * KROW + h * 16;
+  // V^T operand of the output MFMAs: lane (h, j) needs V[16a + 8h + t][32dq + j], t = 0..7,
+  // fetched as two transposing reads of 4 keys; lane s of its 16-lane group addresses key row
+  // 16a + 8h + 4r + s/4, dims 32dq + 16(j/16) + 4(s%4) .. + 3 for read r.
+  const int s16 = lane & 15;
+  const int v_lds = VOFF + (8 * h + (s16 >> 2)) * VROW + (16 * (j >> 4) + 4 * (s16 & 3)) * 2;
+
+  f32x16 o[NDQ];
+#pragma unroll
+  for (int dq = 0; dq < NDQ; ++dq)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dq][e] = 0.f;
+  float m = kFloor, l = 0.f;
+  float mt = kFloor + kHi;  // m + kHi
+  const float cl2 = a.cl2;
+
+  // The wavefront's share of one step (keys kStep * s ..), its K and V in LDS at `buf`. MASK:
+  // the step holds keys past some row's position or blocks outside the pool (bits of `bad`).
+  auto compute = [&](const char *buf, int32_t s, auto mask_tag, int bad) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    f32x16 sc;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
 #pragma unroll
     for (int c = 0; c < NQK; ++c) {
-      const uint4 kv = *reinterpret_cast<const uint4 *>(kb_lds + j * ROW +
-                                                        (((g + 4 * c) ^ (j & (NCH - 1))) * 16));
-      sacc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_f16x8(kv), as_f16x8(qv[c]), sacc, 0, 0, 0);
+      const uint4 kv = *reinterpret_cast<const uint4 *>(buf + k_lds + c * 32);
+      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kv), as_f16x8(qv[c]), sc, 0, 0, 0);
     }
-    float xs[4];
+    if constexpr (MASK) {
+      // key 16(v/8) + 8h + v%8 of the step is kept when at or before the row's position
+      const int32_t lim = my_pos - s * kStep - 8 * h;
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      xs[e] = kb * kBlock + 4 * g + e <= my_pos ? sacc[e] * a.cl2 : -__builtin_inff();
-    float mx = fmaxf(fmaxf(xs[0], xs[1]), fmaxf(xs[2], xs[3]));
-    {
-      float u, v;
-      lane_pair<16>(mx, u, v);
-      mx = fmaxf(u, v);
-      lane_pair<32>(mx, u, v);
-      mx = fmaxf(u, v);
+      for (int v = 0; v < 16; ++v) {
+        const bool keep = 16 * (v >> 3) + (v & 7) <= lim && !((bad >> (v >> 3)) & 1);
+        sc[v] = keep ? sc[v] : -__builtin_inff();
+      }
     }
-    const bool up = mx > m + kHi;
-    if (__ballot(up) != 0) {
-      const float mnew = up ? mx - kHead : m;
+    float mx = sc[0];
+#pragma unroll
+    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+    // a score that would put a weight above 2^kHi moves the row's reference (rare)
+    if (__ballot(mx * cl2 > mt) != 0) {
+      float u, t;
+      lane_pair<32>(mx * cl2, u, t);
+      const float rmax = fmaxf(u, t);
+      const float mnew = rmax > mt ? rmax - kHead : m;
       const float f = __builtin_amdgcn_exp2f(m - mnew);
       l *= f;
 #pragma unroll
-      for (int dc = 0; dc < NDC; ++dc) o[dc] *= f;
+      for (int dq = 0; dq < NDQ; ++dq) o[dq] *= f;
       m = mnew;
+      mt = m + kHi;
     }
-    f16x4 ph, pl;
+    const float nm = -m;
+    uint32_t ph[2][4], pl[2][4];  // keys 16 a16 + 8h + 2i, + 1 as fp16 pairs, hi and lo terms
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float p = __builtin_amdgcn_exp2f(xs[e] - m);
-      l += p;
-      ph[e] = static_cast<_Float16>(p);
-      pl[e] = static_cast<_Float16>(p - static_cast<float>(ph[e]));
+    for (int v = 0; v < 16; v += 2) {
+      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], cl2, nm));
+      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], cl2, nm));
+      l += p0;
+      l += p1;
+      split_pair(p0, p1, ph[v >> 3][(v & 7) >> 1], pl[v >> 3][(v & 7) >> 1]);
     }
-    const _Float16 *vr = vb_lds + (4 * g) * D + (j & 7);
+    // O^T += V^T P^T: per 32 dims and 16 keys, the hi and the lo weights share one V^T operand
 #pragma unroll
-    for (int dc = 0; dc < NDC; ++dc) {
-      const int col = (2 * dc + (j >> 3)) ^ (2 * g);
-      f16x4 va;
+    for (int a16 = 0; a16 < 2; ++a16) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) va[e] = vr[e * D + col * 8];
-      o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, o[dc], 0, 0, 0);
-      o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, o[dc], 0, 0, 0);
+      for (int dq = 0; dq < NDQ; ++dq) {
+        const char *vp = buf + v_lds + a16 * 16 * VROW + dq * 64;
+        const f16x4 v0 = lds_read_tr(vp);
+        const f16x4 v1 = lds_read_tr(vp + 4 * VROW);
+        const f16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const f16x8 bh = __builtin_bit_cast(
+            f16x8, make_uint4(ph[a16][0], ph[a16][1], ph[a16][2], ph[a16][3]));
+        const f16x8 bl = __builtin_bit_cast(
+            f16x8, make_uint4(pl[a16][0], pl[a16][1], pl[a16][2], pl[a16][3]));
+        o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bh, o[dq], 0, 0, 0);
+        o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bl, o[dq], 0, 0, 0);
+      }
     }
+  };
+
+  // One step s with its K/V in LDS buffer s & 1: store the registers loaded for it, start the
+  // next step's loads, one barrier, compute. The buffer written here was last read two steps
+  // ago, before every wavefront passed the previous barrier.
+  int bad_next = load_step(0);
+  auto step = [&](auto buf_tag, int32_t s) {
+    char *buf = kv_lds + decltype(buf_tag)::value * BUF;
+    const int bad = bad_next;
+    store_step(buf, bad);
+    if (s + 1 < nstep) bad_next = load_step(s + 1);
+    __syncthreads();
+    if (nrow > 0 && s * kStep <= wave_last) {
+      if (bad != 0 || s * kStep + kStep - 1 > wave_first)
+        compute(buf, s, std::true_type{}, bad);
+      else
+        compute(buf, s, std::false_type{}, 0);
+    }
+  };
+  for (int32_t s = 0; s < nstep; s += 2) {
+    step(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nstep) step(std::integral_constant<int, 1>{}, s + 1);
   }
   if (nrow == 0) return;
-  float u, v;
-  lane_pair<16>(l, u, v);
-  l = u + v;
-  lane_pair<32>(l, u, v);
-  l = u + v;
+  {
+    float u, t;
+    lane_pair<32>(l, u, t);
+    l = u + t;
+  }
   if (j >= nrow) return;
   const float inv = l > 0.f ? 1.0f / l : 0.f;
+  // lane (h, j) holds dims 32dq + 8(v/4) + 4h + v%4 of row j
   const int64_t orow = (static_cast<int64_t>(ch.r0 + rw0 + j) * a.Hq + hq) * D;
 #pragma unroll
-  for (int dc = 0; dc < NDC; ++dc) {
-    const int64_t i = orow + 16 * dc + 4 * g;
-    const f32x4 r = o[dc] * inv;
-    if (a.out_f16) {
-      const f16x4 h = {static_cast<_Float16>(r[0]), static_cast<_Float16>(r[1]),
-                       static_cast<_Float16>(r[2]), static_cast<_Float16>(r[3])};
-      *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(a.out) + i) = h;
-    } else {
-      *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + i) = r;
+  for (int dq = 0; dq < NDQ; ++dq) {
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int64_t i = orow + 32 * dq + 8 * q4 + 4 * h;
+      const f32x4 r = {o[dq][4 * q4] * inv, o[dq][4 * q4 + 1] * inv, o[dq][4 * q4 + 2] * inv,
+                       o[dq][4 * q4 + 3] * inv};
+      if (a.out_f16) {
+        const f16x4 hv = {static_cast<_Float16>(r[0]), static_cast<_Float16>(r[1]),
+                          static_cast<_Float16>(r[2]), static_cast<_Float16>(r[3])};
+        *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(a.out) + i) = hv;
+      } else {
+        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + i) = r;
+      }
     }
   }
 }
@@ -301,18 +431,24 @@ static kvc_status launch_prefill(bool paged, PrefillArgs &a, int32_t D, kvc_dtyp
   a.Hq = a.H * a.G;
   a.gh = a.G % 4 == 0 ? 4 : (a.G % 2 == 0 ? 2 : 1);
   a.out_f16 = out_dtype == KVC_F16;
-  a.cl2 = scale * kLog2e;
+  // scores are taken as (sign(scale) q) . k times |scale| log2(e); a zero scale takes the
+  // smallest normal float, which leaves every weight of a row equal, as a zero scale does
+  a.neg_q = scale < 0.f;
+  a.cl2 = scale == 0.f ? 1.17549435e-38f : fabsf(scale) * kLog2e;
   const int32_t pt = kPfRows / a.gh;
   // an upper bound on the workgroups along x: sum_b ceil(n_b / pt) <= total / pt + B
   const int64_t gx = (static_cast<int64_t>(a.total) + pt - 1) / pt + a.B;
   const int64_t gy = static_cast<int64_t>(a.H) * (a.G / a.gh);
-  if (gx > INT32_MAX || gy > 65535) return KVC_E_INVALID;
+  const int64_t n8 = (gx * gy + 7) / 8 * 8;  // a multiple of the 8 XCDs
+  if (n8 > INT32_MAX) return KVC_E_INVALID;
+  a.gx = static_cast<int32_t>(gx);
+  a.gy = static_cast<int32_t>(gy);
   const size_t shmem = static_cast<size_t>((a.B + 1 + kPfWaves + 3) / 4) * 16 +
-                       static_cast<size_t>(2) * 2 * kBlock * D * 2;
+                       static_cast<size_t>(2) * kStep * (2 * (2 * D) + 16 + 64);
   PrefillKernel kern = paged ? pick_prefill<true>(D) : pick_prefill<false>(D);
   if (!kern) return KVC_E_UNSUPPORTED;
-  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(gx), static_cast<uint32_t>(gy)),
-                     dim3(kPfThreads), shmem, static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(n8)), dim3(kPfThreads), shmem,
+                     static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
