@@ -38,6 +38,14 @@ constexpr int kWaveRows = 32;                   // query rows per wavefront
 constexpr int kPfRows = kWaveRows * kPfWaves;  // query rows per workgroup
 constexpr int kStep = 2 * kBlock;               // keys per step (two cache blocks)
 constexpr int kMaxSeqs = 4096;
+// steps whose K/V loads are in flight in registers, and the loop unroll that keeps both the LDS
+// buffer (2) and the register set (kAhead) of every step a compile-time choice
+#ifndef KVC_PF_AHEAD
+#define KVC_PF_AHEAD 2
+#endif
+constexpr int kAhead = KVC_PF_AHEAD;
+constexpr int kUnroll = kAhead == 3 ? 6 : 2;
+static_assert(kAhead >= 1 && kAhead <= 3, "prefetch depth");
 // weight headroom (log2 units): weights stay below 2^kHi, so both fp16 terms stay finite
 constexpr float kHead = 7.f;
 constexpr float kHi = 15.f;
@@ -78,7 +86,8 @@ static __device__ __forceinline__ Chunk chunk_of(const PrefillArgs &a, int32_t b
   return c;
 }
 
-// pre[b] = workgroups before sequence b along x (ceil(n_b / pt) each), pre[B] = total, in LDS.
+// pre[b] = workgroups before sequence b along x, pre[B] = total, in LDS. Sequence b has
+// ceil(n_b / pt) tiles of pt rows and takes one workgroup per pair of them.
 static __device__ void tile_prefix(const PrefillArgs &a, int32_t pt, int32_t *pre, int32_t *wsum) {
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
@@ -87,7 +96,7 @@ static __device__ void tile_prefix(const PrefillArgs &a, int32_t pt, int32_t *pr
   const int lo = min(a.B, tid * per);
   const int hi = min(a.B, lo + per);
   int32_t sum = 0;
-  for (int i = lo; i < hi; ++i) sum += (chunk_of(a, i).n + pt - 1) / pt;
+  for (int i = lo; i < hi; ++i) sum += ((chunk_of(a, i).n + pt - 1) / pt + 1) / 2;
   int32_t inc = sum;
 #pragma unroll
   for (int off = 1; off < kWave; off <<= 1) {
@@ -100,7 +109,7 @@ static __device__ void tile_prefix(const PrefillArgs &a, int32_t pt, int32_t *pr
   int32_t run = inc - sum;
   for (int i = lo; i < hi; ++i) {
     pre[i] = run;
-    run += (chunk_of(a, i).n + pt - 1) / pt;
+    run += ((chunk_of(a, i).n + pt - 1) / pt + 1) / 2;
   }
   if (tid == kPfThreads - 1) pre[a.B] = inc;
   __syncthreads();
@@ -168,239 +177,262 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
   const int32_t b = lo;
   const Chunk ch = chunk_of(a, b);
   const int32_t ntile = (ch.n + pt - 1) / pt;
-  const int32_t tile = ntile - 1 - (x - pre[b]);  // the longest tiles of a sequence start first
-  const int32_t rt0 = tile * pt;                  // chunk-relative rows of the workgroup
-  const int32_t rt1 = min(rt0 + pt, ch.n);
-  const int32_t base_pos = ch.L - ch.n;           // position of chunk row 0
+  // Under the causal mask tile t (rows t pt ..) takes about t + 1 units of work: the workgroup
+  // runs tile ntile - 1 - p and then tile p, so that every pair of a sequence costs about the
+  // same and no long tile starts last.
+  const int32_t pair = x - pre[b];
+  auto run_tile = [&](const int32_t tile) {
+    const int32_t rt0 = tile * pt;                  // chunk-relative rows of the workgroup
+    const int32_t rt1 = min(rt0 + pt, ch.n);
+    const int32_t base_pos = ch.L - ch.n;           // position of chunk row 0
 
-  const int32_t nsub = a.G / a.gh;
-  const int32_t hk = hgroup / nsub;
-  const int32_t hq0 = hk * a.G + (hgroup % nsub) * a.gh;
+    const int32_t nsub = a.G / a.gh;
+    const int32_t hk = hgroup / nsub;
+    const int32_t hq0 = hk * a.G + (hgroup % nsub) * a.gh;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & (kWave - 1);
-  const int w = tid >> 6;
-  const int h = lane >> 5;   // half of the wavefront
-  const int j = lane & 31;   // query row of the wavefront (and K row / output dim in the MFMAs)
-  const int32_t hq = hq0 + w % a.gh;
-  const int32_t rw0 = rt0 + kWaveRows * (w / a.gh);  // the wavefront's first row
-  const int32_t nrow = max(0, min(kWaveRows, rt1 - rw0));
-  const int32_t wave_first = base_pos + rw0;         // its first and last rows' positions
-  const int32_t wave_last = wave_first + nrow - 1;
-  const int32_t last_pos = base_pos + rt1 - 1;       // the workgroup's last position
-  const int32_t nstep = last_pos / kStep + 1;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid >> 6;
+    const int h = lane >> 5;   // half of the wavefront
+    const int j = lane & 31;   // query row of the wavefront (and K row / output dim in the MFMAs)
+    const int32_t hq = hq0 + w % a.gh;
+    const int32_t rw0 = rt0 + kWaveRows * (w / a.gh);  // the wavefront's first row
+    const int32_t nrow = max(0, min(kWaveRows, rt1 - rw0));
+    const int32_t wave_first = base_pos + rw0;         // its first and last rows' positions
+    const int32_t wave_last = wave_first + nrow - 1;
+    const int32_t last_pos = base_pos + rt1 - 1;       // the workgroup's last position
+    const int32_t nstep = last_pos / kStep + 1;
 
-  // q operand of the score MFMAs: row j of the wavefront (rows past its end repeat its last row;
-  // a wavefront with no rows reads the workgroup's first row and stores nothing), dims
-  // 16c + 8h .. 16c + 8h + 7 for MFMA c; sign flipped for a negative scale
-  const int32_t my_rel = nrow > 0 ? rw0 + min(j, nrow - 1) : rt0;
-  uint4 qv[NQK];
-  {
-    const char *qr = a.q + (static_cast<int64_t>(ch.r0 + my_rel) * a.Hq + hq) * ROW;
-    const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
+    // q operand of the score MFMAs: row j of the wavefront (rows past its end repeat its last row;
+    // a wavefront with no rows reads the workgroup's first row and stores nothing), dims
+    // 16c + 8h .. 16c + 8h + 7 for MFMA c; sign flipped for a negative scale
+    const int32_t my_rel = nrow > 0 ? rw0 + min(j, nrow - 1) : rt0;
+    uint4 qv[NQK];
+    {
+      const char *qr = a.q + (static_cast<int64_t>(ch.r0 + my_rel) * a.Hq + hq) * ROW;
+      const uint32_t flip = a.neg_q ? 0x80008000u : 0u;
 #pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      uint4 t = *reinterpret_cast<const uint4 *>(qr + (2 * c + h) * 16);
-      t.x ^= flip;
-      t.y ^= flip;
-      t.z ^= flip;
-      t.w ^= flip;
-      qv[c] = t;
+      for (int c = 0; c < NQK; ++c) {
+        uint4 t = *reinterpret_cast<const uint4 *>(qr + (2 * c + h) * 16);
+        t.x ^= flip;
+        t.y ^= flip;
+        t.z ^= flip;
+        t.w ^= flip;
+        qv[c] = t;
+      }
     }
-  }
-  const int32_t my_pos = base_pos + my_rel;
+    const int32_t my_pos = base_pos + my_rel;
 
-  // Step loads: piece i of thread t is 16-byte column (t + i * threads) % NCH of step row
-  // (t + i * threads) / NCH, of K and of V. Rows past the sequence's end read its last row, and a
-  // second block past the end reads the first block's rows (finite; those keys are masked). A
-  // block whose table entry lies outside the pool is stored as zeros and its keys are masked.
-  const int32_t L = ch.L;
-  const int64_t kv_head_off = PAGED ? static_cast<int64_t>(hk) * BLK
-                                    : (static_cast<int64_t>(b) * a.H + hk) * a.seq_stride * ROW;
-  const int32_t *trow = PAGED ? a.tables + static_cast<int64_t>(b) * a.mbps : nullptr;
-  uint4 kr[LPT], vr[LPT];
-  // loads step s (32 s <= L - 1, so its first block holds positions); returns bit i set when
-  // block i holds positions but is not in the pool
-  auto load_step = [&](int32_t s) -> int {
-    const int32_t nv0 = min(kBlock, L - s * kStep);
-    const int32_t nv1 = min(kBlock, L - s * kStep - kBlock);
-    int64_t base0, base1;
-    int bad = 0;
-    if constexpr (PAGED) {
-      const int32_t p0 = trow[2 * s];
-      const int32_t p1 = nv1 > 0 ? trow[2 * s + 1] : p0;
-      const bool in0 = static_cast<uint32_t>(p0) < static_cast<uint32_t>(a.num_blocks);
-      const bool in1 = static_cast<uint32_t>(p1) < static_cast<uint32_t>(a.num_blocks);
-      bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
-      base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
-      base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
-    } else {
-      base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
-      base1 = nv1 > 0 ? base0 + BLK : base0;
-    }
-    const int32_t lim0 = nv0 - 1;
-    const int32_t lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
-#pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int p = tid + i * kPfThreads;
-      const int row = p / NCH;
-      const bool sb = (row >> 4) != 0;  // block of the step
-      const int32_t r = min(row & 15, sb ? lim1 : lim0);
-      const int64_t off = (sb ? base1 : base0) + r * ROW + (p % NCH) * 16;
-      kr[i] = *reinterpret_cast<const uint4 *>(a.k + off);
-      vr[i] = *reinterpret_cast<const uint4 *>(a.v + off);
-    }
-    return bad;
-  };
-  auto store_step = [&](char *buf, int bad) {
-    if (bad != 0) {
+    // Step loads: piece i of thread t is 16-byte column (t + i * threads) % NCH of step row
+    // (t + i * threads) / NCH, of K and of V. Rows past the sequence's end read its last row, and a
+    // second block past the end reads the first block's rows (finite; those keys are masked). A
+    // block whose table entry lies outside the pool is stored as zeros and its keys are masked.
+    const int32_t L = ch.L;
+    const int64_t kv_head_off = PAGED ? static_cast<int64_t>(hk) * BLK
+                                      : (static_cast<int64_t>(b) * a.H + hk) * a.seq_stride * ROW;
+    const int32_t *trow = PAGED ? a.tables + static_cast<int64_t>(b) * a.mbps : nullptr;
+    // kAhead steps are in flight in registers while one is computed from LDS
+    uint4 kr[kAhead][LPT], vr[kAhead][LPT];
+    // loads step s (32 s <= L - 1, so its first block holds positions); returns bit i set when
+    // block i holds positions but is not in the pool
+    auto load_step = [&](int32_t s, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) -> int {
+      const int32_t nv0 = min(kBlock, L - s * kStep);
+      const int32_t nv1 = min(kBlock, L - s * kStep - kBlock);
+      int64_t base0, base1;
+      int bad = 0;
+      if constexpr (PAGED) {
+        const int32_t p0 = trow[2 * s];
+        const int32_t p1 = nv1 > 0 ? trow[2 * s + 1] : p0;
+        const bool in0 = static_cast<uint32_t>(p0) < static_cast<uint32_t>(a.num_blocks);
+        const bool in1 = static_cast<uint32_t>(p1) < static_cast<uint32_t>(a.num_blocks);
+        bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
+        base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
+        base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
+      } else {
+        base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
+        base1 = nv1 > 0 ? base0 + BLK : base0;
+      }
+      const int32_t lim0 = nv0 - 1;
+      const int32_t lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
-        const int sb = ((tid + i * kPfThreads) / NCH) >> 4;
-        if ((bad >> sb) & 1) kr[i] = vr[i] = make_uint4(0, 0, 0, 0);
+        const int p = tid + i * kPfThreads;
+        const int row = p / NCH;
+        const bool sb = (row >> 4) != 0;  // block of the step
+        const int32_t r = min(row & 15, sb ? lim1 : lim0);
+        const int64_t off = (sb ? base1 : base0) + r * ROW + (p % NCH) * 16;
+        kd[i] = *reinterpret_cast<const uint4 *>(a.k + off);
+        vd[i] = *reinterpret_cast<const uint4 *>(a.v + off);
       }
-    }
+      return bad;
+    };
+    auto store_step = [&](char *buf, int bad, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) {
+      if (bad != 0) {
 #pragma unroll
-    for (int i = 0; i < LPT; ++i) {
-      const int p = tid + i * kPfThreads;
-      const int row = p / NCH, col = p % NCH;
-      *reinterpret_cast<uint4 *>(buf + row * KROW + col * 16) = kr[i];
-      *reinterpret_cast<uint4 *>(buf + VOFF + row * VROW + col * 16) = vr[i];
-    }
-  };
-
-  // Score MFMA: the A operand row j is key perm(j), perm swapping bits 2 and 3, so that lane
-  // (h, j)'s 16 scores (element v: A row 8(v/4) + 4h + v%4) are keys 16(v/8) + 8h + v%8 of query
-  // row j: two runs of 8 consecutive keys, one per cache block.
-  const int kperm = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
-  const int k_lds = kperm * KROW + h * 16;
-  // V^T operand of the output MFMAs: lane (h, j) needs V[16a + 8h + t][32dq + j], t = 0..7,
-  // fetched as two transposing reads of 4 keys; lane s of its 16-lane group addresses key row
-  // 16a + 8h + 4r + s/4, dims 32dq + 16(j/16) + 4(s%4) .. + 3 for read r.
-  const int s16 = lane & 15;
-  const int v_lds = VOFF + (8 * h + (s16 >> 2)) * VROW + (16 * (j >> 4) + 4 * (s16 & 3)) * 2;
-
-  f32x16 o[NDQ];
-#pragma unroll
-  for (int dq = 0; dq < NDQ; ++dq)
-#pragma unroll
-    for (int e = 0; e < 16; ++e) o[dq][e] = 0.f;
-  float m = kFloor, l = 0.f;
-  float mt = kFloor + kHi;  // m + kHi
-  const float cl2 = a.cl2;
-
-  // The wavefront's share of one step (keys kStep * s ..), its K and V in LDS at `buf`. MASK:
-  // the step holds keys past some row's position or blocks outside the pool (bits of `bad`).
-  auto compute = [&](const char *buf, int32_t s, auto mask_tag, int bad) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    f32x16 sc;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
-#pragma unroll
-    for (int c = 0; c < NQK; ++c) {
-      const uint4 kv = *reinterpret_cast<const uint4 *>(buf + k_lds + c * 32);
-      sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kv), as_f16x8(qv[c]), sc, 0, 0, 0);
-    }
-    if constexpr (MASK) {
-      // key 16(v/8) + 8h + v%8 of the step is kept when at or before the row's position
-      const int32_t lim = my_pos - s * kStep - 8 * h;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const bool keep = 16 * (v >> 3) + (v & 7) <= lim && !((bad >> (v >> 3)) & 1);
-        sc[v] = keep ? sc[v] : -__builtin_inff();
+        for (int i = 0; i < LPT; ++i) {
+          const int sb = ((tid + i * kPfThreads) / NCH) >> 4;
+          if ((bad >> sb) & 1) kd[i] = vd[i] = make_uint4(0, 0, 0, 0);
+        }
       }
-    }
-    float mx = sc[0];
 #pragma unroll
-    for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-    // a score that would put a weight above 2^kHi moves the row's reference (rare)
-    if (__ballot(mx * cl2 > mt) != 0) {
-      float u, t;
-      lane_pair<32>(mx * cl2, u, t);
-      const float rmax = fmaxf(u, t);
-      const float mnew = rmax > mt ? rmax - kHead : m;
-      const float f = __builtin_amdgcn_exp2f(m - mnew);
-      l *= f;
-#pragma unroll
-      for (int dq = 0; dq < NDQ; ++dq) o[dq] *= f;
-      m = mnew;
-      mt = m + kHi;
-    }
-    const float nm = -m;
-    uint32_t ph[2][4], pl[2][4];  // keys 16 a16 + 8h + 2i, + 1 as fp16 pairs, hi and lo terms
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) {
-      const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], cl2, nm));
-      const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], cl2, nm));
-      l += p0;
-      l += p1;
-      split_pair(p0, p1, ph[v >> 3][(v & 7) >> 1], pl[v >> 3][(v & 7) >> 1]);
-    }
-    // O^T += V^T P^T: per 32 dims and 16 keys, the hi and the lo weights share one V^T operand
-#pragma unroll
-    for (int a16 = 0; a16 < 2; ++a16) {
-#pragma unroll
-      for (int dq = 0; dq < NDQ; ++dq) {
-        const char *vp = buf + v_lds + a16 * 16 * VROW + dq * 64;
-        const f16x4 v0 = lds_read_tr(vp);
-        const f16x4 v1 = lds_read_tr(vp + 4 * VROW);
-        const f16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-        const f16x8 bh = __builtin_bit_cast(
-            f16x8, make_uint4(ph[a16][0], ph[a16][1], ph[a16][2], ph[a16][3]));
-        const f16x8 bl = __builtin_bit_cast(
-            f16x8, make_uint4(pl[a16][0], pl[a16][1], pl[a16][2], pl[a16][3]));
-        o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bh, o[dq], 0, 0, 0);
-        o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bl, o[dq], 0, 0, 0);
+      for (int i = 0; i < LPT; ++i) {
+        const int p = tid + i * kPfThreads;
+        const int row = p / NCH, col = p % NCH;
+        *reinterpret_cast<uint4 *>(buf + row * KROW + col * 16) = kd[i];
+        *reinterpret_cast<uint4 *>(buf + VOFF + row * VROW + col * 16) = vd[i];
       }
-    }
-  };
+    };
 
-  // One step s with its K/V in LDS buffer s & 1: store the registers loaded for it, start the
-  // next step's loads, one barrier, compute. The buffer written here was last read two steps
-  // ago, before every wavefront passed the previous barrier.
-  int bad_next = load_step(0);
-  auto step = [&](auto buf_tag, int32_t s) {
-    char *buf = kv_lds + decltype(buf_tag)::value * BUF;
-    const int bad = bad_next;
-    store_step(buf, bad);
-    if (s + 1 < nstep) bad_next = load_step(s + 1);
-    __syncthreads();
-    if (nrow > 0 && s * kStep <= wave_last) {
-      if (bad != 0 || s * kStep + kStep - 1 > wave_first)
-        compute(buf, s, std::true_type{}, bad);
+    // Score MFMA: the A operand row j is key perm(j), perm swapping bits 2 and 3, so that lane
+    // (h, j)'s 16 scores (element v: A row 8(v/4) + 4h + v%4) are keys 16(v/8) + 8h + v%8 of query
+    // row j: two runs of 8 consecutive keys, one per cache block.
+    const int kperm = (j & ~12) | ((j & 4) << 1) | ((j & 8) >> 1);
+    const int k_lds = kperm * KROW + h * 16;
+    // V^T operand of the output MFMAs: lane (h, j) needs V[16a + 8h + t][32dq + j], t = 0..7,
+    // fetched as two transposing reads of 4 keys; lane s of its 16-lane group addresses key row
+    // 16a + 8h + 4r + s/4, dims 32dq + 16(j/16) + 4(s%4) .. + 3 for read r.
+    const int s16 = lane & 15;
+    const int v_lds = VOFF + (8 * h + (s16 >> 2)) * VROW + (16 * (j >> 4) + 4 * (s16 & 3)) * 2;
+
+    f32x16 o[NDQ];
+#pragma unroll
+    for (int dq = 0; dq < NDQ; ++dq)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) o[dq][e] = 0.f;
+    float m = kFloor, l = 0.f;
+    float mt = kFloor + kHi;  // m + kHi
+    const float cl2 = a.cl2;
+
+    // The wavefront's share of one step (keys kStep * s ..), its K and V in LDS at `buf`. MASK:
+    // the step holds keys past some row's position or blocks outside the pool (bits of `bad`).
+    auto compute = [&](const char *buf, int32_t s, auto mask_tag, int bad) {
+      constexpr bool MASK = decltype(mask_tag)::value;
+      f32x16 sc;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NQK; ++c) {
+        const uint4 kv = *reinterpret_cast<const uint4 *>(buf + k_lds + c * 32);
+        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kv), as_f16x8(qv[c]), sc, 0, 0, 0);
+      }
+      if constexpr (MASK) {
+        // key 16(v/8) + 8h + v%8 of the step is kept when at or before the row's position
+        const int32_t lim = my_pos - s * kStep - 8 * h;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const bool keep = 16 * (v >> 3) + (v & 7) <= lim && !((bad >> (v >> 3)) & 1);
+          sc[v] = keep ? sc[v] : -__builtin_inff();
+        }
+      }
+      float mx = sc[0];
+#pragma unroll
+      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
+      // a score that would put a weight above 2^kHi moves the row's reference (rare)
+      if (__ballot(mx * cl2 > mt) != 0) {
+        float u, t;
+        lane_pair<32>(mx * cl2, u, t);
+        const float rmax = fmaxf(u, t);
+        const float mnew = rmax > mt ? rmax - kHead : m;
+        const float f = __builtin_amdgcn_exp2f(m - mnew);
+        l *= f;
+#pragma unroll
+        for (int dq = 0; dq < NDQ; ++dq) o[dq] *= f;
+        m = mnew;
+        mt = m + kHi;
+      }
+      const float nm = -m;
+      uint32_t ph[2][4], pl[2][4];  // keys 16 a16 + 8h + 2i, + 1 as fp16 pairs, hi and lo terms
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], cl2, nm));
+        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], cl2, nm));
+        l += p0;
+        l += p1;
+        split_pair(p0, p1, ph[v >> 3][(v & 7) >> 1], pl[v >> 3][(v & 7) >> 1]);
+      }
+      // O^T += V^T P^T: per 32 dims and 16 keys, the hi and the lo weights share one V^T operand
+#pragma unroll
+      for (int a16 = 0; a16 < 2; ++a16) {
+#pragma unroll
+        for (int dq = 0; dq < NDQ; ++dq) {
+          const char *vp = buf + v_lds + a16 * 16 * VROW + dq * 64;
+          const f16x4 v0 = lds_read_tr(vp);
+          const f16x4 v1 = lds_read_tr(vp + 4 * VROW);
+          const f16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+          const f16x8 bh = __builtin_bit_cast(
+              f16x8, make_uint4(ph[a16][0], ph[a16][1], ph[a16][2], ph[a16][3]));
+          const f16x8 bl = __builtin_bit_cast(
+              f16x8, make_uint4(pl[a16][0], pl[a16][1], pl[a16][2], pl[a16][3]));
+          o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bh, o[dq], 0, 0, 0);
+          o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bl, o[dq], 0, 0, 0);
+        }
+      }
+    };
+
+    // One step s, its K/V in LDS buffer s % 2 and in flight in register set s % kAhead: store that
+    // set, reload it with step s + kAhead, one barrier, compute. The LDS buffer written here was
+    // last read two steps ago, before every wavefront passed the previous barrier.
+    int bad_q[kAhead];
+#pragma unroll
+    for (int r = 0; r < kAhead; ++r) bad_q[r] = r < nstep ? load_step(r, kr[r], vr[r]) : 0;
+    auto step = [&](auto u_tag, int32_t s) {
+      constexpr int U = decltype(u_tag)::value;
+      constexpr int RS = U % kAhead;
+      char *buf = kv_lds + (U % 2) * BUF;
+      const int bad = bad_q[RS];
+      store_step(buf, bad, kr[RS], vr[RS]);
+      if (s + kAhead < nstep) bad_q[RS] = load_step(s + kAhead, kr[RS], vr[RS]);
+      __syncthreads();
+      if (nrow > 0 && s * kStep <= wave_last) {
+        if (bad != 0 || s * kStep + kStep - 1 > wave_first)
+          compute(buf, s, std::true_type{}, bad);
+        else
+          compute(buf, s, std::false_type{}, 0);
+      }
+    };
+    // unrolled over a whole number of LDS buffer and register set cycles
+    auto steps = [&](int32_t s0, auto... us) {
+      ((s0 + decltype(us)::value < nstep ? step(us, s0 + decltype(us)::value) : void()), ...);
+    };
+    for (int32_t s0 = 0; s0 < nstep; s0 += kUnroll) {
+      if constexpr (kUnroll == 2)
+        steps(s0, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{});
       else
-        compute(buf, s, std::false_type{}, 0);
+        steps(s0, std::integral_constant<int, 0>{}, std::integral_constant<int, 1>{},
+              std::integral_constant<int, 2>{}, std::integral_constant<int, 3>{},
+              std::integral_constant<int, 4>{}, std::integral_constant<int, 5>{});
     }
-  };
-  for (int32_t s = 0; s < nstep; s += 2) {
-    step(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < nstep) step(std::integral_constant<int, 1>{}, s + 1);
-  }
-  if (nrow == 0) return;
-  {
-    float u, t;
-    lane_pair<32>(l, u, t);
-    l = u + t;
-  }
-  if (j >= nrow) return;
-  const float inv = l > 0.f ? 1.0f / l : 0.f;
-  // lane (h, j) holds dims 32dq + 8(v/4) + 4h + v%4 of row j
-  const int64_t orow = (static_cast<int64_t>(ch.r0 + rw0 + j) * a.Hq + hq) * D;
+    if (nrow == 0) return;
+    {
+      float u, t;
+      lane_pair<32>(l, u, t);
+      l = u + t;
+    }
+    if (j >= nrow) return;
+    const float inv = l > 0.f ? 1.0f / l : 0.f;
+    // lane (h, j) holds dims 32dq + 8(v/4) + 4h + v%4 of row j
+    const int64_t orow = (static_cast<int64_t>(ch.r0 + rw0 + j) * a.Hq + hq) * D;
 #pragma unroll
-  for (int dq = 0; dq < NDQ; ++dq) {
+    for (int dq = 0; dq < NDQ; ++dq) {
 #pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int64_t i = orow + 32 * dq + 8 * q4 + 4 * h;
-      const f32x4 r = {o[dq][4 * q4] * inv, o[dq][4 * q4 + 1] * inv, o[dq][4 * q4 + 2] * inv,
-                       o[dq][4 * q4 + 3] * inv};
-      if (a.out_f16) {
-        const f16x4 hv = {static_cast<_Float16>(r[0]), static_cast<_Float16>(r[1]),
-                          static_cast<_Float16>(r[2]), static_cast<_Float16>(r[3])};
-        *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(a.out) + i) = hv;
-      } else {
-        *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + i) = r;
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int64_t i = orow + 32 * dq + 8 * q4 + 4 * h;
+        const f32x4 r = {o[dq][4 * q4] * inv, o[dq][4 * q4 + 1] * inv, o[dq][4 * q4 + 2] * inv,
+                         o[dq][4 * q4 + 3] * inv};
+        if (a.out_f16) {
+          const f16x4 hv = {static_cast<_Float16>(r[0]), static_cast<_Float16>(r[1]),
+                            static_cast<_Float16>(r[2]), static_cast<_Float16>(r[3])};
+          *reinterpret_cast<f16x4 *>(static_cast<_Float16 *>(a.out) + i) = hv;
+        } else {
+          *reinterpret_cast<f32x4 *>(static_cast<float *>(a.out) + i) = r;
+        }
       }
     }
+  };
+  run_tile(ntile - 1 - pair);
+  if (pair < ntile - 1 - pair) {
+    __syncthreads();  // the LDS buffers of the first tile are free again
+    run_tile(pair);
   }
 }
 
@@ -436,8 +468,8 @@ static kvc_status launch_prefill(bool paged, PrefillArgs &a, int32_t D, kvc_dtyp
   a.neg_q = scale < 0.f;
   a.cl2 = scale == 0.f ? 1.17549435e-38f : fabsf(scale) * kLog2e;
   const int32_t pt = kPfRows / a.gh;
-  // an upper bound on the workgroups along x: sum_b ceil(n_b / pt) <= total / pt + B
-  const int64_t gx = (static_cast<int64_t>(a.total) + pt - 1) / pt + a.B;
+  // an upper bound on the workgroups along x: sum_b ceil(ceil(n_b / pt) / 2) <= total / 2pt + B
+  const int64_t gx = (static_cast<int64_t>(a.total) + 2 * pt - 1) / (2 * pt) + a.B;
   const int64_t gy = static_cast<int64_t>(a.H) * (a.G / a.gh);
   const int64_t n8 = (gx * gy + 7) / 8 * 8;  // a multiple of the 8 XCDs
   if (n8 > INT32_MAX) return KVC_E_INVALID;
