@@ -465,14 +465,21 @@ def blas_threads() -> int:
 
 KERNEL_SRC = os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", "kvc_decode.hip")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_paged_f16_llama13b_traffic.txt")
-PASS1 = "decode_partial_kernel<true, 1, 128, true, 1>"
+PASS1 = "decode_partial_kernel<true, 1, 128, true, 1, false>"
 
 
-def source_hash() -> str:
+def source_hash(path: str = KERNEL_SRC) -> str:
+    """First 16 hex digits of the sha256 of a kernel source (the decode kernels by default)."""
     import hashlib
 
-    with open(KERNEL_SRC, "rb") as f:
+    with open(path, "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def workload_source(w: workloads.Workload) -> str:
+    """The HIP source of the workload's dominant kernel."""
+    name = "kvc_prefill.hip" if w is workloads.LLAMA7B_PREFILL else "kvc_decode.hip"
+    return os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", name)
 
 
 def pmc_summary(fetch_dir: str, write_dir: str, bench_log: str) -> dict:
@@ -642,7 +649,8 @@ def main():
             **roof,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
-            "kernel_source_sha256_16": source_hash(),
+            "kernel_source": os.path.basename(workload_source(w)),
+            "kernel_source_sha256_16": source_hash(workload_source(w)),
         },
     }
     if not args.no_cpu_baseline:

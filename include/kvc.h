@@ -427,8 +427,8 @@ kvc_status kvc_decode_window_partial_paged(const void *q, kvc_dtype q_dtype, int
  *              L_b rows (the rest of out is not written)
  *   caches:    fp16 only, as for kvc_decode_* (contiguous [B][H_kv][S_max][D]; paged layer with
  *              H_kv heads and the block tables of the sequences)
- * D = 64 or 128. No workspace. Each workgroup of 4 wavefronts computes 64 query rows to the end
- * (two HBM passes over K/V per 64 rows at most: no split across workgroups, no merge).
+ * D = 64 or 128. No workspace. Each workgroup of 4 wavefronts computes two tiles of 128 query
+ * rows of one sequence (a long and a short one) to the end: no split across workgroups, no merge.
  * Errors: KVC_E_UNSUPPORTED (dtypes, D), KVC_E_INVALID (shapes, alignment, B > 4096); block ids
  * outside the pool skip their block. */
 kvc_status kvc_prefill_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,

@@ -8,21 +8,23 @@
 // is tiled in on-chip memory ("KV Cache and PagedAttention", section 5.3: FlashAttention within
 // blocks, PagedAttention between them; "LLM Inference Acceleration -- KV Cache", section 6.3).
 //
-// A workgroup of four wavefronts takes one K/V head and 64 query rows: 64 consecutive positions
-// of one query head, or 32 positions of 2 heads, or 16 positions of 4 heads of a group sharing
-// the K/V head. It walks the 16-position key blocks from 0 to its last row's position. Each
-// block's K and V is loaded once, by all 256 threads with 16-byte loads, into LDS (two buffers,
-// one barrier per block) and serves the four wavefronts. Per wavefront and block the arithmetic
-// is that of grouped decode with 16 query rows in place of 16 query heads:
-//   S^T = K . Q^T with D/32 v_mfma_f32_16x16x32_f16: lane (g, j) = (lane/16, lane%16) feeds key
-//     row j (from LDS) and query row j (registers) and receives the scores of keys 4g..4g+3 for
-//     row j; keys past the row's position are masked to -inf;
-//   the online softmax keeps, per row, a reference that moves only when a block's maximum passes
-//     it by the headroom, and per lane the partial sum of its keys' weights;
-//   O^T = V^T . P^T with D/16 x 2 v_mfma_f32_16x16x16_f16, the weights as fp16 hi + lo (about 22
-//     bits) and V^T read from LDS one fp16 at a time.
-// LDS layouts: K rows keep their 16-byte columns XOR-swizzled by the row index (the 16 rows a
-// read instruction takes land on distinct banks); V rows are swizzled by row group as in decode.
+// A workgroup of four wavefronts takes one K/V head and 128 query rows: 128 consecutive
+// positions of one query head, or 64 of 2 heads, or 32 of 4 heads of a group sharing the K/V
+// head; each wavefront owns 32 rows of one head. It walks the keys in steps of 32 (two cache
+// blocks) from 0 to its last row's position. A step's K and V is loaded once, by all 256 threads
+// with 16-byte loads (two steps ahead, in registers), into LDS (two buffers, one barrier per
+// step) and serves the four wavefronts. Per wavefront and step:
+//   S^T = K . Q^T with D/16 v_mfma_f32_32x32x16_f16: lane (h, j) = (lane/32, lane%32) feeds key
+//     row perm(j) (perm swaps bits 2 and 3) and query row j and receives 16 scores of row j, keys
+//     16(v/8) + 8h + v%8; keys past the row's position are masked to -inf on the steps that
+//     reach it;
+//   the online softmax keeps, per row, a reference that moves only when a score passes it by the
+//     headroom, and per lane the partial sum of its keys' weights;
+//   O^T += V^T . P^T with D/32 x 4 v_mfma_f32_32x32x16_f16, the weights as fp16 hi + lo (about 22
+//     bits): for 16 keys the hi and the lo weights each take one instruction on the same V^T
+//     operand, which two transposing LDS reads deliver.
+// LDS rows are padded (K by 16 bytes, V by 64) so that the rows one read instruction takes fall
+// on distinct banks and every read offset is an immediate.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
