@@ -139,7 +139,8 @@ static __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &
 }
 
 template <bool PAGED, int D>
-__global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a) {
+__global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a,
+                                                             const int32_t *__restrict__ tables) {
   constexpr int ROW = D * 2;            // bytes of one fp16 row
   constexpr int NCH = D / 8;            // 16-byte columns per row
   constexpr int BLK = kBlock * ROW;     // bytes of one cache block of one head
@@ -232,41 +233,59 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     const int32_t L = ch.L;
     const int64_t kv_head_off = PAGED ? static_cast<int64_t>(hk) * BLK
                                       : (static_cast<int64_t>(b) * a.H + hk) * a.seq_stride * ROW;
-    const int32_t *trow = PAGED ? a.tables + static_cast<int64_t>(b) * a.mbps : nullptr;
+    // (the table is a kernel argument of its own, marked restrict: the output stores cannot
+    // alias it, so its reads stay scalar loads)
+    const int32_t *trow = PAGED ? tables + static_cast<int64_t>(b) * a.mbps : nullptr;
     // kAhead steps are in flight in registers while one is computed from LDS
     uint4 kr[kAhead][LPT], vr[kAhead][LPT];
-    // loads step s (32 s <= L - 1, so its first block holds positions); returns bit i set when
-    // block i holds positions but is not in the pool
-    auto load_step = [&](int32_t s, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) -> int {
+    // The table entries of the step loaded next are read one step earlier (scalar loads, kept
+    // in scalar registers), and the addresses of a step are planned before the previous step's
+    // LDS stores are issued, so waiting for the entries never waits for LDS work.
+    struct StepPlan {
+      int64_t base0, base1;  // byte offsets of the step's two blocks of this head
+      int32_t lim0, lim1;    // last row of each block that holds a position
+      int bad;               // bit i: block i holds positions but is not in the pool
+    };
+    // entries of step s's blocks (32 s <= L - 1, so its first block holds positions; a second
+    // block past the end takes the first block's entry)
+    auto table_pair = [&](int32_t s, int32_t &p0, int32_t &p1) {
+      if constexpr (PAGED) {
+        p0 = trow[2 * s];
+        p1 = L - s * kStep - kBlock > 0 ? trow[2 * s + 1] : p0;
+      } else {
+        p0 = p1 = 0;
+      }
+    };
+    auto plan_step = [&](int32_t s, int32_t p0, int32_t p1) -> StepPlan {
+      StepPlan pl;
       const int32_t nv0 = min(kBlock, L - s * kStep);
       const int32_t nv1 = min(kBlock, L - s * kStep - kBlock);
-      int64_t base0, base1;
-      int bad = 0;
+      pl.bad = 0;
       if constexpr (PAGED) {
-        const int32_t p0 = trow[2 * s];
-        const int32_t p1 = nv1 > 0 ? trow[2 * s + 1] : p0;
         const bool in0 = static_cast<uint32_t>(p0) < static_cast<uint32_t>(a.num_blocks);
         const bool in1 = static_cast<uint32_t>(p1) < static_cast<uint32_t>(a.num_blocks);
-        bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
-        base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
-        base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
+        pl.bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
+        pl.base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
+        pl.base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
       } else {
-        base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
-        base1 = nv1 > 0 ? base0 + BLK : base0;
+        pl.base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
+        pl.base1 = nv1 > 0 ? pl.base0 + BLK : pl.base0;
       }
-      const int32_t lim0 = nv0 - 1;
-      const int32_t lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
+      pl.lim0 = nv0 - 1;
+      pl.lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
+      return pl;
+    };
+    auto issue_step = [&](const StepPlan &pl, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) {
 #pragma unroll
       for (int i = 0; i < LPT; ++i) {
         const int p = tid + i * kPfThreads;
         const int row = p / NCH;
         const bool sb = (row >> 4) != 0;  // block of the step
-        const int32_t r = min(row & 15, sb ? lim1 : lim0);
-        const int64_t off = (sb ? base1 : base0) + r * ROW + (p % NCH) * 16;
+        const int32_t r = min(row & 15, sb ? pl.lim1 : pl.lim0);
+        const int64_t off = (sb ? pl.base1 : pl.base0) + r * ROW + (p % NCH) * 16;
         kd[i] = *reinterpret_cast<const uint4 *>(a.k + off);
         vd[i] = *reinterpret_cast<const uint4 *>(a.v + off);
       }
-      return bad;
     };
     auto store_step = [&](char *buf, int bad, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) {
       if (bad != 0) {
@@ -375,15 +394,32 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     // set, reload it with step s + kAhead, one barrier, compute. The LDS buffer written here was
     // last read two steps ago, before every wavefront passed the previous barrier.
     int bad_q[kAhead];
+    int32_t tp0 = 0, tp1 = 0;  // table entries of the step loaded next
 #pragma unroll
-    for (int r = 0; r < kAhead; ++r) bad_q[r] = r < nstep ? load_step(r, kr[r], vr[r]) : 0;
+    for (int r = 0; r < kAhead; ++r) {
+      bad_q[r] = 0;
+      if (r < nstep) {
+        table_pair(r, tp0, tp1);
+        const StepPlan pl = plan_step(r, tp0, tp1);
+        issue_step(pl, kr[r], vr[r]);
+        bad_q[r] = pl.bad;
+      }
+    }
+    if (kAhead < nstep) table_pair(kAhead, tp0, tp1);
     auto step = [&](auto u_tag, int32_t s) {
       constexpr int U = decltype(u_tag)::value;
       constexpr int RS = U % kAhead;
       char *buf = kv_lds + (U % 2) * BUF;
       const int bad = bad_q[RS];
+      const bool more = s + kAhead < nstep;
+      StepPlan pl{};
+      if (more) pl = plan_step(s + kAhead, tp0, tp1);
       store_step(buf, bad, kr[RS], vr[RS]);
-      if (s + kAhead < nstep) bad_q[RS] = load_step(s + kAhead, kr[RS], vr[RS]);
+      if (more) {
+        issue_step(pl, kr[RS], vr[RS]);
+        bad_q[RS] = pl.bad;
+        if (s + kAhead + 1 < nstep) table_pair(s + kAhead + 1, tp0, tp1);
+      }
       __syncthreads();
       if (nrow > 0 && s * kStep <= wave_last) {
         if (bad != 0 || s * kStep + kStep - 1 > wave_first)
@@ -438,7 +474,7 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
   }
 }
 
-using PrefillKernel = void (*)(PrefillArgs);
+using PrefillKernel = void (*)(PrefillArgs, const int32_t *);
 
 template <bool PAGED>
 static PrefillKernel pick_prefill(int D) {
@@ -482,7 +518,7 @@ static kvc_status launch_prefill(bool paged, PrefillArgs &a, int32_t D, kvc_dtyp
   PrefillKernel kern = paged ? pick_prefill<true>(D) : pick_prefill<false>(D);
   if (!kern) return KVC_E_UNSUPPORTED;
   hipLaunchKernelGGL(kern, dim3(static_cast<uint32_t>(n8)), dim3(kPfThreads), shmem,
-                     static_cast<hipStream_t>(stream), a);
+                     static_cast<hipStream_t>(stream), a, a.tables);
   return launch_status();
 }
 
