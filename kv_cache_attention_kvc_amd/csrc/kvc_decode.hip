@@ -1265,8 +1265,12 @@ struct PartialPlan {
 
 // Pass-1 wavefronts per compute unit: each wavefront has about one tile of loads in flight, so
 // small tiles (K+V of 16 positions) need more wavefronts to keep enough bytes in flight: 8 for
-// tiles of 8 KiB or more, 12 for 4 KiB, 16 for 2 KiB (register use allows each).
-inline int waves_per_cu(kvc_dtype kv, int D) {
+// tiles of 8 KiB or more, 12 for 4 KiB, 16 for 2 KiB (register use allows each). The matrix-core
+// kernel over fp16 caches runs 4 (one workgroup, one wavefront per SIMD): a wavefront there
+// serves up to 16 query heads, so each split pair costs up to 16 records and merges, and at the
+// grouped-query workload (64 query heads over 8 K/V heads) 4 measured faster than 8 and 6.
+inline int waves_per_cu(kvc_dtype kv, int D, bool mfma) {
+  if (mfma && kv == KVC_F16) return 4;
   const int tile = 2 * kBlock * D * static_cast<int>(elt_bytes(kv));
   return tile >= 8192 ? 8 : tile >= 4096 ? 12 : 16;
 }
@@ -1339,7 +1343,7 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
                            sizeof(int32_t) +
                        (gp.mfma ? static_cast<size_t>(kWgWaves) * kBlock * D * 2 : 0);
   // one round of wavefronts: never more than fit on the GPU at once
-  int wpc = waves_per_cu(kv_dtype, D);
+  int wpc = waves_per_cu(kv_dtype, D, gp.mfma);
   const int fit = resident_waves_per_cu(kern, shmem);
   if (fit > 0) wpc = std::min(wpc, fit);
   int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
