@@ -166,3 +166,34 @@ def i8_write_token(codes: np.ndarray, scale, off: int, x) -> np.float32:
         s = s_new
     codes[:, off, :] = _i8_enc_scaled(x32, s)
     return np.float32(s)
+
+
+# ---- whole-block compression ----------------------------------------------------------------
+# The pages compress the cached history to 8 bits once it grows past a threshold ("KV Cache
+# Mechanism Explained", section 6.1, item 1: dynamic cache compression, fp8 quantisation) and
+# compress inactive blocks with 8-bit quantisation ("KV Cache and PagedAttention", section 7.2,
+# item 1). Reading taken: a block of a 16-bit cache is re-encoded in one shot into a block of an
+# 8-bit cache with the same per-block scale convention as the write rule above: over the block's
+# first n_valid slots of every head, s = fp32(max|x| / limit), each of those values is stored as
+# enc(fp32(x / s)) (a signed zero code while s = 0), and the slots past n_valid hold code 0 and
+# take no part in the scale (their source values are never read).
+
+def compress_block(x, n_valid: int, fmt: str):
+    """One-shot 8-bit encoding of one block.
+
+    x: [H, block_size, D] source values, exact in fp32 (slots >= n_valid are ignored and may
+    hold anything, NaN included); n_valid: slots 0 .. n_valid-1 hold positions; fmt: "e4m3" or
+    "i8". Returns (codes [H, block_size, D] as uint8 for e4m3 / int8 for i8, fp32 scale)."""
+    x = np.asarray(x)
+    H, bs, D = x.shape
+    if not 0 <= n_valid <= bs:
+        raise ValueError("n_valid")
+    limit = np.float32(E4M3_MAX if fmt == "e4m3" else I8_MAX)
+    codes = np.zeros((H, bs, D), dtype=np.uint8 if fmt == "e4m3" else np.int8)
+    if n_valid == 0:
+        return codes, np.float32(0.0)
+    xv = x[:, :n_valid, :].astype(np.float32)
+    amax = np.float32(np.max(np.abs(xv)))
+    s = np.float32(amax / limit)
+    codes[:, :n_valid, :] = _enc_scaled(xv, s) if fmt == "e4m3" else _i8_enc_scaled(xv, s)
+    return codes, s

@@ -246,3 +246,69 @@ def test_i8_token_sequential_error_vs_unquantised():
         bound = 0.5 * sum(sorted(set(scales[t:])))
         assert err[:, t, :].max() <= bound * (1 + 1e-6), t
     assert s == np.float32(np.float32(np.abs(xs).max()) / np.float32(127))
+
+
+# ---- whole-block compression ---------------------------------------------------------------
+from oracle.codecs import E4M3_MAX, compress_block, e4m3_decode  # noqa: E402
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+def test_compress_block_scale_extreme_code_and_error_bound(fmt):
+    """The scale is max|x| / limit over the valid slots of every head; the element of largest
+    magnitude gets the extreme code (+-limit exactly); every stored value is within the
+    format's half step of the source (int8: s/2; e4m3: 2^-4 relative, or 2^-10 s absolute
+    in the subnormal range)."""
+    g = np.random.default_rng(31)
+    x = g.standard_normal((3, 16, 32)).astype(np.float16).astype(np.float32)
+    n = 11
+    x[:, n:, :] = np.nan                               # past the valid slots: never read
+    codes, s = compress_block(x, n, fmt)
+    lim = np.float32(E4M3_MAX if fmt == "e4m3" else I8_MAX)
+    xv = x[:, :n, :]
+    assert s == np.float32(np.float32(np.abs(xv).max()) / lim)
+    dec = e4m3_decode(codes) if fmt == "e4m3" else i8_decode(codes)
+    vals = dec[:, :n, :] * np.float64(s)
+    k = np.unravel_index(np.argmax(np.abs(xv)), xv.shape)
+    assert abs(dec[:, :n, :][k]) == float(lim)
+    err = np.abs(vals - xv.astype(np.float64))
+    if fmt == "i8":
+        assert err.max() <= 0.5 * float(s) * (1 + 1e-6)
+    else:
+        bound = np.maximum(np.abs(xv) * 2.0 ** -4, 2.0 ** -10 * float(s))
+        assert np.all(err <= bound * (1 + 1e-6))
+    assert not codes[:, n:, :].any()                   # past n_valid: code 0
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+def test_compress_block_degenerate_cases(fmt):
+    z = np.zeros((2, 16, 8), np.float32)
+    codes, s = compress_block(z, 16, fmt)
+    assert s == 0.0 and not codes.any()
+    codes, s = compress_block(np.full((2, 16, 8), np.nan, np.float32), 0, fmt)
+    assert s == 0.0 and not codes.any()
+    # negative zeros: e4m3 keeps the sign code, int8 has none
+    neg = np.full((1, 16, 4), -0.0, np.float32)
+    codes, s = compress_block(neg, 16, fmt)
+    assert s == 0.0
+    assert (codes == (0x80 if fmt == "e4m3" else 0)).all()
+    with pytest.raises(ValueError):
+        compress_block(z, 17, fmt)
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "i8"])
+def test_compress_block_equals_writer_when_the_first_token_holds_the_maximum(fmt):
+    """When the block's largest magnitude arrives with its first token, the running-scale
+    writer never requantises, so writing the tokens one by one gives the one-shot encoding."""
+    g = np.random.default_rng(32)
+    x = g.standard_normal((2, 16, 16)).astype(np.float32)
+    x[:, 0, :] *= 8.0
+    x[0, 0, 0] = 40.0                                  # the maximum, in slot 0
+    n = 13
+    write = fp8_write_token if fmt == "e4m3" else i8_write_token
+    codes = np.zeros(x.shape, np.uint8 if fmt == "e4m3" else np.int8)
+    s = 0.0
+    for t in range(n):
+        s = write(codes, s, t, x[:, t, :])
+    c1, s1 = compress_block(x, n, fmt)
+    assert s1 == s
+    np.testing.assert_array_equal(c1, codes)
