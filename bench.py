@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
                     choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
-                             "gqa8-paged", "llama13b-window", "llama7b-prefill", "i8-longctx"])
+                             "gqa8-paged", "llama13b-window", "llama7b-prefill", "i8-longctx",
+                             "i8-compress"])
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
@@ -295,6 +296,98 @@ class PrefillBench:
         return dt, ref, self.T * self.H * self.D * 2 * ELT[self.w.kv_dtype]
 
 
+class CompressBench:
+    """Whole-cache 8-bit compression: every sequence's fp16 blocks re-encoded into an int8 pool
+    with fresh per-block scales, one kvc_compress_blocks launch per layer (the same blocks each
+    step; the destination is overwritten)."""
+
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
+        import torch
+
+        import kv_cache_attention_kvc_amd as kvc
+
+        self.kvc, self.torch, self.w, self.dev, self.L = kvc, torch, w, dev, layers
+        B, H, D, T = w.batch, w.heads, w.head_dim, w.ctx
+        self.B, self.H, self.D, self.T = B, H, D, T
+        N = B * workloads.blocks_for(T)
+        self.pool = kvc.Pool(N, workloads.blocks_for(T), order=workloads.llama13b_pool_order(N, w.seed))
+        self.seqs = [self.pool.alloc() for _ in range(B)]
+        slots = np.concatenate([self.pool.append([s], T)[0] for s in self.seqs])
+        slots_d = torch.from_numpy(slots).to(dev)
+        src_dt = w.extra["compress_from"]
+        self.src = [kvc.PagedLayer.empty(N, H, D, src_dt, device=dev) for _ in range(layers)]
+        self.dst = [kvc.PagedLayer.empty(N, H, D, w.kv_dtype, device=dev) for _ in range(layers)]
+        for li, layer in enumerate(self.src):
+            k = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li)
+            v = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li + 1)
+            kvc.write_paged(layer, slots_d, k, v)
+            del k, v
+        # every block of every sequence, in table order; a block holds min(16, T - 16j) slots
+        tables, lens = self.pool.block_table(self.seqs)
+        ids, nval = [], []
+        for b in range(B):
+            for j in range(workloads.blocks_for(int(lens[b]))):
+                ids.append(int(tables[b][j]))
+                nval.append(min(16, int(lens[b]) - 16 * j))
+        self.ids = np.array(ids, dtype=np.int32)
+        self.nval = np.array(nval, dtype=np.int32)
+        self.ids_d = torch.from_numpy(self.ids).to(dev)
+        self.nval_d = torch.from_numpy(self.nval).to(dev)
+        self.stream = torch.cuda.current_stream()
+        self.first_lens = lens.astype(np.int64)
+        self.lens_now = lens.astype(np.int64)
+        torch.cuda.synchronize()
+
+    def step(self, ev=None):
+        for li in range(self.L):
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li, self.stream)
+            self.kvc.compress_blocks(self.src[li], self.dst[li], self.ids_d, self.ids_d,
+                                     self.nval_d)
+            if ev is not None:
+                ev[0].record(ev[1] + 2 * li + 1, self.stream)
+
+    def bytes_step(self, lens):
+        """Algorithmic HBM bytes of one launch: the valid source rows of K and V read (fp16),
+        every destination slot of K and V written (one byte each), the two scales per block
+        written, and the block ids and counts read."""
+        src_elt = ELT[self.w.extra["compress_from"]]
+        rows = int(self.nval.sum()) * self.H * self.D
+        nblk = len(self.ids)
+        per = rows * 2 * src_elt + nblk * 16 * self.H * self.D * 2 * ELT[self.w.kv_dtype] \
+            + nblk * (2 * 4 + 2 * 4)
+        return per * self.L, per
+
+    SAMPLE = 2048  # blocks of the last layer the CPU oracle compresses (about 15 s)
+
+    def gpu_sample(self):
+        """Stored values (codes x block scale) of the first SAMPLE blocks of the last layer."""
+        dst = self.dst[-1]
+        idx = self.ids_d[:self.SAMPLE].long()
+        k = dst.k_pool[idx].float() * dst.k_scale[idx].view(-1, 1, 1, 1)
+        v = dst.v_pool[idx].float() * dst.v_scale[idx].view(-1, 1, 1, 1)
+        return self.torch.stack([k, v])
+
+    def oracle_layer(self, li):
+        """The CPU oracle's compression of the first SAMPLE blocks of the last layer."""
+        from oracle.codecs import compress_block, i8_decode
+
+        src = self.src[-1]
+        idx = self.ids_d[:self.SAMPLE].long()
+        ks = src.k_pool[idx].float().cpu().numpy()
+        vs = src.v_pool[idx].float().cpu().numpy()
+        n = self.nval[:self.SAMPLE]
+        t0 = time.perf_counter()
+        out = np.zeros((2,) + ks.shape)
+        for i in range(len(n)):
+            for j, x in enumerate((ks[i], vs[i])):
+                c, s = compress_block(x, int(n[i]), self.w.kv_dtype)
+                out[j, i] = i8_decode(c) * np.float64(s)
+        dt = time.perf_counter() - t0
+        nbytes = int(n.sum()) * self.H * self.D * 2 * ELT[self.w.extra["compress_from"]]
+        return dt, out, nbytes
+
+
 class HipEvents:
     """HIP timing events recorded on a stream, created with hipEventDisableSystemFence: a timing
     event then skips the system-scope cache write-back and invalidate that default events do,
@@ -445,6 +538,9 @@ def kernel_name(w: workloads.Workload) -> str:
     win = ", rolling window" if "window" in w.extra else ""
     if w is workloads.LLAMA7B_PREFILL:
         return f"kvc::prefill_kernel<{w.kind}, {w.head_dim}> (causal prefill on the matrix cores)"
+    if w is workloads.COMPRESS_I8:
+        return (f"kvc::compress_blocks_kernel<{w.extra['compress_from']} source, {w.kv_dtype}> "
+                "(one-shot 8-bit block compression)")
     if G == 1:
         return (f"kvc::decode_partial_kernel<{w.kind}, {w.kv_dtype}, {w.head_dim}{win}> "
                 "(attention pass 1)")
@@ -478,7 +574,8 @@ def source_hash(path: str = KERNEL_SRC) -> str:
 
 def workload_source(w: workloads.Workload) -> str:
     """The HIP source of the workload's dominant kernel."""
-    name = "kvc_prefill.hip" if w is workloads.LLAMA7B_PREFILL else "kvc_decode.hip"
+    name = ("kvc_prefill.hip" if w is workloads.LLAMA7B_PREFILL else
+            "kvc_write.hip" if w is workloads.COMPRESS_I8 else "kvc_decode.hip")
     return os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", name)
 
 
@@ -560,7 +657,7 @@ def main():
          "gqa8-paged": workloads.GQA8_PAGED,
          "llama13b-window": workloads.LLAMA13B_WINDOW,
          "llama7b-prefill": workloads.LLAMA7B_PREFILL,
-         "i8-longctx": workloads.LONGCTX_I8}[args.workload]
+         "i8-longctx": workloads.LONGCTX_I8, "i8-compress": workloads.COMPRESS_I8}[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
@@ -576,7 +673,9 @@ def main():
         sys.exit(2)
     path = "fused" if fused else "separate"
     prefill = w is workloads.LLAMA7B_PREFILL
-    cls = PrefillBench if prefill else (PagedBench if w.kind == "paged" else ContigBench)
+    compress = w is workloads.COMPRESS_I8
+    cls = PrefillBench if prefill else (CompressBench if compress else
+                                        (PagedBench if w.kind == "paged" else ContigBench))
     bench = cls(w, K + W, layers, dev, fused)
     for _ in range(W):
         bench.step()
@@ -610,6 +709,10 @@ def main():
                 "frac": round(bench.flops_launch() / p1_avg_s / 1e12 / PEAK_F16_TFLOPS, 4),
                 "traffic": None, "flops_per_launch": bench.flops_launch()}
         tokens = w.batch * bench.T * K
+    elif compress:
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": None}
+        tokens = w.batch * bench.T * K  # cached tokens compressed (in every layer) per step
     else:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / PEAK_GBS, 4),
@@ -637,8 +740,8 @@ def main():
             "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
             if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
-            "ctx_growth_per_step": 0 if w in (workloads.LLAMA7B_CONTIG,
-                                              workloads.LLAMA7B_PREFILL) else 1,
+            "ctx_growth_per_step": 0 if w in (workloads.LLAMA7B_CONTIG, workloads.LLAMA7B_PREFILL,
+                                              workloads.COMPRESS_I8) else 1,
             "window": w.extra.get("window", 0),
             "append": path,
         },
@@ -665,6 +768,8 @@ def main():
             "sample": (f"the first prompt of the last layer: {bench.T} rows x {w.heads} heads, "
                        f"causal; {dt:.2f} s; {bench.T / (dt * layers):.3f} prefill tokens/s over "
                        f"{layers} layers") if prefill else
+                      (f"the first {bench.SAMPLE} blocks of the last layer (K and V); {dt:.2f} s")
+                      if compress else
                       (f"layer 0 of the last step: all {w.batch} sequences x {w.heads} heads, "
                        f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
                        f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers"),

@@ -214,6 +214,25 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
                            const void *k_new, const void *v_new, kvc_dtype new_dtype,
                            void *stream);
 
+/* Compress blocks of a 16-bit (or fp32) layer into an 8-bit layer in one shot ("KV Cache
+ * Mechanism Explained", section 6.1, item 1: compress the cache to 8 bits once it grows past a
+ * threshold; "KV Cache and PagedAttention", section 7.2, item 1: compress inactive blocks with
+ * 8-bit quantisation).
+ *   src: layer with kv_dtype KVC_F16 or KVC_F32; dst: layer with kv_dtype KVC_E4M3 or KVC_I8,
+ *     the same num_heads and head_dim, its own (non-overlapping) device memory.
+ *   src_ids, dst_ids: device int32[n], block pairs; dst ids distinct; a pair with an id outside
+ *     its pool is skipped.
+ *   n_valid: device int32[n], slots of each source block that hold positions (clamped to
+ *     [0, 16]; a sequence's last block may be partial), or null for 16 everywhere.
+ * For each pair the destination block's K scale is fp32(max|K| / limit) over the valid slots of
+ * every head (limit 448 for e4m3, 127 for int8), each valid value is stored as the code of
+ * fp32(x / scale) (the write rule's encoding; signed zero while the scale is 0), the other slots
+ * get code 0, and the same for V. Source values past n_valid are never read. kvc_write_paged can
+ * then continue writing a compressed partial block with its running-maximum rule. */
+kvc_status kvc_compress_blocks(const kvc_paged_layer *src, const kvc_paged_layer *dst,
+                               const int32_t *src_ids, const int32_t *dst_ids,
+                               const int32_t *n_valid, int32_t n, void *stream);
+
 /* ==================================================================================== *
  * Device side: decode attention.
  *

@@ -25,7 +25,7 @@ __all__ = [
     "decode_gqa_contig", "decode_gqa_paged", "decode_gqa_partial_contig",
     "decode_gqa_partial_paged", "decode_gqa_merge", "decode_window_contig", "decode_window_paged",
     "decode_window_partial_contig", "decode_window_partial_paged", "prefill_contig",
-    "prefill_paged",
+    "prefill_paged", "compress_blocks",
 ]
 
 F32, F16, E4M3, I8 = 0, 1, 2, 3
@@ -46,6 +46,7 @@ EXPORTS = [
     "kvc_decode_gqa_partial_contig", "kvc_decode_gqa_partial_paged", "kvc_decode_gqa_merge",
     "kvc_decode_window_contig", "kvc_decode_window_paged", "kvc_decode_window_partial_contig",
     "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
+    "kvc_compress_blocks",
 ]
 
 
@@ -111,6 +112,8 @@ def load_library() -> ctypes.CDLL:
         "kvc_copy_blocks": (ctypes.c_int, [ctypes.POINTER(_Layer), _P, _P, _I32, _P]),
         "kvc_write_paged": (ctypes.c_int, [ctypes.POINTER(_Layer), _P, _I32, _P, _P, ctypes.c_int,
                                            _P]),
+        "kvc_compress_blocks": (ctypes.c_int, [ctypes.POINTER(_Layer), ctypes.POINTER(_Layer), _P,
+                                               _P, _P, _I32, _P]),
         "kvc_decode_workspace_bytes": (ctypes.c_size_t, [_I32, _I32, _I32]),
         "kvc_decode_attn_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _I32,
                                                   _I32, _I32, _I32, _I32, _F, _P, ctypes.c_int, _P,
@@ -410,6 +413,22 @@ def write_paged(layer: PagedLayer, slots, k_new, v_new, stream=None) -> None:
     st = layer.struct()
     _check(_lib().kvc_write_paged(ctypes.byref(st), _ptr(slots), n, _ptr(k_new), _ptr(v_new),
                                   _dtype_code(k_new), _stream(stream)), "kvc_write_paged")
+
+
+def compress_blocks(src: PagedLayer, dst: PagedLayer, src_ids, dst_ids, n_valid=None,
+                    stream=None) -> None:
+    """Re-encode blocks src_ids of a 16-bit (or fp32) layer into blocks dst_ids of an 8-bit
+    layer (int32 device tensors of equal length); n_valid: int32 slots per block that hold
+    positions (None: all 16). Each destination block gets a fresh per-block scale."""
+    n = int(src_ids.numel())
+    if int(dst_ids.numel()) != n or (n_valid is not None and int(n_valid.numel()) != n):
+        raise ValueError("src_ids, dst_ids and n_valid must have one entry per block pair")
+    if n == 0:
+        return
+    s1, s2 = src.struct(), dst.struct()
+    _check(_lib().kvc_compress_blocks(ctypes.byref(s1), ctypes.byref(s2), _ptr(src_ids),
+                                      _ptr(dst_ids), None if n_valid is None else _ptr(n_valid),
+                                      n, _stream(stream)), "kvc_compress_blocks")
 
 
 def _out_for(q, out):

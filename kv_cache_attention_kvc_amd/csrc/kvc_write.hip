@@ -7,6 +7,7 @@
 // with one fp32 scale per block for K and one for V ("KV Cache Mechanism Explained", section 8,
 // item 3: FP8/INT8 history with a scaling factor; "KV Cache and PagedAttention", section 7.2).
 #include "kvc_internal.h"
+#include "kvc_wave.h"
 
 namespace kvc {
 
@@ -265,6 +266,147 @@ write_paged_q8_kernel(uint8_t *kp, uint8_t *vp, float *ks, float *vs, const void
   }
 }
 
+
+// Whole-block compression: one workgroup per (source, destination) pair. The first n slots of
+// every head of source block src[i] (fp16 or fp32) are re-encoded into destination block dst[i]
+// of an 8-bit layer in one shot: the block's K scale (and V scale) is max|x| / limit over those
+// values, every value is stored as enc(x / scale), and slots n .. 15 get code 0. Pairs whose
+// ids lie outside their pools are skipped. Each thread takes 4 consecutive elements of a row.
+template <bool SRC_F16, int FMT>
+__global__ void __launch_bounds__(kThreads)
+compress_blocks_kernel(const void *sk, const void *sv, uint8_t *dk, uint8_t *dv, float *ks,
+                       float *vs, const int32_t *src, const int32_t *dst, const int32_t *nval,
+                       int32_t H, int32_t D, int32_t src_blocks, int32_t dst_blocks) {
+  __shared__ float red[2][kThreads / 64];
+  const int32_t sb = src[blockIdx.x];
+  const int32_t db = dst[blockIdx.x];
+  if (static_cast<uint32_t>(sb) >= static_cast<uint32_t>(src_blocks) ||
+      static_cast<uint32_t>(db) >= static_cast<uint32_t>(dst_blocks))
+    return;
+  const int32_t n = nval ? min(max(nval[blockIdx.x], 0), kBlock) : kBlock;
+  const int32_t per_block = H * kBlock * D;  // elements of one block of K (or V)
+  const int64_t s0 = static_cast<int64_t>(sb) * per_block;
+  const int64_t d0 = static_cast<int64_t>(db) * per_block;
+  float mk = 0.f, mv = 0.f;
+  for (int32_t e0 = threadIdx.x * 4; e0 < per_block; e0 += 4 * kThreads) {
+    if ((e0 / D) % kBlock >= n) continue;  // slot past the valid ones: never read
+    float a[4], b[4];
+    load4<SRC_F16>(sk, s0 + e0, a);
+    load4<SRC_F16>(sv, s0 + e0, b);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      mk = fmaxf(mk, fabsf(a[u]));
+      mv = fmaxf(mv, fabsf(b[u]));
+    }
+  }
+  mk = block_max(mk, red[0]);
+  mv = block_max(mv, red[1]);
+  const float ck = mk / Q8<FMT>::kMax;
+  const float cv = mv / Q8<FMT>::kMax;
+  for (int32_t e0 = threadIdx.x * 4; e0 < per_block; e0 += 4 * kThreads) {
+    uint32_t wk = 0, wv = 0;
+    if ((e0 / D) % kBlock < n) {
+      float a[4], b[4];
+      load4<SRC_F16>(sk, s0 + e0, a);
+      load4<SRC_F16>(sv, s0 + e0, b);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        wk |= enc_scaled<FMT>(a[u], ck) << (8 * u);
+        wv |= enc_scaled<FMT>(b[u], cv) << (8 * u);
+      }
+    }
+    *reinterpret_cast<uint32_t *>(dk + d0 + e0) = wk;
+    *reinterpret_cast<uint32_t *>(dv + d0 + e0) = wv;
+  }
+  if (threadIdx.x == 0) {
+    ks[db] = ck;
+    vs[db] = cv;
+  }
+}
+
+
+// Single-read compression of fp16 blocks: one workgroup of kCompThreads per (pair, K or V). The
+// block (H*16*D fp16, NL 16-byte pieces per thread at most) stays in registers between the
+// maximum and the encoding, so each source byte is read from memory once. Thread t takes pieces
+// t, t + kCompThreads, ...; a piece is 8 consecutive values of one (head, slot) row. NL is the
+// smallest of 4, 8, 16, 32 that covers the block, so that small blocks leave registers for a
+// second workgroup per CU.
+constexpr int kCompThreads = 512;
+constexpr int kCompMaxLoads = 32;  // H*D <= 8192 (e.g. 64 heads of 128)
+
+template <int FMT, int NL>
+__global__ void __launch_bounds__(kCompThreads)
+compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *dv, float *ks,
+                         float *vs, const int32_t *src, const int32_t *dst, const int32_t *nval,
+                         int32_t H, int32_t D, int32_t src_blocks, int32_t dst_blocks) {
+  __shared__ float red[kCompThreads / 64];
+  const int32_t pair = blockIdx.x >> 1;
+  const bool is_v = blockIdx.x & 1;
+  const int32_t sb = src[pair];
+  const int32_t db = dst[pair];
+  if (static_cast<uint32_t>(sb) >= static_cast<uint32_t>(src_blocks) ||
+      static_cast<uint32_t>(db) >= static_cast<uint32_t>(dst_blocks))
+    return;
+  const int32_t n = nval ? min(max(nval[pair], 0), kBlock) : kBlock;
+  const int32_t pieces = H * kBlock * D / 8;  // 16-byte pieces of the block
+  const int32_t rpp = D / 8;                  // pieces per (head, slot) row
+  const char *sp = (is_v ? sv : sk) + static_cast<int64_t>(sb) * pieces * 16;
+  uint8_t *dp = (is_v ? dv : dk) + static_cast<int64_t>(db) * pieces * 8;
+  // Thread t takes the piece pairs (2u, 2u + 1), u = t + i * kCompThreads: both pieces lie in
+  // one (head, slot) row (a row has D/8 >= 8 pieces), and their 16 codes form one 16-byte store.
+  // Every load is issued before any is used (a load per branch would wait for each in turn);
+  // pairs past the block read its first pair instead, and pieces of slots past the valid ones
+  // are zeroed after the load, so their values take no part.
+  uint4 x[NL];
+#pragma unroll
+  for (int i = 0; i < NL / 2; ++i) {
+    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
+    const int64_t off = static_cast<int64_t>(c < pieces ? c : 0) * 16;
+    x[2 * i] = *reinterpret_cast<const uint4 *>(sp + off);
+    x[2 * i + 1] = *reinterpret_cast<const uint4 *>(sp + off + 16);
+  }
+  float m = 0.f;
+#pragma unroll
+  for (int i = 0; i < NL / 2; ++i) {
+    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
+    const uint32_t keep = c < pieces && (c / rpp) % kBlock < n ? ~0u : 0u;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      uint4 &y = x[2 * i + k];
+      y = make_uint4(y.x & keep, y.y & keep, y.z & keep, y.w & keep);
+      const f16x8 h = as_f16x8(y);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(static_cast<float>(h[e])));
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  m = red[0];
+#pragma unroll
+  for (int w = 1; w < kCompThreads / 64; ++w) m = fmaxf(m, red[w]);
+  const float sc = m / Q8<FMT>::kMax;
+#pragma unroll
+  for (int i = 0; i < NL / 2; ++i) {
+    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
+    if (c < pieces) {
+      uint32_t w[4] = {0, 0, 0, 0};
+      if ((c / rpp) % kBlock < n) {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+          const f16x8 h = as_f16x8(x[2 * i + k]);
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            w[2 * k + e / 4] |= enc_scaled<FMT>(static_cast<float>(h[e]), sc) << (8 * (e % 4));
+        }
+      }
+      *reinterpret_cast<uint4 *>(dp + static_cast<int64_t>(c) * 8) =
+          make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+  if (threadIdx.x == 0) (is_v ? vs : ks)[db] = sc;
+}
+
 }  // namespace kvc
 
 using namespace kvc;
@@ -351,6 +493,55 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
                      static_cast<char *>(layer->k_pool), static_cast<char *>(layer->v_pool),
                      static_cast<const char *>(k_new), static_cast<const char *>(v_new), slots,
                      n_tok, H, layer->num_blocks, row_bytes);
+  return launch_status();
+}
+
+kvc_status kvc_compress_blocks(const kvc_paged_layer *src, const kvc_paged_layer *dst,
+                               const int32_t *src_ids, const int32_t *dst_ids,
+                               const int32_t *n_valid, int32_t n, void *stream) {
+  kvc_status st = check_layer(src);
+  if (st != KVC_OK) return st;
+  st = check_layer(dst);
+  if (st != KVC_OK) return st;
+  if (!is_f32_or_f16(src->kv_dtype) || !is_q8(dst->kv_dtype)) return KVC_E_UNSUPPORTED;
+  if (src->num_heads != dst->num_heads || src->head_dim != dst->head_dim) return KVC_E_INVALID;
+  if (static_cast<int64_t>(src->num_heads) * kBlock * src->head_dim > (int64_t{1} << 30))
+    return KVC_E_INVALID;  // element offsets within a block stay 32-bit
+  if (n < 0) return KVC_E_INVALID;
+  if (n == 0) return KVC_OK;
+  if (!src_ids || !dst_ids) return KVC_E_INVALID;
+  const bool f16 = src->kv_dtype == KVC_F16;
+  const bool e4m3 = dst->kv_dtype == KVC_E4M3;
+  const int64_t pieces = static_cast<int64_t>(src->num_heads) * kBlock * src->head_dim / 8;
+  if (f16 && pieces <= static_cast<int64_t>(kCompMaxLoads) * kCompThreads) {
+    if (static_cast<int64_t>(n) * 2 > INT32_MAX) return KVC_E_INVALID;
+    const int64_t per = (pieces + kCompThreads - 1) / kCompThreads;
+    using K = void (*)(const char *, const char *, uint8_t *, uint8_t *, float *, float *,
+                       const int32_t *, const int32_t *, const int32_t *, int32_t, int32_t,
+                       int32_t, int32_t);
+    const K e4[] = {compress_f16_regs_kernel<KVC_E4M3, 4>, compress_f16_regs_kernel<KVC_E4M3, 8>,
+                    compress_f16_regs_kernel<KVC_E4M3, 16>, compress_f16_regs_kernel<KVC_E4M3, 32>};
+    const K i8[] = {compress_f16_regs_kernel<KVC_I8, 4>, compress_f16_regs_kernel<KVC_I8, 8>,
+                    compress_f16_regs_kernel<KVC_I8, 16>, compress_f16_regs_kernel<KVC_I8, 32>};
+    const int sel = per <= 4 ? 0 : per <= 8 ? 1 : per <= 16 ? 2 : 3;
+    const K kr = e4m3 ? e4[sel] : i8[sel];
+    hipLaunchKernelGGL(kr, dim3(static_cast<uint32_t>(n) * 2), dim3(kCompThreads), 0,
+                       static_cast<hipStream_t>(stream), static_cast<const char *>(src->k_pool),
+                       static_cast<const char *>(src->v_pool), static_cast<uint8_t *>(dst->k_pool),
+                       static_cast<uint8_t *>(dst->v_pool), dst->k_scale, dst->v_scale, src_ids,
+                       dst_ids, n_valid, src->num_heads, src->head_dim, src->num_blocks,
+                       dst->num_blocks);
+    return launch_status();
+  }
+  auto kern = e4m3 ? (f16 ? compress_blocks_kernel<true, KVC_E4M3>
+                          : compress_blocks_kernel<false, KVC_E4M3>)
+                   : (f16 ? compress_blocks_kernel<true, KVC_I8>
+                          : compress_blocks_kernel<false, KVC_I8>);
+  hipLaunchKernelGGL(kern, dim3(n), dim3(kThreads), 0, static_cast<hipStream_t>(stream),
+                     src->k_pool, src->v_pool, static_cast<uint8_t *>(dst->k_pool),
+                     static_cast<uint8_t *>(dst->v_pool), dst->k_scale, dst->v_scale, src_ids,
+                     dst_ids, n_valid, src->num_heads, src->head_dim, src->num_blocks,
+                     dst->num_blocks);
   return launch_status();
 }
 

@@ -19,7 +19,7 @@ from __future__ import annotations
 import numpy as np
 
 from .attention import decode_row, full_causal, grouped_decode, kv_head_of, window_start
-from .codecs import e4m3_decode, fp8_write_token, i8_decode, i8_write_token
+from .codecs import compress_block, e4m3_decode, fp8_write_token, i8_decode, i8_write_token
 
 BS = 16
 _NP = {"f32": np.float32, "f16": np.float16}
@@ -95,6 +95,15 @@ class PagedCache:
             if self.k_scale is not None:
                 self.k_scale[d] = self.k_scale[s]
                 self.v_scale[d] = self.v_scale[s]
+
+    def compress_from(self, src: "PagedCache", pairs) -> None:
+        """One-shot 8-bit compression (codecs.compress_block) of blocks of a 16-bit or fp32 cache
+        into this 8-bit cache: pairs of (source block, destination block, valid slots)."""
+        if self.dtype not in ("e4m3", "i8") or src.dtype not in ("f16", "f32"):
+            raise ValueError("compression goes from a 16/32-bit cache into an 8-bit cache")
+        for s, d, n in pairs:
+            self.K[d], self.k_scale[d] = compress_block(src.K[s].astype(np.float32), n, self.dtype)
+            self.V[d], self.v_scale[d] = compress_block(src.V[s].astype(np.float32), n, self.dtype)
 
     def write(self, slots, k_new, v_new) -> None:
         """k_new, v_new: [n, H, D]; entry i goes to slot slots[i]; entries are applied in order."""

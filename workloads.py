@@ -145,6 +145,16 @@ LLAMA7B_PREFILL = Workload(
     extra={"prompt": 2048})
 
 
+# Whole-cache compression to 8 bits ("KV Cache Mechanism Explained", section 6.1, item 1;
+# "KV Cache and PagedAttention", section 7.2, item 1): the long-context shapes' fp16 cache (64
+# sequences of 4096 tokens, LLaMA-7B heads) re-encoded block by block into an int8 cache, 8
+# layers per step (the fp16 and int8 pools of 8 layers take 52 GB).
+COMPRESS_I8 = Workload(
+    name="llama7b-32x32x128-f16-to-i8-compress-paged16-b64-ctx4096-8layers", kind="paged",
+    layers=8, batch=64, heads=32, head_dim=128, kv_dtype="i8", q_dtype="f16", seed=10, ctx=4096,
+    extra={"compress_from": "f16"})
+
+
 def llama13b_lengths(w: Workload = LLAMA13B_PAGED, seed: int | None = None) -> np.ndarray:
     """Attended lengths of the LLaMA-13B paged batch: uniform in [ctx_lo, ctx_hi]."""
     g = rng(w.seed if seed is None else seed)
