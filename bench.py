@@ -370,7 +370,7 @@ class CompressBench:
 
     def oracle_layer(self, li):
         """The CPU oracle's compression of the first SAMPLE blocks of the last layer."""
-        from oracle.codecs import compress_block, i8_decode
+        from oracle.codecs import compress_block, e4m3_decode, i8_decode
 
         src = self.src[-1]
         idx = self.ids_d[:self.SAMPLE].long()
@@ -382,7 +382,8 @@ class CompressBench:
         for i in range(len(n)):
             for j, x in enumerate((ks[i], vs[i])):
                 c, s = compress_block(x, int(n[i]), self.w.kv_dtype)
-                out[j, i] = i8_decode(c) * np.float64(s)
+                dec = e4m3_decode(c) if self.w.kv_dtype == "e4m3" else i8_decode(c)
+                out[j, i] = dec * np.float64(s)
         dt = time.perf_counter() - t0
         nbytes = int(n.sum()) * self.H * self.D * 2 * ELT[self.w.extra["compress_from"]]
         return dt, out, nbytes

@@ -144,3 +144,23 @@ def test_compress_argument_errors():
     with pytest.raises(ValueError):
         kvc.compress_blocks(f16, i8, ids, ids[:1])
     kvc.compress_blocks(f16, i8, ids[:0], ids[:0])        # nothing to do
+
+
+def test_compress_skips_pairs_outside_the_pools():
+    """A pair whose source or destination id lies outside its pool writes nothing; the other
+    pairs of the call are compressed as usual."""
+    d = dev()
+    note("compress skips out-of-pool ids")
+    g = workloads.rng(13)
+    H, D, N = 2, 64, 4
+    src = PagedCache(N, H, D, "f16")
+    src.K[:] = workloads.normal(g, src.K.shape, "f16")
+    src.V[:] = workloads.normal(g, src.V.shape, "f16")
+    layer = kvc.PagedLayer(to_dev(src.K, d), to_dev(src.V, d))
+    out = kvc.PagedLayer.empty(N, H, D, "i8", device=d, fill=float("nan"))
+    ref = PagedCache(N, H, D, "i8", fill=np.nan)
+    s_ids = np.array([0, -1, 2, N, 3], dtype=np.int32)
+    d_ids = np.array([1, 0, N + 5, 2, -7], dtype=np.int32)
+    kvc.compress_blocks(layer, out, to_dev(s_ids, d), to_dev(d_ids, d))
+    ref.compress_from(src, [(0, 1, 16)])          # the only pair inside both pools
+    _compare_pools(out, ref)
