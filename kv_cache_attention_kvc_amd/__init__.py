@@ -299,6 +299,20 @@ def _ptr(t) -> int:
     return t.data_ptr()
 
 
+def _ptr_i32(t) -> int:
+    """Device pointer of an int32 index tensor (block tables, lengths, positions, block ids)."""
+    if t.dtype != _torch().int32:
+        raise ValueError(f"index tensor must be int32, got {t.dtype}")
+    return _ptr(t)
+
+
+def _ptr_i64(t) -> int:
+    """Device pointer of an int64 slot tensor."""
+    if t.dtype != _torch().int64:
+        raise ValueError(f"slot tensor must be int64, got {t.dtype}")
+    return _ptr(t)
+
+
 def _stream(stream) -> int:
     torch = _torch()
     s = torch.cuda.current_stream() if stream is None else stream
@@ -390,7 +404,7 @@ def append_contig(k_cache, v_cache, pos, k_new, v_new, stream=None) -> None:
     if k_new.dtype != k_cache.dtype or v_new.dtype != v_cache.dtype:
         raise ValueError("new K/V must have the cache dtype")
     _check(_lib().kvc_append_contig(_ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), B, H, S,
-                                    D, _ptr(pos), k_new.shape[1], _ptr(k_new), _ptr(v_new),
+                                    D, _ptr_i32(pos), k_new.shape[1], _ptr(k_new), _ptr(v_new),
                                     _stream(stream)), "kvc_append_contig")
 
 
@@ -399,7 +413,7 @@ def copy_blocks(layer: PagedLayer, src, dst, stream=None) -> None:
     if n == 0:
         return
     st = layer.struct()
-    _check(_lib().kvc_copy_blocks(ctypes.byref(st), _ptr(src), _ptr(dst), n, _stream(stream)),
+    _check(_lib().kvc_copy_blocks(ctypes.byref(st), _ptr_i32(src), _ptr_i32(dst), n, _stream(stream)),
            "kvc_copy_blocks")
 
 
@@ -411,7 +425,7 @@ def write_paged(layer: PagedLayer, slots, k_new, v_new, stream=None) -> None:
     if tuple(k_new.shape) != (n, layer.heads, layer.head_dim) or k_new.shape != v_new.shape:
         raise ValueError("k_new/v_new must be [n, H, D]")
     st = layer.struct()
-    _check(_lib().kvc_write_paged(ctypes.byref(st), _ptr(slots), n, _ptr(k_new), _ptr(v_new),
+    _check(_lib().kvc_write_paged(ctypes.byref(st), _ptr_i64(slots), n, _ptr(k_new), _ptr(v_new),
                                   _dtype_code(k_new), _stream(stream)), "kvc_write_paged")
 
 
@@ -426,8 +440,8 @@ def compress_blocks(src: PagedLayer, dst: PagedLayer, src_ids, dst_ids, n_valid=
     if n == 0:
         return
     s1, s2 = src.struct(), dst.struct()
-    _check(_lib().kvc_compress_blocks(ctypes.byref(s1), ctypes.byref(s2), _ptr(src_ids),
-                                      _ptr(dst_ids), None if n_valid is None else _ptr(n_valid),
+    _check(_lib().kvc_compress_blocks(ctypes.byref(s1), ctypes.byref(s2), _ptr_i32(src_ids),
+                                      _ptr_i32(dst_ids), None if n_valid is None else _ptr_i32(n_valid),
                                       n, _stream(stream)), "kvc_compress_blocks")
 
 
@@ -445,7 +459,7 @@ def decode_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, ou
     ws = _workspace(B, H, D, workspace, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(_lib().kvc_decode_partial_contig(
-        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(ctx_lens),
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr_i32(ctx_lens),
         B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_partial_contig")
     return out, ws
@@ -460,8 +474,8 @@ def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, 
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(_lib().kvc_decode_partial_paged(
-        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_partial_paged")
     return out, ws
 
@@ -484,7 +498,7 @@ def decode_attn_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=N
     ws = _workspace(B, H, D, workspace, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(_lib().kvc_decode_attn_contig(
-        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr(ctx_lens),
+        _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache), _ptr_i32(ctx_lens),
         B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_attn_contig")
     return out
@@ -504,8 +518,8 @@ def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, sca
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(_lib().kvc_decode_attn_paged(
-        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_attn_paged")
     return out
 
@@ -528,7 +542,7 @@ def _append_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, max_c
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(getattr(_lib(), name)(
         _ptr(q), _dtype_code(q), _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
-        _ptr(ctx_lens), _ptr(k_new), _ptr(v_new), B, H, S, D, int(max_ctx), float(scale),
+        _ptr_i32(ctx_lens), _ptr(k_new), _ptr(v_new), B, H, S, D, int(max_ctx), float(scale),
         _ptr(out), _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -546,8 +560,8 @@ def _append_paged_call(name, q, layer, block_tables, ctx_lens, k_new, v_new, max
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(getattr(_lib(), name)(
-        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(ctx_lens), _ptr(k_new), _ptr(v_new), B, int(max_ctx), float(scale), _ptr(out),
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), _ptr(k_new), _ptr(v_new), B, int(max_ctx), float(scale), _ptr(out),
         _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -610,7 +624,7 @@ def _gqa_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, scale, out, w
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(getattr(_lib(), name)(
         _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
-        _ptr(ctx_lens), B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out),
+        _ptr_i32(ctx_lens), B, H, S, D, int(max_ctx), float(scale), _ptr(out), _dtype_code(out),
         _ptr(ws), ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -629,8 +643,8 @@ def _gqa_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, scale, out,
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(getattr(_lib(), name)(
-        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -685,7 +699,7 @@ def _window_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, window, sc
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(getattr(_lib(), name)(
         _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
-        _ptr(ctx_lens), B, H, S, D, int(max_ctx), int(window), float(scale), _ptr(out),
+        _ptr_i32(ctx_lens), B, H, S, D, int(max_ctx), int(window), float(scale), _ptr(out),
         _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -704,8 +718,8 @@ def _window_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, window, 
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(getattr(_lib(), name)(
-        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(ctx_lens), B, int(max_ctx), int(window), float(scale), _ptr(out), _dtype_code(out),
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), int(window), float(scale), _ptr(out), _dtype_code(out),
         _ptr(ws), ws.numel(), _stream(stream)), name)
     return out, ws
 
@@ -753,7 +767,7 @@ def prefill_contig(q, k_cache, v_cache, q_start, ctx_lens, scale=None, out=None,
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(_lib().kvc_prefill_contig(
         _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
-        _ptr(q_start), _ptr(ctx_lens), B, H, S, D, q.shape[0], float(scale), _ptr(out),
+        _ptr_i32(q_start), _ptr_i32(ctx_lens), B, H, S, D, q.shape[0], float(scale), _ptr(out),
         _dtype_code(out), _stream(stream)), "kvc_prefill_contig")
     return out
 
@@ -771,7 +785,7 @@ def prefill_paged(q, layer: PagedLayer, block_tables, q_start, ctx_lens, scale=N
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()
     _check(_lib().kvc_prefill_paged(
-        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr(block_tables), block_tables.shape[1],
-        _ptr(q_start), _ptr(ctx_lens), B, q.shape[0], float(scale), _ptr(out), _dtype_code(out),
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(q_start), _ptr_i32(ctx_lens), B, q.shape[0], float(scale), _ptr(out), _dtype_code(out),
         _stream(stream)), "kvc_prefill_paged")
     return out
