@@ -325,21 +325,125 @@ compress_blocks_kernel(const void *sk, const void *sv, uint8_t *dk, uint8_t *dv,
 }
 
 
-// Single-read compression of fp16 blocks: one workgroup of kCompThreads per (pair, K or V). The
+// Single-read compression of fp16 blocks: one workgroup of T threads per (pair, K or V). The
 // block (H*16*D fp16, NL 16-byte pieces per thread at most) stays in registers between the
 // maximum and the encoding, so each source byte is read from memory once. Thread t takes pieces
-// t, t + kCompThreads, ...; a piece is 8 consecutive values of one (head, slot) row. NL is the
-// smallest of 4, 8, 16, 32 that covers the block, so that small blocks leave registers for a
-// second workgroup per CU.
-constexpr int kCompThreads = 512;
-constexpr int kCompMaxLoads = 32;  // H*D <= 8192 (e.g. 64 heads of 128)
+// t, t + T, ...; a piece is 8 consecutive values of one (head, slot) row. NL is the smallest of
+// 4, 8, 16 that covers the block with T = 512 threads (more waves per CU for small blocks);
+// blocks of more than 8192 pieces take T = 1024.
+//
+// Encoding is instruction-bound, not memory-bound, if every value pays an IEEE division, so the
+// codes come from v = x * r with r = RN(1/s), rounded once (fused), and each value whose v lies
+// close to a rounding boundary of the format is redone with the division. Bound: r is within
+// 2^-24 relative of 1/s and the product adds one rounding, so v is within 2^-23 relative of x/s,
+// and RN(x/s) within 2^-24 of it; |x/s| <= limit*(1 + 2^-24) since |x| <= max|x| and
+// s = RN(max|x| / limit). A boundary further from v than that leaves RN(x/s) on v's side, so
+// both round to the same code. The shortcut needs a finite, non-zero s (a block maximum that is
+// 0, infinite or NaN takes the division everywhere).
+constexpr int kCompMaxPieces = 1024 * 16;   // H*D <= 8192 (e.g. 64 heads of 128)
 
-template <int FMT, int NL>
-__global__ void __launch_bounds__(kCompThreads)
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// Lane-wise unsigned maximum of two pairs of 16-bit fields.
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// fma(fp16 x, r, c) with one rounding (v_fma_mix_f32; x is widened exactly).
+__device__ __forceinline__ float fma_f16_f32(_Float16 x, float r, float c) {
+  return __builtin_fmaf(static_cast<float>(x), r, c);
+}
+
+// int8: v = RN(x*r + 128) is within 2^-16 + 2^-17 of x/s + 128 (|x/s| <= 127 + 2^-16), and
+// RN(x/s) within 2^-18 of x/s; a half-integer further than 2^-14 from v therefore lies on neither
+// side, and rint(v) - 128 is the code. The result is the code + 128 as a float (1 .. 255).
+__device__ __forceinline__ float i8_biased_code(_Float16 x, float r, float s) {
+  const float v = fma_f16_f32(x, r, 128.0f);
+  const float t = __builtin_rintf(v);
+  if (__builtin_expect(fabsf(v - t) > 0.5f - 0x1p-14f, 0))  // near a tie: exact quotient
+    return __builtin_rintf(fminf(fmaxf(static_cast<float>(x) / s, -127.0f), 127.0f)) + 128.0f;
+  return t;
+}
+
+// e4m3: v = RN(x*r) (sign of zero kept) is within 3 units in the last place (fp32) of RN(x/s).
+// In the normal range the code is v's top 3 mantissa bits rounded to nearest even, unless the 20
+// bits below lie within 8 units of the half-way pattern; codes below 2^-6 (subnormal steps)
+// and zeros take the exact path. No saturation arises: |v| < 464 rounds to at most 448.
+__device__ __forceinline__ uint32_t e4m3_code(_Float16 x, float r, float s) {
+  const uint32_t u = __float_as_uint(fma_f16_f32(x, r, -0.0f));
+  const uint32_t a = u & 0x7FFFFFFFu;
+  const uint32_t rem = a & 0xFFFFFu;
+  const bool hard = a < 0x3C800000u || (rem - 0x7FFF8u) <= 16u;
+  if (__builtin_expect(hard, 0)) return e4m3_encode(static_cast<float>(x) / s);
+  // exponent rebias 127 -> 7 and round-to-nearest-even on the 20 dropped bits; the sign moves
+  // from bit 11 to bit 7 (bits 7..10 are zero for |v| in [2^-6, 464))
+  const uint32_t c = (u + 0x7FFFFu - (120u << 23) + ((u >> 20) & 1u)) >> 20;
+  return (c & 0x7Fu) | ((c >> 4) & 0x80u);
+}
+
+// Code of x/s for a scale that is 0 (the block holds only zeros), +inf (an infinite value in
+// the block) or NaN (a NaN in the block), without the division: x/0 is never formed (zeros keep
+// their sign in e4m3); x/inf is a signed zero for finite x and NaN for infinite x; x/NaN is NaN.
+// NaN codes are 0 in int8 and 0x7F in e4m3 (the quotient NaN is the positive default NaN).
+template <int FMT>
+__device__ __forceinline__ uint32_t degenerate_code(_Float16 x, float s) {
+  if constexpr (FMT == KVC_I8) {
+    return 0u;
+  } else {
+    const uint32_t b = __builtin_bit_cast(uint16_t, x);
+    const uint32_t sign = (b >> 8) & 0x80u;
+    const bool x_finite = (b & 0x7C00u) != 0x7C00u;
+    if (s == 0.f || (s > 0.f && x_finite)) return sign;
+    return 0x7Fu;
+  }
+}
+
+// Codes of the thread's piece pairs (see compress_f16_regs_kernel), stored 16 bytes a pair; FAST
+// takes the reciprocal path (finite, non-zero scale), else every value is divided.
+template <int FMT, int NL, int T, bool FAST>
+__device__ __forceinline__ void encode_pairs(const uint4 (&x)[NL], uint32_t keep_bits,
+                                             int32_t pieces, uint8_t *dp, float sc) {
+  const float r = FAST ? 1.0f / sc : 0.f;
+#pragma unroll
+  for (int i = 0; i < NL / 2; ++i) {
+    // the pair index is formed here, not kept from the loads: holding NL/2 offsets across the
+    // encoding would take registers the data needs
+    int32_t t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    const int32_t c = 2 * (t + i * T);
+    if (c >= pieces) continue;
+    const uint32_t keep = 0u - ((keep_bits >> i) & 1u);
+    uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const f16x8 h = as_f16x8(x[2 * i + k]);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        uint32_t &wd = w[2 * k + e / 4];
+        if constexpr (!FAST)
+          wd |= degenerate_code<FMT>(h[e], sc) << (8 * (e % 4));
+        else if constexpr (FMT == KVC_I8)
+          wd = __builtin_amdgcn_cvt_pk_u8_f32(i8_biased_code(h[e], r, sc), e % 4, wd);
+        else
+          wd |= e4m3_code(h[e], r, sc) << (8 * (e % 4));
+      }
+    }
+    if constexpr (FAST && FMT == KVC_I8) {  // biased bytes back to two's complement
+#pragma unroll
+      for (int j = 0; j < 4; ++j) w[j] ^= 0x80808080u;
+    }
+    *reinterpret_cast<uint4 *>(dp + static_cast<int64_t>(c) * 8) =
+        make_uint4(w[0] & keep, w[1] & keep, w[2] & keep, w[3] & keep);
+  }
+}
+
+template <int FMT, int NL, int T>
+__global__ void __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(T == 512 ? 6 : 4)))
 compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *dv, float *ks,
                          float *vs, const int32_t *src, const int32_t *dst, const int32_t *nval,
                          int32_t H, int32_t D, int32_t src_blocks, int32_t dst_blocks) {
-  __shared__ float red[kCompThreads / 64];
+  __shared__ uint32_t red[T / 64];
   const int32_t pair = blockIdx.x >> 1;
   const bool is_v = blockIdx.x & 1;
   const int32_t sb = src[pair];
@@ -352,58 +456,53 @@ compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *d
   const int32_t rpp = D / 8;                  // pieces per (head, slot) row
   const char *sp = (is_v ? sv : sk) + static_cast<int64_t>(sb) * pieces * 16;
   uint8_t *dp = (is_v ? dv : dk) + static_cast<int64_t>(db) * pieces * 8;
-  // Thread t takes the piece pairs (2u, 2u + 1), u = t + i * kCompThreads: both pieces lie in
+  // Thread t takes the piece pairs (2u, 2u + 1), u = t + i * T: both pieces lie in
   // one (head, slot) row (a row has D/8 >= 8 pieces), and their 16 codes form one 16-byte store.
   // Every load is issued before any is used (a load per branch would wait for each in turn);
-  // pairs past the block read its first pair instead, and pieces of slots past the valid ones
-  // are zeroed after the load, so their values take no part.
+  // pairs past the block read its first pair instead. Pieces of slots past the valid ones and
+  // pairs past the block are masked out of the maximum, and their codes are cleared.
   uint4 x[NL];
 #pragma unroll
   for (int i = 0; i < NL / 2; ++i) {
-    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
+    const int32_t c = 2 * (threadIdx.x + i * T);
     const int64_t off = static_cast<int64_t>(c < pieces ? c : 0) * 16;
     x[2 * i] = *reinterpret_cast<const uint4 *>(sp + off);
     x[2 * i + 1] = *reinterpret_cast<const uint4 *>(sp + off + 16);
   }
-  float m = 0.f;
+  // Block maximum of |x| over fp16 bit patterns: without the sign bit, the order of the patterns
+  // of numbers is the order of their magnitudes, and a NaN pattern exceeds every number, so a
+  // NaN among the values gives a NaN maximum (and scale).
+  uint32_t mx = 0u;
+  uint32_t keep_bits = 0u;  // bit i: piece pair i is in the block and in a valid slot
 #pragma unroll
   for (int i = 0; i < NL / 2; ++i) {
-    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
-    const uint32_t keep = c < pieces && (c / rpp) % kBlock < n ? ~0u : 0u;
+    const int32_t c = 2 * (threadIdx.x + i * T);
+    const bool keep = c < pieces && (c / rpp) % kBlock < n;
+    keep_bits |= static_cast<uint32_t>(keep) << i;
+    const uint32_t am = keep ? 0x7FFF7FFFu : 0u;
 #pragma unroll
     for (int k = 0; k < 2; ++k) {
-      uint4 &y = x[2 * i + k];
-      y = make_uint4(y.x & keep, y.y & keep, y.z & keep, y.w & keep);
-      const f16x8 h = as_f16x8(y);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(static_cast<float>(h[e])));
+      const uint4 &y = x[2 * i + k];
+      mx = max_u16x2(mx, y.x & am);
+      mx = max_u16x2(mx, y.y & am);
+      mx = max_u16x2(mx, y.z & am);
+      mx = max_u16x2(mx, y.w & am);
     }
   }
-  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  uint32_t m = max(mx & 0xFFFFu, mx >> 16);
+  for (int off = 32; off > 0; off >>= 1) m = max(m, static_cast<uint32_t>(__shfl_xor(m, off)));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   m = red[0];
 #pragma unroll
-  for (int w = 1; w < kCompThreads / 64; ++w) m = fmaxf(m, red[w]);
-  const float sc = m / Q8<FMT>::kMax;
-#pragma unroll
-  for (int i = 0; i < NL / 2; ++i) {
-    const int32_t c = 2 * (threadIdx.x + i * kCompThreads);
-    if (c < pieces) {
-      uint32_t w[4] = {0, 0, 0, 0};
-      if ((c / rpp) % kBlock < n) {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-          const f16x8 h = as_f16x8(x[2 * i + k]);
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            w[2 * k + e / 4] |= enc_scaled<FMT>(static_cast<float>(h[e]), sc) << (8 * (e % 4));
-        }
-      }
-      *reinterpret_cast<uint4 *>(dp + static_cast<int64_t>(c) * 8) =
-          make_uint4(w[0], w[1], w[2], w[3]);
-    }
-  }
+  for (int w = 1; w < T / 64; ++w) m = max(m, red[w]);
+  const float amax = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(m)));
+  const float sc = amax / Q8<FMT>::kMax;
+  // one of two loops, chosen once per workgroup
+  if (sc > 0.f && sc < __builtin_inff())
+    encode_pairs<FMT, NL, T, true>(x, keep_bits, pieces, dp, sc);
+  else
+    encode_pairs<FMT, NL, T, false>(x, keep_bits, pieces, dp, sc);
   if (threadIdx.x == 0) (is_v ? vs : ks)[db] = sc;
 }
 
@@ -513,19 +612,23 @@ kvc_status kvc_compress_blocks(const kvc_paged_layer *src, const kvc_paged_layer
   const bool f16 = src->kv_dtype == KVC_F16;
   const bool e4m3 = dst->kv_dtype == KVC_E4M3;
   const int64_t pieces = static_cast<int64_t>(src->num_heads) * kBlock * src->head_dim / 8;
-  if (f16 && pieces <= static_cast<int64_t>(kCompMaxLoads) * kCompThreads) {
+  if (f16 && pieces <= kCompMaxPieces) {
     if (static_cast<int64_t>(n) * 2 > INT32_MAX) return KVC_E_INVALID;
-    const int64_t per = (pieces + kCompThreads - 1) / kCompThreads;
     using K = void (*)(const char *, const char *, uint8_t *, uint8_t *, float *, float *,
                        const int32_t *, const int32_t *, const int32_t *, int32_t, int32_t,
                        int32_t, int32_t);
-    const K e4[] = {compress_f16_regs_kernel<KVC_E4M3, 4>, compress_f16_regs_kernel<KVC_E4M3, 8>,
-                    compress_f16_regs_kernel<KVC_E4M3, 16>, compress_f16_regs_kernel<KVC_E4M3, 32>};
-    const K i8[] = {compress_f16_regs_kernel<KVC_I8, 4>, compress_f16_regs_kernel<KVC_I8, 8>,
-                    compress_f16_regs_kernel<KVC_I8, 16>, compress_f16_regs_kernel<KVC_I8, 32>};
-    const int sel = per <= 4 ? 0 : per <= 8 ? 1 : per <= 16 ? 2 : 3;
+    // pieces per thread at 512 threads: 4, 8 or 16; beyond, 16 at 1024 threads
+    const K e4[] = {compress_f16_regs_kernel<KVC_E4M3, 4, 512>,
+                    compress_f16_regs_kernel<KVC_E4M3, 8, 512>,
+                    compress_f16_regs_kernel<KVC_E4M3, 16, 512>,
+                    compress_f16_regs_kernel<KVC_E4M3, 16, 1024>};
+    const K i8[] = {compress_f16_regs_kernel<KVC_I8, 4, 512>,
+                    compress_f16_regs_kernel<KVC_I8, 8, 512>,
+                    compress_f16_regs_kernel<KVC_I8, 16, 512>,
+                    compress_f16_regs_kernel<KVC_I8, 16, 1024>};
+    const int sel = pieces <= 4 * 512 ? 0 : pieces <= 8 * 512 ? 1 : pieces <= 16 * 512 ? 2 : 3;
     const K kr = e4m3 ? e4[sel] : i8[sel];
-    hipLaunchKernelGGL(kr, dim3(static_cast<uint32_t>(n) * 2), dim3(kCompThreads), 0,
+    hipLaunchKernelGGL(kr, dim3(static_cast<uint32_t>(n) * 2), dim3(sel == 3 ? 1024 : 512), 0,
                        static_cast<hipStream_t>(stream), static_cast<const char *>(src->k_pool),
                        static_cast<const char *>(src->v_pool), static_cast<uint8_t *>(dst->k_pool),
                        static_cast<uint8_t *>(dst->v_pool), dst->k_scale, dst->v_scale, src_ids,

@@ -164,3 +164,97 @@ def test_compress_skips_pairs_outside_the_pools():
     kvc.compress_blocks(layer, out, to_dev(s_ids, d), to_dev(d_ids, d))
     ref.compress_from(src, [(0, 1, 16)])          # the only pair inside both pools
     _compare_pools(out, ref)
+
+
+def _boundary_blocks(fmt, H, D, g):
+    """Source blocks [N, H, 16, D] (fp16) whose quotients x/scale sit on or next to the format's
+    rounding boundaries, plus degenerate maxima."""
+    n = H * 16 * D
+    blocks = []
+    if fmt == "i8":
+        # maximum 127 gives scale 1: every k + 1/2 is an exact tie between two codes
+        ties = np.arange(-127, 127, dtype=np.float64) + 0.5
+    else:
+        # maximum 448 gives scale 1: midpoints of neighbouring e4m3 values are exact ties (four
+        # significant bits, so exact in fp16), subnormal steps included
+        from oracle.codecs import e4m3_decode
+        vals = np.unique(np.abs(e4m3_decode(np.arange(0x7F, dtype=np.uint8))))
+        ties = np.concatenate([(vals[1:] + vals[:-1]) / 2, vals])
+    x = np.resize(ties, n) * np.where(g.random(n) < 0.5, -1.0, 1.0)
+    x[0] = 127.0 if fmt == "i8" else 448.0
+    blocks.append(x)
+    blocks.append(np.where(g.random(n) < 0.5, -0.0, 0.0))          # all zeros: scale 0
+    wide = g.standard_normal(n) * 10.0 ** g.uniform(-7, 0, n)       # many tiny quotients
+    blocks.append(wide)
+    blocks.append(g.standard_normal(n) * 1e-4)                      # fp16 subnormals
+    if fmt == "i8":                                                 # non-finite maxima
+        inf = g.standard_normal(n)
+        inf[5] = np.inf
+        blocks.append(inf)
+        nan = g.standard_normal(n)
+        nan[9] = np.nan
+        blocks.append(nan)
+    return np.stack([b.reshape(H, 16, D) for b in blocks]).astype(np.float16)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "e4m3"])
+def test_compress_rounding_boundaries(fmt):
+    """Ties, near-ties and degenerate block maxima at the long-context shape (32 heads of 128,
+    the register-resident kernel): codes and scales equal the oracle's bit for bit."""
+    d = dev()
+    note(f"compress rounding boundaries -> {fmt}")
+    H, D = 32, 128
+    g = workloads.rng(33)
+    blocks = _boundary_blocks(fmt, H, D, g)
+    N = blocks.shape[0]
+    src = PagedCache(N, H, D, "f16")
+    src.K[:] = blocks
+    src.V[:] = -blocks[::-1]
+    layer = kvc.PagedLayer(to_dev(src.K, d), to_dev(src.V, d))
+    out = kvc.PagedLayer.empty(N, H, D, fmt, device=d, fill=float("nan"))
+    ref = PagedCache(N, H, D, fmt, fill=np.nan)
+    ids = np.arange(N, dtype=np.int32)
+    kvc.compress_blocks(layer, out, to_dev(ids, d), to_dev(ids[::-1].copy(), d))
+    ref.compress_from(src, [(i, N - 1 - i, 16) for i in range(N)])
+    _compare_pools(out, ref)
+
+
+@pytest.mark.parametrize("fmt", ["i8", "e4m3"])
+def test_compress_full_layer_sampled(fmt):
+    """The benchmark's compression at full size (64 sequences x 4096 tokens, 32 heads x 128, one
+    layer over a shuffled pool), in its launch configuration: every block compressed in one
+    call; sampled blocks' codes and scales bit-exact against the oracle, which takes each
+    block's values from the generated tensors through the slot map."""
+    from oracle.codecs import compress_block
+    d = dev()
+    note(f"compress full layer -> {fmt}")
+    w = workloads.COMPRESS_I8
+    B, H, D, T = w.batch, w.heads, w.head_dim, w.ctx
+    nblk = workloads.blocks_for(T)
+    N = B * nblk
+    pool = kvc.Pool(N, nblk, order=workloads.llama13b_pool_order(N, w.seed))
+    seqs = [pool.alloc() for _ in range(B)]
+    slots = np.concatenate([pool.append([s], T)[0] for s in seqs])
+    src = kvc.PagedLayer.empty(N, H, D, "f16", device=d, fill=float("nan"))
+    k = workloads.torch_normal((len(slots), H, D), torch.float16, d, 61)
+    v = workloads.torch_normal((len(slots), H, D), torch.float16, d, 62)
+    kvc.write_paged(src, torch.from_numpy(slots).to(d), k, v)
+    tables, lens = pool.block_table(seqs)
+    ids = np.concatenate([tables[b][:nblk] for b in range(B)]).astype(np.int32)
+    nval = np.full(len(ids), 16, np.int32)
+    dst = kvc.PagedLayer.empty(N, H, D, fmt, device=d, fill=float("nan"))
+    ids_d = to_dev(ids, d)
+    kvc.compress_blocks(src, dst, ids_d, ids_d, to_dev(nval, d))
+    torch.cuda.synchronize()
+    blk_of = slots // 16
+    rng = np.random.default_rng(12)
+    for p in rng.choice(ids, size=24, replace=False):
+        tok = np.nonzero(blk_of == p)[0]
+        assert len(tok) == 16
+        order = np.argsort(slots[tok] % 16)
+        tok_d = torch.from_numpy(tok[order]).to(d)
+        for pool_g, sc_g, x in ((dst.k_pool, dst.k_scale, k), (dst.v_pool, dst.v_scale, v)):
+            xb = x[tok_d].float().cpu().numpy().transpose(1, 0, 2)      # [H, 16, D]
+            codes, s = compress_block(xb, 16, fmt)
+            np.testing.assert_array_equal(pool_g[int(p)].cpu().numpy(), codes)
+            assert sc_g[int(p)].item() == s

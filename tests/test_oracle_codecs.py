@@ -312,3 +312,28 @@ def test_compress_block_equals_writer_when_the_first_token_holds_the_maximum(fmt
     c1, s1 = compress_block(x, n, fmt)
     assert s1 == s
     np.testing.assert_array_equal(c1, codes)
+
+
+def test_compress_block_ties_go_to_even_codes():
+    """At scale 1 (block maximum equal to the limit) a value half-way between two codes takes
+    the even one: int8 k + 1/2 -> the even integer; e4m3 midpoints -> the code with an even
+    last mantissa bit. A NaN among the valid values makes the scale NaN (and int8 codes 0)."""
+    k = np.arange(-127, 127, dtype=np.float64)
+    x = np.zeros((1, 16, 256), np.float32)
+    x[0, 0, :254] = k + 0.5
+    x[0, 1, 0] = 127.0
+    codes, s = compress_block(x, 16, "i8")
+    assert s == 1.0
+    want = np.where(np.mod(k, 2) == 0, k, k + 1)
+    np.testing.assert_array_equal(codes[0, 0, :254].astype(np.int64), want.astype(np.int64))
+    # e4m3: 1.0 (0x38) and 1.125 (0x39) -> midpoint 1.0625 goes to 0x38; 1.1875 to 0x3A (1.25)
+    y = np.zeros((1, 16, 4), np.float32)
+    y[0, 0, :3] = [1.0625, 1.1875, -1.0625]
+    y[0, 1, 0] = 448.0
+    c8, s8 = compress_block(y, 16, "e4m3")
+    assert s8 == 1.0
+    assert list(c8[0, 0, :3]) == [0x38, 0x3A, 0xB8]
+    nan = x.copy()
+    nan[0, 2, 3] = np.nan
+    c, s = compress_block(nan, 16, "i8")
+    assert np.isnan(s) and not c.any()
