@@ -227,8 +227,11 @@ kvc_status kvc_write_paged(const kvc_paged_layer *layer, const int64_t *slots, i
  * For each pair the destination block's K scale is fp32(max|K| / limit) over the valid slots of
  * every head (limit 448 for e4m3, 127 for int8), each valid value is stored as the code of
  * fp32(x / scale) (the write rule's encoding; signed zero while the scale is 0), the other slots
- * get code 0, and the same for V. Source values past n_valid are never read. kvc_write_paged can
- * then continue writing a compressed partial block with its running-maximum rule. */
+ * get code 0, and the same for V. Source values past n_valid take no part (they may hold
+ * anything, NaN included). A NaN among the valid values makes the scale NaN (codes 0 for int8,
+ * 0x7F for e4m3); an infinite one makes it +inf (finite values then get zero codes).
+ * kvc_write_paged can then continue writing a compressed partial block with its running-maximum
+ * rule. */
 kvc_status kvc_compress_blocks(const kvc_paged_layer *src, const kvc_paged_layer *dst,
                                const int32_t *src_ids, const int32_t *dst_ids,
                                const int32_t *n_valid, int32_t n, void *stream);
