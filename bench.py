@@ -6,7 +6,7 @@ block copies, the new token's K/V write, decode attention pass 1 (split-context 
 softmax) and pass 2 (merge of split sequence-heads). With `--append fused` (the default for
 f32/f16 caches) the new token's K/V is stored by pass 1 itself, which takes that row from the
 new K/V instead of reading it back; `--append separate` runs the cache writer first (always the
-case for 8-bit (e4m3, int8) caches, whose block scale may change). Inputs are
+case for 8-bit (e4m3, int8) caches, whose block scale may change, and rolling windows). Inputs are
 synthetic and already resident in device memory when timing starts; each step grows every
 sequence by one token.
 
@@ -150,7 +150,12 @@ class PagedBench:
                 kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li, self.stream)
-            if self.fused:
+            if self.fused and self.G > 1:
+                kvc.append_decode_gqa_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
+                                                    self.knew[li], self.vnew[li], self.max_ctx,
+                                                    scale=self.scale, out=self.out[li],
+                                                    workspace=self.ws)
+            elif self.fused:
                 kvc.append_decode_partial_paged(self.q[li], layer, self.tab_d, self.len_d,
                                                 self.knew[li], self.vnew[li], self.max_ctx,
                                                 scale=self.scale, out=self.out[li],
@@ -665,12 +670,12 @@ def main():
         K, W = w.extra["decode_steps"], 0
     print(f"[bench] setting up {w.name}: {layers} layers, {K} timed + {W} warm-up steps",
           file=sys.stderr, flush=True)
-    separate = (w.kv_dtype in ("e4m3", "i8") or w.extra.get("group", 1) > 1
-                or "window" in w.extra or w is workloads.LLAMA7B_PREFILL)
+    separate = (w.kv_dtype in ("e4m3", "i8") or "window" in w.extra
+                or w is workloads.LLAMA7B_PREFILL)
     fused = args.append == "fused" or (args.append == "auto" and not separate)
     if fused and separate:
-        print("--append fused: 8-bit caches, shared K/V heads and rolling windows take the "
-              "separate writer", file=sys.stderr)
+        print("--append fused: 8-bit caches and rolling windows take the separate writer",
+              file=sys.stderr)
         sys.exit(2)
     path = "fused" if fused else "separate"
     prefill = w is workloads.LLAMA7B_PREFILL

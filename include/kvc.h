@@ -358,7 +358,7 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
  * query heads of a group from each K/V tile it loads, on the matrix cores, gq being the largest
  * divisor of G up to 16; each K/V byte is then read from HBM G/gq times (once for G <= 16).
  * Other dtype combinations run one query head per wavefront (each K/V byte read G times).
- * No append variant. */
+ * kvc_append_decode_gqa_* below are the append-and-attend variants. */
 size_t kvc_gqa_workspace_bytes(int32_t B, int32_t H_kv, int32_t G, int32_t D);
 
 kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
@@ -387,6 +387,43 @@ kvc_status kvc_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_
 kvc_status kvc_decode_gqa_merge(int32_t B, int32_t H_kv, int32_t G, int32_t D, void *out,
                                 kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                 void *stream);
+/* Append and attend in one pass with shared K/V heads: the kvc_append_decode_* contract
+ * (section 3.1 of "LLM Inference Acceleration -- KV Cache", as above) with G query heads per K/V
+ * head as for kvc_decode_gqa_*. k_new, v_new: [B][H_kv][D], one row per sequence and K/V head,
+ * of the cache's dtype (KVC_F32 or KVC_F16; 8-bit caches return KVC_E_UNSUPPORTED). Every query
+ * head of a group scores the new row from k_new/v_new; the row is stored into the cache once.
+ * Output and cache contents equal kvc_write_paged / kvc_append_contig of the same rows followed
+ * by kvc_decode_gqa_*, bit for bit. The _partial forms are pass 1 alone; follow them with
+ * kvc_decode_gqa_merge. */
+kvc_status kvc_append_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                        void *k_cache, void *v_cache, kvc_dtype kv_dtype,
+                                        const int32_t *ctx_lens, const void *k_new,
+                                        const void *v_new, int32_t B, int32_t H_kv, int32_t S_max,
+                                        int32_t D, int32_t max_ctx, float scale, void *out,
+                                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                        void *stream);
+kvc_status kvc_append_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                       const kvc_paged_layer *layer, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                       const void *k_new, const void *v_new, int32_t B,
+                                       int32_t max_ctx, float scale, void *out,
+                                       kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                       void *stream);
+kvc_status kvc_append_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                                void *k_cache, void *v_cache, kvc_dtype kv_dtype,
+                                                const int32_t *ctx_lens, const void *k_new,
+                                                const void *v_new, int32_t B, int32_t H_kv,
+                                                int32_t S_max, int32_t D, int32_t max_ctx,
+                                                float scale, void *out, kvc_dtype out_dtype,
+                                                void *workspace, size_t ws_bytes, void *stream);
+kvc_status kvc_append_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                               const kvc_paged_layer *layer,
+                                               const int32_t *block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                               const void *k_new, const void *v_new, int32_t B,
+                                               int32_t max_ctx, float scale, void *out,
+                                               kvc_dtype out_dtype, void *workspace,
+                                               size_t ws_bytes, void *stream);
 
 /* ==================================================================================== *
  * Rolling window ("KV Cache Mechanism Explained", section 8, item 2: the cache keeps only the

@@ -25,7 +25,8 @@ __all__ = [
     "decode_gqa_contig", "decode_gqa_paged", "decode_gqa_partial_contig",
     "decode_gqa_partial_paged", "decode_gqa_merge", "decode_window_contig", "decode_window_paged",
     "decode_window_partial_contig", "decode_window_partial_paged", "prefill_contig",
-    "prefill_paged", "compress_blocks",
+    "prefill_paged", "compress_blocks", "append_decode_gqa_contig", "append_decode_gqa_paged",
+    "append_decode_gqa_partial_contig", "append_decode_gqa_partial_paged",
 ]
 
 F32, F16, E4M3, I8 = 0, 1, 2, 3
@@ -46,7 +47,8 @@ EXPORTS = [
     "kvc_decode_gqa_partial_contig", "kvc_decode_gqa_partial_paged", "kvc_decode_gqa_merge",
     "kvc_decode_window_contig", "kvc_decode_window_paged", "kvc_decode_window_partial_contig",
     "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
-    "kvc_compress_blocks",
+    "kvc_compress_blocks", "kvc_append_decode_gqa_contig", "kvc_append_decode_gqa_paged",
+    "kvc_append_decode_gqa_partial_contig", "kvc_append_decode_gqa_partial_paged",
 ]
 
 
@@ -147,6 +149,12 @@ def load_library() -> ctypes.CDLL:
     for name in ("kvc_decode_gqa_paged", "kvc_decode_gqa_partial_paged"):
         sig[name] = (ctypes.c_int, paged_gqa)
     sig["kvc_gqa_workspace_bytes"] = (ctypes.c_size_t, [_I32, _I32, _I32, _I32])
+    contig_gqa_append = contig_gqa[:7] + [_P, _P] + contig_gqa[7:]   # k_new, v_new after lens
+    paged_gqa_append = paged_gqa[:7] + [_P, _P] + paged_gqa[7:]
+    for name in ("kvc_append_decode_gqa_contig", "kvc_append_decode_gqa_partial_contig"):
+        sig[name] = (ctypes.c_int, contig_gqa_append)
+    for name in ("kvc_append_decode_gqa_paged", "kvc_append_decode_gqa_partial_paged"):
+        sig[name] = (ctypes.c_int, paged_gqa_append)
     contig_win = contig_gqa[:12] + [_I32] + contig_gqa[12:]   # window after max_ctx
     paged_win = paged_gqa[:9] + [_I32] + paged_gqa[9:]
     for name in ("kvc_decode_window_contig", "kvc_decode_window_partial_contig"):
@@ -685,6 +693,74 @@ def decode_gqa_merge(B, H_kv, G, D, out, workspace, stream=None):
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "kvc_decode_gqa_merge")
     return out
+
+
+def _append_gqa_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx, scale,
+                            out, workspace, stream):
+    B, H, S, D = k_cache.shape
+    if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    G = _gqa_group(q, H)
+    _check_new(k_new, v_new, B, H, D, k_cache.dtype)
+    out = _out_for(q, out)
+    ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
+    scale = 1.0 / math.sqrt(D) if scale is None else scale
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, _ptr(k_cache), _ptr(v_cache), _dtype_code(k_cache),
+        _ptr_i32(ctx_lens), _ptr(k_new), _ptr(v_new), B, H, S, D, int(max_ctx), float(scale),
+        _ptr(out), _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def _append_gqa_paged_call(name, q, layer, block_tables, ctx_lens, k_new, v_new, max_ctx, scale,
+                           out, workspace, stream):
+    B = q.shape[0]
+    if q.dim() != 3 or q.shape[2] != layer.head_dim:
+        raise ValueError("q must be [B, H_kv*G, D]")
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+    G = _gqa_group(q, layer.heads)
+    _check_new(k_new, v_new, B, layer.heads, layer.head_dim, layer.k_pool.dtype)
+    out = _out_for(q, out)
+    ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
+          else workspace)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(getattr(_lib(), name)(
+        _ptr(q), _dtype_code(q), G, ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), _ptr(k_new), _ptr(v_new), B, int(max_ctx), float(scale), _ptr(out),
+        _dtype_code(out), _ptr(ws), ws.numel(), _stream(stream)), name)
+    return out, ws
+
+
+def append_decode_gqa_contig(q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx, scale=None,
+                             out=None, workspace=None, stream=None):
+    """Grouped-query append and attend: store k_new/v_new [B, H_kv, D] at position
+    ctx_lens[b]-1 of the contiguous cache and attend with q [B, H_kv*G, D] in the same pass."""
+    return _append_gqa_contig_call("kvc_append_decode_gqa_contig", q, k_cache, v_cache, ctx_lens,
+                                   k_new, v_new, max_ctx, scale, out, workspace, stream)[0]
+
+
+def append_decode_gqa_partial_contig(q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx,
+                                     scale=None, out=None, workspace=None, stream=None):
+    """Pass 1 of append_decode_gqa_contig; returns (out, workspace) for decode_gqa_merge."""
+    return _append_gqa_contig_call("kvc_append_decode_gqa_partial_contig", q, k_cache, v_cache,
+                                   ctx_lens, k_new, v_new, max_ctx, scale, out, workspace, stream)
+
+
+def append_decode_gqa_paged(q, layer: PagedLayer, block_tables, ctx_lens, k_new, v_new, max_ctx,
+                            scale=None, out=None, workspace=None, stream=None):
+    """Grouped-query append and attend over a paged cache: k_new/v_new [B, H_kv, D] go to
+    position ctx_lens[b]-1 of each sequence's blocks; q is [B, H_kv*G, D]. Returns out."""
+    return _append_gqa_paged_call("kvc_append_decode_gqa_paged", q, layer, block_tables, ctx_lens,
+                                  k_new, v_new, max_ctx, scale, out, workspace, stream)[0]
+
+
+def append_decode_gqa_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, k_new, v_new,
+                                    max_ctx, scale=None, out=None, workspace=None, stream=None):
+    """Pass 1 of append_decode_gqa_paged; returns (out, workspace) for decode_gqa_merge."""
+    return _append_gqa_paged_call("kvc_append_decode_gqa_partial_paged", q, layer, block_tables,
+                                  ctx_lens, k_new, v_new, max_ctx, scale, out, workspace, stream)
 
 
 # ---- rolling window --------------------------------------------------------------------------

@@ -290,8 +290,9 @@ struct TileRegs {
   uint4 v[G::LOADS];
   int32_t nt;       // valid rows (0: the tile contributes nothing)
   int32_t lo;       // rolling window: rows below lo lie before the window (first tile only)
-  int32_t new_row;  // append mode: the row of the new token in this tile, else -1
-  const char *kt;   // the tile's K and V in the cache (where the new row is stored)
+  int32_t new_row;    // append mode: the row of the new token in this tile, else -1
+  int32_t store_row;  // new_row if this wavefront stores it into the cache, else -1
+  const char *kt;     // the tile's K and V in the cache (where the new row is stored)
   const char *vt;
   float ks, vs;     // fp8 block scales
 };
@@ -336,6 +337,9 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
   // That tile is the last of its sequence-head, so it always takes the general path below and
   // the full-tile path carries no per-lane address choice.
   t.new_row = (a.k_new && t.nt > 0 && j == (L - 1) / kBlock) ? (L - 1) % kBlock : -1;
+  // query heads sharing the K/V head as several pairs all read the new row from k_new/v_new;
+  // the pair of the group's first query head (q row a multiple of G) stores it
+  t.store_row = t.new_row >= 0 && qrow % a.G == 0 ? t.new_row : -1;
   if (t.nt == kBlock && t.new_row < 0 && (!WIN || t.lo == 0)) {
     const int lane_off = g * G::ROW + c * 16;
 #pragma unroll
@@ -363,11 +367,11 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
 template <int KV, int D, bool QF16, int GQ>
 __device__ __forceinline__ void store_new_row(const TileRegs<KV, D, QF16, GQ> &t, int g, int c) {
   using G = Geo<KV, D>;
-  if (t.new_row < 0) return;
+  if (t.store_row < 0) return;
   const int lane_off = g * G::ROW + c * 16;
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
-    if (g + i * G::TPL == t.new_row) {
+    if (g + i * G::TPL == t.store_row) {
       *reinterpret_cast<uint4 *>(const_cast<char *>(t.kt) + lane_off + i * G::TPL * G::ROW) =
           t.k[i];
       *reinterpret_cast<uint4 *>(const_cast<char *>(t.vt) + lane_off + i * G::TPL * G::ROW) =
@@ -719,6 +723,11 @@ struct MfmaCore {
     int32_t nt;
     int32_t lo;  // rolling window: rows below lo lie before the window
     float ks, vs;
+    // append mode (fp16 cache), as in TileRegs: the new token's row, read from k_new/v_new, and
+    // the row this wavefront stores into the cache at kt/vt (-1: none)
+    int32_t new_row, store_row;
+    const char *kt;
+    const char *vt;
   };
   struct State {
     uint4 q[NQK];  // q operand, 8 fp16 dims per score MFMA
@@ -736,7 +745,7 @@ struct MfmaCore {
   // LDS column (8 fp16) of 16-byte column c of row t
   static __device__ __forceinline__ int swz(int t, int c) { return c ^ (2 * ((t >> 2) & 3)); }
 
-  __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t,
+  __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t qrow,
                         int32_t jt, int32_t phys, int32_t L, bool live) const {
     const char *kt;
     const char *vt;
@@ -763,12 +772,55 @@ struct MfmaCore {
     // its first row: their weights are 0, and their V values are finite, so 0 * v stays 0
     const int last = max(t.nt, 1) - 1;
     auto row_of = [&](int r) { return min(WIN ? max(r, t.lo) : r, last); };
+    t.new_row = t.store_row = -1;
+    if constexpr (KV == KVC_F16 && !WIN) {
+      t.kt = kt;
+      t.vt = vt;
+      if (a.k_new && t.nt > 0 && jt == (L - 1) / kBlock) {
+        // the tile of the new token (its last row, so rows past the end repeat it): lanes of
+        // that row load it from k_new/v_new; the group's first pair stores it when consumed
+        t.new_row = last;
+        t.store_row = qrow % a.G == 0 ? last : -1;
+        const int64_t new_off = bkv * G::ROW;
+        const char *kr = row_of(j) == last ? a.k_new + new_off + g * 16
+                                           : kt + row_of(j) * G::ROW + g * 16;
+#pragma unroll
+        for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
+#pragma unroll
+        for (int i = 0; i < G::LOADS; ++i) {
+          const int r = row_of(gv + i * G::TPL);
+          t.v[i] = load_stream(r == last ? a.v_new + new_off + cv * 16
+                                         : vt + r * G::ROW + cv * 16);
+        }
+        return;
+      }
+    }
     const char *kr = kt + row_of(j) * G::ROW + g * 16;
 #pragma unroll
     for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i)
       t.v[i] = load_stream(vt + row_of(gv + i * G::TPL) * G::ROW + cv * 16);
+  }
+
+  // Append mode: the lanes holding the new row store it into the cache (K: lanes of MFMA row
+  // store_row, 64 bytes apart; V: the wave-contiguous lanes of that row).
+  __device__ void store_new(const Tile &t) const {
+    if constexpr (KV == KVC_F16 && !WIN) {
+      if (t.store_row < 0) return;
+      if (j == t.store_row) {
+#pragma unroll
+        for (int c = 0; c < KL; ++c)
+          *reinterpret_cast<uint4 *>(const_cast<char *>(t.kt) + t.store_row * G::ROW + g * 16 +
+                                     c * 64) = t.k[c];
+      }
+#pragma unroll
+      for (int i = 0; i < G::LOADS; ++i) {
+        if (gv + i * G::TPL == t.store_row)
+          *reinterpret_cast<uint4 *>(const_cast<char *>(t.vt) + t.store_row * G::ROW +
+                                     cv * 16) = t.v[i];
+      }
+    }
   }
 
   // q operand of head j of the pair: 16-byte chunk of the fp16 q row for score MFMA n (the dims
@@ -820,6 +872,7 @@ struct MfmaCore {
             q8x8_to_f16(t.v[i].z, t.v[i].w);
       }
     }
+    store_new(t);
     // scores of positions 4g..4g+3 for head j
     f32x4 sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -1396,8 +1449,9 @@ kvc_status launch_partial(const PartialPlan &pl, void *stream) {
 using namespace kvc;
 
 // Pass 1 for both layouts. G query heads share each K/V head (q and out have H*G heads);
-// k_new/v_new non-null selects append mode (G = 1 only); window > 0 attends only the last
-// `window` positions of each sequence.
+// k_new/v_new non-null selects append mode (k_new/v_new hold one row per sequence and K/V
+// head; not with a window); window > 0 attends only the last `window` positions of each
+// sequence.
 static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
                                  const void *v_cache, kvc_dtype kv_dtype, const int32_t *ctx_lens,
                                  const void *k_new, const void *v_new, int32_t B, int32_t H,
@@ -1412,7 +1466,7 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, co
   if (st != KVC_OK || pl.grid == 0) return st;
   if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || G != 1)) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || window > 0)) return KVC_E_INVALID;
   pl.a.k = static_cast<const char *>(k_cache);
   pl.a.v = static_cast<const char *>(v_cache);
   pl.a.k_new = static_cast<const char *>(k_new);
@@ -1443,7 +1497,7 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
     return KVC_E_INVALID;
   if (is_q8(kv) && (!layer->k_scale || !layer->v_scale)) return KVC_E_INVALID;
   if ((k_new != nullptr) != (v_new != nullptr)) return KVC_E_INVALID;
-  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || G != 1)) return KVC_E_INVALID;
+  if (k_new && (!aligned16(k_new) || !aligned16(v_new) || window > 0)) return KVC_E_INVALID;
   pl.a.k = static_cast<const char *>(layer->k_pool);
   pl.a.v = static_cast<const char *>(layer->v_pool);
   pl.a.k_scale = layer->k_scale;
@@ -1705,6 +1759,63 @@ kvc_status kvc_append_decode_paged(const void *q, kvc_dtype q_dtype, const kvc_p
   if (st != KVC_OK) return st;
   return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
                           ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                                void *k_cache, void *v_cache, kvc_dtype kv_dtype,
+                                                const int32_t *ctx_lens, const void *k_new,
+                                                const void *v_new, int32_t B, int32_t H_kv,
+                                                int32_t S_max, int32_t D, int32_t max_ctx,
+                                                float scale, void *out, kvc_dtype out_dtype,
+                                                void *workspace, size_t ws_bytes, void *stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  return partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B,
+                        H_kv, S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes,
+                        stream);
+}
+
+kvc_status kvc_append_decode_gqa_partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                               const kvc_paged_layer *layer,
+                                               const int32_t *block_tables,
+                                               int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                               const void *k_new, const void *v_new, int32_t B,
+                                               int32_t max_ctx, float scale, void *out,
+                                               kvc_dtype out_dtype, void *workspace,
+                                               size_t ws_bytes, void *stream) {
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  return partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
+                       v_new, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G,
+                                        void *k_cache, void *v_cache, kvc_dtype kv_dtype,
+                                        const int32_t *ctx_lens, const void *k_new,
+                                        const void *v_new, int32_t B, int32_t H_kv, int32_t S_max,
+                                        int32_t D, int32_t max_ctx, float scale, void *out,
+                                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                        void *stream) {
+  kvc_status st = kvc_append_decode_gqa_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
+                                                       ctx_lens, k_new, v_new, B, H_kv, S_max, D,
+                                                       max_ctx, scale, out, out_dtype, workspace,
+                                                       ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_append_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
+                                       const kvc_paged_layer *layer, const int32_t *block_tables,
+                                       int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                       const void *k_new, const void *v_new, int32_t B,
+                                       int32_t max_ctx, float scale, void *out,
+                                       kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
+                                       void *stream) {
+  kvc_status st = kvc_append_decode_gqa_partial_paged(q, q_dtype, G, layer, block_tables,
+                                                      max_blocks_per_seq, ctx_lens, k_new, v_new,
+                                                      B, max_ctx, scale, out, out_dtype,
+                                                      workspace, ws_bytes, stream);
+  if (st != KVC_OK) return st;
+  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
+                              ws_bytes, stream);
 }
 
 }  // extern "C"

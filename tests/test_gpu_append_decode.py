@@ -210,3 +210,99 @@ def test_fused_two_phase_and_refusals():
     bad = flat[1:].view(3, H, D)
     with pytest.raises(kvc.KvcError, match="INVALID"):
         kvc.append_decode_paged(q, layer, tdv, tlv, bad, bad, 1000)
+
+
+# (dtype, D, G): fp16 runs the matrix-core kernel (G = 32 splits each group into two pairs of
+# 16 query heads that share the K/V tile); fp32 runs one query head per wavefront (G pairs per
+# K/V head). Either way the new row is stored once and every pair scores it from k_new/v_new.
+GQA_CASES = [("f16", 128, 2), ("f16", 128, 8), ("f16", 64, 3), ("f16", 128, 32), ("f32", 64, 4)]
+
+
+@pytest.mark.parametrize("dtype,D,G", GQA_CASES)
+def test_paged_gqa_fused_equals_write_then_decode(dtype, D, G):
+    d = dev()
+    note(f"append-decode gqa paged {dtype} D={D} G={G}")
+    H = 2
+    prior = [max(L - 1, 0) for L in LENS]
+    g, pool, model, seqs, layer, ref, data = _paged_setup(d, dtype, D, prior, H=H, seed=D + G)
+    live = [s for s, L in zip(seqs, LENS) if L > 0]
+    slots, src, dst = pool.append(live, 1)
+    ms, cow = model.append(live, 1)
+    assert list(slots) == ms and not cow
+    tables, tl = pool.block_table(seqs)
+    assert list(tl) == LENS
+    B = len(LENS)
+    k_new = workloads.normal(g, (B, H, D), dtype)
+    v_new = workloads.normal(g, (B, H, D), dtype)
+    q = workloads.normal(g, (B, H * G, D), dtype)
+    rows = [b for b, L in enumerate(LENS) if L > 0]
+    ref.write(slots, k_new[rows], v_new[rows])
+    tdv, tlv = to_dev(tables, d), to_dev(tl, d)
+    qd, kd, vd = to_dev(q, d), to_dev(k_new, d), to_dev(v_new, d)
+    other = _clone_layer(layer)
+    fused = kvc.append_decode_gqa_paged(qd, layer, tdv, tlv, kd, vd, max(LENS), scale=scale_of(D))
+    kvc.write_paged(other, to_dev(slots, d), to_dev(k_new[rows], d), to_dev(v_new[rows], d))
+    plain = kvc.decode_gqa_paged(qd, other, tdv, tlv, max(LENS), scale=scale_of(D))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    assert torch.equal(layer.k_pool.view(torch.int8), other.k_pool.view(torch.int8))
+    assert torch.equal(layer.v_pool.view(torch.int8), other.v_pool.view(torch.int8))
+    _compare_pools(layer, ref)
+    check(fused.float().cpu().numpy(), ref.decode(q, tables, tl, scale_of(D)), TOL[dtype])
+    assert fused[LENS.index(0)].float().abs().sum().item() == 0.0
+
+
+@pytest.mark.parametrize("dtype,D,G", [("f16", 128, 8), ("f16", 128, 32), ("f32", 64, 4)])
+def test_contig_gqa_fused_equals_append_then_decode(dtype, D, G):
+    d = dev()
+    note(f"append-decode gqa contig {dtype} D={D} G={G}")
+    H, S = 2, 528
+    B = len(LENS)
+    g = workloads.rng(300 + D + G)
+    K = workloads.normal(g, (B, S, H, D), dtype)
+    V = workloads.normal(g, (B, S, H, D), dtype)
+    q = workloads.normal(g, (B, H * G, D), dtype)
+    ref = ContigCache(B, H, S, D, dtype, fill=np.nan)
+    kc = torch.full((B, H, S, D), float("nan"), dtype=TD[dtype], device=d)
+    vc = torch.full_like(kc, float("nan"))
+    for b, L in enumerate(LENS):           # prefill positions [0, L-1)
+        if L > 1:
+            p = np.full(B, S, np.int32)
+            p[b] = 0
+            kvc.append_contig(kc, vc, to_dev(p, d), to_dev(K[:, :L - 1], d),
+                              to_dev(V[:, :L - 1], d))
+            ref.append(p, K[:, :L - 1], V[:, :L - 1])
+    pos = np.array([L - 1 if L > 0 else S for L in LENS], np.int32)
+    k_new, v_new = K[np.arange(B), np.maximum(pos, 0) % S], V[np.arange(B), np.maximum(pos, 0) % S]
+    ref.append(pos, k_new[:, None], v_new[:, None])
+    kc2, vc2 = kc.clone(), vc.clone()
+    lens = to_dev(np.array(LENS, np.int32), d)
+    qd, kd, vd = to_dev(q, d), to_dev(k_new, d), to_dev(v_new, d)
+    fused = kvc.append_decode_gqa_contig(qd, kc, vc, lens, kd, vd, max(LENS), scale=scale_of(D))
+    kvc.append_contig(kc2, vc2, to_dev(pos, d), kd[:, None].contiguous(), vd[:, None].contiguous())
+    plain = kvc.decode_gqa_contig(qd, kc2, vc2, lens, max(LENS), scale=scale_of(D))
+    torch.cuda.synchronize()
+    assert torch.equal(fused, plain)
+    np.testing.assert_array_equal(kc.cpu().numpy(), ref.K)
+    np.testing.assert_array_equal(vc.cpu().numpy(), ref.V)
+    check(fused.float().cpu().numpy(), ref.decode(q, LENS, scale_of(D)), TOL[dtype])
+
+
+def test_gqa_fused_refusals():
+    """8-bit caches refuse the fused call (their block scale may change); k_new of the wrong
+    head count is refused by the binding."""
+    d = dev()
+    note("append-decode gqa refusals")
+    H, D, G = 2, 128, 4
+    g, pool, model, seqs, layer, ref, data = _paged_setup(d, "e4m3", D, [5, 9], H=H, seed=3)
+    tables, tl = pool.block_table(seqs)
+    q = to_dev(workloads.normal(g, (2, H * G, D), "f16"), d)
+    kn = torch.zeros((2, H, D), dtype=layer.k_pool.dtype, device=d)   # codes of the cache dtype
+    with pytest.raises(kvc.KvcError):
+        kvc.append_decode_gqa_paged(q, layer, to_dev(tables, d), to_dev(tl, d), kn, kn.clone(), 9)
+    g, pool, model, seqs, layer, ref, data = _paged_setup(d, "f16", D, [5, 9], H=H, seed=4)
+    tables, tl = pool.block_table(seqs)
+    wrong = to_dev(workloads.normal(g, (2, H * G, D), "f16"), d)
+    with pytest.raises(ValueError):
+        kvc.append_decode_gqa_paged(q, layer, to_dev(tables, d), to_dev(tl, d), wrong,
+                                    wrong.clone(), 9)
