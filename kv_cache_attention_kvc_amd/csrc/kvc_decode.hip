@@ -339,7 +339,10 @@ __device__ __forceinline__ void fetch_tile(const DecodeArgs &a, TileRegs<KV, D, 
   t.new_row = (a.k_new && t.nt > 0 && j == (L - 1) / kBlock) ? (L - 1) % kBlock : -1;
   // query heads sharing the K/V head as several pairs all read the new row from k_new/v_new;
   // the pair of the group's first query head (q row a multiple of G) stores it
-  t.store_row = t.new_row >= 0 && qrow % a.G == 0 ? t.new_row : -1;
+  // (q rows number below 2^32: at most 4096 sequences of 2^20 query heads)
+  t.store_row = -1;
+  if (t.new_row >= 0 && static_cast<uint32_t>(qrow) % static_cast<uint32_t>(a.G) == 0)
+    t.store_row = t.new_row;
   if (t.nt == kBlock && t.new_row < 0 && (!WIN || t.lo == 0)) {
     const int lane_off = g * G::ROW + c * 16;
 #pragma unroll
@@ -702,9 +705,10 @@ struct VecCore {
 //     scale multiplies the scores. O is held in units of a reference V scale; a tile's weights
 //     are multiplied by its block's scale over the reference (kept within [1/16, 16], else the
 //     reference moves to this block's scale and O is rescaled).
-template <bool PAGED, int KV, int D, bool WIN>
+template <bool PAGED, int KV, int D, bool WIN, bool APPEND>
 struct MfmaCore {
   static_assert(KV == KVC_F16 || is_q8(KV), "fp16 or 8-bit cache");
+  static_assert(!APPEND || (KV == KVC_F16 && !WIN), "append mode: fp16 cache, no window");
   using G = Geo<KV, D>;            // wave-contiguous geometry (V loads)
   static constexpr int kD = D;
   static constexpr bool kWin = WIN;
@@ -723,8 +727,8 @@ struct MfmaCore {
     int32_t nt;
     int32_t lo;  // rolling window: rows below lo lie before the window
     float ks, vs;
-    // append mode (fp16 cache), as in TileRegs: the new token's row, read from k_new/v_new, and
-    // the row this wavefront stores into the cache at kt/vt (-1: none)
+    // append mode (APPEND instances), as in TileRegs: the new token's row, read from
+    // k_new/v_new, and the row this wavefront stores into the cache at kt/vt (-1: none)
     int32_t new_row, store_row;
     const char *kt;
     const char *vt;
@@ -772,28 +776,28 @@ struct MfmaCore {
     // its first row: their weights are 0, and their V values are finite, so 0 * v stays 0
     const int last = max(t.nt, 1) - 1;
     auto row_of = [&](int r) { return min(WIN ? max(r, t.lo) : r, last); };
-    t.new_row = t.store_row = -1;
-    if constexpr (KV == KVC_F16 && !WIN) {
+    if constexpr (APPEND) {
+      // the tile of the new token (its last row, so rows past the end repeat it): lanes of that
+      // row load it from k_new/v_new; the group's first pair stores it when the tile is consumed
       t.kt = kt;
       t.vt = vt;
-      if (a.k_new && t.nt > 0 && jt == (L - 1) / kBlock) {
-        // the tile of the new token (its last row, so rows past the end repeat it): lanes of
-        // that row load it from k_new/v_new; the group's first pair stores it when consumed
-        t.new_row = last;
-        t.store_row = qrow % a.G == 0 ? last : -1;
-        const int64_t new_off = bkv * G::ROW;
-        const char *kr = row_of(j) == last ? a.k_new + new_off + g * 16
-                                           : kt + row_of(j) * G::ROW + g * 16;
+      const bool has_new = t.nt > 0 && jt == (L - 1) / kBlock;  // wave-uniform
+      t.new_row = has_new ? last : -1;
+      t.store_row = -1;
+      if (has_new && static_cast<uint32_t>(qrow) % static_cast<uint32_t>(a.G) == 0)
+        t.store_row = last;
+      const int64_t new_off = bkv * G::ROW;
+      const int rk = row_of(j);
+      const char *kr = rk == t.new_row ? a.k_new + new_off + g * 16 : kt + rk * G::ROW + g * 16;
 #pragma unroll
-        for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
+      for (int c = 0; c < KL; ++c) t.k[c] = load_stream(kr + c * 64);
 #pragma unroll
-        for (int i = 0; i < G::LOADS; ++i) {
-          const int r = row_of(gv + i * G::TPL);
-          t.v[i] = load_stream(r == last ? a.v_new + new_off + cv * 16
-                                         : vt + r * G::ROW + cv * 16);
-        }
-        return;
+      for (int i = 0; i < G::LOADS; ++i) {
+        const int r = row_of(gv + i * G::TPL);
+        t.v[i] = load_stream(r == t.new_row ? a.v_new + new_off + cv * 16
+                                            : vt + r * G::ROW + cv * 16);
       }
+      return;
     }
     const char *kr = kt + row_of(j) * G::ROW + g * 16;
 #pragma unroll
@@ -806,7 +810,7 @@ struct MfmaCore {
   // Append mode: the lanes holding the new row store it into the cache (K: lanes of MFMA row
   // store_row, 64 bytes apart; V: the wave-contiguous lanes of that row).
   __device__ void store_new(const Tile &t) const {
-    if constexpr (KV == KVC_F16 && !WIN) {
+    if constexpr (APPEND) {
       if (t.store_row < 0) return;
       if (j == t.store_row) {
 #pragma unroll
@@ -1124,10 +1128,10 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
   run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
 }
 
-template <bool PAGED, int KV, int D, bool WIN>
+template <bool PAGED, int KV, int D, bool WIN, bool APPEND>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_mfma_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
-  using Core = MfmaCore<PAGED, KV, D, WIN>;
+  using Core = MfmaCore<PAGED, KV, D, WIN, APPEND>;
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, a.gq, f0, f1, b0, w);
   if (f0 >= f1) return;
@@ -1278,22 +1282,27 @@ PartialKernel pick_vec_d(kvc_dtype kv) {
   return nullptr;
 }
 
+// append: the instance that stores the new token's row (fp16 caches without a window); the
+// other instances carry none of that code
 template <bool PAGED, int D, bool WIN>
-PartialKernel pick_mfma_d(kvc_dtype kv) {
-  if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D, WIN>;
+PartialKernel pick_mfma_d(kvc_dtype kv, bool append) {
+  if constexpr (!WIN)
+    if (append) return kv == KVC_F16 ? decode_partial_mfma_kernel<PAGED, KVC_F16, D, false, true>
+                                     : nullptr;
+  if (kv == KVC_F16) return decode_partial_mfma_kernel<PAGED, KVC_F16, D, WIN, false>;
   if constexpr (PAGED)
-    if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D, WIN>;
+    if (kv == KVC_E4M3) return decode_partial_mfma_kernel<PAGED, KVC_E4M3, D, WIN, false>;
   if constexpr (PAGED)
-    if (kv == KVC_I8) return decode_partial_mfma_kernel<PAGED, KVC_I8, D, WIN>;
+    if (kv == KVC_I8) return decode_partial_mfma_kernel<PAGED, KVC_I8, D, WIN, false>;
   return nullptr;
 }
 
 template <bool PAGED, bool WIN>
-PartialKernel pick_kernel_w(kvc_dtype kv, int D, bool q_f16, bool mfma) {
+PartialKernel pick_kernel_w(kvc_dtype kv, int D, bool q_f16, bool mfma, bool append) {
   if (mfma) {
     if (!q_f16) return nullptr;
-    if (D == 64) return pick_mfma_d<PAGED, 64, WIN>(kv);
-    if (D == 128) return pick_mfma_d<PAGED, 128, WIN>(kv);
+    if (D == 64) return pick_mfma_d<PAGED, 64, WIN>(kv, append);
+    if (D == 128) return pick_mfma_d<PAGED, 128, WIN>(kv, append);
     return nullptr;
   }
   if (D == 64)
@@ -1304,9 +1313,9 @@ PartialKernel pick_kernel_w(kvc_dtype kv, int D, bool q_f16, bool mfma) {
 }
 
 template <bool PAGED>
-PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, bool mfma, bool window) {
-  return window ? pick_kernel_w<PAGED, true>(kv, D, q_f16, mfma)
-                : pick_kernel_w<PAGED, false>(kv, D, q_f16, mfma);
+PartialKernel pick_kernel(kvc_dtype kv, int D, bool q_f16, bool mfma, bool window, bool append) {
+  return window ? pick_kernel_w<PAGED, true>(kv, D, q_f16, mfma, append)
+                : pick_kernel_w<PAGED, false>(kv, D, q_f16, mfma, append);
 }
 
 struct PartialPlan {
@@ -1356,8 +1365,9 @@ int resident_waves_per_cu(PartialKernel k, size_t shmem) {
 }
 
 // Shared validation and planning for both layouts.
-kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype kv_dtype,
-                        const int32_t *ctx_lens, int32_t B, int32_t H, int32_t G, int32_t D,
+kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtype,
+                        kvc_dtype kv_dtype, const int32_t *ctx_lens, int32_t B, int32_t H,
+                        int32_t G, int32_t D,
                         int32_t cap, int32_t max_ctx, int32_t window, float scale, void *out,
                         kvc_dtype out_dtype, void *workspace, size_t ws_bytes, PartialPlan &pl) {
   if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0 || window < 0) return KVC_E_INVALID;
@@ -1389,8 +1399,9 @@ kvc_status plan_partial(bool paged, const void *q, kvc_dtype q_dtype, kvc_dtype 
                                                       static_cast<int64_t>(window) + kBlock - 1)
                                   : std::min(max_ctx, cap);
   const int64_t tiles_hint = static_cast<int64_t>(B) * Hp * ((span + kBlock - 1) / kBlock);
-  PartialKernel kern = paged ? pick_kernel<true>(kv_dtype, D, q_f16, gp.mfma, window > 0)
-                             : pick_kernel<false>(kv_dtype, D, q_f16, gp.mfma, window > 0);
+  PartialKernel kern =
+      paged ? pick_kernel<true>(kv_dtype, D, q_f16, gp.mfma, window > 0, append)
+            : pick_kernel<false>(kv_dtype, D, q_f16, gp.mfma, window > 0, append);
   if (!kern) return KVC_E_UNSUPPORTED;
   // staged rows per wavefront: a segment stages GQ rows at once; the matrix-core kernel also
   // holds one fp16 V tile per wavefront
@@ -1461,7 +1472,8 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, co
   if (S_max < 0) return KVC_E_INVALID;
   if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
   PartialPlan pl;
-  kvc_status st = plan_partial(false, q, q_dtype, kv_dtype, ctx_lens, B, H, G, D, S_max, max_ctx,
+  kvc_status st = plan_partial(false, k_new != nullptr, q, q_dtype, kv_dtype, ctx_lens, B, H, G,
+                               D, S_max, max_ctx,
                                window, scale, out, out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
   if (!k_cache || !v_cache || !aligned16(k_cache) || !aligned16(v_cache)) return KVC_E_INVALID;
@@ -1488,7 +1500,8 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
   if (kv != KVC_F32 && kv != KVC_F16 && !is_q8(kv)) return KVC_E_UNSUPPORTED;
   if (k_new && is_q8(kv)) return KVC_E_UNSUPPORTED;  // the block scale may change
   PartialPlan pl;
-  kvc_status st = plan_partial(true, q, q_dtype, kv, ctx_lens, B, layer->num_heads, G,
+  kvc_status st = plan_partial(true, k_new != nullptr, q, q_dtype, kv, ctx_lens, B,
+                               layer->num_heads, G,
                                layer->head_dim, max_blocks_per_seq * kBlock, max_ctx, window, scale,
                                out, out_dtype, workspace, ws_bytes, pl);
   if (st != KVC_OK || pl.grid == 0) return st;
