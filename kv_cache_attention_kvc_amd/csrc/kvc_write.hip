@@ -325,12 +325,12 @@ compress_blocks_kernel(const void *sk, const void *sv, uint8_t *dk, uint8_t *dv,
 }
 
 
-// Single-read compression of fp16 blocks: one workgroup of T threads per (pair, K or V). The
-// block (H*16*D fp16, NL 16-byte pieces per thread at most) stays in registers between the
-// maximum and the encoding, so each source byte is read from memory once. Thread t takes pieces
-// t, t + T, ...; a piece is 8 consecutive values of one (head, slot) row. NL is the smallest of
-// 4, 8, 16 that covers the block with T = 512 threads (more waves per CU for small blocks);
-// blocks of more than 8192 pieces take T = 1024.
+// Single-read compression of fp16 blocks. A unit is (pair, K or V); its block (H*16*D fp16) is
+// held in registers between the block maximum and the encoding, NL 16-byte pieces per thread at
+// most, so each source byte is read from memory once. Thread t takes pieces t, t + T, ...; a
+// piece is 8 consecutive values of one (head, slot) row. Blocks of up to 8192 pieces run on the
+// streaming kernel below (T = 512, NL = 4, 8 or 16, the smallest that covers the block); larger
+// ones, up to 16384 pieces, take one 1024-thread workgroup per unit.
 //
 // Encoding is instruction-bound, not memory-bound, if every value pays an IEEE division, so the
 // codes come from v = x * r with r = RN(1/s), rounded once (fused), and each value whose v lies
@@ -338,8 +338,8 @@ compress_blocks_kernel(const void *sk, const void *sv, uint8_t *dk, uint8_t *dv,
 // 2^-24 relative of 1/s and the product adds one rounding, so v is within 2^-23 relative of x/s,
 // and RN(x/s) within 2^-24 of it; |x/s| <= limit*(1 + 2^-24) since |x| <= max|x| and
 // s = RN(max|x| / limit). A boundary further from v than that leaves RN(x/s) on v's side, so
-// both round to the same code. The shortcut needs a finite, non-zero s (a block maximum that is
-// 0, infinite or NaN takes the division everywhere).
+// both round to the same code. The shortcut needs a finite, non-zero s; a block maximum that is
+// 0, infinite or NaN gives fixed codes (degenerate_code), with no division at all.
 constexpr int kCompMaxPieces = 1024 * 16;   // H*D <= 8192 (e.g. 64 heads of 128)
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
@@ -438,30 +438,55 @@ __device__ __forceinline__ void encode_pairs(const uint4 (&x)[NL], uint32_t keep
   }
 }
 
-template <int FMT, int NL, int T>
-__global__ void __launch_bounds__(T) __attribute__((amdgpu_waves_per_eu(T == 512 ? 6 : 4)))
-compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *dv, float *ks,
-                         float *vs, const int32_t *src, const int32_t *dst, const int32_t *nval,
-                         int32_t H, int32_t D, int32_t src_blocks, int32_t dst_blocks) {
-  __shared__ uint32_t red[T / 64];
-  const int32_t pair = blockIdx.x >> 1;
-  const bool is_v = blockIdx.x & 1;
-  const int32_t sb = src[pair];
-  const int32_t db = dst[pair];
-  if (static_cast<uint32_t>(sb) >= static_cast<uint32_t>(src_blocks) ||
-      static_cast<uint32_t>(db) >= static_cast<uint32_t>(dst_blocks))
-    return;
-  const int32_t n = nval ? min(max(nval[pair], 0), kBlock) : kBlock;
-  const int32_t pieces = H * kBlock * D / 8;  // 16-byte pieces of the block
-  const int32_t rpp = D / 8;                  // pieces per (head, slot) row
-  const char *sp = (is_v ? sv : sk) + static_cast<int64_t>(sb) * pieces * 16;
-  uint8_t *dp = (is_v ? dv : dk) + static_cast<int64_t>(db) * pieces * 8;
-  // Thread t takes the piece pairs (2u, 2u + 1), u = t + i * T: both pieces lie in
-  // one (head, slot) row (a row has D/8 >= 8 pieces), and their 16 codes form one 16-byte store.
-  // Every load is issued before any is used (a load per branch would wait for each in turn);
-  // pairs past the block read its first pair instead. Pieces of slots past the valid ones and
-  // pairs past the block are masked out of the maximum, and their codes are cleared.
-  uint4 x[NL];
+// One (pair, K or V) unit of a compression call: its source pieces, destination codes and scale
+// slot, its valid slots, and whether both ids lie in their pools (a unit outside them is skipped;
+// its loads read block 0 of the source instead).
+struct CompUnit {
+  const char *sp;
+  uint8_t *dp;
+  float *scale;
+  int32_t n;
+  bool ok;
+};
+
+struct CompArgs {
+  const char *sk, *sv;
+  uint8_t *dk, *dv;
+  float *ks, *vs;
+  const int32_t *src, *dst, *nval;
+  int32_t H, D, src_blocks, dst_blocks;
+  int32_t n_units;  // 2 * pairs
+};
+
+// Read-only int32 at a wave-uniform address, through the scalar cache: its completion is counted
+// apart from the vector loads, so waiting for a unit's ids never waits for block data in flight.
+typedef const __attribute__((address_space(4))) int32_t comp_const_i32;
+__device__ __forceinline__ int32_t comp_sload(const int32_t *p) {
+  return *(comp_const_i32 *)(p);
+}
+
+__device__ __forceinline__ CompUnit comp_unit(const CompArgs &a, int32_t u) {
+  const int32_t pair = u >> 1;
+  const bool is_v = u & 1;
+  const int32_t sb = comp_sload(a.src + pair);
+  const int32_t db = comp_sload(a.dst + pair);
+  CompUnit c;
+  c.ok = static_cast<uint32_t>(sb) < static_cast<uint32_t>(a.src_blocks) &&
+         static_cast<uint32_t>(db) < static_cast<uint32_t>(a.dst_blocks);
+  const int64_t pieces = static_cast<int64_t>(a.H) * kBlock * a.D / 8;
+  c.sp = (is_v ? a.sv : a.sk) + (c.ok ? sb : 0) * pieces * 16;
+  c.dp = (is_v ? a.dv : a.dk) + (c.ok ? db : 0) * pieces * 8;
+  c.scale = (is_v ? a.vs : a.ks) + (c.ok ? db : 0);
+  c.n = a.nval ? min(max(comp_sload(a.nval + pair), 0), kBlock) : kBlock;
+  return c;
+}
+
+// Thread t takes the piece pairs (2u, 2u + 1), u = t + i * T: both pieces lie in one (head, slot)
+// row (a row has D/8 >= 8 pieces), and their 16 codes form one 16-byte store. Every load is
+// issued before any is used (a load per branch would wait for each in turn); pairs past the block
+// read its first pair instead.
+template <int NL, int T>
+__device__ __forceinline__ void load_pieces(const char *sp, int32_t pieces, uint4 (&x)[NL]) {
 #pragma unroll
   for (int i = 0; i < NL / 2; ++i) {
     const int32_t c = 2 * (threadIdx.x + i * T);
@@ -469,15 +494,23 @@ compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *d
     x[2 * i] = *reinterpret_cast<const uint4 *>(sp + off);
     x[2 * i + 1] = *reinterpret_cast<const uint4 *>(sp + off + 16);
   }
-  // Block maximum of |x| over fp16 bit patterns: without the sign bit, the order of the patterns
-  // of numbers is the order of their magnitudes, and a NaN pattern exceeds every number, so a
-  // NaN among the values gives a NaN maximum (and scale).
+}
+
+// The unit's scale and codes from its pieces in registers (all T threads of the workgroup take
+// part; `red` is T/64 words of LDS). Pieces of slots past the valid ones and pairs past the block
+// are masked out of the maximum, and their codes are cleared. The block maximum of |x| is taken
+// over fp16 bit patterns: without the sign bit, the order of the patterns of numbers is the order
+// of their magnitudes, and a NaN pattern exceeds every number, so a NaN among the values gives a
+// NaN maximum (and scale).
+template <int FMT, int NL, int T>
+__device__ __forceinline__ void encode_unit(const uint4 (&x)[NL], const CompUnit &u,
+                                            int32_t pieces, int32_t rpp, uint32_t *red) {
   uint32_t mx = 0u;
   uint32_t keep_bits = 0u;  // bit i: piece pair i is in the block and in a valid slot
 #pragma unroll
   for (int i = 0; i < NL / 2; ++i) {
     const int32_t c = 2 * (threadIdx.x + i * T);
-    const bool keep = c < pieces && (c / rpp) % kBlock < n;
+    const bool keep = c < pieces && (c / rpp) % kBlock < u.n;
     keep_bits |= static_cast<uint32_t>(keep) << i;
     const uint32_t am = keep ? 0x7FFF7FFFu : 0u;
 #pragma unroll
@@ -498,12 +531,61 @@ compress_f16_regs_kernel(const char *sk, const char *sv, uint8_t *dk, uint8_t *d
   for (int w = 1; w < T / 64; ++w) m = max(m, red[w]);
   const float amax = static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(m)));
   const float sc = amax / Q8<FMT>::kMax;
-  // one of two loops, chosen once per workgroup
+  // one of two loops, chosen once per unit
   if (sc > 0.f && sc < __builtin_inff())
-    encode_pairs<FMT, NL, T, true>(x, keep_bits, pieces, dp, sc);
+    encode_pairs<FMT, NL, T, true>(x, keep_bits, pieces, u.dp, sc);
   else
-    encode_pairs<FMT, NL, T, false>(x, keep_bits, pieces, dp, sc);
-  if (threadIdx.x == 0) (is_v ? vs : ks)[db] = sc;
+    encode_pairs<FMT, NL, T, false>(x, keep_bits, pieces, u.dp, sc);
+  if (threadIdx.x == 0) *u.scale = sc;
+}
+
+// One workgroup of T threads per unit (blocks of more than 8192 pieces).
+template <int FMT, int NL, int T>
+__global__ void __launch_bounds__(T) compress_f16_regs_kernel(const CompArgs a) {
+  __shared__ uint32_t red[T / 64];
+  const CompUnit u = comp_unit(a, blockIdx.x);
+  if (!u.ok) return;
+  const int32_t pieces = a.H * kBlock * a.D / 8;
+  uint4 x[NL];
+  load_pieces<NL, T>(u.sp, pieces, x);
+  encode_unit<FMT, NL, T>(x, u, pieces, a.D / 8, red);
+}
+
+// One workgroup of 512 threads per CU walks units blockIdx.x, + gridDim.x, ...: the loads of its
+// next unit are issued before the current one is encoded, into the other of two register sets,
+// so they stay in flight while it encodes and stores. (A workgroup per unit loads, then encodes:
+// its loads and its encoding never overlap, and a read-only kernel of that shape reaches only
+// about 5.8 TB/s.) The two halves of the loop reduce through separate LDS words: a wavefront
+// reaching one half's reduction has passed the other half's barrier, which every wavefront
+// reaches only after reading the words of the reduction before it.
+template <int FMT, int NL>
+__global__ void __launch_bounds__(512) compress_f16_stream_kernel(const CompArgs a) {
+  constexpr int T = 512;
+  __shared__ uint32_t red[2][T / 64];
+  const int32_t pieces = a.H * kBlock * a.D / 8;
+  const int32_t rpp = a.D / 8;
+  int32_t u = blockIdx.x;
+  if (u >= a.n_units) return;
+  // Loads are issued unconditionally (after the last unit, that unit again stands in, and is not
+  // encoded twice): a register set loaded on one path only would be merged across the loop edge
+  // with copies that wait for every load in flight.
+  uint4 xa[NL], xb[NL];
+  CompUnit ua = comp_unit(a, u), ub;
+  load_pieces<NL, T>(ua.sp, pieces, xa);
+  for (;;) {
+    const int32_t u1 = u + gridDim.x;  // uniform over the workgroup, as every test below
+    const bool more1 = u1 < a.n_units;
+    ub = comp_unit(a, more1 ? u1 : u);
+    load_pieces<NL, T>(ub.sp, pieces, xb);
+    if (ua.ok) encode_unit<FMT, NL, T>(xa, ua, pieces, rpp, red[0]);
+    if (!more1) break;
+    u = u1 + gridDim.x;
+    const bool more2 = u < a.n_units;
+    ua = comp_unit(a, more2 ? u : u1);
+    load_pieces<NL, T>(ua.sp, pieces, xa);
+    if (ub.ok) encode_unit<FMT, NL, T>(xb, ub, pieces, rpp, red[1]);
+    if (!more2) break;
+  }
 }
 
 }  // namespace kvc
@@ -614,26 +696,28 @@ kvc_status kvc_compress_blocks(const kvc_paged_layer *src, const kvc_paged_layer
   const int64_t pieces = static_cast<int64_t>(src->num_heads) * kBlock * src->head_dim / 8;
   if (f16 && pieces <= kCompMaxPieces) {
     if (static_cast<int64_t>(n) * 2 > INT32_MAX) return KVC_E_INVALID;
-    using K = void (*)(const char *, const char *, uint8_t *, uint8_t *, float *, float *,
-                       const int32_t *, const int32_t *, const int32_t *, int32_t, int32_t,
-                       int32_t, int32_t);
-    // pieces per thread at 512 threads: 4, 8 or 16; beyond, 16 at 1024 threads
-    const K e4[] = {compress_f16_regs_kernel<KVC_E4M3, 4, 512>,
-                    compress_f16_regs_kernel<KVC_E4M3, 8, 512>,
-                    compress_f16_regs_kernel<KVC_E4M3, 16, 512>,
-                    compress_f16_regs_kernel<KVC_E4M3, 16, 1024>};
-    const K i8[] = {compress_f16_regs_kernel<KVC_I8, 4, 512>,
-                    compress_f16_regs_kernel<KVC_I8, 8, 512>,
-                    compress_f16_regs_kernel<KVC_I8, 16, 512>,
-                    compress_f16_regs_kernel<KVC_I8, 16, 1024>};
-    const int sel = pieces <= 4 * 512 ? 0 : pieces <= 8 * 512 ? 1 : pieces <= 16 * 512 ? 2 : 3;
-    const K kr = e4m3 ? e4[sel] : i8[sel];
-    hipLaunchKernelGGL(kr, dim3(static_cast<uint32_t>(n) * 2), dim3(sel == 3 ? 1024 : 512), 0,
-                       static_cast<hipStream_t>(stream), static_cast<const char *>(src->k_pool),
-                       static_cast<const char *>(src->v_pool), static_cast<uint8_t *>(dst->k_pool),
-                       static_cast<uint8_t *>(dst->v_pool), dst->k_scale, dst->v_scale, src_ids,
-                       dst_ids, n_valid, src->num_heads, src->head_dim, src->num_blocks,
-                       dst->num_blocks);
+    const CompArgs ca{static_cast<const char *>(src->k_pool), static_cast<const char *>(src->v_pool),
+                      static_cast<uint8_t *>(dst->k_pool), static_cast<uint8_t *>(dst->v_pool),
+                      dst->k_scale, dst->v_scale, src_ids, dst_ids, n_valid, src->num_heads,
+                      src->head_dim, src->num_blocks, dst->num_blocks, n * 2};
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    using K = void (*)(CompArgs);
+    if (pieces > 16 * 512) {  // 16 pieces per thread at 1024 threads, a workgroup per unit
+      const K kr = e4m3 ? compress_f16_regs_kernel<KVC_E4M3, 16, 1024>
+                        : compress_f16_regs_kernel<KVC_I8, 16, 1024>;
+      hipLaunchKernelGGL(kr, dim3(static_cast<uint32_t>(n) * 2), dim3(1024), 0, s, ca);
+      return launch_status();
+    }
+    // pieces per thread at 512 threads: 4, 8 or 16; one streaming workgroup per CU
+    const K e4[] = {compress_f16_stream_kernel<KVC_E4M3, 4>,
+                    compress_f16_stream_kernel<KVC_E4M3, 8>,
+                    compress_f16_stream_kernel<KVC_E4M3, 16>};
+    const K i8[] = {compress_f16_stream_kernel<KVC_I8, 4>, compress_f16_stream_kernel<KVC_I8, 8>,
+                    compress_f16_stream_kernel<KVC_I8, 16>};
+    const int sel = pieces <= 4 * 512 ? 0 : pieces <= 8 * 512 ? 1 : 2;
+    const int64_t grid = std::min<int64_t>(static_cast<int64_t>(n) * 2, device_cu_count());
+    hipLaunchKernelGGL(e4m3 ? e4[sel] : i8[sel], dim3(static_cast<uint32_t>(grid)), dim3(512), 0,
+                       s, ca);
     return launch_status();
   }
   auto kern = e4m3 ? (f16 ? compress_blocks_kernel<true, KVC_E4M3>
