@@ -106,7 +106,9 @@ def test_gqa_two_phase_equals_single_call_and_workspace_reuse():
 
 def test_gqa_full_layer_sampled():
     """The grouped-query workload at full size (B=32, 64 query heads over 8 K/V heads, D=128,
-    lengths U[64,2048]) for one layer: sampled (sequence, query head) rows against the oracle."""
+    lengths U[64,2048]) for one layer: the separate writer + decode, and the fused call the
+    benchmark times (equal bit for bit, output and cache); sampled (sequence, query head) rows
+    against the oracle over the generated inputs."""
     from oracle.attention import decode_row
     d = dev()
     w = workloads.GQA8_PAGED
@@ -118,23 +120,31 @@ def test_gqa_full_layer_sampled():
     pool = kvc.Pool(N, MB, order=workloads.llama13b_pool_order(N, w.seed))
     seqs = [pool.alloc() for _ in range(B)]
     slots = np.concatenate([pool.append([s], int(L))[0] for s, L in zip(seqs, lens)])
-    layer = kvc.PagedLayer.empty(N, H, D, "f16", device=d)
     k = workloads.torch_normal((len(slots), H, D), torch.float16, d, w.seed * 100 + 1)
     v = workloads.torch_normal((len(slots), H, D), torch.float16, d, w.seed * 100 + 2)
+    # token rows in sequence order: sequence b's are off_b .. off_b + L_b - 1, the last the new one
+    off = np.concatenate([[0], np.cumsum(lens)])
+    last = torch.from_numpy(off[1:] - 1).to(d)
+    prior = np.concatenate([np.arange(off[b], off[b + 1] - 1) for b in range(B)])
+    prior_d = torch.from_numpy(prior).to(d)
+    layer = kvc.PagedLayer.empty(N, H, D, "f16", device=d)
+    fused_layer = kvc.PagedLayer.empty(N, H, D, "f16", device=d)
     kvc.write_paged(layer, torch.from_numpy(slots).to(d), k, v)
+    kvc.write_paged(fused_layer, torch.from_numpy(slots[prior]).to(d), k[prior_d], v[prior_d])
     tables, tl = pool.block_table(seqs)
     q = workloads.torch_normal((B, H * G, D), torch.float16, d, w.seed * 100 + 3)
-    out = kvc.decode_gqa_paged(q, layer, torch.from_numpy(tables).to(d),
-                               torch.from_numpy(tl).to(d), int(tl.max()), scale=w.scale)
+    td, tld = torch.from_numpy(tables).to(d), torch.from_numpy(tl).to(d)
+    out = kvc.decode_gqa_paged(q, layer, td, tld, int(tl.max()), scale=w.scale)
+    fused = kvc.append_decode_gqa_paged(q, fused_layer, td, tld, k[last].contiguous(),
+                                        v[last].contiguous(), int(tl.max()), scale=w.scale)
     torch.cuda.synchronize()
-    Kp, Vp = layer.k_pool.cpu().numpy(), layer.v_pool.cpu().numpy()
+    assert torch.equal(fused, out)
+    assert torch.equal(fused_layer.k_pool.view(torch.int16), layer.k_pool.view(torch.int16))
+    assert torch.equal(fused_layer.v_pool.view(torch.int16), layer.v_pool.view(torch.int16))
     qh, oh = q.float().cpu().numpy(), out.float().cpu().numpy()
     gen = np.random.default_rng(0)
     for i in gen.choice(B * H * G, size=24, replace=False):
         b, hq = int(i) // (H * G), int(i) % (H * G)
-        L = int(tl[b])
-        rows = [tables[b][t // 16] for t in range(L)]
-        offs = [t % 16 for t in range(L)]
-        Kr = Kp[rows, hq // G, offs]
-        Vr = Vp[rows, hq // G, offs]
+        Kr = k[off[b]:off[b + 1], hq // G].double().cpu().numpy()
+        Vr = v[off[b]:off[b + 1], hq // G].double().cpu().numpy()
         check(oh[b, hq], decode_row(qh[b, hq], Kr, Vr, w.scale), TOL["f16"], f"b={b} hq={hq}")

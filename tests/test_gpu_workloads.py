@@ -21,7 +21,9 @@ def _sample_pairs(rng, B, H, n):
 
 
 def test_llama7b_contiguous_full_layer():
-    """B=16, H=32, D=128, fp16, S_max=2048: prefill 2047 positions, append one, attend 2048."""
+    """B=16, H=32, D=128, fp16, S_max=2048: prefill 2047 positions, append one, attend 2048 --
+    with the separate writer and with the fused call the benchmark times (equal bit for bit);
+    sampled rows against the oracle over the generated inputs."""
     d = dev()
     w = workloads.LLAMA7B_CONTIG
     B, H, D, S = w.batch, w.heads, w.head_dim, w.s_max
@@ -32,20 +34,25 @@ def test_llama7b_contiguous_full_layer():
     vn = workloads.torch_normal((B, S, H, D), torch.float16, d, w.seed * 10 + 2)
     zeros = torch.zeros(B, dtype=torch.int32, device=d)
     kvc.append_contig(kc, vc, zeros, kn[:, :S - 1].contiguous(), vn[:, :S - 1].contiguous())
+    kf, vf = kc.clone(), vc.clone()   # the fused call's cache: positions 0 .. S-2
     kvc.append_contig(kc, vc, torch.full((B,), S - 1, dtype=torch.int32, device=d),
                       kn[:, S - 1:].contiguous(), vn[:, S - 1:].contiguous())
     q = workloads.torch_normal((B, H, D), torch.float16, d, w.seed * 10 + 3)
     lens = torch.full((B,), S, dtype=torch.int32, device=d)
     out = kvc.decode_attn_contig(q, kc, vc, lens, S, scale=w.scale)
+    fused = kvc.append_decode_contig(q, kf, vf, lens, kn[:, S - 1].contiguous(),
+                                     vn[:, S - 1].contiguous(), S, scale=w.scale)
     torch.cuda.synchronize()
     # the cache holds exactly the appended values (bitwise), in [B, H, S, D] order
     assert torch.equal(kc, kn.permute(0, 2, 1, 3)) and torch.equal(vc, vn.permute(0, 2, 1, 3))
+    assert torch.equal(fused, out)
+    assert torch.equal(kf, kc) and torch.equal(vf, vc)
     rng = np.random.default_rng(0)
     got = out.float().cpu().numpy()
     qh = q.float().cpu().numpy()
     for b, h in _sample_pairs(rng, B, H, 12):
-        want = decode_row(qh[b, h], kc[b, h].float().cpu().numpy(), vc[b, h].float().cpu().numpy(),
-                          w.scale)
+        want = decode_row(qh[b, h], kn[b, :, h].float().cpu().numpy(),
+                          vn[b, :, h].float().cpu().numpy(), w.scale)
         check(got[b, h], want, TOL["f16"], f"b={b} h={h}")
 
 
@@ -83,30 +90,38 @@ def test_llama13b_paged_full_layer():
     assert step.tolist() == mstep and len(src) == 0 and cow == []
     kn = workloads.torch_normal((B, H, D), torch.float16, d, 33)
     vn = workloads.torch_normal((B, H, D), torch.float16, d, 34)
+    fused_layer = kvc.PagedLayer(layer.k_pool.clone(), layer.v_pool.clone())  # before the append
     kvc.write_paged(layer, torch.from_numpy(step).to(d), kn, vn)
     tables, tl = pool.block_table(seqs)
     mt, ml = model.block_table(seqs)
     assert tables.tolist() == mt and tl.tolist() == ml == lens.tolist()
     q = workloads.torch_normal((B, H, D), torch.float16, d, 35)
-    out = kvc.decode_attn_paged(q, layer, torch.from_numpy(tables).to(d),
-                                torch.from_numpy(tl).to(d), int(lens.max()), scale=w.scale)
+    td, tld = torch.from_numpy(tables).to(d), torch.from_numpy(tl).to(d)
+    out = kvc.decode_attn_paged(q, layer, td, tld, int(lens.max()), scale=w.scale)
+    # the call the benchmark times: the new token stored by pass 1 itself
+    fused = kvc.append_decode_paged(q, fused_layer, td, tld, kn, vn, int(lens.max()),
+                                    scale=w.scale)
     torch.cuda.synchronize()
+    assert torch.equal(fused, out)
+    assert torch.equal(fused_layer.k_pool.view(torch.int16), layer.k_pool.view(torch.int16))
+    assert torch.equal(fused_layer.v_pool.view(torch.int16), layer.v_pool.view(torch.int16))
     got = out.float().cpu().numpy()
     qh = q.float().cpu().numpy()
-    kp = layer.k_pool.cpu().numpy()
-    vp = layer.v_pool.cpu().numpy()
+    # oracle rows from the generated inputs: sequence b's first L_b - 1 tokens are rows
+    # off_b .. off_b + L_b - 2 of k/v (appended in sequence order), its last is kn[b]/vn[b]
+    off = np.concatenate([[0], np.cumsum(lens - 1)])
     rng = np.random.default_rng(1)
     for b, h in _sample_pairs(rng, B, H, 16):
         L = int(tl[b])
-        ids = [tables[b][t // 16] for t in range(L)]
-        Kb = np.stack([kp[ids[t], h, t % 16] for t in range(L)]).astype(np.float64)
-        Vb = np.stack([vp[ids[t], h, t % 16] for t in range(L)]).astype(np.float64)
+        Kb = torch.cat([k[off[b]:off[b] + L - 1, h], kn[b, h][None]]).double().cpu().numpy()
+        Vb = torch.cat([v[off[b]:off[b] + L - 1, h], vn[b, h][None]]).double().cpu().numpy()
         check(got[b, h], decode_row(qh[b, h], Kb, Vb, w.scale), TOL["f16"], f"b={b} h={h}")
     # the appended token of every sequence is where its slot says, bit for bit
+    kp = layer.k_pool.cpu().numpy()
     knh = kn.cpu().numpy()
     for b in range(B):
-        blk, off = divmod(int(step[b]), 16)
-        np.testing.assert_array_equal(kp[blk, :, off], knh[b])
+        blk, o = divmod(int(step[b]), 16)
+        np.testing.assert_array_equal(kp[blk, :, o], knh[b])
 
 
 @pytest.mark.parametrize("prompt,copies", [(1024, 0), (1020, 7)])
