@@ -780,7 +780,10 @@ def main():
                        f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
                        f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers"),
         }
-        line["parity_layer0_max_abs_err"] = float(np.abs(got - ref).max())
+        # a sanity check of the timed run, not a parity claim: the oracle reads the cache as the
+        # library stored it (the parity tests build every oracle input from the generated data)
+        line["spot_check"] = {"max_abs_err": float(np.abs(got - ref).max()),
+                              "oracle_input": "the cache as stored on the device"}
     if args.copy_calibration:
         a = torch.ones(1 << 30, dtype=torch.uint8, device=dev)
         b = torch.empty_like(a)
