@@ -172,3 +172,20 @@ def test_parallel_sampling_counts_through_library():
         p.append(seqs, 1)
     st = p.stats()
     assert st["used"] == 135 and st["cow_copies"] == 7
+
+
+def test_binding_refuses_index_tensors_of_the_wrong_width():
+    """Block tables, lengths, positions and block ids are int32 and slots int64 in the C ABI; a
+    tensor of another integer width is refused before any call (its bytes would otherwise be
+    read as a different layout)."""
+    import torch
+    for name, good, bad in (("_ptr_i32", torch.int32, torch.int64), ("_ptr_i64", torch.int64,
+                                                                     torch.int32)):
+        fn = getattr(kvc, name)
+        width = "int32" if good == torch.int32 else "int64"
+        # the right width passes the dtype check (and then needs device memory)
+        with pytest.raises(ValueError, match="device memory"):
+            fn(torch.zeros(4, dtype=good))
+        for wrong in (bad, torch.float32):
+            with pytest.raises(ValueError, match=f"must be {width}"):
+                fn(torch.zeros(4, dtype=wrong))
