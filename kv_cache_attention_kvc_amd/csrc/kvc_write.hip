@@ -557,7 +557,8 @@ __global__ void __launch_bounds__(T) compress_f16_regs_kernel(const CompArgs a) 
 // its loads and its encoding never overlap, and a read-only kernel of that shape reaches only
 // about 5.8 TB/s.) The two halves of the loop reduce through separate LDS words: a wavefront
 // reaching one half's reduction has passed the other half's barrier, which every wavefront
-// reaches only after reading the words of the reduction before it.
+// reaches only after reading the words of the reduction before it. A skipped unit still takes
+// that barrier, so the alternation holds whichever units are skipped.
 template <int FMT, int NL>
 __global__ void __launch_bounds__(512) compress_f16_stream_kernel(const CompArgs a) {
   constexpr int T = 512;
@@ -577,13 +578,19 @@ __global__ void __launch_bounds__(512) compress_f16_stream_kernel(const CompArgs
     const bool more1 = u1 < a.n_units;
     ub = comp_unit(a, more1 ? u1 : u);
     load_pieces<NL, T>(ub.sp, pieces, xb);
-    if (ua.ok) encode_unit<FMT, NL, T>(xa, ua, pieces, rpp, red[0]);
+    if (ua.ok)
+      encode_unit<FMT, NL, T>(xa, ua, pieces, rpp, red[0]);
+    else
+      __syncthreads();
     if (!more1) break;
     u = u1 + gridDim.x;
     const bool more2 = u < a.n_units;
     ua = comp_unit(a, more2 ? u : u1);
     load_pieces<NL, T>(ua.sp, pieces, xa);
-    if (ub.ok) encode_unit<FMT, NL, T>(xb, ub, pieces, rpp, red[1]);
+    if (ub.ok)
+      encode_unit<FMT, NL, T>(xb, ub, pieces, rpp, red[1]);
+    else
+      __syncthreads();
     if (!more2) break;
   }
 }

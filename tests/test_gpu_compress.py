@@ -166,6 +166,34 @@ def test_compress_skips_pairs_outside_the_pools():
     _compare_pools(out, ref)
 
 
+@pytest.mark.parametrize("fmt", ["i8", "e4m3"])
+def test_compress_many_units_per_workgroup_with_skips(fmt):
+    """3000 pairs (6000 units: each streaming workgroup walks about 23 of them) with every fifth
+    pair outside a pool, so skipped units fall between encoded ones in each workgroup's walk:
+    every encoded block against the oracle, bit for bit, and the skipped destinations untouched."""
+    d = dev()
+    note(f"compress many units with skips -> {fmt}")
+    g = workloads.rng(14)
+    H, D, N = 4, 64, 3000
+    src = PagedCache(N, H, D, "f16")
+    src.K[:] = workloads.normal(g, src.K.shape, "f16")
+    src.V[:] = workloads.normal(g, src.V.shape, "f16")
+    src.K[:, :, :, 3] *= g.uniform(0.01, 100.0, size=(N, 1, 1)).astype(np.float16)  # scales vary
+    layer = kvc.PagedLayer(to_dev(src.K, d), to_dev(src.V, d))
+    out = kvc.PagedLayer.empty(N, H, D, fmt, device=d, fill=float("nan"))
+    ref = PagedCache(N, H, D, fmt, fill=np.nan)
+    s_ids = g.permutation(N).astype(np.int32)
+    d_ids = g.permutation(N).astype(np.int32)
+    skip = np.arange(N) % 5 == 2
+    s_ids[skip & (np.arange(N) % 2 == 0)] = N + 3       # source outside its pool
+    d_ids[skip & (np.arange(N) % 2 == 1)] = -1          # destination outside its pool
+    n_valid = g.integers(1, 17, size=N).astype(np.int32)
+    kvc.compress_blocks(layer, out, to_dev(s_ids, d), to_dev(d_ids, d), to_dev(n_valid, d))
+    ref.compress_from(src, [(int(s_ids[i]), int(d_ids[i]), int(n_valid[i]))
+                            for i in range(N) if not skip[i]])
+    _compare_pools(out, ref)
+
+
 def _boundary_blocks(fmt, H, D, g):
     """Source blocks [N, H, 16, D] (fp16) whose quotients x/scale sit on or next to the format's
     rounding boundaries, plus degenerate maxima."""
