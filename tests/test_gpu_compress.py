@@ -21,9 +21,10 @@ pytestmark = pytest.mark.gpu
 @pytest.mark.parametrize("src_dt,fmt,D,H", [
     ("f16", "i8", 128, 3), ("f16", "e4m3", 128, 3), ("f32", "i8", 64, 3), ("f32", "e4m3", 64, 3),
     ("f16", "i8", 64, 3),
-    # fp16 blocks held in registers at 8, 16 and 32 pieces per thread, and one too wide for that
+    # fp16 blocks on the streaming kernel at 8 and 16 pieces per thread, on one 1024-thread
+    # workgroup per unit (64 heads of 128), and too wide for either (two-pass kernel)
     ("f16", "i8", 128, 12), ("f16", "e4m3", 128, 32), ("f16", "i8", 128, 64),
-    ("f16", "i8", 128, 70)])
+    ("f16", "e4m3", 128, 64), ("f16", "i8", 128, 70), ("f16", "e4m3", 64, 140)])
 def test_compress_blocks_against_oracle(src_dt, fmt, D, H):
     d = dev()
     note(f"compress blocks {src_dt} -> {fmt} D={D} H={H}")
