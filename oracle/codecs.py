@@ -68,28 +68,19 @@ def e4m3_decode(codes) -> np.ndarray:
 
 def e4m3_encode(y) -> np.ndarray:
     """Nearest finite e4m3 code to each value of y (ties to the even code, saturating at 448,
-    sign bit kept, NaN -> 0x7F with the sign). Brute force over all 127 magnitudes."""
+    sign bit kept, NaN -> 0x7F with the sign). The magnitudes of the finite codes increase with
+    the code, so the two candidates for |y| are the first magnitude not below it (binary search
+    in that table) and the one before; the nearer wins, and of two equally near the even code."""
     y = np.asarray(y, dtype=np.float64)
-    flat = y.reshape(-1)
-    out = np.empty(flat.shape, dtype=np.uint8)
-    step = 4096
-    for i in range(0, flat.size, step):
-        v = flat[i:i + step]
-        a = np.abs(v)
-        nan = np.isnan(v)
-        a = np.where(nan, 0.0, a)
-        a = np.minimum(a, E4M3_MAX)          # saturation: beyond 448 (and inf) -> 448
-        dist = np.abs(a[:, None] - _MAGS[None, :])
-        dmin = dist.min(axis=1, keepdims=True)
-        cand = dist == dmin
-        # at most two candidates and they are adjacent codes; prefer the even one
-        even = cand & ((np.arange(0x7F) % 2) == 0)[None, :]
-        pick = np.where(even.any(axis=1), even.argmax(axis=1), cand.argmax(axis=1))
-        code = pick.astype(np.uint8)
-        code = np.where(nan, np.uint8(E4M3_NAN), code)
-        code = code | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
-        out[i:i + step] = code
-    return out.reshape(y.shape)
+    nan = np.isnan(y)
+    a = np.minimum(np.where(nan, 0.0, np.abs(y)), E4M3_MAX)   # beyond 448 (and inf) -> 448
+    hi = np.searchsorted(_MAGS, a, side="left")                # a <= 448 = _MAGS[-1]
+    lo = np.maximum(hi - 1, 0)
+    d_lo = a - _MAGS[lo]
+    d_hi = _MAGS[hi] - a
+    pick = np.where(d_lo < d_hi, lo, np.where(d_hi < d_lo, hi, np.where(lo % 2 == 0, lo, hi)))
+    code = np.where(nan, E4M3_NAN, pick).astype(np.uint8)
+    return (code | np.where(np.signbit(y), np.uint8(0x80), np.uint8(0))).astype(np.uint8)
 
 
 def _enc_scaled(y32: np.ndarray, s: np.float32) -> np.ndarray:
@@ -145,7 +136,8 @@ def i8_encode(y) -> np.ndarray:
 def _i8_enc_scaled(y32: np.ndarray, s: np.float32) -> np.ndarray:
     if s == 0:
         return np.zeros(y32.shape, dtype=np.int8)
-    return i8_encode((y32 / np.float32(s)).astype(np.float32))
+    with np.errstate(invalid="ignore"):   # a NaN or infinite scale is a defined case (NaN codes)
+        return i8_encode((y32 / np.float32(s)).astype(np.float32))
 
 
 def i8_write_token(codes: np.ndarray, scale, off: int, x) -> np.float32:
