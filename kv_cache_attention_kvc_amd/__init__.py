@@ -27,6 +27,7 @@ __all__ = [
     "decode_window_partial_contig", "decode_window_partial_paged", "prefill_contig",
     "prefill_paged", "compress_blocks", "append_decode_gqa_contig", "append_decode_gqa_paged",
     "append_decode_gqa_partial_contig", "append_decode_gqa_partial_paged",
+    "decode_attn_paged_noalloc",
 ]
 
 F32, F16, E4M3, I8 = 0, 1, 2, 3
@@ -49,6 +50,7 @@ EXPORTS = [
     "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
     "kvc_compress_blocks", "kvc_append_decode_gqa_contig", "kvc_append_decode_gqa_paged",
     "kvc_append_decode_gqa_partial_contig", "kvc_append_decode_gqa_partial_paged",
+    "kvc_decode_attn_paged_noalloc",
 ]
 
 
@@ -123,6 +125,9 @@ def load_library() -> ctypes.CDLL:
         "kvc_decode_attn_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P, _I32,
                                                  _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
                                                  ctypes.c_size_t, _P]),
+        "kvc_decode_attn_paged_noalloc": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer),
+                                                         _P, _I32, _P, _I32, _I32, _F, _P,
+                                                         ctypes.c_int, _P]),
         "kvc_decode_partial_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
                                                      _I32, _I32, _I32, _I32, _I32, _F, _P,
                                                      ctypes.c_int, _P, ctypes.c_size_t, _P]),
@@ -454,15 +459,53 @@ def compress_blocks(src: PagedLayer, dst: PagedLayer, src_ids, dst_ids, n_valid=
 
 
 def _out_for(q, out):
+    """The output tensor: a new one like q, or the caller's, which must have q's shape and an
+    fp32 or fp16 dtype (the library cannot see the size of device arrays)."""
     torch = _torch()
-    return torch.empty_like(q) if out is None else out
+    if out is None:
+        return torch.empty_like(q)
+    if tuple(out.shape) != tuple(q.shape):
+        raise ValueError(f"out must have q's shape {tuple(q.shape)}, got {tuple(out.shape)}")
+    if out.dtype not in (torch.float32, torch.float16):
+        raise ValueError(f"out must be float32 or float16, got {out.dtype}")
+    return out
 
+
+def _check_lens(ctx_lens, B: int) -> None:
+    """ctx_lens holds one int32 length per sequence."""
+    if ctx_lens.dim() != 1 or int(ctx_lens.numel()) != B:
+        raise ValueError(f"ctx_lens must be int32[{B}], got shape {tuple(ctx_lens.shape)}")
+
+
+def _check_tables(block_tables, B: int) -> None:
+    if block_tables.dim() != 2 or block_tables.shape[0] != B:
+        raise ValueError("block_tables must be [B, max_blocks]")
+
+
+def _check_q_start(q_start, B: int) -> None:
+    if q_start.dim() != 1 or int(q_start.numel()) != B + 1:
+        raise ValueError(f"q_start must be int32[{B + 1}], got shape {tuple(q_start.shape)}")
+
+
+def _check_merge_out(out, rows: int, D: int) -> None:
+    """The merge writes rows x D elements of out (fp32 or fp16)."""
+    torch = _torch()
+    if int(out.numel()) != rows * D or out.dtype not in (torch.float32, torch.float16):
+        raise ValueError(f"out must hold {rows} x {D} float32/float16 elements, got "
+                         f"{tuple(out.shape)} {out.dtype}")
+
+
+def _check_q_mha(q, B: int, H: int, D: int) -> None:
+    if tuple(q.shape) != (B, H, D):
+        raise ValueError(f"q must be [B, H, D] = {(B, H, D)}, got {tuple(q.shape)}")
 
 
 def decode_partial_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,
                           workspace=None, stream=None):
     """Pass 1 only (see decode_attn_contig); returns (out, workspace) for decode_merge."""
     B, H, S, D = k_cache.shape
+    _check_q_mha(q, B, H, D)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = _workspace(B, H, D, workspace, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -477,6 +520,9 @@ def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, 
                          out=None, workspace=None, stream=None):
     """Pass 1 only (see decode_attn_paged); returns (out, workspace) for decode_merge."""
     B = q.shape[0]
+    _check_q_mha(q, B, layer.heads, layer.head_dim)
+    _check_tables(block_tables, B)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
@@ -490,6 +536,7 @@ def decode_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, 
 
 def decode_merge(B, H, D, out, workspace, stream=None):
     """Pass 2: combine the split sequence-heads that pass 1 left in `workspace`."""
+    _check_merge_out(out, B * H, D)
     _check(_lib().kvc_decode_merge(B, H, D, _ptr(out), _dtype_code(out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "kvc_decode_merge")
     return out
@@ -500,8 +547,8 @@ def decode_attn_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=N
     """Single-query attention over a contiguous cache: q [B,H,D], caches [B,H,S_max,D],
     ctx_lens int32[B] on the device. Returns out [B,H,D] (q's dtype unless `out` is given)."""
     B, H, S, D = k_cache.shape
-    if tuple(q.shape) != (B, H, D):
-        raise ValueError("q must be [B, H, D]")
+    _check_q_mha(q, B, H, D)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = _workspace(B, H, D, workspace, q.device)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -517,10 +564,9 @@ def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, sca
     """Single-query attention over a paged cache: q [B,H,D], block_tables int32 [B, max_blocks]
     and ctx_lens int32[B] on the device. Returns out [B,H,D]."""
     B = q.shape[0]
-    if tuple(q.shape) != (B, layer.heads, layer.head_dim):
-        raise ValueError("q must be [B, H, D]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B:
-        raise ValueError("block_tables must be [B, max_blocks]")
+    _check_q_mha(q, B, layer.heads, layer.head_dim)
+    _check_tables(block_tables, B)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
@@ -529,6 +575,25 @@ def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, sca
         _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
         _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_attn_paged")
+    return out
+
+
+def decode_attn_paged_noalloc(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
+                              out=None, stream=None):
+    """decode_attn_paged with the library's own static workspace (kvc_decode_attn_paged_noalloc:
+    no device allocation in the call, B <= 4096). Pass `out` to allocate nothing at all. Calls
+    that may overlap in time on one GPU share that workspace and must be serialised."""
+    B = q.shape[0]
+    _check_q_mha(q, B, layer.heads, layer.head_dim)
+    _check_tables(block_tables, B)
+    _check_lens(ctx_lens, B)
+    out = _out_for(q, out)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(_lib().kvc_decode_attn_paged_noalloc(
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out),
+        _stream(stream)), "kvc_decode_attn_paged_noalloc")
     return out
 
 
@@ -542,8 +607,8 @@ def _check_new(k_new, v_new, B, H, D, dtype):
 def _append_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, max_ctx, scale, out,
                         workspace, stream):
     B, H, S, D = k_cache.shape
-    if tuple(q.shape) != (B, H, D):
-        raise ValueError("q must be [B, H, D]")
+    _check_q_mha(q, B, H, D)
+    _check_lens(ctx_lens, B)
     _check_new(k_new, v_new, B, H, D, k_cache.dtype)
     out = _out_for(q, out)
     ws = _workspace(B, H, D, workspace, q.device)
@@ -558,10 +623,9 @@ def _append_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, max_c
 def _append_paged_call(name, q, layer, block_tables, ctx_lens, k_new, v_new, max_ctx, scale, out,
                        workspace, stream):
     B = q.shape[0]
-    if tuple(q.shape) != (B, layer.heads, layer.head_dim):
-        raise ValueError("q must be [B, H, D]")
-    if block_tables.dim() != 2 or block_tables.shape[0] != B:
-        raise ValueError("block_tables must be [B, max_blocks]")
+    _check_q_mha(q, B, layer.heads, layer.head_dim)
+    _check_tables(block_tables, B)
+    _check_lens(ctx_lens, B)
     _check_new(k_new, v_new, B, layer.heads, layer.head_dim, layer.k_pool.dtype)
     out = _out_for(q, out)
     ws = _workspace(B, layer.heads, layer.head_dim, workspace, q.device)
@@ -627,6 +691,7 @@ def _gqa_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, scale, out, w
     if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
         raise ValueError("q must be [B, H_kv*G, D]")
     G = _gqa_group(q, H)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -645,6 +710,7 @@ def _gqa_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, scale, out,
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
     G = _gqa_group(q, layer.heads)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
           else workspace)
@@ -689,6 +755,7 @@ def decode_gqa_partial_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_c
 
 def decode_gqa_merge(B, H_kv, G, D, out, workspace, stream=None):
     """Pass 2 of grouped-query decode."""
+    _check_merge_out(out, B * H_kv * G, D)
     _check(_lib().kvc_decode_gqa_merge(B, H_kv, G, D, _ptr(out), _dtype_code(out),
                                        _ptr(workspace), workspace.numel(), _stream(stream)),
            "kvc_decode_gqa_merge")
@@ -701,6 +768,7 @@ def _append_gqa_contig_call(name, q, k_cache, v_cache, ctx_lens, k_new, v_new, m
     if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
         raise ValueError("q must be [B, H_kv*G, D]")
     G = _gqa_group(q, H)
+    _check_lens(ctx_lens, B)
     _check_new(k_new, v_new, B, H, D, k_cache.dtype)
     out = _out_for(q, out)
     ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
@@ -720,6 +788,7 @@ def _append_gqa_paged_call(name, q, layer, block_tables, ctx_lens, k_new, v_new,
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
     G = _gqa_group(q, layer.heads)
+    _check_lens(ctx_lens, B)
     _check_new(k_new, v_new, B, layer.heads, layer.head_dim, layer.k_pool.dtype)
     out = _out_for(q, out)
     ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
@@ -770,6 +839,7 @@ def _window_contig_call(name, q, k_cache, v_cache, ctx_lens, max_ctx, window, sc
     if q.dim() != 3 or q.shape[0] != B or q.shape[2] != D:
         raise ValueError("q must be [B, H_kv*G, D]")
     G = _gqa_group(q, H)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = new_gqa_workspace(B, H, G, D, q.device) if workspace is None else workspace
     scale = 1.0 / math.sqrt(D) if scale is None else scale
@@ -788,6 +858,7 @@ def _window_paged_call(name, q, layer, block_tables, ctx_lens, max_ctx, window, 
     if block_tables.dim() != 2 or block_tables.shape[0] != B:
         raise ValueError("block_tables must be [B, max_blocks]")
     G = _gqa_group(q, layer.heads)
+    _check_lens(ctx_lens, B)
     out = _out_for(q, out)
     ws = (new_gqa_workspace(B, layer.heads, G, layer.head_dim, q.device) if workspace is None
           else workspace)
@@ -839,6 +910,8 @@ def prefill_contig(q, k_cache, v_cache, q_start, ctx_lens, scale=None, out=None,
     if q.dim() != 3 or q.shape[2] != D:
         raise ValueError("q must be [total, H_kv*G, D]")
     G = _gqa_group(q, H)
+    _check_lens(ctx_lens, B)
+    _check_q_start(q_start, B)
     out = _out_for(q, out)
     scale = 1.0 / math.sqrt(D) if scale is None else scale
     _check(_lib().kvc_prefill_contig(
@@ -857,6 +930,8 @@ def prefill_paged(q, layer: PagedLayer, block_tables, q_start, ctx_lens, scale=N
         raise ValueError("block_tables must be [B, max_blocks]")
     B = block_tables.shape[0]
     G = _gqa_group(q, layer.heads)
+    _check_lens(ctx_lens, B)
+    _check_q_start(q_start, B)
     out = _out_for(q, out)
     scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
     st = layer.struct()

@@ -42,10 +42,7 @@ constexpr int kStep = 2 * kBlock;               // keys per step (two cache bloc
 constexpr int kMaxSeqs = 4096;
 // steps whose K/V loads are in flight in registers, and the loop unroll that keeps both the LDS
 // buffer (2) and the register set (kAhead) of every step a compile-time choice
-#ifndef KVC_PF_AHEAD
-#define KVC_PF_AHEAD 2
-#endif
-constexpr int kAhead = KVC_PF_AHEAD;
+constexpr int kAhead = 2;
 constexpr int kUnroll = kAhead == 3 ? 6 : 2;
 static_assert(kAhead >= 1 && kAhead <= 3, "prefetch depth");
 // weight headroom (log2 units): weights stay below 2^kHi, so both fp16 terms stay finite

@@ -189,3 +189,54 @@ def test_binding_refuses_index_tensors_of_the_wrong_width():
         for wrong in (bad, torch.float32):
             with pytest.raises(ValueError, match=f"must be {width}"):
                 fn(torch.zeros(4, dtype=wrong))
+
+
+def test_binding_checks_shapes_before_any_call():
+    """The C ABI cannot see the size of a device array, so the binding checks every shape it
+    can before a call: q against the cache, one length per sequence, q_start of B + 1 entries,
+    and a caller's out of q's shape (or the merge's row count). CPU tensors suffice: each check
+    raises before any pointer is taken."""
+    import torch
+    B, H, D, S = 3, 4, 64, 32
+    q = torch.zeros((B, H, D), dtype=torch.float16)
+    kc = torch.zeros((B, H, S, D), dtype=torch.float16)
+    lens = torch.zeros(B, dtype=torch.int32)
+    layer = kvc.PagedLayer(torch.zeros((8, H, 16, D), dtype=torch.float16),
+                           torch.zeros((8, H, 16, D), dtype=torch.float16))
+    tables = torch.zeros((B, 2), dtype=torch.int32)
+    for fn in (kvc.decode_attn_contig, kvc.decode_partial_contig):
+        with pytest.raises(ValueError, match="q must be"):
+            fn(q[:, :2].contiguous(), kc, kc, lens, S)
+        with pytest.raises(ValueError, match="ctx_lens must be"):
+            fn(q, kc, kc, lens[:2], S)
+        with pytest.raises(ValueError, match="out must have"):
+            fn(q, kc, kc, lens, S, out=torch.zeros((B, H, D - 1)))
+        with pytest.raises(ValueError, match="out must be float32 or float16"):
+            fn(q, kc, kc, lens, S, out=torch.zeros((B, H, D), dtype=torch.int32))
+    for fn in (kvc.decode_attn_paged, kvc.decode_partial_paged):
+        with pytest.raises(ValueError, match="q must be"):
+            fn(torch.zeros((B, H, 2 * D), dtype=torch.float16), layer, tables, lens, S)
+        with pytest.raises(ValueError, match="block_tables must be"):
+            fn(q, layer, tables[:1], lens, S)
+        with pytest.raises(ValueError, match="ctx_lens must be"):
+            fn(q, layer, tables, torch.zeros(B + 1, dtype=torch.int32), S)
+        with pytest.raises(ValueError, match="out must have"):
+            fn(q, layer, tables, lens, S, out=torch.zeros((B + 1, H, D)))
+    kn = torch.zeros((B, H, D), dtype=torch.float16)
+    with pytest.raises(ValueError, match="ctx_lens must be"):
+        kvc.append_decode_partial_paged(q, layer, tables, lens[:1], kn, kn, S)
+    with pytest.raises(ValueError, match="q must be"):
+        kvc.append_decode_contig(q[:2].contiguous(), kc, kc, lens, kn, kn, S)
+    with pytest.raises(ValueError, match="ctx_lens must be"):
+        kvc.decode_gqa_paged(torch.zeros((B, 2 * H, D), dtype=torch.float16), layer, tables,
+                             lens[:2], S)
+    with pytest.raises(ValueError, match="out must have"):
+        kvc.decode_window_contig(q, kc, kc, lens, S, 8, out=torch.zeros((B, 2 * H, D)))
+    with pytest.raises(ValueError, match="q_start must be"):
+        kvc.prefill_paged(q, layer, tables, torch.zeros(B, dtype=torch.int32), lens)
+    with pytest.raises(ValueError, match="q_start must be"):
+        kvc.prefill_contig(q, kc, kc, torch.zeros(B + 2, dtype=torch.int32), lens)
+    with pytest.raises(ValueError, match="out must hold"):
+        kvc.decode_merge(B, H, D, torch.zeros((B, H - 1, D)), torch.zeros(16, dtype=torch.uint8))
+    with pytest.raises(ValueError, match="out must hold"):
+        kvc.decode_gqa_merge(B, H, 2, D, q, torch.zeros(16, dtype=torch.uint8))
