@@ -121,6 +121,35 @@ def test_pool_matches_model_on_every_short_op_sequence():
                 m.op(*OPS[i])
 
 
+def test_pool_matches_model_on_every_op_sequence_up_to_six():
+    """Every sequence of at most 6 operations of the same 12-operation alphabet on a 4-block pool
+    (tables of 3): the C++ pool, driven through its C ABI by tests/pool_enum.cpp, folds each
+    outcome (status, results, statistics, every live table and length) into a hash that must
+    equal the one tests/golden/make_pool_enum.py computed with the oracle's PoolModel."""
+    import json
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("g++") is None:
+        pytest.skip("g++ not available")
+    want = json.load(open(os.path.join(ROOT, "tests", "golden", "pool_enum.json")))
+    with tempfile.TemporaryDirectory() as d:
+        exe = os.path.join(d, "pool_enum")
+        r = subprocess.run(["g++", "-std=c++17", "-O2", "-I", os.path.join(ROOT, "include"),
+                            os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc",
+                                         "kvc_pool.cpp"),
+                            os.path.join(ROOT, "tests", "pool_enum.cpp"), "-o", exe],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-3000:]
+        r = subprocess.run([exe, str(want["depth"])], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stdout + r.stderr
+    words = r.stdout.split()
+    nodes = [int(x) for x in words[1:1 + want["depth"]]]
+    assert nodes == want["nodes_per_depth"]
+    assert int(words[words.index("failed") + 1]) == want["failed_calls"]
+    assert words[words.index("fnv1a64") + 1] == want["fnv1a64"]
+
+
 @pytest.mark.parametrize("seed", range(6))
 def test_pool_matches_model_on_random_long_sequences(seed):
     rng = np.random.default_rng(seed)
