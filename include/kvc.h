@@ -501,6 +501,23 @@ kvc_status kvc_prefill_paged(const void *q, kvc_dtype q_dtype, int32_t G,
                              const int32_t *ctx_lens, int32_t B, int32_t total_q, float scale,
                              void *out, kvc_dtype out_dtype, void *stream);
 
+/* ==================================================================================== *
+ * Measurement: the read ceiling of an access pattern ("LLM Inference Acceleration -- KV Cache",
+ * section 6.3: decode is bound by memory bandwidth, so its rate is compared with a pure read of
+ * the same bytes in the same pattern).
+ *
+ * kvc_read_pieces reads n pieces of piece_bytes (1024, 2048, 4096 or 8192) bytes: piece i at
+ * a + offsets[i] and, when b is not NULL, at b + offsets[i] as well (the K and V tiles of one
+ * work-list entry). Wavefront w of a grid of P = waves_per_cu (1..32) x compute units reads
+ * pieces w*C .. w*C + C - 1 (C = ceil(n / P)) in order, with 16-byte non-temporal loads, and
+ * writes a checksum word to sink[w] (device uint32[sink_words], sink_words >= P; P <= 65536).
+ * a, b: 16-byte aligned device memory; offsets: device int64[n], multiples of 16, each piece
+ * inside the caller's buffers (the probe cannot check device arrays). Nothing else is computed;
+ * the caller times the launch. */
+kvc_status kvc_read_pieces(const void *a, const void *b, const int64_t *offsets, int32_t n,
+                           int32_t piece_bytes, int32_t waves_per_cu, uint32_t *sink,
+                           size_t sink_words, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,7 @@ BUILD_DIR = os.path.join(PKG, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
-SOURCES = ["kvc_pool.cpp", "kvc_decode.hip", "kvc_write.hip", "kvc_prefill.hip"]
+SOURCES = ["kvc_pool.cpp", "kvc_decode.hip", "kvc_write.hip", "kvc_prefill.hip", "kvc_probe.hip"]
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-I", INCLUDE, "-I", HERE]
 # The matrix-core decode accumulates in VGPRs (gfx950 MFMA takes C/D there): its softmax
 # rescale is VALU work on the accumulator, and AGPR accumulators would need copies both ways
