@@ -37,20 +37,35 @@ PEAK_F16_TFLOPS = 2500.0  # MI355X dense fp16 matrix-core peak, AMD's published 
 ELT = {"f32": 4, "f16": 2, "e4m3": 1, "i8": 1}
 
 
+WORKLOADS = {
+    "llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
+    "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
+    "parallel-sampling": workloads.PARALLEL_SAMPLING,
+    "parallel-sampling-cow": workloads.PARALLEL_SAMPLING_COW,
+    "gqa8-paged": workloads.GQA8_PAGED, "llama13b-window": workloads.LLAMA13B_WINDOW,
+    "llama7b-prefill": workloads.LLAMA7B_PREFILL, "i8-longctx": workloads.LONGCTX_I8,
+    "i8-compress": workloads.COMPRESS_I8,
+}
+SAMPLING = (workloads.PARALLEL_SAMPLING, workloads.PARALLEL_SAMPLING_COW)
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama13b-paged",
-                    choices=["llama13b-paged", "fp8-longctx", "llama7b-contig", "tiny-gpt",
-                             "gqa8-paged", "llama13b-window", "llama7b-prefill", "i8-longctx",
-                             "i8-compress"])
+                    choices=list(WORKLOADS))
     ap.add_argument("--layers", type=int, default=0, help="override the layer count (0: model's)")
     ap.add_argument("--append", choices=["auto", "fused", "separate"], default="auto",
                     help="store the new K/V inside attention pass 1 (fused) or with the cache "
                          "writer first (separate); auto = fused unless the cache is 8-bit")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="CPU oracle sample: layers of the last step until this many seconds "
+                         "(all BLAS threads), then the same layers on one thread")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the read-ceiling probe of the paged multi-head workloads")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv output) "
                          "of this script with --copy-calibration, and print the traffic record")
@@ -62,6 +77,8 @@ def parse():
 
 class PagedBench:
     """Paged workloads: LLaMA-13B shapes with drawn lengths, or fp8 long context."""
+
+    ORACLE_PER_LAYER = True
 
     def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
@@ -75,7 +92,6 @@ class PagedBench:
         self.B, self.H, self.D = B, H, D
         self.G = w.extra.get("group", 1)   # query heads per K/V head
         self.W = w.extra.get("window", 0)  # rolling window (0: none)
-        Hq = H * self.G
         if w.ctx:
             lens = np.full(B, w.ctx, dtype=np.int64)
         else:
@@ -87,7 +103,6 @@ class PagedBench:
         order = workloads.llama13b_pool_order(nblk, w.seed)
         self.pool = kvc.Pool(nblk, self.mbps, order=order)
         self.seqs = [self.pool.alloc() for _ in range(B)]
-        src = "f16"
         self.layers = [kvc.PagedLayer.empty(nblk, H, D, w.kv_dtype, device=dev, fill=0.0)
                        for _ in range(layers)]
         # prefill: every sequence holds L_b - 1 tokens, written per layer in one call
@@ -95,21 +110,36 @@ class PagedBench:
                                 for s, L in zip(self.seqs, lens)])
         if self.W:
             self.pool.slide(self.seqs, self.W)
-        slots_d = torch.from_numpy(slots).to(dev)
+        self._fill(slots)
+        self._step_buffers(int(lens.max()) + grow)
+        self.lens_now = lens.copy() - 1
+
+    def _fill(self, slots) -> None:
+        """Write synthetic K/V rows at `slots` of every layer (one call per layer)."""
+        torch, w = self.torch, self.w
+        slots_d = torch.from_numpy(slots).to(self.dev)
         for li, layer in enumerate(self.layers):
-            k = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li)
-            v = workloads.torch_normal((len(slots), H, D), torch.float16, dev, w.seed * 1000 + 2 * li + 1)
-            kvc.write_paged(layer, slots_d, k, v)
+            k = workloads.torch_normal((len(slots), self.H, self.D), torch.float16, self.dev,
+                                       w.seed * 1000 + 2 * li)
+            v = workloads.torch_normal((len(slots), self.H, self.D), torch.float16, self.dev,
+                                       w.seed * 1000 + 2 * li + 1)
+            self.kvc.write_paged(layer, slots_d, k, v)
             del k, v
         torch.cuda.synchronize()
-        # per-step inputs, resident in device memory: new K/V and q for every layer
+
+    def _step_buffers(self, max_ctx: int) -> None:
+        """Per-step inputs resident in device memory (new K/V and q of every layer), the output,
+        the workspace, and a ring of pinned host buffers for the table/length/slot uploads."""
+        torch, w, dev, layers = self.torch, self.w, self.dev, self.L
+        B, H, D = self.B, self.H, self.D
+        Hq = H * self.G
         self.knew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 1)
         self.vnew = workloads.torch_normal((layers, B, H, D), torch.float16, dev, w.seed * 7 + 2)
         self.q = workloads.torch_normal((layers, B, Hq, D), torch.float16, dev, w.seed * 7 + 3)
         self.out = torch.empty((layers, B, Hq, D), dtype=torch.float16, device=dev)
-        self.ws = kvc.new_gqa_workspace(B, H, self.G, D, device=dev)
-        # pinned host staging, a ring of buffers: a buffer is refilled only after the copy that
-        # last read it has executed (the host may run several steps ahead of the GPU)
+        self.ws = self.kvc.new_gqa_workspace(B, H, self.G, D, device=dev)
+        # a buffer is refilled only after the copy that last read it has executed (the host may
+        # run several steps ahead of the GPU)
         self.ring = [(torch.empty((B, self.mbps), dtype=torch.int32, pin_memory=True),
                       torch.empty(B, dtype=torch.int32, pin_memory=True),
                       torch.empty(B, dtype=torch.int64, pin_memory=True),
@@ -119,10 +149,10 @@ class PagedBench:
         self.len_d = torch.empty(B, dtype=torch.int32, device=dev)
         self.slot_d = torch.empty(B, dtype=torch.int64, device=dev)
         self.cow_d = torch.empty((2, B), dtype=torch.int32, device=dev)
-        self.max_ctx = int(lens.max()) + grow
+        self.max_ctx = max_ctx
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.stream = torch.cuda.current_stream()
-        self.lens_now = lens.copy() - 1
+        self.cow_ev = None   # list collecting (start, end) events around copy-on-write copies
 
     def step(self, ev=None):
         kvc, torch = self.kvc, self.torch
@@ -145,7 +175,13 @@ class PagedBench:
         self.lens_now += 1
         for li, layer in enumerate(self.layers):
             if ncow:
+                if self.cow_ev is not None:
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(self.stream)
                 kvc.copy_blocks(layer, self.cow_d[0, :ncow], self.cow_d[1, :ncow])
+                if self.cow_ev is not None:
+                    e1.record(self.stream)
+                    self.cow_ev.append((e0, e1))
             if not self.fused:
                 kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
             if ev is not None:
@@ -220,10 +256,105 @@ class PagedBench:
         return dt, out, int((lens - first).sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
 
 
+    def tile_pieces(self):
+        """Pass 1's K/V reads of the current step as (offset, pool pairs): the byte offset of
+        every (sequence, K/V head, block) tile in work-list order, and each layer's K and V
+        pools (None for workloads whose list is not that: rolling windows)."""
+        if self.W:
+            return None
+        tables, lens = self.pool.block_table(self.seqs)
+        tile = 16 * self.D * ELT[self.w.kv_dtype]
+        offs = []
+        for b in range(len(lens)):
+            ids = tables[b][:workloads.blocks_for(int(lens[b]))].astype(np.int64)
+            offs.append(((ids[None, :] * self.H + np.arange(self.H)[:, None]) * tile).reshape(-1))
+        return np.concatenate(offs), tile, [(l.k_pool, l.v_pool) for l in self.layers]
+
+
+class SamplingBench(PagedBench):
+    """Parallel sampling: 8 candidates share one prompt's blocks (the prompt's sequence and 7
+    forks, refcount 8), then each step appends one token to every candidate -- copy-on-write of
+    the shared partial block at the first step when the prompt ends inside a block -- and attends,
+    in every layer. After `generate` steps the candidates are freed and the prompt is taken again
+    (first fit in block-id order gives it the same blocks, whose K/V are still in place) and
+    forked; that host work is part of the step that follows."""
+
+    def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
+        import torch
+
+        import kv_cache_attention_kvc_amd as kvc
+
+        self.kvc, self.torch, self.w, self.dev = kvc, torch, w, dev
+        self.L, self.fused = layers, fused
+        self.B, self.H, self.D = w.batch, w.heads, w.head_dim
+        self.G, self.W = 1, 0
+        self.prompt, self.gen_len = w.extra["prompt"], w.extra["generate"]
+        nblk = workloads.blocks_for(self.prompt) + self.B * (workloads.blocks_for(self.gen_len) + 1)
+        self.mbps = workloads.blocks_for(self.prompt + self.gen_len)
+        self.pool = kvc.Pool(nblk, self.mbps)       # first fit in block-id order
+        self.layers = [kvc.PagedLayer.empty(nblk, self.H, self.D, "f16", device=dev, fill=0.0)
+                       for _ in range(layers)]
+        self.prompt_slots = self._start()
+        self._fill(self.prompt_slots)
+        self._step_buffers(self.prompt + self.gen_len)
+        self.first_lens = np.full(self.B, self.prompt + 1, dtype=np.int64)
+        self.lens_now = np.full(self.B, self.prompt, dtype=np.int64)
+        self.gen_step = 0
+        self.cow_ev = []
+        self.step_ev = None          # (HipEvents, index) per step when timing steps
+        self.step_index = []         # generation step of every timed step
+        self.cow_per_step = []       # copy-on-write pairs of every timed step
+
+    def _start(self):
+        """The prompt's sequence and its 7 forks; returns the prompt's slots."""
+        parent = self.pool.alloc()
+        slots = self.pool.append([parent], self.prompt)[0]
+        self.seqs = [parent] + [self.pool.fork(parent) for _ in range(self.B - 1)]
+        return slots
+
+    def step(self, ev=None):
+        if self.gen_step == self.gen_len:
+            for s in self.seqs:
+                self.pool.free(s)
+            slots = self._start()
+            if not np.array_equal(slots, self.prompt_slots):
+                raise RuntimeError("the prompt did not get its blocks back")
+            self.lens_now[:] = self.prompt
+            self.gen_step = 0
+        before = self.pool.stats()["cow_copies"]
+        timed = ev is not None and self.step_ev is not None
+        if timed:
+            i = ev[1] // (2 * self.L)        # timed step number
+            self.step_ev.record(2 * i, self.stream)
+        super().step(ev)
+        if timed:
+            self.step_ev.record(2 * i + 1, self.stream)
+            self.cow_per_step.append(self.pool.stats()["cow_copies"] - before)
+            self.step_index.append(self.gen_step)
+        self.gen_step += 1
+
+    def unique_bytes(self):
+        """Bytes of K/V one layer holds for the current step: every physical block the
+        candidates' tables name, once, times its valid slots (shared prompt blocks once)."""
+        tables, lens = self.pool.block_table(self.seqs)
+        valid = {}
+        for b in range(len(lens)):
+            L = int(lens[b])
+            for j in range(workloads.blocks_for(L)):
+                p = int(tables[b][j])
+                valid[p] = max(valid.get(p, 0), min(16, L - 16 * j))
+        return sum(valid.values()) * self.H * self.D * 2 * ELT["f16"]
+
+
 class PrefillBench:
     """Prefill: every sequence's whole prompt enters at once. One step = per layer, the prompt's
     K/V written into the paged cache, then causal attention of every prompt row (matrix cores).
     The same slots are rewritten each step."""
+
+    ORACLE_PER_LAYER = False   # the oracle sample is one fixed piece of the last layer
+
+    def tile_pieces(self):
+        return None
 
     def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
@@ -305,6 +436,11 @@ class CompressBench:
     """Whole-cache 8-bit compression: every sequence's fp16 blocks re-encoded into an int8 pool
     with fresh per-block scales, one kvc_compress_blocks launch per layer (the same blocks each
     step; the destination is overwritten)."""
+
+    ORACLE_PER_LAYER = False   # the oracle sample is one fixed piece of the last layer
+
+    def tile_pieces(self):
+        return None
 
     def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
@@ -443,6 +579,8 @@ class ContigBench:
     attends. Tiny char-GPT: a 16-token prefill, then each step appends at the next position and
     attends (context 17 .. 256)."""
 
+    ORACLE_PER_LAYER = True
+
     def __init__(self, w: workloads.Workload, steps: int, layers: int, dev, fused: bool):
         import torch
 
@@ -522,6 +660,16 @@ class ContigBench:
     def gpu_sample(self):
         return self.out[0]
 
+    def tile_pieces(self):
+        """Pass 1's K/V reads of the current step: the byte offset of every (sequence, head,
+        16-position tile) in work-list order, and each layer's K and V caches."""
+        row = self.D * ELT[self.w.kv_dtype]
+        offs = [((b * self.H + h) * self.S + 16 * j) * row
+                for b in range(self.B) for h in range(self.H)
+                for j in range(workloads.blocks_for(int(self.lens_now[b])))]
+        return (np.array(offs, dtype=np.int64), 16 * row,
+                [(self.kc[li], self.vc[li]) for li in range(self.L)])
+
     def oracle_layer(self, li):
         from oracle.caches import ContigCache
 
@@ -534,6 +682,29 @@ class ContigBench:
         out = ref.decode(q, lens, self.scale)
         dt = time.perf_counter() - t0
         return dt, out, int(lens.sum()) * self.H * self.D * 2 * ELT[self.w.kv_dtype]
+
+
+KV_CODE = {"f32": 0, "f16": 1, "e4m3": 2, "i8": 3}
+
+
+def _b(x: bool) -> str:
+    return "true" if x else "false"
+
+
+def kernel_match(w: workloads.Workload, fused: bool) -> str:
+    """The dominant kernel's instance as rocprofv3 names it (template arguments as printed)."""
+    if w is workloads.LLAMA7B_PREFILL:
+        return "prefill_kernel<true, 128>"
+    if w is workloads.COMPRESS_I8:
+        return "compress_f16_stream_kernel<3"
+    G = w.extra.get("group", 1)
+    paged = w.kind == "paged"
+    win = "window" in w.extra
+    if G == 1:
+        return (f"decode_partial_kernel<{_b(paged)}, {KV_CODE[w.kv_dtype]}, {w.head_dim}, "
+                f"{_b(w.q_dtype == 'f16')}, 1, {_b(win)}>")
+    return (f"decode_partial_mfma_kernel<{_b(paged)}, {KV_CODE[w.kv_dtype]}, {w.head_dim}, "
+            f"{_b(win)}, {_b(fused)}>")
 
 
 def kernel_name(w: workloads.Workload) -> str:
@@ -565,13 +736,25 @@ def blas_threads() -> int:
         return 1
 
 
-KERNEL_SRC = os.path.join(ROOT, "kv_cache_attention_kvc_amd", "csrc", "kvc_decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_partial_paged_f16_llama13b_traffic.txt")
-PASS1 = "decode_partial_kernel<true, 1, 128, true, 1, false>"
+# committed HBM traffic records (rocprofv3 FETCH_SIZE / WRITE_SIZE), one per workload
+PROFILE_TAG = {
+    workloads.LLAMA13B_PAGED.name: "decode_partial_paged_f16_llama13b",
+    workloads.LLAMA7B_CONTIG.name: "decode_partial_contig_f16_llama7b",
+    workloads.LONGCTX_FP8.name: "decode_partial_paged_e4m3_longctx",
+    workloads.GQA8_PAGED.name: "decode_partial_mfma_paged_f16_gqa8",
+    workloads.PARALLEL_SAMPLING.name: "decode_partial_paged_f16_parallel_sampling",
+    workloads.PARALLEL_SAMPLING_COW.name: "decode_partial_paged_f16_parallel_sampling_cow",
+    workloads.COMPRESS_I8.name: "compress_f16_to_i8_longctx",
+}
 
 
-def source_hash(path: str = KERNEL_SRC) -> str:
-    """First 16 hex digits of the sha256 of a kernel source (the decode kernels by default)."""
+def traffic_file(w: workloads.Workload):
+    tag = PROFILE_TAG.get(w.name)
+    return os.path.join(ROOT, "profiles", f"{tag}_traffic.txt") if tag else None
+
+
+def source_hash(path: str) -> str:
+    """First 16 hex digits of the sha256 of a kernel source."""
     import hashlib
 
     with open(path, "rb") as f:
@@ -586,60 +769,161 @@ def workload_source(w: workloads.Workload) -> str:
 
 
 def pmc_summary(fetch_dir: str, write_dir: str, bench_log: str) -> dict:
-    """HBM bytes per pass-1 launch from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB per dispatch),
-    each scaled by what the same counter reads for a plain 1 GiB device copy."""
+    """HBM bytes per launch of the dominant kernel from rocprofv3 FETCH_SIZE / WRITE_SIZE (KiB
+    per dispatch), each scaled by what the same counter reads for a plain 1 GiB device copy.
+    Only the timed launches count (the last steps x layers dispatches of the kernel), so the
+    figure describes the same launches as the bench line's `achieved`."""
     import csv
     import glob
 
+    rec = None
+    for ln in open(bench_log):
+        if ln.startswith("{"):
+            rec = json.loads(ln)
+    roof, cfg = rec["roofline"], rec["config"]
+    match = roof["kernel_match"]
+    n_timed = rec["steps"] * cfg["layers"]
+
     def rows(d):
-        (f,) = glob.glob(os.path.join(d, "*counter_collection.csv"))
+        (f,) = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         return list(csv.DictReader(open(f)))
 
-    def per_kernel(rs, pred):
-        v = [float(r["Counter_Value"]) for r in rs if pred(r["Kernel_Name"])]
+    def dispatch_key(r):
+        for k in ("Dispatch_Id", "Correlation_Id"):
+            if k in r and r[k] != "":
+                return int(r[k])
+        return 0
+
+    def per_kernel(rs):
+        v = sorted(((dispatch_key(r), float(r["Counter_Value"])) for r in rs
+                    if match in r["Kernel_Name"]))
+        v = [x for _, x in v][-n_timed:]
         return sum(v) / len(v), len(v)
 
-    fr, wr = rows(fetch_dir), rows(write_dir)
-    cal = float(1 << 30)
-    # the calibration copies: the three largest copy dispatches at the end of the run
     def copy_kib(rs):
         v = sorted(float(r["Counter_Value"]) for r in rs if "copyBuffer" in r["Kernel_Name"]
                    and int(r["Grid_Size"]) >= 65536)
         return v[-1]
+
+    fr, wr = rows(fetch_dir), rows(write_dir)
+    cal = float(1 << 30)
     f_fac = cal / (copy_kib(fr) * 1024)
     w_fac = cal / (copy_kib(wr) * 1024)
-    fk, nf = per_kernel(fr, lambda n: PASS1 in n)
-    wk, nw = per_kernel(wr, lambda n: PASS1 in n)
-    alg = src = None
-    for ln in open(bench_log):
-        if ln.startswith("{"):
-            rec = json.loads(ln)
-            alg = rec["roofline"]["algorithmic_bytes_per_launch"]
-            src = rec["roofline"]["kernel_source_sha256_16"]
-            path = rec["config"]["append"]
+    fk, nf = per_kernel(fr)
+    wk, nw = per_kernel(wr)
+    alg = roof["algorithmic_bytes_per_launch"]
     fetch_b = fk * 1024 * f_fac
     write_b = wk * 1024 * w_fac
-    return {"kernel": PASS1, "source_sha256_16": src, "append": path, "dispatches": [nf, nw],
-            "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
-            "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5),
-            "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
-            "traffic_bytes": int(fetch_b + write_b),
-            "algorithmic_bytes_per_launch_same_run": alg,
-            "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4) if alg else None}
+    out = {"kernel": match, "workload": cfg["workload"], "steps": rec["steps"],
+           "warmup": rec["warmup"], "layers": cfg["layers"],
+           "source_sha256_16": roof["kernel_source_sha256_16"], "append": cfg["append"],
+           "dispatches_averaged": [nf, nw],
+           "fetch_kib_raw": round(fk, 1), "write_kib_raw": round(wk, 1),
+           "fetch_scale": round(f_fac, 5), "write_scale": round(w_fac, 5),
+           "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "traffic_bytes": int(fetch_b + write_b),
+           "algorithmic_bytes_per_launch_same_run": alg,
+           "traffic_over_algorithmic": round((fetch_b + write_b) / alg, 4)}
+    if "sampling" in rec:
+        u = rec["sampling"]["unique_bytes_per_launch"]
+        out["unique_bytes_per_launch_same_run"] = u
+        out["fetch_over_unique"] = round(fetch_b / u, 4)
+    return out
 
 
-def measured_traffic(path: str):
-    """Traffic per pass-1 launch from the committed counter summary, if it was taken on the
-    current kernel source with the same append path (else None)."""
+def measured_traffic(w: workloads.Workload, path: str, steps: int, warmup: int, layers: int):
+    """Traffic per launch of the dominant kernel from the committed counter record, if that
+    record was taken over the same launches as this run (workload, steps, warm-up, layers, append
+    path) on the current kernel source; else None."""
+    f = traffic_file(w)
+    if not f:
+        return None
     try:
-        for ln in open(TRAFFIC_FILE):
+        for ln in open(f):
             if ln.startswith("{"):
                 rec = json.loads(ln)
-                if rec.get("source_sha256_16") == source_hash() and rec.get("append") == path:
-                    return rec["traffic_bytes"]
+                same = (rec.get("workload") == w.name and rec.get("steps") == steps
+                        and rec.get("warmup") == warmup and rec.get("layers") == layers
+                        and rec.get("append") == path
+                        and rec.get("source_sha256_16") == source_hash(workload_source(w)))
+                return rec["traffic_bytes"] if same else None
     except OSError:
         pass
     return None
+
+
+def cpu_baseline(bench, layers: int, budget_s: float):
+    """The CPU oracle timed on the last step: layer after layer until budget_s seconds have
+    passed (all BLAS threads), then the same layers on one thread. Returns (record fields,
+    total seconds, layer count, the oracle's output of layer 0)."""
+    from threadpoolctl import threadpool_limits
+
+    t_all, nbytes, used, ref0 = 0.0, 0, 0, None
+    for li in range(layers if bench.ORACLE_PER_LAYER else 1):
+        dt, ref, nb = bench.oracle_layer(li)
+        if ref0 is None:
+            ref0 = ref
+        t_all += dt
+        nbytes += nb
+        used += 1
+        if t_all >= budget_s:
+            break
+    with threadpool_limits(limits=1):
+        t_one = sum(bench.oracle_layer(li)[0] for li in range(used))
+    threads = blas_threads()
+    rec = {"value": round(nbytes / t_all / 1e9, 4), "unit": "GB/s", "cores": threads,
+           "kind": "oracle", "value_1thread": round(nbytes / t_one / 1e9, 4),
+           "cpu_count": os.cpu_count(), "blas_threads": threads,
+           "seconds": round(t_all, 2), "seconds_1thread": round(t_one, 2)}
+    return rec, used, ref0
+
+
+def read_ceiling(bench, p1_achieved: float):
+    """The read ceiling of pass 1's access pattern: kvc_read_pieces over exactly the K/V tiles
+    of the last step in work-list order, each layer's pools in turn (as the timed run reads
+    them), at 8, 12 and 16 wavefronts per CU; and a sequential read of the same bytes from the
+    start of each layer's pools. HIP events on the launch stream, three passes over the layers,
+    median launch time."""
+    import torch
+
+    import kv_cache_attention_kvc_amd as kvc
+
+    pieces = bench.tile_pieces()
+    if pieces is None:
+        return None
+    offs, tile, pools = pieces
+    n = len(offs)
+    nbytes = n * 2 * tile
+    dev = bench.dev
+    patterns = {"pass1_tiles": torch.from_numpy(offs).to(dev),
+                "sequential": torch.arange(n, dtype=torch.int64, device=dev) * tile}
+    sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
+    res = {}
+    reps = 3
+    for name, off_d in patterns.items():
+        best = None
+        for wpc in (8, 12, 16):
+            ev = HipEvents(2 * reps * len(pools))
+            k = 0
+            for _ in range(reps):
+                for kp, vp in pools:
+                    ev.record(2 * k, bench.stream)
+                    kvc.read_pieces(kp, off_d, tile, wpc, sink, b=vp)
+                    ev.record(2 * k + 1, bench.stream)
+                    k += 1
+            torch.cuda.synchronize()
+            t = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(k)])) / 1e3
+            ev.close()
+            gbs = nbytes / t / 1e9
+            if best is None or gbs > best[0]:
+                best = (gbs, wpc, t)
+        res[name] = best
+    return {"gbs": round(res["pass1_tiles"][0], 1),
+            "pattern": "pass 1's K/V tiles of the last step, work-list order, one layer per launch",
+            "waves_per_cu": res["pass1_tiles"][1],
+            "sequential_gbs": round(res["sequential"][0], 1),
+            "bytes_per_launch": nbytes,
+            "pass1_over_ceiling": round(p1_achieved / res["pass1_tiles"][0], 4)}
 
 
 def main():
@@ -658,12 +942,7 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    w = {"llama13b-paged": workloads.LLAMA13B_PAGED, "fp8-longctx": workloads.LONGCTX_FP8,
-         "llama7b-contig": workloads.LLAMA7B_CONTIG, "tiny-gpt": workloads.TINY_GPT,
-         "gqa8-paged": workloads.GQA8_PAGED,
-         "llama13b-window": workloads.LLAMA13B_WINDOW,
-         "llama7b-prefill": workloads.LLAMA7B_PREFILL,
-         "i8-longctx": workloads.LONGCTX_I8, "i8-compress": workloads.COMPRESS_I8}[args.workload]
+    w = WORKLOADS[args.workload]
     layers = args.layers or w.layers
     K, W = args.steps, args.warmup
     if w is workloads.TINY_GPT and K + W > w.extra["decode_steps"]:
@@ -680,8 +959,9 @@ def main():
     path = "fused" if fused else "separate"
     prefill = w is workloads.LLAMA7B_PREFILL
     compress = w is workloads.COMPRESS_I8
-    cls = PrefillBench if prefill else (CompressBench if compress else
-                                        (PagedBench if w.kind == "paged" else ContigBench))
+    sampling = w in SAMPLING
+    cls = (PrefillBench if prefill else CompressBench if compress else
+           SamplingBench if sampling else PagedBench if w.kind == "paged" else ContigBench)
     bench = cls(w, K + W, layers, dev, fused)
     for _ in range(W):
         bench.step()
@@ -689,8 +969,12 @@ def main():
     print("[bench] warm-up done", file=sys.stderr, flush=True)
 
     evs = HipEvents(2 * layers * K)
+    if sampling:
+        bench.step_ev = HipEvents(2 * K)
+        bench.cow_ev = []
+        bench.gen_step = bench.gen_len     # the timed steps start a fresh generation
     total_bytes = 0
-    pass1_bytes = []
+    pass1_bytes, unique = [], []
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
@@ -708,6 +992,7 @@ def main():
     p1_bytes_avg = float(np.mean(pass1_bytes))
     achieved = p1_bytes_avg / p1_avg_s / 1e9
     value = total_bytes / elapsed / 1e9
+    traffic = measured_traffic(w, path, K, W, layers)
     if prefill:
         # compute-bound: the roofline is the matrix cores' fp16 peak over the useful flops
         roof = {"bound": "mfma", "achieved": round(bench.flops_launch() / p1_avg_s / 1e12, 1),
@@ -717,12 +1002,11 @@ def main():
         tokens = w.batch * bench.T * K
     elif compress:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4), "traffic": None}
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic}
         tokens = w.batch * bench.T * K  # cached tokens compressed (in every layer) per step
     else:
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / PEAK_GBS, 4),
-                "traffic": measured_traffic(path) if w is workloads.LLAMA13B_PAGED else None}
+                "frac": round(achieved / PEAK_GBS, 4), "traffic": traffic}
         tokens = w.batch * K
     print(f"[bench] timed: {elapsed * 1e3 / K:.3f} ms/step, pass 1 {p1_avg_s * 1e6:.1f} us/launch",
           file=sys.stderr, flush=True)
@@ -745,7 +1029,8 @@ def main():
             "kv_heads": w.heads, "head_dim": w.head_dim,
             "layers": layers, "block_size": 16, "kv_dtype": w.kv_dtype, "q_dtype": w.q_dtype,
             "ctx_first_step": ("U[%d,%d] mean %.1f" % (w.ctx_lo, w.ctx_hi, bench.first_lens.mean()))
-            if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else w.ctx),
+            if w.ctx_hi else (w.extra["prefill"] + 1 if "prefill" in w.extra else
+                              w.extra["prompt"] + 1 if sampling else w.ctx),
             "ctx_growth_per_step": 0 if w in (workloads.LLAMA7B_CONTIG, workloads.LLAMA7B_PREFILL,
                                               workloads.COMPRESS_I8) else 1,
             "window": w.extra.get("window", 0),
@@ -755,6 +1040,7 @@ def main():
         "tokens_per_s": round(tokens / elapsed, 1),
         "roofline": {
             "kernel": kernel_name(w),
+            "kernel_match": kernel_match(w, fused),
             **roof,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
@@ -762,24 +1048,47 @@ def main():
             "kernel_source_sha256_16": source_hash(workload_source(w)),
         },
     }
-    if not args.no_cpu_baseline:
-        print("[bench] CPU oracle on one layer", file=sys.stderr, flush=True)
-        dt, ref, nbytes = bench.oracle_layer(0)
-        got = bench.gpu_sample().float().cpu().numpy()
-        line["cpu_baseline"] = {
-            "value": round(nbytes / dt / 1e9, 4),
-            "unit": "GB/s",
-            "cores": blas_threads(),
-            "kind": "oracle",
-            "sample": (f"the first prompt of the last layer: {bench.T} rows x {w.heads} heads, "
-                       f"causal; {dt:.2f} s; {bench.T / (dt * layers):.3f} prefill tokens/s over "
-                       f"{layers} layers") if prefill else
-                      (f"the first {bench.SAMPLE} blocks of the last layer (K and V); {dt:.2f} s")
-                      if compress else
-                      (f"layer 0 of the last step: all {w.batch} sequences x {w.heads} heads, "
-                       f"{int(bench.lens_now.sum())} positions; {dt:.2f} s; "
-                       f"{w.batch / (dt * layers):.3f} tokens/s over {layers} layers"),
+    if traffic is not None:
+        line["roofline"]["traffic_over_algorithmic"] = round(traffic / p1_bytes_avg, 4)
+    if sampling:
+        step_us = np.array([bench.step_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]) * 1e3
+        bench.step_ev.close()
+        idx = np.array(bench.step_index)
+        cow_us = sum(a.elapsed_time(b) for a, b in bench.cow_ev) * 1e3
+        n_cow_steps = int(sum(1 for c in bench.cow_per_step if c))
+        ub = bench.unique_bytes()
+        line["sampling"] = {
+            "candidates": w.batch, "prompt": bench.prompt, "generate": bench.gen_len,
+            "cow_copies_per_generation": int(sum(c for c, i in zip(bench.cow_per_step, idx)
+                                                 if i == 0) / max(1, int((idx == 0).sum()))),
+            "blocks_used_last_step": bench.pool.stats()["used"],
+            "first_step_us": round(float(step_us[idx == 0].mean()), 1) if (idx == 0).any() else None,
+            "other_steps_median_us": round(float(np.median(step_us[idx != 0])), 1),
+            "cow_copy_us_per_copy_step": round(cow_us / n_cow_steps, 1) if n_cow_steps else 0.0,
+            "logical_gbs": round(value, 1),
+            "unique_bytes_per_launch": int(ub),
+            "logical_bytes_per_launch_last_step": int(pass1_bytes[-1]),
         }
+    if not args.no_ceiling and not prefill and not compress and not sampling:
+        print("[bench] read ceiling", file=sys.stderr, flush=True)
+        ceil = read_ceiling(bench, achieved)
+        if ceil is not None:
+            line["roofline"]["ceiling"] = ceil
+    if not args.no_cpu_baseline:
+        print("[bench] CPU oracle", file=sys.stderr, flush=True)
+        rec, used, ref = cpu_baseline(bench, layers, args.cpu_seconds)
+        got = bench.gpu_sample().float().cpu().numpy()
+        per_layer = rec["seconds"] / used
+        rec["sample"] = (
+            (f"the first prompt of the last layer: {bench.T} rows x {w.heads} heads, causal; "
+             f"{bench.T / (per_layer * layers):.3f} prefill tokens/s over {layers} layers")
+            if prefill else
+            (f"the first {bench.SAMPLE} blocks of the last layer (K and V)") if compress else
+            (f"layers 0..{used - 1} of the last step: all {w.batch} sequences x "
+             f"{w.heads * w.extra.get('group', 1)} query heads, {int(bench.lens_now.sum())} "
+             f"positions per layer; {w.batch / (per_layer * layers):.3f} tokens/s over "
+             f"{layers} layers (all threads)"))
+        line["cpu_baseline"] = rec
         # a sanity check of the timed run, not a parity claim: the oracle reads the cache as the
         # library stored it (the parity tests build every oracle input from the generated data)
         line["spot_check"] = {"max_abs_err": float(np.abs(got - ref).max()),

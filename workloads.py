@@ -102,10 +102,19 @@ LLAMA13B_PAGED = Workload(
     name="llama13b-40x40x128-f16-paged16-b32-ctxU64-2048", kind="paged", layers=40, batch=32,
     heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=3, ctx_lo=64, ctx_hi=2048)
 
+# Parallel sampling runs LLaMA-13B's 40 layers (one block table per candidate serves all of
+# them), so a step reads each layer's shared prompt from memory as a model would.
 PARALLEL_SAMPLING = Workload(
-    name="parallel-sampling-8x(1024+128)-40x128-f16-paged16", kind="paged", layers=1, batch=8,
+    name="parallel-sampling-8x(1024+128)-40x128-f16-paged16", kind="paged", layers=40, batch=8,
     heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=4,
     extra={"prompt": 1024, "generate": 128, "cow_variant_prompt": 1020})
+
+# The copy-on-write variant: a 1020-token prompt ends inside a block, so the first generated
+# token of candidates 0-6 copies the shared partial block; candidate 7 writes in place.
+PARALLEL_SAMPLING_COW = Workload(
+    name="parallel-sampling-8x(1020+128)-40x128-f16-paged16-cow", kind="paged", layers=40,
+    batch=8, heads=40, head_dim=128, kv_dtype="f16", q_dtype="f16", seed=4,
+    extra={"prompt": 1020, "generate": 128})
 
 LONGCTX_FP8 = Workload(
     name="llama7b-32x32x128-e4m3-paged16-b64-ctx4096", kind="paged", layers=32, batch=64,
