@@ -279,6 +279,23 @@ kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_pag
                                  void *out, kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                  void *stream);
 
+/* kvc_decode_attn_paged without a workspace argument, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * It allocates nothing: its workspace is a file-scope device array of this library
+ * (8,667,648 bytes on each GPU it runs on, held until the process ends), looked up on the first
+ * call on each device. The caller still passes q, the layer, tables, lengths and out; all other
+ * arguments, layouts, results and errors are those of kvc_decode_attn_paged (the same kernels,
+ * so the same output bit for bit). Limits: B <= 4096 and head_dim 64 or 128, else
+ * KVC_E_INVALID / KVC_E_UNSUPPORTED before anything is queued; KVC_E_HIP if the runtime cannot
+ * give the array's address. The array needs no initialisation and keeps the last call's
+ * contents. Every call on one GPU shares that array: calls that may overlap in time (other
+ * streams, other host threads) race and must be serialised, for example on one stream. */
+kvc_status kvc_decode_attn_paged_noalloc(const void *q, kvc_dtype q_dtype,
+                                         const kvc_paged_layer *layer, const int32_t *block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                         int32_t B, int32_t max_ctx, float scale, void *out,
+                                         kvc_dtype out_dtype, void *stream);
+
 /* The two passes as separate launches, for callers that time or schedule them apart.
  * kvc_decode_attn_{contig,paged} == the matching *_partial call followed by kvc_decode_merge
  * on the same stream, workspace and out. Pass 1 leaves a record of its split in the workspace;

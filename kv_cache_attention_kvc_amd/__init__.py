@@ -27,7 +27,7 @@ __all__ = [
     "decode_window_partial_contig", "decode_window_partial_paged", "prefill_contig",
     "prefill_paged", "compress_blocks", "append_decode_gqa_contig", "append_decode_gqa_paged",
     "append_decode_gqa_partial_contig", "append_decode_gqa_partial_paged",
-    "read_pieces",
+    "decode_attn_paged_noalloc", "read_pieces",
 ]
 
 F32, F16, E4M3, I8 = 0, 1, 2, 3
@@ -50,7 +50,7 @@ EXPORTS = [
     "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
     "kvc_compress_blocks", "kvc_append_decode_gqa_contig", "kvc_append_decode_gqa_paged",
     "kvc_append_decode_gqa_partial_contig", "kvc_append_decode_gqa_partial_paged",
-    "kvc_read_pieces",
+    "kvc_decode_attn_paged_noalloc", "kvc_read_pieces",
 ]
 
 
@@ -125,6 +125,9 @@ def load_library() -> ctypes.CDLL:
         "kvc_decode_attn_paged": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer), _P, _I32,
                                                  _P, _I32, _I32, _F, _P, ctypes.c_int, _P,
                                                  ctypes.c_size_t, _P]),
+        "kvc_decode_attn_paged_noalloc": (ctypes.c_int, [_P, ctypes.c_int, ctypes.POINTER(_Layer),
+                                                         _P, _I32, _P, _I32, _I32, _F, _P,
+                                                         ctypes.c_int, _P]),
         "kvc_read_pieces": (ctypes.c_int, [_P, _P, _P, _I32, _I32, _I32, _P, ctypes.c_size_t,
                                            _P]),
         "kvc_decode_partial_contig": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P,
@@ -574,6 +577,25 @@ def decode_attn_paged(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, sca
         _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
         _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out), _ptr(ws),
         ws.numel(), _stream(stream)), "kvc_decode_attn_paged")
+    return out
+
+
+def decode_attn_paged_noalloc(q, layer: PagedLayer, block_tables, ctx_lens, max_ctx, scale=None,
+                              out=None, stream=None):
+    """decode_attn_paged with the library's own static workspace (kvc_decode_attn_paged_noalloc:
+    no device allocation in the call, B <= 4096). Pass `out` to allocate nothing at all. Calls
+    that may overlap in time on one GPU share that workspace and must be serialised."""
+    B = q.shape[0]
+    _check_q_mha(q, B, layer.heads, layer.head_dim)
+    _check_tables(block_tables, B)
+    _check_lens(ctx_lens, B)
+    out = _out_for(q, out)
+    scale = 1.0 / math.sqrt(layer.head_dim) if scale is None else scale
+    st = layer.struct()
+    _check(_lib().kvc_decode_attn_paged_noalloc(
+        _ptr(q), _dtype_code(q), ctypes.byref(st), _ptr_i32(block_tables), block_tables.shape[1],
+        _ptr_i32(ctx_lens), B, int(max_ctx), float(scale), _ptr(out), _dtype_code(out),
+        _stream(stream)), "kvc_decode_attn_paged_noalloc")
     return out
 
 

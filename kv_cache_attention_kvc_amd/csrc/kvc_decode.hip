@@ -52,15 +52,23 @@ struct WsLayout {
   size_t pre_off, rec_off, total;
 };
 
-inline size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
+constexpr size_t align256(size_t x) { return (x + 255) & ~static_cast<size_t>(255); }
 
-inline WsLayout ws_layout(int B, int D, int GQ) {
-  WsLayout l;
+constexpr WsLayout ws_layout(int B, int D, int GQ) {
+  WsLayout l{};
   l.pre_off = 256;
   l.rec_off = l.pre_off + align256((static_cast<size_t>(B) + 1) * sizeof(int32_t));
   l.total = l.rec_off + static_cast<size_t>(kMaxWorkers) * 2 * GQ * (D + 4) * sizeof(float);
   return l;
 }
+
+// Workspace of kvc_decode_attn_paged_noalloc: a file-scope device array, one copy per GPU, held
+// until the process ends, sized for the largest call that entry point takes (4096 sequences,
+// D = 128, one query head per pair): 8,667,648 bytes. Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): it passes the device address
+// that hipGetSymbolAddress returns for the current GPU.
+constexpr size_t kScratchBytes = ws_layout(kMaxBatch, 128, 1).total;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
 
 struct DecodeArgs {
   const void *q;
@@ -1448,6 +1456,29 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   return KVC_OK;
 }
 
+// Device address of `scratch` on the current GPU, looked up once per device (with that device
+// current) and kept; null if the runtime cannot give it.
+void *scratch_address() {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void *addr[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    addr[dev] = p;
+  }
+  return addr[dev];
+}
+
 kvc_status launch_partial(const PartialPlan &pl, void *stream) {
   if (pl.grid == 0) return KVC_OK;
   hipLaunchKernelGGL(pl.kern, dim3(pl.grid), dim3(kWgThreads), pl.shmem,
@@ -1663,6 +1694,22 @@ kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_pag
   if (st != KVC_OK) return st;
   return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
                           ws_bytes, stream);
+}
+
+kvc_status kvc_decode_attn_paged_noalloc(const void *q, kvc_dtype q_dtype,
+                                         const kvc_paged_layer *layer, const int32_t *block_tables,
+                                         int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                         int32_t B, int32_t max_ctx, float scale, void *out,
+                                         kvc_dtype out_dtype, void *stream) {
+  if (!layer || B < 0 || B > kMaxBatch) return KVC_E_INVALID;
+  const int32_t D = layer->head_dim;
+  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
+  if (ws_layout(B, D, 1).total > kScratchBytes) return KVC_E_INVALID;
+  if (B == 0) return KVC_OK;
+  void *ws = scratch_address();
+  if (!ws) return KVC_E_HIP;
+  return kvc_decode_attn_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq, ctx_lens, B,
+                               max_ctx, scale, out, out_dtype, ws, kScratchBytes, stream);
 }
 
 kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, const void *k_cache,
