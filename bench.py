@@ -152,7 +152,8 @@ class PagedBench:
         self.max_ctx = max_ctx
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.stream = torch.cuda.current_stream()
-        self.cow_ev = None   # list collecting (start, end) events around copy-on-write copies
+        self.cow_ev = None   # HipEvents around copy-on-write copy launches (when timing them)
+        self.cow_n = 0       # copy launches timed so far
 
     def step(self, ev=None):
         kvc, torch = self.kvc, self.torch
@@ -175,13 +176,13 @@ class PagedBench:
         self.lens_now += 1
         for li, layer in enumerate(self.layers):
             if ncow:
-                if self.cow_ev is not None:
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(self.stream)
+                timed_copy = self.cow_ev is not None and self.cow_n < self.cow_ev.n // 2
+                if timed_copy:
+                    self.cow_ev.record(2 * self.cow_n, self.stream)
                 kvc.copy_blocks(layer, self.cow_d[0, :ncow], self.cow_d[1, :ncow])
-                if self.cow_ev is not None:
-                    e1.record(self.stream)
-                    self.cow_ev.append((e0, e1))
+                if timed_copy:
+                    self.cow_ev.record(2 * self.cow_n + 1, self.stream)
+                    self.cow_n += 1
             if not self.fused:
                 kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
             if ev is not None:
@@ -300,7 +301,6 @@ class SamplingBench(PagedBench):
         self.first_lens = np.full(self.B, self.prompt + 1, dtype=np.int64)
         self.lens_now = np.full(self.B, self.prompt, dtype=np.int64)
         self.gen_step = 0
-        self.cow_ev = []
         self.step_ev = None          # (HipEvents, index) per step when timing steps
         self.step_index = []         # generation step of every timed step
         self.cow_per_step = []       # copy-on-write pairs of every timed step
@@ -540,6 +540,7 @@ class HipEvents:
     def __init__(self, n: int):
         import ctypes
 
+        self.n = n
         self.ct = ctypes
         self.hip = ctypes.CDLL("libamdhip64.so")
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
@@ -971,7 +972,8 @@ def main():
     evs = HipEvents(2 * layers * K)
     if sampling:
         bench.step_ev = HipEvents(2 * K)
-        bench.cow_ev = []
+        bench.cow_ev = HipEvents(2 * layers * (K // bench.gen_len + 1))
+        bench.cow_n = 0
         bench.gen_step = bench.gen_len     # the timed steps start a fresh generation
     total_bytes = 0
     pass1_bytes, unique = [], []
@@ -1054,7 +1056,8 @@ def main():
         step_us = np.array([bench.step_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]) * 1e3
         bench.step_ev.close()
         idx = np.array(bench.step_index)
-        cow_us = sum(a.elapsed_time(b) for a, b in bench.cow_ev) * 1e3
+        cow_us = sum(bench.cow_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(bench.cow_n)) * 1e3
+        bench.cow_ev.close()
         n_cow_steps = int(sum(1 for c in bench.cow_per_step if c))
         ub = bench.unique_bytes()
         line["sampling"] = {

@@ -59,23 +59,44 @@ write_paged_kernel(char *kp, char *vp, const char *kn, const char *vn, const int
   *reinterpret_cast<uint4 *>(vp + dst) = v;
 }
 
-// One workgroup per copy pair: the whole block (all heads) of K and V, and the fp8 scales.
+// Copy-on-write copies: workgroup (pair i, slice z) copies 16-byte pieces z*kCopyPieces ..
+// + kCopyPieces - 1 of pair i's block (all heads) of K and of V; the first slice also copies the
+// 8-bit scales. Every thread issues all its loads before its first store, so a workgroup makes
+// one memory round trip, and a pair's block is spread over many workgroups.
+constexpr int kCopyUnroll = 4;
+constexpr int kCopyPieces = kThreads * kCopyUnroll;
+
 __global__ void __launch_bounds__(kThreads)
 copy_blocks_kernel(char *kp, char *vp, float *ks, float *vs, const int32_t *src,
-                   const int32_t *dst, int32_t num_blocks, int64_t block_bytes) {
-  const int32_t s = src[blockIdx.x];
-  const int32_t d = dst[blockIdx.x];
+                   const int32_t *dst, int32_t num_blocks, int64_t block_bytes, int32_t slices) {
+  const int32_t pair = blockIdx.x / slices;
+  const int32_t z = blockIdx.x % slices;
+  const int32_t s = src[pair];
+  const int32_t d = dst[pair];
   if (static_cast<uint32_t>(s) >= static_cast<uint32_t>(num_blocks) ||
       static_cast<uint32_t>(d) >= static_cast<uint32_t>(num_blocks) || s == d)
     return;
-  const int64_t chunks = block_bytes / 16;
+  const int64_t pieces = block_bytes / 16;
   const int64_t so = static_cast<int64_t>(s) * block_bytes;
   const int64_t dof = static_cast<int64_t>(d) * block_bytes;
-  for (int64_t c = threadIdx.x; c < chunks; c += kThreads) {
-    *reinterpret_cast<uint4 *>(kp + dof + c * 16) = *reinterpret_cast<const uint4 *>(kp + so + c * 16);
-    *reinterpret_cast<uint4 *>(vp + dof + c * 16) = *reinterpret_cast<const uint4 *>(vp + so + c * 16);
+  uint4 kx[kCopyUnroll], vx[kCopyUnroll];
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t c = static_cast<int64_t>(z) * kCopyPieces + u * kThreads + threadIdx.x;
+    if (c < pieces) {
+      kx[u] = *reinterpret_cast<const uint4 *>(kp + so + c * 16);
+      vx[u] = *reinterpret_cast<const uint4 *>(vp + so + c * 16);
+    }
   }
-  if (threadIdx.x == 0 && ks) {
+#pragma unroll
+  for (int u = 0; u < kCopyUnroll; ++u) {
+    const int64_t c = static_cast<int64_t>(z) * kCopyPieces + u * kThreads + threadIdx.x;
+    if (c < pieces) {
+      *reinterpret_cast<uint4 *>(kp + dof + c * 16) = kx[u];
+      *reinterpret_cast<uint4 *>(vp + dof + c * 16) = vx[u];
+    }
+  }
+  if (z == 0 && threadIdx.x == 0 && ks) {
     ks[d] = ks[s];
     vs[d] = vs[s];
   }
@@ -643,10 +664,14 @@ kvc_status kvc_copy_blocks(const kvc_paged_layer *layer, const int32_t *src, con
   const int64_t block_bytes = static_cast<int64_t>(layer->num_heads) * kBlock * layer->head_dim *
                               elt_bytes(layer->kv_dtype);
   const bool fp8 = is_q8(layer->kv_dtype);
-  hipLaunchKernelGGL(copy_blocks_kernel, dim3(n), dim3(kThreads), 0,
+  const int64_t slices = (block_bytes / 16 + kCopyPieces - 1) / kCopyPieces;
+  const int64_t grid = static_cast<int64_t>(n) * slices;
+  if (grid > INT32_MAX) return KVC_E_INVALID;
+  hipLaunchKernelGGL(copy_blocks_kernel, dim3(static_cast<uint32_t>(grid)), dim3(kThreads), 0,
                      static_cast<hipStream_t>(stream), static_cast<char *>(layer->k_pool),
                      static_cast<char *>(layer->v_pool), fp8 ? layer->k_scale : nullptr,
-                     fp8 ? layer->v_scale : nullptr, src, dst, layer->num_blocks, block_bytes);
+                     fp8 ? layer->v_scale : nullptr, src, dst, layer->num_blocks, block_bytes,
+                     static_cast<int32_t>(slices));
   return launch_status();
 }
 
