@@ -40,6 +40,7 @@ constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
+constexpr int kPairTiles = 8;      // pair mode: tiles per wavefront at most
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
 constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
@@ -93,6 +94,7 @@ struct DecodeArgs {
   int32_t gq;          // query heads per pair (G / nsub)
   int32_t window;      // rolling window: attend positions max(0, L - window) .. L-1 (0: none)
   int32_t stage_rows;  // staged output rows per wavefront (LDS)
+  int32_t pair_mode;   // one workgroup per pair, combined in LDS (no merge), else equal chunks
   int32_t q_f16, out_f16;
   float cl2;  // scale * log2(e)
 };
@@ -1004,7 +1006,8 @@ struct MfmaCore {
 template <bool PAGED, class Core>
 __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pre,
                                           const int32_t *len, int32_t f0, int32_t f1, int32_t b0,
-                                          int32_t w, Stage &st, const Core &core) {
+                                          int32_t w, Stage &st, const Core &core,
+                                          bool flush_at_end) {
   using Tile = typename Core::Tile;
   const int32_t GQ = core.gq(a);
   int32_t f = f0;
@@ -1069,7 +1072,7 @@ __device__ __forceinline__ void run_chunk(const DecodeArgs &a, const int32_t *pr
     if (!step(ta, tb)) break;
     if (!step(tb, ta)) break;
   }
-  flush_stage<Core::kD>(a, st);
+  if (flush_at_end) flush_stage<Core::kD>(a, st);
 }
 
 // The body of both pass-1 kernels: block prefix, header, the wavefront's chunk, the walk. LDS:
@@ -1082,11 +1085,41 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   int32_t *pre = smem;
   int32_t *len = smem + a.B + 1;
   int32_t *wsum = len + a.B;
-  block_prefix<Core::kWin>(a.lens, a.B, a.cap, a.window, pre, len, wsum);
   Stage st;
   st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
             (threadIdx.x >> 6) * a.stage_rows * (D + 4);
   st.n = 0;
+  if (a.pair_mode) {
+    // workgroup x takes pair x = (b, h) whole; its tiles are numbered from 0 at the start of
+    // sequence b (pre[b] = 0, pre[b+1] = tiles per pair) and cut into one chunk per wavefront
+    const int32_t x = static_cast<int32_t>(blockIdx.x);
+    const int32_t b = x / a.Hp;
+    const int32_t h = x - b * a.Hp;
+    const int32_t L = min(max(a.lens[b], 0), a.cap);
+    const int32_t nb = (L + kBlock - 1) / kBlock - window_block<Core::kWin>(L, a.window);
+    if (threadIdx.x == 0) {
+      pre[b] = 0;
+      pre[b + 1] = nb;
+      len[b] = L;
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+      a.ws_hdr[0] = 0;
+      a.ws_hdr[1] = a.B;
+      a.ws_hdr[2] = a.Hp;
+      a.ws_hdr[3] = D;
+      a.ws_hdr[4] = gq;
+      a.ws_hdr[5] = 1;  // every output row is written by pass 1: the merge has nothing to do
+    }
+    __syncthreads();
+    const int32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int32_t c = (nb + kWgWaves - 1) / kWgWaves;
+    w_out = x * kWgWaves + wave;
+    f0_out = h * nb + min(wave * c, nb);
+    f1_out = h * nb + min(wave * c + c, nb);
+    b0_out = b;
+    return st;
+  }
+  block_prefix<Core::kWin>(a.lens, a.B, a.cap, a.window, pre, len, wsum);
 
   const int32_t total = a.Hp * pre[a.B];
   const int32_t C = max(a.cmin, (total + a.P - 1) / a.P);
@@ -1098,6 +1131,7 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
       a.ws_hdr[2] = a.Hp;
       a.ws_hdr[3] = D;
       a.ws_hdr[4] = gq;
+      a.ws_hdr[5] = 0;
     }
   }
   const int32_t w = __builtin_amdgcn_readfirstlane(blockIdx.x * kWgWaves + (threadIdx.x >> 6));
@@ -1125,15 +1159,55 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   return st;
 }
 
+// Pair mode, after every wavefront of the workgroup has run its chunk of pair x and staged one
+// entry per query head (none if its chunk was empty): the entries of each head are combined as
+// the merge kernel combines records (maximum, rescaled sums) and the output row is stored; a
+// pair with no position gets a zero row. Wavefront w takes heads w, w + 4, ...
+template <int D>
+__device__ __forceinline__ void combine_pair(const DecodeArgs &a, const int32_t *smem,
+                                             int32_t gq) {
+  const int32_t x = static_cast<int32_t>(blockIdx.x);
+  const int32_t b = x / a.Hp;
+  const int32_t h = x - b * a.Hp;
+  const int32_t nb = smem[b + 1];  // pre[b + 1]: tiles of the pair
+  const int32_t c = (nb + kWgWaves - 1) / kWgWaves;
+  const int lane = threadIdx.x & (kWave - 1);
+  const float *stage0 = reinterpret_cast<const float *>(smem + stage_offset(a.B));
+  for (int32_t r = threadIdx.x >> 6; r < gq; r += kWgWaves) {
+    float M = kFloor;
+    for (int i = 0; i < kWgWaves; ++i)
+      if (i * c < nb) M = fmaxf(M, stage0[(i * a.stage_rows + r) * (D + 4) + D]);
+    float lsum = 0.f, o0 = 0.f, o1 = 0.f;
+    for (int i = 0; i < kWgWaves; ++i) {
+      if (i * c >= nb) continue;
+      const float *e = stage0 + (i * a.stage_rows + r) * (D + 4);
+      const float f = __builtin_amdgcn_exp2f(e[D] - M);
+      lsum += e[D + 1] * f;
+      o0 += e[lane] * f;
+      if (D > kWave) o1 += e[lane + kWave] * f;
+    }
+    const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+    const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(h) * gq + r;
+    store_elem(a.out, row * D + lane, o0 * inv, a.out_f16);
+    if (D > kWave) store_elem(a.out, row * D + lane + kWave, o1 * inv, a.out_f16);
+  }
+}
+
 template <bool PAGED, int KV, int D, bool QF16, int GQ, bool WIN>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
   using Core = VecCore<PAGED, KV, D, QF16, GQ, WIN>;
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, GQ, f0, f1, b0, w);
-  if (f0 >= f1) return;
   const Core core(threadIdx.x & (kWave - 1));
-  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
+  if (a.pair_mode) {
+    if (f0 < f1) run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, false);
+    __syncthreads();
+    combine_pair<D>(a, smem, GQ);
+    return;
+  }
+  if (f0 >= f1) return;
+  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, true);
 }
 
 template <bool PAGED, int KV, int D, bool WIN, bool APPEND>
@@ -1142,13 +1216,19 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_mfma_kernel(const D
   using Core = MfmaCore<PAGED, KV, D, WIN, APPEND>;
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, a.gq, f0, f1, b0, w);
-  if (f0 >= f1) return;
   _Float16 *vbuf = reinterpret_cast<_Float16 *>(
       reinterpret_cast<char *>(smem + stage_offset(a.B)) +
       static_cast<size_t>(kWgWaves) * a.stage_rows * (D + 4) * sizeof(float) +
       (threadIdx.x >> 6) * Core::kVbufBytes);
   const Core core(threadIdx.x & (kWave - 1), vbuf);
-  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core);
+  if (a.pair_mode) {
+    if (f0 < f1) run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, false);
+    __syncthreads();
+    combine_pair<D>(a, smem, a.gq);
+    return;
+  }
+  if (f0 >= f1) return;
+  run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, true);
 }
 
 // ---- pass 2 ------------------------------------------------------------------------------
@@ -1167,6 +1247,7 @@ __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArg
   const int32_t Hq = a.H * a.G;
   const int64_t bh = static_cast<int64_t>(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
   if (bh >= static_cast<int64_t>(a.B) * Hq) return;
+  if (a.ws_hdr[5] != 0) return;  // pass 1 ran one workgroup per pair and wrote every row
   const int32_t b = static_cast<int32_t>(bh / Hq);
   const int32_t hq = static_cast<int32_t>(bh % Hq);
   const int D = a.D;
@@ -1425,6 +1506,15 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
   P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
   P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
+  // Few, short pairs (every pair's wavefronts resident at once, at most kPairTiles tiles per
+  // wavefront by the caller's bound max_ctx): one workgroup per pair, its wavefronts splitting
+  // the pair's tiles and combining in LDS, so no pair is left for the merge launch.
+  const int64_t pairs = static_cast<int64_t>(B) * Hp;
+  const int64_t pair_span =
+      window > 0 ? std::min<int64_t>(max_ctx, static_cast<int64_t>(window) + kBlock - 1) : max_ctx;
+  const int64_t pair_tiles = (pair_span + kBlock - 1) / kBlock;
+  const bool pair_mode = pair_tiles <= static_cast<int64_t>(kWgWaves) * kPairTiles &&
+                         pairs * kWgWaves <= static_cast<int64_t>(device_cu_count()) * wpc;
 
   DecodeArgs &a = pl.a;
   a = DecodeArgs{};
@@ -1442,6 +1532,7 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   a.gq = GQ;
   a.window = window;
   a.stage_rows = stage_rows;
+  a.pair_mode = pair_mode ? 1 : 0;
   a.Hp = Hp;
   a.Hq = H * G;
   a.cap = cap;
@@ -1451,7 +1542,7 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   a.out_f16 = out_dtype == KVC_F16;
   a.cl2 = scale * kLog2e;
   pl.kern = kern;
-  pl.grid = static_cast<int>(P / kWgWaves);
+  pl.grid = pair_mode ? static_cast<int>(pairs) : static_cast<int>(P / kWgWaves);
   pl.shmem = shmem;
   return KVC_OK;
 }
@@ -1499,7 +1590,7 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, co
                                  const void *k_new, const void *v_new, int32_t B, int32_t H,
                                  int32_t S_max, int32_t D, int32_t max_ctx, int32_t window,
                                  float scale, void *out, kvc_dtype out_dtype, void *workspace,
-                                 size_t ws_bytes, void *stream) {
+                                 size_t ws_bytes, void *stream, bool *merged = nullptr) {
   if (S_max < 0) return KVC_E_INVALID;
   if (!is_f32_or_f16(kv_dtype)) return KVC_E_UNSUPPORTED;
   PartialPlan pl;
@@ -1515,6 +1606,7 @@ static kvc_status partial_contig(const void *q, kvc_dtype q_dtype, int32_t G, co
   pl.a.k_new = static_cast<const char *>(k_new);
   pl.a.v_new = static_cast<const char *>(v_new);
   pl.a.seq_stride = S_max;
+  if (merged) *merged = pl.a.pair_mode != 0;
   return launch_partial(pl, stream);
 }
 
@@ -1523,7 +1615,8 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
                                 int32_t max_blocks_per_seq, const int32_t *ctx_lens,
                                 const void *k_new, const void *v_new, int32_t B, int32_t max_ctx,
                                 int32_t window, float scale, void *out, kvc_dtype out_dtype,
-                                void *workspace, size_t ws_bytes, void *stream) {
+                                void *workspace, size_t ws_bytes, void *stream,
+                                bool *merged = nullptr) {
   if (!layer || max_blocks_per_seq < 1 || max_blocks_per_seq > INT32_MAX / kBlock)
     return KVC_E_INVALID;
   if (layer->num_blocks < 1 || layer->num_heads < 1) return KVC_E_INVALID;
@@ -1551,6 +1644,7 @@ static kvc_status partial_paged(const void *q, kvc_dtype q_dtype, int32_t G,
   pl.a.num_blocks = layer->num_blocks;
   pl.a.k_new = static_cast<const char *>(k_new);
   pl.a.v_new = static_cast<const char *>(v_new);
+  if (merged) *merged = pl.a.pair_mode != 0;
   return launch_partial(pl, stream);
 }
 
@@ -1676,11 +1770,13 @@ kvc_status kvc_decode_attn_contig(const void *q, kvc_dtype q_dtype, const void *
                                   int32_t B, int32_t H, int32_t S_max, int32_t D, int32_t max_ctx,
                                   float scale, void *out, kvc_dtype out_dtype, void *workspace,
                                   size_t ws_bytes, void *stream) {
-  kvc_status st = kvc_decode_partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype, ctx_lens, B,
-                                            H, S_max, D, max_ctx, scale, out, out_dtype,
-                                            workspace, ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_merge(B, H, D, out, out_dtype, workspace, ws_bytes, stream);
+  bool merged = false;
+  const kvc_status st =
+      partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B, H,
+                     S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                     &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, H, 1, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
@@ -1688,12 +1784,14 @@ kvc_status kvc_decode_attn_paged(const void *q, kvc_dtype q_dtype, const kvc_pag
                                  const int32_t *ctx_lens, int32_t B, int32_t max_ctx, float scale,
                                  void *out, kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                  void *stream) {
-  kvc_status st = kvc_decode_partial_paged(q, q_dtype, layer, block_tables, max_blocks_per_seq,
-                                           ctx_lens, B, max_ctx, scale, out, out_dtype, workspace,
-                                           ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
-                          ws_bytes, stream);
+  bool merged = false;
+  const kvc_status st =
+      partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                    nullptr, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                    &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, layer->num_heads, 1, layer->head_dim, out, out_dtype, workspace, ws_bytes,
+               stream);
 }
 
 kvc_status kvc_decode_attn_paged_noalloc(const void *q, kvc_dtype q_dtype,
@@ -1717,11 +1815,13 @@ kvc_status kvc_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_t G, co
                                  int32_t B, int32_t H_kv, int32_t S_max, int32_t D,
                                  int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                                  void *workspace, size_t ws_bytes, void *stream) {
-  kvc_status st = kvc_decode_gqa_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
-                                                ctx_lens, B, H_kv, S_max, D, max_ctx, scale, out,
-                                                out_dtype, workspace, ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+  bool merged = false;
+  const kvc_status st =
+      partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
+                     H_kv, S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes,
+                     stream, &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1729,12 +1829,14 @@ kvc_status kvc_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
                                 int32_t max_blocks_per_seq, const int32_t *ctx_lens, int32_t B,
                                 int32_t max_ctx, float scale, void *out, kvc_dtype out_dtype,
                                 void *workspace, size_t ws_bytes, void *stream) {
-  kvc_status st = kvc_decode_gqa_partial_paged(q, q_dtype, G, layer, block_tables,
-                                               max_blocks_per_seq, ctx_lens, B, max_ctx, scale,
-                                               out, out_dtype, workspace, ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
-                              ws_bytes, stream);
+  bool merged = false;
+  const kvc_status st =
+      partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                    nullptr, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                    &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace, ws_bytes,
+               stream);
 }
 
 kvc_status kvc_decode_window_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1769,12 +1871,14 @@ kvc_status kvc_decode_window_contig(const void *q, kvc_dtype q_dtype, int32_t G,
                                     int32_t S_max, int32_t D, int32_t max_ctx, int32_t window,
                                     float scale, void *out, kvc_dtype out_dtype, void *workspace,
                                     size_t ws_bytes, void *stream) {
-  kvc_status st = kvc_decode_window_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
-                                                   ctx_lens, B, H_kv, S_max, D, max_ctx, window,
-                                                   scale, out, out_dtype, workspace, ws_bytes,
-                                                   stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+  if (window < 1) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, nullptr, nullptr, B,
+                     H_kv, S_max, D, max_ctx, window, scale, out, out_dtype, workspace, ws_bytes,
+                     stream, &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_decode_window_paged(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1783,13 +1887,15 @@ kvc_status kvc_decode_window_paged(const void *q, kvc_dtype q_dtype, int32_t G,
                                    int32_t max_ctx, int32_t window, float scale, void *out,
                                    kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                    void *stream) {
-  kvc_status st = kvc_decode_window_partial_paged(q, q_dtype, G, layer, block_tables,
-                                                  max_blocks_per_seq, ctx_lens, B, max_ctx, window,
-                                                  scale, out, out_dtype, workspace, ws_bytes,
-                                                  stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
-                              ws_bytes, stream);
+  if (window < 1) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, nullptr,
+                    nullptr, B, max_ctx, window, scale, out, out_dtype, workspace, ws_bytes,
+                    stream, &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace, ws_bytes,
+               stream);
 }
 
 kvc_status kvc_append_decode_contig(const void *q, kvc_dtype q_dtype, void *k_cache,
@@ -1798,12 +1904,14 @@ kvc_status kvc_append_decode_contig(const void *q, kvc_dtype q_dtype, void *k_ca
                                     int32_t S_max, int32_t D, int32_t max_ctx, float scale,
                                     void *out, kvc_dtype out_dtype, void *workspace,
                                     size_t ws_bytes, void *stream) {
-  kvc_status st = kvc_append_decode_partial_contig(q, q_dtype, k_cache, v_cache, kv_dtype,
-                                                   ctx_lens, k_new, v_new, B, H, S_max, D,
-                                                   max_ctx, scale, out, out_dtype, workspace,
-                                                   ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_merge(B, H, D, out, out_dtype, workspace, ws_bytes, stream);
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_contig(q, q_dtype, 1, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H,
+                     S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                     &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, H, 1, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_append_decode_paged(const void *q, kvc_dtype q_dtype, const kvc_paged_layer *layer,
@@ -1812,13 +1920,15 @@ kvc_status kvc_append_decode_paged(const void *q, kvc_dtype q_dtype, const kvc_p
                                    int32_t B, int32_t max_ctx, float scale, void *out,
                                    kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                    void *stream) {
-  kvc_status st = kvc_append_decode_partial_paged(q, q_dtype, layer, block_tables,
-                                                  max_blocks_per_seq, ctx_lens, k_new, v_new, B,
-                                                  max_ctx, scale, out, out_dtype, workspace,
-                                                  ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_merge(B, layer->num_heads, layer->head_dim, out, out_dtype, workspace,
-                          ws_bytes, stream);
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
+                    v_new, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                    &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, layer->num_heads, 1, layer->head_dim, out, out_dtype, workspace, ws_bytes,
+               stream);
 }
 
 kvc_status kvc_append_decode_gqa_partial_contig(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1854,12 +1964,14 @@ kvc_status kvc_append_decode_gqa_contig(const void *q, kvc_dtype q_dtype, int32_
                                         int32_t D, int32_t max_ctx, float scale, void *out,
                                         kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                         void *stream) {
-  kvc_status st = kvc_append_decode_gqa_partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype,
-                                                       ctx_lens, k_new, v_new, B, H_kv, S_max, D,
-                                                       max_ctx, scale, out, out_dtype, workspace,
-                                                       ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_contig(q, q_dtype, G, k_cache, v_cache, kv_dtype, ctx_lens, k_new, v_new, B, H_kv,
+                     S_max, D, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                     &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, H_kv, G, D, out, out_dtype, workspace, ws_bytes, stream);
 }
 
 kvc_status kvc_append_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t G,
@@ -1869,13 +1981,15 @@ kvc_status kvc_append_decode_gqa_paged(const void *q, kvc_dtype q_dtype, int32_t
                                        int32_t max_ctx, float scale, void *out,
                                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes,
                                        void *stream) {
-  kvc_status st = kvc_append_decode_gqa_partial_paged(q, q_dtype, G, layer, block_tables,
-                                                      max_blocks_per_seq, ctx_lens, k_new, v_new,
-                                                      B, max_ctx, scale, out, out_dtype,
-                                                      workspace, ws_bytes, stream);
-  if (st != KVC_OK) return st;
-  return kvc_decode_gqa_merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace,
-                              ws_bytes, stream);
+  if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
+  bool merged = false;
+  const kvc_status st =
+      partial_paged(q, q_dtype, G, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
+                    v_new, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream,
+                    &merged);
+  if (st != KVC_OK || merged) return st;
+  return merge(B, layer->num_heads, G, layer->head_dim, out, out_dtype, workspace, ws_bytes,
+               stream);
 }
 
 }  // extern "C"

@@ -43,20 +43,23 @@ def test_random_paged_decode(seed):
     qdt = "f32" if dtype == "f32" else "f16"
     q = workloads.normal(gen, (B, H * G, D), qdt)
     qd, td, tld = to_dev(q, d), to_dev(tables, d), to_dev(tl, d)
-    if window:
-        got = kvc.decode_window_paged(qd, layer, td, tld, max(lens), window, scale=scale_of(D))
-    elif G > 1:
-        got = kvc.decode_gqa_paged(qd, layer, td, tld, max(lens), scale=scale_of(D))
-    else:
-        got = kvc.decode_attn_paged(qd, layer, td, tld, max(lens), scale=scale_of(D))
-    torch.cuda.synchronize()
     want = ref.decode(q, tables, tl, scale_of(D), window=window)
-    check(got.float().cpu().numpy(), want, TOL["f32"] if dtype == "f32" else TOL["f16"],
-          f"seed={seed}")
-    # empty sequences give zero rows
-    for b, L in enumerate(lens):
-        if L == 0:
-            assert got[b].float().abs().sum().item() == 0.0
+    # a tight bound (one workgroup per pair when the pairs are few and short) and a loose one
+    # (equal chunks of the whole work list and the merge)
+    for max_ctx in (max(lens), max(lens) + 1024):
+        if window:
+            got = kvc.decode_window_paged(qd, layer, td, tld, max_ctx, window, scale=scale_of(D))
+        elif G > 1:
+            got = kvc.decode_gqa_paged(qd, layer, td, tld, max_ctx, scale=scale_of(D))
+        else:
+            got = kvc.decode_attn_paged(qd, layer, td, tld, max_ctx, scale=scale_of(D))
+        torch.cuda.synchronize()
+        check(got.float().cpu().numpy(), want, TOL["f32"] if dtype == "f32" else TOL["f16"],
+              f"seed={seed} max_ctx={max_ctx}")
+        # empty sequences give zero rows
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert got[b].float().abs().sum().item() == 0.0
 
 
 @pytest.mark.parametrize("seed", range(24))
