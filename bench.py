@@ -64,6 +64,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="CPU oracle sample: layers of the last step until this many seconds "
                          "(all BLAS threads), then the same layers on one thread")
+    ap.add_argument("--time-every", type=int, default=4,
+                    help="time attention pass 1 with HIP events on every Nth layer (events "
+                         "between launches cost time themselves; 1 times every launch)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the read-ceiling probe of the paged multi-head workloads")
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
@@ -152,8 +155,6 @@ class PagedBench:
         self.max_ctx = max_ctx
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.stream = torch.cuda.current_stream()
-        self.cow_ev = None   # HipEvents around copy-on-write copy launches (when timing them)
-        self.cow_n = 0       # copy launches timed so far
 
     def step(self, ev=None):
         kvc, torch = self.kvc, self.torch
@@ -176,13 +177,7 @@ class PagedBench:
         self.lens_now += 1
         for li, layer in enumerate(self.layers):
             if ncow:
-                timed_copy = self.cow_ev is not None and self.cow_n < self.cow_ev.n // 2
-                if timed_copy:
-                    self.cow_ev.record(2 * self.cow_n, self.stream)
                 kvc.copy_blocks(layer, self.cow_d[0, :ncow], self.cow_d[1, :ncow])
-                if timed_copy:
-                    self.cow_ev.record(2 * self.cow_n + 1, self.stream)
-                    self.cow_n += 1
             if not self.fused:
                 kvc.write_paged(layer, self.slot_d, self.knew[li], self.vnew[li])
             if ev is not None:
@@ -572,6 +567,32 @@ class HipEvents:
         for e in self.ev:
             self.hip.hipEventDestroy(e)
         self.ev = []
+
+
+class SampledEvents:
+    """HipEvents recorded only around the launches of every `every`-th layer: event index i
+    belongs to layer (i // 2) % layers; the others' records are skipped."""
+
+    def __init__(self, layers: int, steps: int, every: int):
+        self.layers, self.steps, self.every = layers, steps, max(1, every)
+        self.ev = HipEvents(2 * layers * steps)
+
+    def sampled(self, li: int) -> bool:
+        return li % self.every == 0
+
+    def record(self, i: int, stream) -> None:
+        if self.sampled((i // 2) % self.layers):
+            self.ev.record(i, stream)
+
+    def launch_ms(self):
+        """Pass-1 launch times of the sampled layers, [steps, sampled layers]."""
+        return np.array([[self.ev.elapsed_ms(2 * (self.layers * s + li),
+                                             2 * (self.layers * s + li) + 1)
+                          for li in range(self.layers) if self.sampled(li)]
+                         for s in range(self.steps)])
+
+    def close(self) -> None:
+        self.ev.close()
 
 
 class ContigBench:
@@ -988,11 +1009,9 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warm-up done", file=sys.stderr, flush=True)
 
-    evs = HipEvents(2 * layers * K)
+    evs = SampledEvents(layers, K, args.time_every)
     if sampling:
         bench.step_ev = HipEvents(2 * K)
-        bench.cow_ev = HipEvents(2 * layers * (K // bench.gen_len + 1))
-        bench.cow_n = 0
         bench.gen_step = bench.gen_len     # the timed steps start a fresh generation
     total_bytes = 0
     pass1_bytes, unique = [], []
@@ -1006,8 +1025,7 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
-    p1_ms = np.array([[evs.elapsed_ms(2 * (layers * s + li), 2 * (layers * s + li) + 1)
-                       for li in range(layers)] for s in range(K)])  # [K, L]
+    p1_ms = evs.launch_ms()   # [K, sampled layers]
     evs.close()
     p1_avg_s = float(p1_ms.mean()) / 1e3
     p1_bytes_avg = float(np.mean(pass1_bytes))
@@ -1064,6 +1082,7 @@ def main():
             "kernel_match": kernel_match(w, fused),
             **roof,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
+            "timed_launches": int(p1_ms.size),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
             "kernel_source": os.path.basename(workload_source(w)),
             "kernel_source_sha256_16": source_hash(workload_source(w)),
@@ -1075,9 +1094,6 @@ def main():
         step_us = np.array([bench.step_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]) * 1e3
         bench.step_ev.close()
         idx = np.array(bench.step_index)
-        cow_us = sum(bench.cow_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(bench.cow_n)) * 1e3
-        bench.cow_ev.close()
-        n_cow_steps = int(sum(1 for c in bench.cow_per_step if c))
         ub = bench.unique_bytes()
         line["sampling"] = {
             "candidates": w.batch, "prompt": bench.prompt, "generate": bench.gen_len,
@@ -1086,7 +1102,8 @@ def main():
             "blocks_used_last_step": bench.pool.stats()["used"],
             "first_step_us": round(float(step_us[idx == 0].mean()), 1) if (idx == 0).any() else None,
             "other_steps_median_us": round(float(np.median(step_us[idx != 0])), 1),
-            "cow_copy_us_per_copy_step": round(cow_us / n_cow_steps, 1) if n_cow_steps else 0.0,
+            "first_step_extra_us": (round(float(step_us[idx == 0].mean() - np.median(step_us[idx != 0])),
+                                          1) if (idx == 0).any() else None),
             "logical_gbs": round(value, 1),
             "unique_bytes_per_launch": int(ub),
             "logical_bytes_per_launch_last_step": int(pass1_bytes[-1]),
