@@ -41,6 +41,7 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
 constexpr int kPairTiles = 8;      // pair mode: tiles per wavefront at most
+constexpr int kMfmaWgWaves = 8;    // matrix-core pass 1 with workgroup combine: wavefronts per CU
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
 constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
@@ -95,6 +96,7 @@ struct DecodeArgs {
   int32_t window;      // rolling window: attend positions max(0, L - window) .. L-1 (0: none)
   int32_t stage_rows;  // staged output rows per wavefront (LDS)
   int32_t pair_mode;   // one workgroup per pair, combined in LDS (no merge), else equal chunks
+  int32_t wg_combine;  // equal chunks; pairs cut between a workgroup's wavefronts combined in LDS
   int32_t q_f16, out_f16;
   float cl2;  // scale * log2(e)
 };
@@ -564,8 +566,25 @@ __device__ __forceinline__ void merge_lanes(float &m, float &l, float *acc) {
 }
 
 // LDS of a pass-1 workgroup: pre[B+1], len[B], wsum[kWgWaves], then (16-byte aligned) the
-// stages of its wavefronts.
+// stages of its wavefronts, then (workgroup combine) their edge slots and the slots'
+// descriptions, then (matrix cores) one fp16 V tile per wavefront.
 __host__ __device__ inline int32_t stage_offset(int32_t B) { return (2 * B + 1 + kWgWaves + 3) & ~3; }
+
+struct LdsPlan {
+  size_t edge, einfo, vbuf, total;  // byte offsets from the start of LDS, and the total
+};
+
+__host__ __device__ inline LdsPlan lds_plan(int32_t B, int32_t D, int32_t stage_rows, int32_t gq,
+                                            bool wg_combine, bool mfma) {
+  LdsPlan p;
+  p.edge = (static_cast<size_t>(stage_offset(B)) +
+            static_cast<size_t>(kWgWaves) * stage_rows * (D + 4)) * sizeof(float);
+  p.einfo = p.edge + (wg_combine ? static_cast<size_t>(kWgWaves) * 2 * gq * (D + 4) * sizeof(float)
+                                 : 0);
+  p.vbuf = p.einfo + (wg_combine ? static_cast<size_t>(kWgWaves) * 4 * sizeof(int32_t) : 0);
+  p.total = p.vbuf + (mfma ? static_cast<size_t>(kWgWaves) * kBlock * D * 2 : 0);
+  return p;
+}
 
 // Finished segments wait in LDS until the wavefront's loads are done (or the stage is full), so
 // that no global store sits between a tile's loads and the wait for them: a wait for loads on
@@ -575,7 +594,18 @@ __host__ __device__ inline int32_t stage_offset(int32_t B) { return (2 * B + 1 +
 struct Stage {
   float *base;  // this wavefront's entries (DecodeArgs::stage_rows of them)
   int32_t n;    // entries in use
+  // workgroup combine: the wavefront's two edge slots (0: the segment cut at its chunk's start,
+  // 1: the one cut at its end; GQ entries each) and their descriptions {pair, flags} (flags bit
+  // 0: holds an entry, bit 1: cut at the start, bit 2: cut at the end); null otherwise
+  float *edge;
+  int32_t *einfo;
 };
+
+// Where a finished segment's entries go: an edge slot when the workgroup combines cut pairs and
+// the segment was cut, else the stage (flushed first if its GQ entries do not fit).
+template <int D>
+__device__ __forceinline__ float *segment_entries(const DecodeArgs &a, const Seg &sg, int32_t gq,
+                                                  int32_t stage_rows, Stage &st, bool &to_edge);
 
 // Store the staged entries: output rows normalised by 1/l (fp16 rounded to nearest even, or
 // fp32), records copied with their m and l. Every lane takes columns lane, lane+64, ...
@@ -605,15 +635,33 @@ __device__ __forceinline__ void flush_stage(const DecodeArgs &a, Stage &st) {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+template <int D>
+__device__ __forceinline__ float *segment_entries(const DecodeArgs &a, const Seg &sg, int32_t gq,
+                                                  int32_t stage_rows, Stage &st, bool &to_edge) {
+  to_edge = st.edge != nullptr && (sg.cut_start || sg.cut_end);
+  if (to_edge) {
+    const int slot = sg.cut_start ? 0 : 1;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      st.einfo[2 * slot] = sg.b * a.Hp + sg.h;
+      st.einfo[2 * slot + 1] = 1 | (sg.cut_start ? 2 : 0) | (sg.cut_end ? 4 : 0);
+    }
+    return st.edge + slot * gq * (D + 4);
+  }
+  if (st.n + gq > stage_rows) flush_stage<D>(a, st);
+  return st.base + st.n * (D + 4);
+}
+
 // Finish a segment: for each of its GQ query heads combine the TPL lane groups, then stage
 // either the output row (the whole pair was in this chunk) or a record (slot 0 if the pair
-// began before the chunk, else 1; the record of head r is row (2w+slot)*GQ + r).
+// began before the chunk, else 1; the record of head r is row (2w+slot)*GQ + r), or, when the
+// workgroup combines cut pairs, put a cut segment's entries in its edge slot.
 template <int KV, int D, int GQ>
 __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, int32_t w, int g,
                                            int c, float *m, float *l,
                                            float (*acc)[Geo<KV, D>::EPL], Stage &st) {
   using G = Geo<KV, D>;
-  if (st.n + GQ > kStageRows) flush_stage<D>(a, st);
+  bool to_edge;
+  float *const e0 = segment_entries<D>(a, s, GQ, kStageRows, st, to_edge);
   const bool whole = !s.cut_start && !s.cut_end;
   const int32_t out0 = s.b * a.Hq + s.h * GQ;
   const int32_t rec0 = (w * 2 + (s.cut_start ? 0 : 1)) * GQ;
@@ -624,7 +672,7 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
     if constexpr (G::LPT <= 16) merge_lanes<16, G::EPL>(m[r], l[r], acc[r]);
     merge_lanes<32, G::EPL>(m[r], l[r], acc[r]);
     const int32_t dest = whole ? out0 + r : -1 - (rec0 + r);
-    float *e = st.base + (st.n + r) * (D + 4);
+    float *e = e0 + r * (D + 4);
     if (g == 0) {
 #pragma unroll
       for (int k = 0; k < G::EPL; ++k) e[c * G::EPL + k] = acc[r][k];
@@ -635,7 +683,7 @@ __device__ __forceinline__ void finish_seg(const DecodeArgs &a, const Seg &s, in
       }
     }
   }
-  st.n += GQ;
+  if (!to_edge) st.n += GQ;
 }
 
 // ---- pass-1 cores ---------------------------------------------------------------------------
@@ -977,12 +1025,13 @@ struct MfmaCore {
     lane_pair<32>(l, u, v);
     l = u + v;
     const int32_t GQ = a.gq;
-    if (st.n + GQ > a.stage_rows) flush_stage<D>(a, st);
+    bool to_edge;
+    float *const e0 = segment_entries<D>(a, sg, GQ, a.stage_rows, st, to_edge);
     const bool whole = !sg.cut_start && !sg.cut_end;
     const int32_t out0 = sg.b * a.Hq + sg.h * GQ;
     const int32_t rec0 = (w * 2 + (sg.cut_start ? 0 : 1)) * GQ;
     if (j < GQ) {
-      float *e = st.base + (st.n + j) * (D + 4);
+      float *e = e0 + j * (D + 4);
       const float vr = is_q8(KV) ? s.vref : 1.f;
 #pragma unroll
       for (int dc = 0; dc < NDC; ++dc)
@@ -993,7 +1042,7 @@ struct MfmaCore {
         e[D + 2] = __int_as_float(whole ? out0 + j : -1 - (rec0 + j));
       }
     }
-    st.n += GQ;
+    if (!to_edge) st.n += GQ;
   }
 };
 
@@ -1089,6 +1138,19 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   st.base = reinterpret_cast<float *>(smem + stage_offset(a.B)) +
             (threadIdx.x >> 6) * a.stage_rows * (D + 4);
   st.n = 0;
+  st.edge = nullptr;
+  st.einfo = nullptr;
+  if (a.wg_combine) {
+    const LdsPlan lp = lds_plan(a.B, D, a.stage_rows, gq, true, false);
+    char *lds = reinterpret_cast<char *>(smem);
+    const int wave = threadIdx.x >> 6;
+    st.edge = reinterpret_cast<float *>(lds + lp.edge) + wave * 2 * gq * (D + 4);
+    st.einfo = reinterpret_cast<int32_t *>(lds + lp.einfo) + wave * 4;
+    if ((threadIdx.x & (kWave - 1)) == 0) {
+      st.einfo[1] = 0;
+      st.einfo[3] = 0;
+    }
+  }
   if (a.pair_mode) {
     // workgroup x takes pair x = (b, h) whole; its tiles are numbered from 0 at the start of
     // sequence b (pre[b] = 0, pre[b+1] = tiles per pair) and cut into one chunk per wavefront
@@ -1126,7 +1188,8 @@ __device__ __forceinline__ Stage partial_setup(const DecodeArgs &a, int32_t *sme
   if (blockIdx.x == 0) {
     for (int i = threadIdx.x; i <= a.B; i += kWgThreads) a.ws_pre[i] = pre[i];
     if (threadIdx.x == 0) {
-      a.ws_hdr[0] = C;
+      // the merge's parts: wavefronts, or whole workgroups when they combine their own cuts
+      a.ws_hdr[0] = a.wg_combine ? C * kWgWaves : C;
       a.ws_hdr[1] = a.B;
       a.ws_hdr[2] = a.Hp;
       a.ws_hdr[3] = D;
@@ -1193,6 +1256,78 @@ __device__ __forceinline__ void combine_pair(const DecodeArgs &a, const int32_t 
   }
 }
 
+// Workgroup combine, after every wavefront of the workgroup has run its chunk: the cut segments
+// in the edge slots are taken in chunk order (wavefront 0's start slot, its end slot, wavefront
+// 1's ...); consecutive entries of one pair are combined (maximum, rescaled sums). A pair found
+// whole inside the workgroup gets its output row; one that began before the workgroup's first
+// tile becomes the workgroup's record in slot 0, one that goes on past its last tile the record
+// in slot 1 (the merge takes workgroups as its parts). Wavefront w takes heads w, w + 4, ...
+template <int D>
+__device__ __forceinline__ void combine_wg(const DecodeArgs &a, int32_t *smem, int32_t gq) {
+  const LdsPlan lp = lds_plan(a.B, D, a.stage_rows, gq, true, false);
+  const char *lds = reinterpret_cast<const char *>(smem);
+  const float *edge = reinterpret_cast<const float *>(lds + lp.edge);
+  const int32_t *einfo = reinterpret_cast<const int32_t *>(lds + lp.einfo);
+  const int lane = threadIdx.x & (kWave - 1);
+  const int64_t wg = blockIdx.x;
+  for (int32_t r = threadIdx.x >> 6; r < gq; r += kWgWaves) {
+    bool have = false, began = false, ends = false;
+    int32_t pair = -1;
+    float m = kFloor, l = 0.f, o0 = 0.f, o1 = 0.f;
+    auto emit = [&]() {
+      if (!have) return;
+      if (began || ends) {
+        float *rec = a.ws_rec + ((wg * 2 + (began ? 0 : 1)) * gq + r) * (D + 4);
+        rec[lane] = o0;
+        if (D > kWave) rec[lane + kWave] = o1;
+        if (lane == 0) {
+          rec[D] = m;
+          rec[D + 1] = l;
+        }
+      } else {
+        const int32_t b = pair / a.Hp;
+        const int32_t h = pair - b * a.Hp;
+        const int64_t row = static_cast<int64_t>(b) * a.Hq + static_cast<int64_t>(h) * gq + r;
+        const float inv = l > 0.f ? 1.0f / l : 0.f;
+        store_elem(a.out, row * D + lane, o0 * inv, a.out_f16);
+        if (D > kWave) store_elem(a.out, row * D + lane + kWave, o1 * inv, a.out_f16);
+      }
+      have = false;
+    };
+    for (int w = 0; w < kWgWaves; ++w) {
+      for (int slot = 0; slot < 2; ++slot) {
+        const int32_t flags = einfo[w * 4 + 2 * slot + 1];
+        if (!(flags & 1)) continue;
+        const int32_t p = einfo[w * 4 + 2 * slot];
+        const float *e = edge + ((w * 2 + slot) * gq + r) * (D + 4);
+        const float em = e[D], el = e[D + 1];
+        const float x0 = e[lane];
+        const float x1 = D > kWave ? e[lane + kWave] : 0.f;
+        if (have && p == pair) {
+          const float M = fmaxf(m, em);
+          const float fa = __builtin_amdgcn_exp2f(m - M);
+          const float fb = __builtin_amdgcn_exp2f(em - M);
+          l = l * fa + el * fb;
+          o0 = o0 * fa + x0 * fb;
+          o1 = o1 * fa + x1 * fb;
+          m = M;
+        } else {
+          emit();
+          have = true;
+          pair = p;
+          m = em;
+          l = el;
+          o0 = x0;
+          o1 = x1;
+          began = w == 0 && slot == 0 && (flags & 2);
+        }
+        ends = w == kWgWaves - 1 && (flags & 4);
+      }
+    }
+    emit();
+  }
+}
+
 template <bool PAGED, int KV, int D, bool QF16, int GQ, bool WIN>
 __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const DecodeArgs a) {
   extern __shared__ int32_t smem[];
@@ -1206,6 +1341,12 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_kernel(const Decode
     combine_pair<D>(a, smem, GQ);
     return;
   }
+  if (a.wg_combine) {
+    if (f0 < f1) run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, true);
+    __syncthreads();
+    combine_wg<D>(a, smem, GQ);
+    return;
+  }
   if (f0 >= f1) return;
   run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, true);
 }
@@ -1217,14 +1358,20 @@ __global__ void __launch_bounds__(kWgThreads) decode_partial_mfma_kernel(const D
   int32_t f0, f1, b0, w;
   Stage st = partial_setup<PAGED, Core, D>(a, smem, a.gq, f0, f1, b0, w);
   _Float16 *vbuf = reinterpret_cast<_Float16 *>(
-      reinterpret_cast<char *>(smem + stage_offset(a.B)) +
-      static_cast<size_t>(kWgWaves) * a.stage_rows * (D + 4) * sizeof(float) +
+      reinterpret_cast<char *>(smem) +
+      lds_plan(a.B, D, a.stage_rows, a.gq, a.wg_combine != 0, true).vbuf +
       (threadIdx.x >> 6) * Core::kVbufBytes);
   const Core core(threadIdx.x & (kWave - 1), vbuf);
   if (a.pair_mode) {
     if (f0 < f1) run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, false);
     __syncthreads();
     combine_pair<D>(a, smem, a.gq);
+    return;
+  }
+  if (a.wg_combine) {
+    if (f0 < f1) run_chunk<PAGED, Core>(a, smem, smem + a.B + 1, f0, f1, b0, w, st, core, true);
+    __syncthreads();
+    combine_wg<D>(a, smem, a.gq);
     return;
   }
   if (f0 >= f1) return;
@@ -1495,17 +1642,11 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   // staged rows per wavefront: a segment stages GQ rows at once; the matrix-core kernel also
   // holds one fp16 V tile per wavefront
   const int stage_rows = GQ <= kStageRows ? kStageRows : 2 * kStageRows;
-  const size_t shmem = (static_cast<size_t>(stage_offset(B)) +
-                        static_cast<size_t>(kWgWaves) * stage_rows * (D + 4)) *
-                           sizeof(int32_t) +
-                       (gp.mfma ? static_cast<size_t>(kWgWaves) * kBlock * D * 2 : 0);
+  size_t shmem = lds_plan(B, D, stage_rows, GQ, false, gp.mfma).total;
   // one round of wavefronts: never more than fit on the GPU at once
   int wpc = waves_per_cu(kv_dtype, D, gp.mfma, paged);
   const int fit = resident_waves_per_cu(kern, shmem);
   if (fit > 0) wpc = std::min(wpc, fit);
-  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
-  P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
-  P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
   // Few, short pairs (every pair's wavefronts resident at once, at most kPairTiles tiles per
   // wavefront by the caller's bound max_ctx): one workgroup per pair, its wavefronts splitting
   // the pair's tiles and combining in LDS, so no pair is left for the merge launch.
@@ -1515,6 +1656,23 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   const int64_t pair_tiles = (pair_span + kBlock - 1) / kBlock;
   const bool pair_mode = pair_tiles <= static_cast<int64_t>(kWgWaves) * kPairTiles &&
                          pairs * kWgWaves <= static_cast<int64_t>(device_cu_count()) * wpc;
+  // The matrix-core kernel holds one tile in flight per wavefront; with one wavefront per SIMD
+  // that is too few bytes in flight, and with two, twice the cut pairs, each leaving up to 16
+  // records. So it runs two wavefronts per SIMD whose workgroups combine the pairs cut between
+  // their own wavefronts in LDS: only pairs cut at workgroup edges leave records for the merge.
+  bool wg_combine = false;
+  if (gp.mfma && !pair_mode) {
+    const size_t sh_wg = lds_plan(B, D, stage_rows, GQ, true, true).total;
+    const int fit_wg = resident_waves_per_cu(kern, sh_wg);
+    if (fit_wg >= kMfmaWgWaves) {
+      wg_combine = true;
+      shmem = sh_wg;
+      wpc = kMfmaWgWaves;
+    }
+  }
+  int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
+  P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
+  P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
 
   DecodeArgs &a = pl.a;
   a = DecodeArgs{};
@@ -1533,6 +1691,7 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   a.window = window;
   a.stage_rows = stage_rows;
   a.pair_mode = pair_mode ? 1 : 0;
+  a.wg_combine = wg_combine ? 1 : 0;
   a.Hp = Hp;
   a.Hq = H * G;
   a.cap = cap;
