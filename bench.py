@@ -299,6 +299,7 @@ class SamplingBench(PagedBench):
         self.step_ev = None          # (HipEvents, index) per step when timing steps
         self.step_index = []         # generation step of every timed step
         self.cow_per_step = []       # copy-on-write pairs of every timed step
+        self.unique_per_step = []    # unique K/V bytes of one layer at every timed step
 
     def _start(self):
         """The prompt's sequence and its 7 forks; returns the prompt's slots."""
@@ -326,6 +327,7 @@ class SamplingBench(PagedBench):
             self.step_ev.record(2 * i + 1, self.stream)
             self.cow_per_step.append(self.pool.stats()["cow_copies"] - before)
             self.step_index.append(self.gen_step)
+            self.unique_per_step.append(self.unique_bytes())
         self.gen_step += 1
 
     def unique_bytes(self):
@@ -1094,7 +1096,6 @@ def main():
         step_us = np.array([bench.step_ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(K)]) * 1e3
         bench.step_ev.close()
         idx = np.array(bench.step_index)
-        ub = bench.unique_bytes()
         line["sampling"] = {
             "candidates": w.batch, "prompt": bench.prompt, "generate": bench.gen_len,
             "cow_copies_per_generation": int(sum(c for c, i in zip(bench.cow_per_step, idx)
@@ -1105,7 +1106,7 @@ def main():
             "first_step_extra_us": (round(float(step_us[idx == 0].mean() - np.median(step_us[idx != 0])),
                                           1) if (idx == 0).any() else None),
             "logical_gbs": round(value, 1),
-            "unique_bytes_per_launch": int(ub),
+            "unique_bytes_per_launch": int(np.mean(bench.unique_per_step)),
             "logical_bytes_per_launch_last_step": int(pass1_bytes[-1]),
         }
     if not args.no_ceiling and not prefill and not compress and not sampling:
