@@ -10,19 +10,22 @@
 //
 // A workgroup of four wavefronts takes one K/V head and 128 query rows: 128 consecutive
 // positions of one query head, or 64 of 2 heads, or 32 of 4 heads of a group sharing the K/V
-// head; each wavefront owns 32 rows of one head. It walks the keys in steps of 32 (two cache
+// head; each wavefront owns 32 rows of one head. It walks the keys in steps of 64 (four cache
 // blocks) from 0 to its last row's position. A step's K and V is loaded once, by all 256 threads
-// with 16-byte loads (two steps ahead, in registers), into LDS (two buffers, one barrier per
-// step) and serves the four wavefronts. Per wavefront and step:
+// with 16-byte loads (one step ahead, in registers), into LDS (two buffers, one barrier per
+// step) and serves the four wavefronts. Per wavefront and step, for each 32-key tile of it:
 //   S^T = K . Q^T with D/16 v_mfma_f32_32x32x16_f16: lane (h, j) = (lane/32, lane%32) feeds key
 //     row perm(j) (perm swaps bits 2 and 3) and query row j and receives 16 scores of row j, keys
-//     16(v/8) + 8h + v%8; keys past the row's position are masked to -inf on the steps that
-//     reach it;
+//     16(v/8) + 8h + v%8 of the tile; keys past the row's position are masked to -inf on the
+//     steps that reach it;
 //   the online softmax keeps, per row, a reference that moves only when a score passes it by the
 //     headroom, and per lane the partial sum of its keys' weights;
 //   O^T += V^T . P^T with D/32 x 4 v_mfma_f32_32x32x16_f16, the weights as fp16 hi + lo (about 22
 //     bits): for 16 keys the hi and the lo weights each take one instruction on the same V^T
 //     operand, which two transposing LDS reads deliver.
+// Both tiles' score products are issued before the first tile's softmax, so that the vector
+// ALUs work on one tile while the matrix cores work on the other (64-key steps measured 4-5 %
+// faster than 32-key steps with two steps of loads in flight).
 // LDS rows are padded (K by 16 bytes, V by 64) so that the rows one read instruction takes fall
 // on distinct banks and every read offset is an immediate.
 #include <algorithm>
@@ -38,13 +41,16 @@ constexpr int kPfWaves = 4;
 constexpr int kPfThreads = kPfWaves * kWave;
 constexpr int kWaveRows = 32;                   // query rows per wavefront
 constexpr int kPfRows = kWaveRows * kPfWaves;  // query rows per workgroup
-constexpr int kStep = 2 * kBlock;               // keys per step (two cache blocks)
+constexpr int kStepBlocks = 4;                  // cache blocks per step
+constexpr int kStep = kStepBlocks * kBlock;     // keys per step
+constexpr int kTiles = kStep / 32;              // 32-key score tiles per step
 constexpr int kMaxSeqs = 4096;
 // steps whose K/V loads are in flight in registers, and the loop unroll that keeps both the LDS
 // buffer (2) and the register set (kAhead) of every step a compile-time choice
-constexpr int kAhead = 2;
+constexpr int kAhead = 1;
 constexpr int kUnroll = kAhead == 3 ? 6 : 2;
 static_assert(kAhead >= 1 && kAhead <= 3, "prefetch depth");
+static_assert(kStep % 32 == 0, "whole score tiles");
 // weight headroom (log2 units): weights stay below 2^kHi, so both fp16 terms stay finite
 constexpr float kHead = 7.f;
 constexpr float kHi = 15.f;
@@ -122,17 +128,30 @@ static __device__ __forceinline__ f16x4 lds_read_tr(const char *p) {
                  (__attribute__((address_space(3))) i16x4 *)(p)));
 }
 
-// The weights p0, p1 as fp16 pairs: hi = (p0, p1) rounded to nearest, lo = the rounding errors
-// p - hi rounded to nearest. v_fma_mix takes hi's half as fp16 and computes fma(hi, -1, p) in
-// fp32, which is p - hi exactly, then rounds once to fp16 into the low or the high half.
-static __device__ __forceinline__ void split_pair(float p0, float p1, uint32_t &hi,
-                                                  uint32_t &lo) {
-  const f16x2 h = {static_cast<_Float16>(p0), static_cast<_Float16>(p1)};
-  hi = __builtin_bit_cast(uint32_t, h);
-  asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(lo) : "v"(hi), "v"(p0));
-  asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]"
-      : "+v"(lo)
-      : "v"(hi), "v"(p1));
+// The weights of 8 consecutive keys as fp16 pairs: hi[i] = (p[2i], p[2i+1]) rounded to nearest,
+// lo[i] = the rounding errors p - hi rounded to nearest. v_fma_mix takes hi's half as fp16 and
+// computes fma(hi, -1, p) in fp32, which is p - hi exactly, then rounds once to fp16 into the low
+// or the high half. The compiler does not see these writes as vector-ALU writes, so the statement
+// ends with the two wait states a matrix-core instruction reading lo needs after them.
+static __device__ __forceinline__ void split8(const float (&p)[8], uint32_t (&hi)[4],
+                                              uint32_t (&lo)[4]) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 h = {static_cast<_Float16>(p[2 * i]), static_cast<_Float16>(p[2 * i + 1])};
+    hi[i] = __builtin_bit_cast(uint32_t, h);
+  }
+  asm("v_fma_mixlo_f16 %0, %4, -1.0, %8 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %1, %5, -1.0, %10 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %2, %6, -1.0, %12 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixlo_f16 %3, %7, -1.0, %14 op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %0, %4, -1.0, %9 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %1, %5, -1.0, %11 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %2, %6, -1.0, %13 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "v_fma_mixhi_f16 %3, %7, -1.0, %15 op_sel:[1,0,0] op_sel_hi:[1,0,0]\n\t"
+      "s_nop 1"
+      : "=&v"(lo[0]), "=&v"(lo[1]), "=&v"(lo[2]), "=&v"(lo[3])
+      : "v"(hi[0]), "v"(hi[1]), "v"(hi[2]), "v"(hi[3]), "v"(p[0]), "v"(p[1]), "v"(p[2]),
+        "v"(p[3]), "v"(p[4]), "v"(p[5]), "v"(p[6]), "v"(p[7]));
 }
 
 template <bool PAGED, int D>
@@ -239,37 +258,40 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     // in scalar registers), and the addresses of a step are planned before the previous step's
     // LDS stores are issued, so waiting for the entries never waits for LDS work.
     struct StepPlan {
-      int64_t base0, base1;  // byte offsets of the step's two blocks of this head
-      int32_t lim0, lim1;    // last row of each block that holds a position
-      int bad;               // bit i: block i holds positions but is not in the pool
+      int64_t base[kStepBlocks];  // byte offsets of the step's blocks of this head
+      int32_t lim[kStepBlocks];   // last row of each block that holds a position
+      int bad;                    // bit i: block i holds positions but is not in the pool
     };
-    // entries of step s's blocks (32 s <= L - 1, so its first block holds positions; a second
-    // block past the end takes the first block's entry)
-    auto table_pair = [&](int32_t s, int32_t &p0, int32_t &p1) {
+    // entries of step s's blocks (kStep s <= L - 1, so its first block holds positions; a block
+    // past the end takes the first block's entry)
+    auto table_step = [&](int32_t s, int32_t (&p)[kStepBlocks]) {
       if constexpr (PAGED) {
-        p0 = trow[2 * s];
-        p1 = L - s * kStep - kBlock > 0 ? trow[2 * s + 1] : p0;
+        p[0] = trow[kStepBlocks * s];
+#pragma unroll
+        for (int i = 1; i < kStepBlocks; ++i)
+          p[i] = L - s * kStep - i * kBlock > 0 ? trow[kStepBlocks * s + i] : p[0];
       } else {
-        p0 = p1 = 0;
+#pragma unroll
+        for (int i = 0; i < kStepBlocks; ++i) p[i] = 0;
       }
     };
-    auto plan_step = [&](int32_t s, int32_t p0, int32_t p1) -> StepPlan {
+    auto plan_step = [&](int32_t s, const int32_t (&p)[kStepBlocks]) -> StepPlan {
       StepPlan pl;
       const int32_t nv0 = min(kBlock, L - s * kStep);
-      const int32_t nv1 = min(kBlock, L - s * kStep - kBlock);
       pl.bad = 0;
-      if constexpr (PAGED) {
-        const bool in0 = static_cast<uint32_t>(p0) < static_cast<uint32_t>(a.num_blocks);
-        const bool in1 = static_cast<uint32_t>(p1) < static_cast<uint32_t>(a.num_blocks);
-        pl.bad = (in0 ? 0 : 1) | (nv1 > 0 && !in1 ? 2 : 0);
-        pl.base0 = static_cast<int64_t>(in0 ? p0 : 0) * a.H * BLK + kv_head_off;
-        pl.base1 = static_cast<int64_t>(in1 ? p1 : 0) * a.H * BLK + kv_head_off;
-      } else {
-        pl.base0 = kv_head_off + static_cast<int64_t>(2 * s) * BLK;
-        pl.base1 = nv1 > 0 ? pl.base0 + BLK : pl.base0;
+#pragma unroll
+      for (int i = 0; i < kStepBlocks; ++i) {
+        const int32_t nv = min(kBlock, L - s * kStep - i * kBlock);
+        if constexpr (PAGED) {
+          // a block past the end holds block 0's entry and is zeroed with it
+          const bool in = static_cast<uint32_t>(p[i]) < static_cast<uint32_t>(a.num_blocks);
+          pl.bad |= in ? 0 : 1 << i;
+          pl.base[i] = static_cast<int64_t>(in ? p[i] : 0) * a.H * BLK + kv_head_off;
+        } else {
+          pl.base[i] = kv_head_off + static_cast<int64_t>(kStepBlocks * s + (nv > 0 ? i : 0)) * BLK;
+        }
+        pl.lim[i] = (nv > 0 ? nv : nv0) - 1;
       }
-      pl.lim0 = nv0 - 1;
-      pl.lim1 = (nv1 > 0 ? nv1 : nv0) - 1;
       return pl;
     };
     auto issue_step = [&](const StepPlan &pl, uint4 (&kd)[LPT], uint4 (&vd)[LPT]) {
@@ -277,9 +299,16 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
       for (int i = 0; i < LPT; ++i) {
         const int p = tid + i * kPfThreads;
         const int row = p / NCH;
-        const bool sb = (row >> 4) != 0;  // block of the step
-        const int32_t r = min(row & 15, sb ? pl.lim1 : pl.lim0);
-        const int64_t off = (sb ? pl.base1 : pl.base0) + r * ROW + (p % NCH) * 16;
+        const int sb = row >> 4;  // block of the step
+        int64_t base = pl.base[0];
+        int32_t lim = pl.lim[0];
+#pragma unroll
+        for (int k = 1; k < kStepBlocks; ++k) {
+          base = sb == k ? pl.base[k] : base;
+          lim = sb == k ? pl.lim[k] : lim;
+        }
+        const int32_t r = min(row & 15, lim);
+        const int64_t off = base + r * ROW + (p % NCH) * 16;
         kd[i] = *reinterpret_cast<const uint4 *>(a.k + off);
         vd[i] = *reinterpret_cast<const uint4 *>(a.v + off);
       }
@@ -323,66 +352,85 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
 
     // The wavefront's share of one step (keys kStep * s ..), its K and V in LDS at `buf`. MASK:
     // the step holds keys past some row's position or blocks outside the pool (bits of `bad`).
+    // The scores of every 32-key tile are issued first; the softmax of tile t then runs on the
+    // vector ALUs while the matrix cores still work on the scores of tile t + 1 or on the
+    // products of tile t - 1.
     auto compute = [&](const char *buf, int32_t s, auto mask_tag, int bad) {
       constexpr bool MASK = decltype(mask_tag)::value;
-      f32x16 sc;
+      // tiles holding a key at or before the wavefront's last row (every tile unless MASK)
+      const int nt = MASK ? min(kTiles, (wave_last - s * kStep) / 32 + 1) : kTiles;
+      // (a skipped tile's scores are never read; the first product of a tile takes a zero
+      // accumulator as an immediate)
+      f32x16 sc[kTiles];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) sc[e] = 0.f;
+      for (int t = 0; t < kTiles; ++t) {
+        if (MASK && t >= nt) continue;
 #pragma unroll
-      for (int c = 0; c < NQK; ++c) {
-        const uint4 kv = *reinterpret_cast<const uint4 *>(buf + k_lds + c * 32);
-        sc = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kv), as_f16x8(qv[c]), sc, 0, 0, 0);
-      }
-      if constexpr (MASK) {
-        // key 16(v/8) + 8h + v%8 of the step is kept when at or before the row's position
-        const int32_t lim = my_pos - s * kStep - 8 * h;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const bool keep = 16 * (v >> 3) + (v & 7) <= lim && !((bad >> (v >> 3)) & 1);
-          sc[v] = keep ? sc[v] : -__builtin_inff();
+        for (int c = 0; c < NQK; ++c) {
+          const uint4 kv = *reinterpret_cast<const uint4 *>(buf + t * 32 * KROW + k_lds + c * 32);
+          sc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(as_f16x8(kv), as_f16x8(qv[c]),
+                                                         c == 0 ? f32x16{} : sc[t], 0, 0, 0);
         }
       }
-      float mx = sc[0];
 #pragma unroll
-      for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[v]);
-      // a score that would put a weight above 2^kHi moves the row's reference (rare)
-      if (__ballot(mx * cl2 > mt) != 0) {
-        float u, t;
-        lane_pair<32>(mx * cl2, u, t);
-        const float rmax = fmaxf(u, t);
-        const float mnew = rmax > mt ? rmax - kHead : m;
-        const float f = __builtin_amdgcn_exp2f(m - mnew);
-        l *= f;
+      for (int t = 0; t < kTiles; ++t) {
+        if (MASK && t >= nt) break;
+        if constexpr (MASK) {
+          // key 32t + 16(v/8) + 8h + v%8 of the step (block 2t + v/8) is kept when at or before
+          // the row's position
+          const int32_t lim = my_pos - s * kStep - 32 * t - 8 * h;
 #pragma unroll
-        for (int dq = 0; dq < NDQ; ++dq) o[dq] *= f;
-        m = mnew;
-        mt = m + kHi;
-      }
-      const float nm = -m;
-      uint32_t ph[2][4], pl[2][4];  // keys 16 a16 + 8h + 2i, + 1 as fp16 pairs, hi and lo terms
+          for (int v = 0; v < 16; ++v) {
+            const bool keep =
+                16 * (v >> 3) + (v & 7) <= lim && !((bad >> (2 * t + (v >> 3))) & 1);
+            sc[t][v] = keep ? sc[t][v] : -__builtin_inff();
+          }
+        }
+        float mx = sc[t][0];
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v], cl2, nm));
-        const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[v + 1], cl2, nm));
-        l += p0;
-        l += p1;
-        split_pair(p0, p1, ph[v >> 3][(v & 7) >> 1], pl[v >> 3][(v & 7) >> 1]);
-      }
-      // O^T += V^T P^T: per 32 dims and 16 keys, the hi and the lo weights share one V^T operand
+        for (int v = 1; v < 16; ++v) mx = fmaxf(mx, sc[t][v]);
+        // a score that would put a weight above 2^kHi moves the row's reference (rare)
+        if (__ballot(mx * cl2 > mt) != 0) {
+          float u, w2;
+          lane_pair<32>(mx * cl2, u, w2);
+          const float rmax = fmaxf(u, w2);
+          const float mnew = rmax > mt ? rmax - kHead : m;
+          const float f = __builtin_amdgcn_exp2f(m - mnew);
+          l *= f;
 #pragma unroll
-      for (int a16 = 0; a16 < 2; ++a16) {
+          for (int dq = 0; dq < NDQ; ++dq) o[dq] *= f;
+          m = mnew;
+          mt = m + kHi;
+        }
+        const float nm = -m;
+        uint32_t ph[2][4], pl[2][4];  // keys 16 a16 + 8h + 2i, + 1 as fp16 pairs, hi and lo terms
 #pragma unroll
-        for (int dq = 0; dq < NDQ; ++dq) {
-          const char *vp = buf + v_lds + a16 * 16 * VROW + dq * 64;
-          const f16x4 v0 = lds_read_tr(vp);
-          const f16x4 v1 = lds_read_tr(vp + 4 * VROW);
-          const f16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
-          const f16x8 bh = __builtin_bit_cast(
-              f16x8, make_uint4(ph[a16][0], ph[a16][1], ph[a16][2], ph[a16][3]));
-          const f16x8 bl = __builtin_bit_cast(
-              f16x8, make_uint4(pl[a16][0], pl[a16][1], pl[a16][2], pl[a16][3]));
-          o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bh, o[dq], 0, 0, 0);
-          o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bl, o[dq], 0, 0, 0);
+        for (int a16 = 0; a16 < 2; ++a16) {
+          float p[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            p[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][8 * a16 + i], cl2, nm));
+            l += p[i];
+          }
+          split8(p, ph[a16], pl[a16]);
+        }
+        // O^T += V^T P^T: per 32 dims and 16 keys, the hi and the lo weights share one V^T
+        // operand
+#pragma unroll
+        for (int a16 = 0; a16 < 2; ++a16) {
+#pragma unroll
+          for (int dq = 0; dq < NDQ; ++dq) {
+            const char *vp = buf + v_lds + (2 * t + a16) * 16 * VROW + dq * 64;
+            const f16x4 v0 = lds_read_tr(vp);
+            const f16x4 v1 = lds_read_tr(vp + 4 * VROW);
+            const f16x8 va = __builtin_shufflevector(v0, v1, 0, 1, 2, 3, 4, 5, 6, 7);
+            const f16x8 bh = __builtin_bit_cast(
+                f16x8, make_uint4(ph[a16][0], ph[a16][1], ph[a16][2], ph[a16][3]));
+            const f16x8 bl = __builtin_bit_cast(
+                f16x8, make_uint4(pl[a16][0], pl[a16][1], pl[a16][2], pl[a16][3]));
+            o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bh, o[dq], 0, 0, 0);
+            o[dq] = __builtin_amdgcn_mfma_f32_32x32x16_f16(va, bl, o[dq], 0, 0, 0);
+          }
         }
       }
     };
@@ -391,18 +439,18 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
     // set, reload it with step s + kAhead, one barrier, compute. The LDS buffer written here was
     // last read two steps ago, before every wavefront passed the previous barrier.
     int bad_q[kAhead];
-    int32_t tp0 = 0, tp1 = 0;  // table entries of the step loaded next
+    int32_t tp[kStepBlocks];  // table entries of the step loaded next
 #pragma unroll
     for (int r = 0; r < kAhead; ++r) {
       bad_q[r] = 0;
       if (r < nstep) {
-        table_pair(r, tp0, tp1);
-        const StepPlan pl = plan_step(r, tp0, tp1);
+        table_step(r, tp);
+        const StepPlan pl = plan_step(r, tp);
         issue_step(pl, kr[r], vr[r]);
         bad_q[r] = pl.bad;
       }
     }
-    if (kAhead < nstep) table_pair(kAhead, tp0, tp1);
+    if (kAhead < nstep) table_step(kAhead, tp);
     auto step = [&](auto u_tag, int32_t s) {
       constexpr int U = decltype(u_tag)::value;
       constexpr int RS = U % kAhead;
@@ -410,12 +458,12 @@ __global__ void __launch_bounds__(kPfThreads) prefill_kernel(const PrefillArgs a
       const int bad = bad_q[RS];
       const bool more = s + kAhead < nstep;
       StepPlan pl{};
-      if (more) pl = plan_step(s + kAhead, tp0, tp1);
+      if (more) pl = plan_step(s + kAhead, tp);
       store_step(buf, bad, kr[RS], vr[RS]);
       if (more) {
         issue_step(pl, kr[RS], vr[RS]);
         bad_q[RS] = pl.bad;
-        if (s + kAhead + 1 < nstep) table_pair(s + kAhead + 1, tp0, tp1);
+        if (s + kAhead + 1 < nstep) table_step(s + kAhead + 1, tp);
       }
       __syncthreads();
       if (nrow > 0 && s * kStep <= wave_last) {
