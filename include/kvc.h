@@ -299,7 +299,8 @@ kvc_status kvc_decode_attn_paged_noalloc(const void *q, kvc_dtype q_dtype,
 /* The two passes as separate launches, for callers that time or schedule them apart.
  * kvc_decode_attn_{contig,paged} == the matching *_partial call followed by kvc_decode_merge
  * on the same stream, workspace and out. Pass 1 leaves a record of its split in the workspace;
- * kvc_decode_merge must follow it with the same B, H, D and out before the workspace is reused. */
+ * kvc_decode_merge must follow it with the same B, H, D and out before the workspace is reused.
+ * The merges return KVC_E_INVALID when B times the query heads exceeds 2^31 - 1. */
 kvc_status kvc_decode_partial_contig(const void *q, kvc_dtype q_dtype, const void *k_cache,
                                      const void *v_cache, kvc_dtype kv_dtype,
                                      const int32_t *ctx_lens, int32_t B, int32_t H, int32_t S_max,

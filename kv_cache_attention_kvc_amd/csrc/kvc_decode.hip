@@ -1387,74 +1387,82 @@ struct MergeArgs {
   int32_t B, H, G, D, out_f16;  // H: K/V heads; G: query heads per K/V head
 };
 
-constexpr int kMaxParts = 16;  // parts whose loads are in flight together
+constexpr int kMaxParts = 4;  // parts whose loads are in flight together (a cut pair spans 2-3)
 
+// Every load of a wavefront's first round (the workspace header and its sequence's two prefix
+// entries) is issued before any is waited for: every decision is taken from all of them at once.
+// So are the record loads of each round of parts: a part index past the pair's last is clamped
+// to it and its weight set to zero, so the loads need no branch. Two memory round trips for a
+// pair of up to kMaxParts parts.
+template <int D>
 __global__ void __launch_bounds__(kWgThreads) decode_merge_kernel(const MergeArgs a) {
   const int lane = threadIdx.x & (kWave - 1);
   const int32_t Hq = a.H * a.G;
-  const int64_t bh = static_cast<int64_t>(blockIdx.x) * kWgWaves + (threadIdx.x >> 6);
-  if (bh >= static_cast<int64_t>(a.B) * Hq) return;
-  if (a.ws_hdr[5] != 0) return;  // pass 1 ran one workgroup per pair and wrote every row
-  const int32_t b = static_cast<int32_t>(bh / Hq);
-  const int32_t hq = static_cast<int32_t>(bh % Hq);
-  const int D = a.D;
-  const int32_t C = a.ws_hdr[0];
+  // (the host keeps B * Hq below 2^31, so the row index divides in 32 bits)
+  const uint32_t row = blockIdx.x * kWgWaves + (threadIdx.x >> 6);
+  if (row >= static_cast<uint32_t>(a.B) * static_cast<uint32_t>(Hq)) return;
+  const int64_t bh = row;
+  const int32_t b = static_cast<int32_t>(row / static_cast<uint32_t>(Hq));
+  const int32_t hq = static_cast<int32_t>(row % static_cast<uint32_t>(Hq));
+  const int4 h03 = *reinterpret_cast<const int4 *>(a.ws_hdr);
+  const int2 h45 = *reinterpret_cast<const int2 *>(a.ws_hdr + 4);
+  const int32_t pb = a.ws_pre[b];
+  const int32_t nb = a.ws_pre[b + 1] - pb;
+  const int32_t C = h03.x;
   // query heads pass 1 served per wavefront (1 to 16, dividing G); the pass-1 pair of this
   // query head and its place among the pair's GQ heads
-  const int32_t GQ = a.ws_hdr[4];
+  const int32_t GQ = h45.x;
   const bool gq_ok = GQ >= 1 && GQ <= kMaxGroup && a.G % GQ == 0;
   const int32_t gq = gq_ok ? GQ : 1;
   const int32_t nsub = a.G / gq;
   const int32_t rr = hq % a.G;
   const int32_t h = (hq / a.G) * nsub + rr / gq;
   const int32_t r = rr % gq;
-  const int32_t pb = a.ws_pre[b];
-  const int32_t nb = a.ws_pre[b + 1] - pb;
-  if (nb == 0) {
+  const int32_t start = a.H * nsub * pb + h * nb;
+  // worker indices are clamped into the record array whatever the workspace holds
+  const int32_t C1 = max(C, 1);
+  const int32_t fw = min(max(start / C1, 0), kMaxWorkers - 1);
+  const int32_t lw = min(max((start + nb - 1) / C1, fw), kMaxWorkers - 1);
+  // h45.y != 0: pass 1 ran one workgroup per pair and wrote every row; C < 1 or a bad GQ: no
+  // pass-1 record in this workspace; fw == lw: the pair was finished by pass 1
+  const bool pair_mode = h45.y != 0;
+  if (!pair_mode && nb == 0) {  // an empty sequence
     for (int d = lane; d < D; d += kWave) store_elem(a.out, bh * D + d, 0.f, a.out_f16);
     return;
   }
-  if (C < 1 || nb < 0 || !gq_ok) return;  // no pass-1 record in this workspace
-  const int32_t start = a.H * nsub * pb + h * nb;
-  // worker indices are clamped into the record array whatever the workspace holds
-  const int32_t fw = min(max(start / C, 0), kMaxWorkers - 1);
-  const int32_t lw = min(max((start + nb - 1) / C, fw), kMaxWorkers - 1);
-  if (fw == lw) return;  // finished by pass 1
-  const int RS = D + 4;
+  if (pair_mode || C < 1 || nb < 0 || !gq_ok || fw == lw) return;
+  constexpr int RS = D + 4;
   const int32_t nparts = lw - fw + 1;
   auto rec = [&](int32_t i) -> const float * {  // part i of the pair: the first is in slot 1
     return a.ws_rec + ((static_cast<int64_t>(fw + i) * 2 + (i == 0 ? 1 : 0)) * gq + r) * RS;
   };
-  // the loads of up to kMaxParts parts are issued before any is used
   float M = kFloor, lsum = 0.f, o0 = 0.f, o1 = 0.f;
   for (int32_t i0 = 0; i0 < nparts; i0 += kMaxParts) {
     const int32_t n = min(nparts - i0, kMaxParts);
     float mi[kMaxParts], li[kMaxParts], x0[kMaxParts], x1[kMaxParts];
 #pragma unroll
     for (int k = 0; k < kMaxParts; ++k) {
-      mi[k] = kFloor;
-      li[k] = x0[k] = x1[k] = 0.f;
-      if (k < n) {
-        const float *p = rec(i0 + k);
-        mi[k] = p[D];
-        li[k] = p[D + 1];
-        x0[k] = p[lane];
-        if (D > kWave) x1[k] = p[lane + kWave];
-      }
+      const float *p = rec(i0 + min(k, n - 1));
+      mi[k] = p[D];
+      li[k] = p[D + 1];
+      x0[k] = p[lane];
+      x1[k] = D > kWave ? p[lane + kWave] : 0.f;
     }
     float Mn = M;
 #pragma unroll
-    for (int k = 0; k < kMaxParts; ++k) Mn = fmaxf(Mn, mi[k]);
+    for (int k = 0; k < kMaxParts; ++k) Mn = k < n ? fmaxf(Mn, mi[k]) : Mn;
     const float fo = __builtin_amdgcn_exp2f(M - Mn);
     lsum *= fo;
     o0 *= fo;
     o1 *= fo;
 #pragma unroll
     for (int k = 0; k < kMaxParts; ++k) {
-      const float f = k < n ? __builtin_amdgcn_exp2f(mi[k] - Mn) : 0.f;
-      lsum += li[k] * f;
-      o0 += x0[k] * f;
-      o1 += x1[k] * f;
+      if (k < n) {
+        const float f = __builtin_amdgcn_exp2f(mi[k] - Mn);
+        lsum += li[k] * f;
+        o0 += x0[k] * f;
+        o1 += x1[k] * f;
+      }
     }
     M = Mn;
   }
@@ -1830,9 +1838,10 @@ static kvc_status merge(int32_t B, int32_t H, int32_t G, int32_t D, void *out, k
   a.D = D;
   a.out_f16 = out_dtype == KVC_F16;
   const int64_t rows = static_cast<int64_t>(B) * H * G;
+  if (rows > INT32_MAX) return KVC_E_INVALID;
   const int grid = static_cast<int>((rows + kWgWaves - 1) / kWgWaves);
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(grid), dim3(kWgThreads), 0,
-                     static_cast<hipStream_t>(stream), a);
+  hipLaunchKernelGGL(D == 64 ? decode_merge_kernel<64> : decode_merge_kernel<128>, dim3(grid),
+                     dim3(kWgThreads), 0, static_cast<hipStream_t>(stream), a);
   return launch_status();
 }
 
