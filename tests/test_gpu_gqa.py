@@ -92,12 +92,18 @@ def test_gqa_two_phase_equals_single_call_and_workspace_reuse():
     a = kvc.decode_gqa_paged(q, layer, tdv, tlv, 1000)
     ws = kvc.new_gqa_workspace(4, H, G, D, device=d)
     ws.fill_(0x5A)
+    # the two passes on a reused workspace equal the one-shot call with the same batch bit for
+    # bit (the split of the work list depends on the batch, so a smaller batch is compared with
+    # its own one-shot call, and with the full batch's rows within the fp16 tolerance)
     for B in (4, 2, 3):
+        one = kvc.decode_gqa_paged(q[:B].contiguous(), layer, tdv[:B].contiguous(),
+                                   tlv[:B].contiguous(), 1000)
         out, _ = kvc.decode_gqa_partial_paged(q[:B].contiguous(), layer, tdv[:B].contiguous(),
                                               tlv[:B].contiguous(), 1000, workspace=ws)
         kvc.decode_gqa_merge(B, H, G, D, out, ws)
         torch.cuda.synchronize()
-        assert torch.equal(out, a[:B]), B
+        assert torch.equal(out, one), B
+        check(out.float().cpu().numpy(), a[:B].float().cpu().numpy(), TOL["f16"], f"B={B}")
     # a workspace sized for multi-head decode is too small for G = 8 and is refused
     small = kvc.new_workspace(4, H, D, device=d)
     with pytest.raises(kvc.KvcError):
