@@ -941,7 +941,7 @@ def read_ceiling(bench, p1_achieved: float):
     patterns = {"pass1_tiles": torch.from_numpy(offs).to(dev),
                 "sequential": torch.arange(n, dtype=torch.int64, device=dev) * tile}
     sink = torch.empty(1 << 16, dtype=torch.int32, device=dev)
-    res = {}
+    res, by_wpc = {}, {}
     reps = 3
     for name, off_d in patterns.items():
         best = None
@@ -958,12 +958,15 @@ def read_ceiling(bench, p1_achieved: float):
             t = float(np.median([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(k)])) / 1e3
             ev.close()
             gbs = nbytes / t / 1e9
+            if name == "pass1_tiles":
+                by_wpc[str(wpc)] = round(gbs, 1)
             if best is None or gbs > best[0]:
                 best = (gbs, wpc, t)
         res[name] = best
     return {"gbs": round(res["pass1_tiles"][0], 1),
             "pattern": "pass 1's K/V tiles of the last step, work-list order, one layer per launch",
             "waves_per_cu": res["pass1_tiles"][1],
+            "gbs_by_waves_per_cu": by_wpc,
             "sequential_gbs": round(res["sequential"][0], 1),
             "bytes_per_launch": nbytes,
             "pass1_over_ceiling": round(p1_achieved / res["pass1_tiles"][0], 4)}
