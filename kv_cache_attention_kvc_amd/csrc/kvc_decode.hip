@@ -415,16 +415,52 @@ __device__ __forceinline__ void touch_tile(const TileRegs<KV, D, QF16, GQ> &t) {
   }
 }
 
-// Partial dot product of this lane's 16 loaded bytes of one K row with its q slice.
+// The 16 loaded bytes of a K row as fp16 pairs (element pairs 2u, 2u + 1), exactly: fp16 as
+// stored; every e4m3 code and every int8 code is an fp16 value.
+template <int KV, int NP>
+__device__ __forceinline__ void unpack_pairs(const uint4 &r, f16x2 *h) {
+  const uint32_t w[4] = {r.x, r.y, r.z, r.w};
+  if constexpr (KV == KVC_F16) {
+    static_assert(NP == 4, "8 fp16 per 16 bytes");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = __builtin_bit_cast(f16x2, w[i]);
+  } else if constexpr (KV == KVC_I8) {
+    static_assert(NP == 8, "16 codes per 16 bytes");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) i8x4_to_f16(w[i], h[2 * i], h[2 * i + 1]);
+  } else {
+    static_assert(NP == 8, "16 codes per 16 bytes");
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      h[2 * i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w[i]), 1.0f, false);
+      h[2 * i + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(static_cast<int>(w[i]), 1.0f, true);
+    }
+  }
+}
+
+// Partial dot product of this lane's 16 loaded bytes of one K row with its q slice. With an fp16
+// q and an fp16 or 8-bit cache, both sides are fp16 pairs and v_dot2_f32_f16 takes two products
+// (exact in fp32) per instruction into the fp32 sum; otherwise the elements are widened to fp32
+// and summed with FMAs.
 template <int KV, bool QF16, int EPL>
 __device__ __forceinline__ float dot_slice(const uint4 &kr, const QWords<QF16, EPL> &q) {
-  float kf[EPL], qv[EPL];
-  unpack<KV>(kr, kf);
-  q_floats<QF16, EPL>(q, qv);
-  float d = 0.f;
+  if constexpr (QF16 && KV != KVC_F32) {
+    f16x2 kh[EPL / 2];
+    unpack_pairs<KV, EPL / 2>(kr, kh);
+    float d = 0.f;
 #pragma unroll
-  for (int e = 0; e < EPL; ++e) d = __builtin_fmaf(kf[e], qv[e], d);
-  return d;
+    for (int u = 0; u < EPL / 2; ++u)
+      d = __builtin_amdgcn_fdot2(kh[u], __builtin_bit_cast(f16x2, q.w[u]), d, false);
+    return d;
+  } else {
+    float kf[EPL], qv[EPL];
+    unpack<KV>(kr, kf);
+    q_floats<QF16, EPL>(q, qv);
+    float d = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) d = __builtin_fmaf(kf[e], qv[e], d);
+    return d;
+  }
 }
 
 // ---- one tile: online-softmax update of the group state ---------------------------------
