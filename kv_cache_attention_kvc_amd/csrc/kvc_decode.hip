@@ -17,7 +17,8 @@
 //     covers TPL = 64/LPT consecutive rows (1 KiB contiguous); a tile takes LOADS such loads;
 //   * each lane forms partial dot products over its 16 bytes of k; a butterfly of DPP adds
 //     inside each LPT-lane group gives every lane of the group the full score;
-//   * each group keeps its own online-softmax state (running max m, running sum l, and the
+//   * each group keeps its own online-softmax state (a reference m that moves only when a score
+//     passes it by a fixed headroom, the sum l of the weights relative to it, and the
 //     unnormalised output for the lane's 16-byte column), so the loop has no cross-group
 //     traffic; the groups are combined once per (sequence, head) segment.
 // Scores are kept in log2 units (multiplied by scale*log2(e)) and exponentials use v_exp_f32.
@@ -490,23 +491,30 @@ __device__ __forceinline__ void consume_tile(const TileRegs<KV, D, QF16, GQ> &t,
       s[r][i] = ok ? d : -__builtin_inff();
     }
   }
+  // The reference m moves only when a score passes it by more than kRefHeadroom (always on the
+  // first tile, which starts at kFloor), and then to the tile's maximum: most tiles rescale
+  // nothing. Weights stay below 2^kRefHeadroom, far inside the fp32 range.
+  constexpr float kRefHeadroom = 32.f;
 #pragma unroll
   for (int r = 0; r < GQ; ++r) {
     float mb = s[r][0];
 #pragma unroll
     for (int i = 1; i < G::LOADS; ++i) mb = fmaxf(mb, s[r][i]);
-    const float mn = fmaxf(m[r], mb);
-    const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);
+    if (__ballot(mb > m[r] + kRefHeadroom) != 0) {
+      const float mn = fmaxf(m[r], mb);
+      const float alpha = __builtin_amdgcn_exp2f(m[r] - mn);
+      l[r] *= alpha;
+#pragma unroll
+      for (int e = 0; e < G::EPL; ++e) acc[r][e] *= alpha;
+      m[r] = mn;
+    }
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < G::LOADS; ++i) {
-      s[r][i] = __builtin_amdgcn_exp2f(s[r][i] - mn);  // now the weight p
+      s[r][i] = __builtin_amdgcn_exp2f(s[r][i] - m[r]);  // now the weight p
       psum += s[r][i];
     }
-    l[r] = l[r] * alpha + psum;
-    m[r] = mn;
-#pragma unroll
-    for (int e = 0; e < G::EPL; ++e) acc[r][e] *= alpha;
+    l[r] += psum;
   }
 #pragma unroll
   for (int i = 0; i < G::LOADS; ++i) {
