@@ -38,6 +38,8 @@
 
 namespace kvc {
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
 constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
@@ -835,9 +837,10 @@ struct VecCore {
 //     weights enter as two fp16 terms, p = hi + lo with hi = fp16(p) and lo = fp16(p - hi), so
 //     about 22 bits of each weight reach the fp32 accumulator. A needs V transposed (four
 //     positions of one dim per lane): the tile goes through LDS. It is loaded in the
-//     wave-contiguous layout, written as fp16 rows with 16-byte columns swizzled by row group,
-//     and read back one fp16 at a time; the swizzle puts the four lane groups of a read on
-//     distinct banks. Lane (g, j) accumulates dims 16*dc + 4g .. +3 of head j.
+//     wave-contiguous layout, written as fp16 rows with 16-byte columns swizzled by row, and
+//     read back with one transposing read (ds_read_b64_tr_b16) per 16 dims; the swizzle puts
+//     the rows of a read on distinct banks. Lane (g, j) accumulates dims 16*dc + 4g .. +3 of
+//     head j.
 //   8-bit caches: e4m3 codes convert exactly to fp16 (v_cvt_scalef32_pk_f16_fp8 with scale 1),
 //     int8 codes too (through a biased fp16 exponent, i8x8_to_f16). The K block
 //     scale multiplies the scores. O is held in units of a reference V scale; a tile's weights
@@ -884,8 +887,14 @@ struct MfmaCore {
       : g(lane >> 4), j(lane & 15), gv(lane / G::LPT), cv(lane % G::LPT), vbuf(buf) {}
   __device__ int32_t gq(const DecodeArgs &a) const { return a.gq; }
 
-  // LDS column (8 fp16) of 16-byte column c of row t
-  static __device__ __forceinline__ int swz(int t, int c) { return c ^ (2 * ((t >> 2) & 3)); }
+  // LDS column (8 fp16) of 16-byte column c of row t. The transposing V reads take, per 32
+  // lanes, 2 adjacent columns (from an even one) of 8 consecutive rows, 8 bytes a lane: with
+  // 256-byte rows (D = 128) the row's low three bits move the column's upper three; with 128-byte
+  // rows (D = 64, two rows per 256-byte bank line) bits 1-2 of the row move them. The 16-byte
+  // row writes stay on distinct banks too.
+  static __device__ __forceinline__ int swz(int t, int c) {
+    return D == 128 ? c ^ (2 * (t & 7)) : c ^ (2 * ((t >> 1) & 3));
+  }
 
   __device__ void fetch(const DecodeArgs &a, Tile &t, int64_t bkv, int32_t hkv, int64_t qrow,
                         int32_t jt, int32_t phys, int32_t L, bool live) const {
@@ -1081,14 +1090,18 @@ struct MfmaCore {
       pl[e] = static_cast<_Float16>(pv - static_cast<float>(ph[e]));
     }
     wave_lds_sync();
-    // V^T: dims 16dc + j of positions 4g..4g+3
-    const _Float16 *vr = vbuf + (4 * g) * D + (j & 7);
+    // V^T: dims 16dc + j of positions 4g..4g+3, one gfx950 transposing read per 16 dims (in
+    // each 16-lane group, lane 4i + e receives element e of the 8 bytes that lanes i, i + 4,
+    // i + 8 and i + 12 address): lane s of group g addresses row 4g + s/4, dims
+    // 16dc + 4(s%4) .. + 3
+    const int vrow = 4 * g + (j >> 2);
+    const char *vr = reinterpret_cast<const char *>(vbuf + vrow * D) + (j & 1) * 8;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
-      const int col = (2 * dc + (j >> 3)) ^ (2 * g);
-      f16x4 va;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) va[e] = vr[e * D + col * 8];
+      const f16x4 va = __builtin_bit_cast(
+          f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                     (__attribute__((address_space(3))) i16x4 *)(vr +
+                                                                 swz(vrow, 2 * dc + ((j >> 1) & 1)) * 16)));
       s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, s.o[dc], 0, 0, 0);
       s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, s.o[dc], 0, 0, 0);
     }
