@@ -1098,10 +1098,10 @@ struct MfmaCore {
     const char *vr = reinterpret_cast<const char *>(vbuf + vrow * D) + (j & 1) * 8;
 #pragma unroll
     for (int dc = 0; dc < NDC; ++dc) {
+      const char *vp = vr + swz(vrow, 2 * dc + ((j >> 1) & 1)) * 16;
       const f16x4 va = __builtin_bit_cast(
           f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                     (__attribute__((address_space(3))) i16x4 *)(vr +
-                                                                 swz(vrow, 2 * dc + ((j >> 1) & 1)) * 16)));
+                     (__attribute__((address_space(3))) i16x4 *)(vp)));
       s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, ph, s.o[dc], 0, 0, 0);
       s.o[dc] = __builtin_amdgcn_mfma_f32_16x16x16f16(va, pl, s.o[dc], 0, 0, 0);
     }
