@@ -784,6 +784,9 @@ PROFILE_TAG = {
     workloads.PARALLEL_SAMPLING.name: "decode_partial_paged_f16_parallel_sampling",
     workloads.PARALLEL_SAMPLING_COW.name: "decode_partial_paged_f16_parallel_sampling_cow",
     workloads.COMPRESS_I8.name: "compress_f16_to_i8_longctx",
+    workloads.LLAMA13B_WINDOW.name: "decode_partial_paged_f16_llama13b_window1024",
+    workloads.LONGCTX_I8.name: "decode_partial_paged_i8_longctx",
+    workloads.LLAMA7B_PREFILL.name: "prefill_paged_f16_llama7b_b4x2048",
 }
 
 
