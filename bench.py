@@ -981,8 +981,9 @@ def main():
         print(json.dumps(pmc_summary(*args.pmc_summary)))
         return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (this build runs "
-              "on a single MI355X; see the sharding notes in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: decode attention "
+              "here runs on a single MI355X, and sharding across GPUs is not implemented",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 
