@@ -72,6 +72,11 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_LOG"),
                     help="summarise two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; csv output) "
                          "of this script with --copy-calibration, and print the traffic record")
+    ap.add_argument("--graph", action="store_true",
+                    help="contiguous workloads (no host work per step): after the eager warm-up, "
+                         "capture the timed steps once as a HIP graph (torch.cuda.CUDAGraph) and "
+                         "time one replay; the time per launch is then the replay's GPU time over "
+                         "its steps x layers, gaps between launches included")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after timing, run a plain 1 GiB device copy (torch) 3 times; its "
                          "FETCH_SIZE/WRITE_SIZE counters calibrate the HBM traffic figures")
@@ -1018,24 +1023,50 @@ def main():
     torch.cuda.synchronize()
     print("[bench] warm-up done", file=sys.stderr, flush=True)
 
-    evs = SampledEvents(layers, K, args.time_every)
     if sampling:
         bench.step_ev = HipEvents(2 * K)
         bench.gen_step = bench.gen_len     # the timed steps start a fresh generation
     total_bytes = 0
     pass1_bytes, unique = [], []
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(K):
-        bench.step((evs, 2 * layers * s))
-        b_all, b_p1 = bench.bytes_step(bench.lens_now)
-        total_bytes += b_all
-        pass1_bytes.append(b_p1)
-    torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    elapsed = t1 - t0
-    p1_ms = evs.launch_ms()   # [K, sampled layers]
-    evs.close()
+    if args.graph:
+        if cls is not ContigBench:
+            print("--graph: only contiguous workloads, which do no host work per step, are "
+                  "captured", file=sys.stderr)
+            sys.exit(2)
+        # the K timed steps captured once (nothing runs during capture), then one replay timed
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for s in range(K):
+                bench.step(None)
+                b_all, b_p1 = bench.bytes_step(bench.lens_now)
+                total_bytes += b_all
+                pass1_bytes.append(b_p1)
+        rep = HipEvents(2)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        rep.record(0, torch.cuda.current_stream())
+        graph.replay()
+        rep.record(1, torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        elapsed = t1 - t0
+        p1_ms = np.full((K, layers), rep.elapsed_ms(0, 1) / (K * layers))
+        rep.close()
+        del graph
+    else:
+        evs = SampledEvents(layers, K, args.time_every)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            bench.step((evs, 2 * layers * s))
+            b_all, b_p1 = bench.bytes_step(bench.lens_now)
+            total_bytes += b_all
+            pass1_bytes.append(b_p1)
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        elapsed = t1 - t0
+        p1_ms = evs.launch_ms()   # [K, sampled layers]
+        evs.close()
     p1_avg_s = float(p1_ms.mean()) / 1e3
     p1_bytes_avg = float(np.mean(pass1_bytes))
     achieved = p1_bytes_avg / p1_avg_s / 1e9
@@ -1083,6 +1114,7 @@ def main():
                                               workloads.COMPRESS_I8) else 1,
             "window": w.extra.get("window", 0),
             "append": path,
+            **({"launch": "hip graph of the timed steps, one replay"} if args.graph else {}),
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(tokens / elapsed, 1),
@@ -1092,6 +1124,9 @@ def main():
             **roof,
             "avg_launch_us": round(p1_avg_s * 1e6, 2),
             "timed_launches": int(p1_ms.size),
+            **({"launch_timing": "one graph replay's GPU time over steps x layers (pass 1, the "
+                                 "merge where it runs, and the gaps between launches)"}
+               if args.graph else {}),
             "algorithmic_bytes_per_launch": int(p1_bytes_avg),
             "kernel_source": os.path.basename(workload_source(w)),
             "kernel_source_sha256_16": source_hash(workload_source(w)),

@@ -56,3 +56,67 @@ def test_paged_decode_replayed_from_a_graph(fused):
         want = call(torch.empty_like(q), kvc.new_workspace(B, H, D, device=d))
         torch.cuda.synchronize()
         assert torch.equal(out, want), f"replay {i}"
+
+
+def test_tiny_gpt_decode_loop_replayed_from_a_graph():
+    """The fp32 tiny char-GPT decode loop (16-token prefill, then 240 steps of append + attend,
+    one fused call per step) captured once as a graph of 240 launches, every step's write
+    position and length already in device memory. Each replay follows eager work and a
+    synchronisation; every step's output must equal the eager loop's bit for bit and the oracle's
+    cached loop within the fp32 tolerance, and the cache must hold the inputs."""
+    import numpy as np
+
+    from oracle.attention import cached_decode
+    from tests.gpu_util import TOL, check
+    d = dev()
+    w = workloads.TINY_GPT
+    note("tiny gpt decode loop in a graph")
+    g = workloads.rng(w.seed)
+    T, H, D = w.ctx, w.heads, w.head_dim
+    P = w.extra["prefill"]
+    Q = workloads.normal(g, (1, T, H, D), "f32")
+    K = workloads.normal(g, (1, T, H, D), "f32")
+    V = workloads.normal(g, (1, T, H, D), "f32")
+    Kd, Vd, Qd = to_dev(K, d), to_dev(V, d), to_dev(Q, d)
+    qs = [Qd[:, t].contiguous() for t in range(T)]
+    ks = [Kd[:, t].contiguous() for t in range(T)]
+    vs = [Vd[:, t].contiguous() for t in range(T)]
+    lens = torch.arange(1, T + 1, dtype=torch.int32, device=d).view(T, 1)  # lens[t] = [t + 1]
+
+    def fresh_cache():
+        kc = torch.full((1, H, w.s_max, D), float("nan"), device=d)
+        vc = torch.full_like(kc, float("nan"))
+        kvc.append_contig(kc, vc, torch.zeros(1, dtype=torch.int32, device=d), Kd[:, :P], Vd[:, :P])
+        return kc, vc
+
+    def loop(kc, vc, outs, ws):
+        for t in range(P, T):
+            kvc.append_decode_contig(qs[t], kc, vc, lens[t], ks[t], vs[t], t + 1, scale=w.scale,
+                                     out=outs[t - P], workspace=ws)
+
+    steps = T - P
+    kc_e, vc_e = fresh_cache()
+    outs_e = torch.empty((steps, 1, H, D), device=d)
+    loop(kc_e, vc_e, outs_e, kvc.new_workspace(1, H, D, device=d))   # eager, also the warm-up
+    torch.cuda.synchronize()
+    kc_g, vc_g = fresh_cache()
+    outs_g = torch.full((steps, 1, H, D), float("nan"), device=d)
+    ws_g = kvc.new_workspace(1, H, D, device=d)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        loop(kc_g, vc_g, outs_g, ws_g)
+    torch.cuda.synchronize()
+    for i in range(3):
+        outs_g.fill_(float("nan"))      # eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(outs_g, outs_e), f"replay {i}"
+    got = outs_g.cpu().numpy()[:, 0]    # [steps, H, D]
+    for h in range(H):
+        want = cached_decode(Q[0, P:, h], K[0, P:, h], V[0, P:, h], w.scale,
+                             prefix_K=K[0, :P, h], prefix_V=V[0, :P, h])
+        check(got[:, h], want, TOL["f32"])
+    np.testing.assert_array_equal(kc_g.cpu().numpy()[0], K[0].transpose(1, 0, 2))
+    np.testing.assert_array_equal(vc_g.cpu().numpy()[0], V[0].transpose(1, 0, 2))
