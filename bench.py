@@ -259,16 +259,18 @@ class PagedBench:
 
     def tile_pieces(self):
         """Pass 1's K/V reads of the current step as (offset, pool pairs): the byte offset of
-        every (sequence, K/V head, block) tile in work-list order, and each layer's K and V
-        pools (None for workloads whose list is not that: rolling windows)."""
+        every (K/V head, sequence, block) tile in the order of pass 1's work list on a paged
+        pool (pair-major: one head of every sequence, then the next head), and each layer's K
+        and V pools (None for workloads whose list is not that: rolling windows). The probe's
+        wavefronts take consecutive runs of it in launch order; pass 1 also places each XCD's
+        runs contiguously, which the probe does not."""
         if self.W:
             return None
         tables, lens = self.pool.block_table(self.seqs)
         tile = 16 * self.D * ELT[self.w.kv_dtype]
-        offs = []
-        for b in range(len(lens)):
-            ids = tables[b][:workloads.blocks_for(int(lens[b]))].astype(np.int64)
-            offs.append(((ids[None, :] * self.H + np.arange(self.H)[:, None]) * tile).reshape(-1))
+        ids = [tables[b][:workloads.blocks_for(int(lens[b]))].astype(np.int64)
+               for b in range(len(lens))]
+        offs = [(blk * self.H + h) * tile for h in range(self.H) for blk in ids]
         return np.concatenate(offs), tile, [(l.k_pool, l.v_pool) for l in self.layers]
 
 
