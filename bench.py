@@ -160,6 +160,10 @@ class PagedBench:
         self.max_ctx = max_ctx
         self.scale = float(np.float32(1.0 / math.sqrt(D)))
         self.stream = torch.cuda.current_stream()
+        # pass 1 of few, short sequence-heads finishes every row itself: no merge launch then
+        self.need_merge = self.kvc.decode_merge_needed(
+            True, "f16", w.kv_dtype, B, H, D, self.mbps * 16, max_ctx, G=self.G, window=self.W,
+            append=self.fused)
 
     def step(self, ev=None):
         kvc, torch = self.kvc, self.torch
@@ -210,6 +214,8 @@ class PagedBench:
                                          scale=self.scale, out=self.out[li], workspace=self.ws)
             if ev is not None:
                 ev[0].record(ev[1] + 2 * li + 1, self.stream)
+            if not self.need_merge:
+                continue
             if self.G > 1 or self.W:
                 kvc.decode_gqa_merge(self.B, self.H, self.G, self.D, self.out[li], self.ws)
             else:
@@ -1117,6 +1123,7 @@ def main():
             "window": w.extra.get("window", 0),
             "append": path,
             **({"launch": "hip graph of the timed steps, one replay"} if args.graph else {}),
+            **({"merge_launch": bool(bench.need_merge)} if hasattr(bench, "need_merge") else {}),
         },
         "pct_of_peak": round(100 * value / PEAK_GBS, 2),
         "tokens_per_s": round(tokens / elapsed, 1),

@@ -315,6 +315,25 @@ kvc_status kvc_decode_partial_paged(const void *q, kvc_dtype q_dtype,
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,
                             void *workspace, size_t ws_bytes, void *stream);
 
+/* Whether pass 1 of a problem of these sizes leaves partial records for the merge, for callers
+ * of the two-pass interface: *needed = 0 means pass 1 finishes every output row itself (few,
+ * short sequence-heads run one workgroup each), so the merge launch can be skipped (it would
+ * find nothing to do); 1 means the merge must follow. The one-shot calls make the same choice
+ * internally. Host only: no device memory is read and nothing is queued; the answer depends on
+ * the current device (its CU count and how many pass-1 wavefronts fit on a CU).
+ *   paged:   1 for the paged entry points, 0 for the contiguous ones
+ *   append:  1 for the kvc_append_decode_* (fused append) entry points, else 0
+ *   q_dtype, kv_dtype, B, D, max_ctx, window: as passed to the pass-1 call (window 0: none)
+ *   H, G:    K/V heads and query heads per K/V head (G = 1 for the multi-head calls)
+ *   cap:     positions a sequence can hold: S_max (contiguous) or 16 * max_blocks_per_seq
+ * Returns the status the matching pass-1 call would return for these sizes (KVC_E_INVALID,
+ * KVC_E_UNSUPPORTED; the pointer checks aside), KVC_E_INVALID if needed is null. B = 0 gives
+ * *needed = 0. */
+kvc_status kvc_decode_merge_needed(int32_t paged, int32_t append, kvc_dtype q_dtype,
+                                   kvc_dtype kv_dtype, int32_t B, int32_t H, int32_t G, int32_t D,
+                                   int32_t cap, int32_t max_ctx, int32_t window,
+                                   int32_t *needed);
+
 /* Append and attend in one pass ("LLM Inference Acceleration -- KV Cache", section 3.1: each
  * decode step stores the new token's k/v in the cache and then attends over the whole cache,
  * itself included). Same arguments and result as the matching kvc_decode_* call, plus

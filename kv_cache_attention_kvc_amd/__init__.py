@@ -50,7 +50,7 @@ EXPORTS = [
     "kvc_decode_window_partial_paged", "kvc_prefill_contig", "kvc_prefill_paged",
     "kvc_compress_blocks", "kvc_append_decode_gqa_contig", "kvc_append_decode_gqa_paged",
     "kvc_append_decode_gqa_partial_contig", "kvc_append_decode_gqa_partial_paged",
-    "kvc_decode_attn_paged_noalloc", "kvc_read_pieces",
+    "kvc_decode_attn_paged_noalloc", "kvc_read_pieces", "kvc_decode_merge_needed",
 ]
 
 
@@ -138,6 +138,8 @@ def load_library() -> ctypes.CDLL:
                                                     ctypes.c_size_t, _P]),
         "kvc_decode_merge": (ctypes.c_int, [_I32, _I32, _I32, _P, ctypes.c_int, _P,
                                             ctypes.c_size_t, _P]),
+        "kvc_decode_merge_needed": (ctypes.c_int, [_I32, _I32, ctypes.c_int, ctypes.c_int, _I32,
+                                                   _I32, _I32, _I32, _I32, _I32, _I32, _PI32]),
     }
     contig_append = [_P, ctypes.c_int, _P, _P, ctypes.c_int, _P, _P, _P, _I32, _I32, _I32, _I32,
                      _I32, _F, _P, ctypes.c_int, _P, ctypes.c_size_t, _P]
@@ -542,6 +544,24 @@ def decode_merge(B, H, D, out, workspace, stream=None):
     _check(_lib().kvc_decode_merge(B, H, D, _ptr(out), _dtype_code(out), _ptr(workspace),
                                    workspace.numel(), _stream(stream)), "kvc_decode_merge")
     return out
+
+
+_DTYPE_NAMES = {"f32": F32, "f16": F16, "e4m3": E4M3, "i8": I8}
+
+
+def decode_merge_needed(paged: bool, q_dtype: str, kv_dtype: str, B: int, H: int, D: int,
+                        cap: int, max_ctx: int, G: int = 1, window: int = 0,
+                        append: bool = False) -> bool:
+    """Whether pass 1 of these sizes leaves records for the merge (kvc_decode_merge_needed);
+    False means it finishes every row itself and the merge launch can be skipped. dtypes by
+    name ("f32", "f16", "e4m3", "i8"); cap: S_max or 16 * max_blocks_per_seq."""
+    needed = ctypes.c_int32(0)
+    _check(_lib().kvc_decode_merge_needed(int(bool(paged)), int(bool(append)),
+                                          _DTYPE_NAMES[q_dtype], _DTYPE_NAMES[kv_dtype], int(B),
+                                          int(H), int(G), int(D), int(cap), int(max_ctx),
+                                          int(window), ctypes.byref(needed)),
+           "kvc_decode_merge_needed")
+    return needed.value != 0
 
 
 def decode_attn_contig(q, k_cache, v_cache, ctx_lens, max_ctx, scale=None, out=None,

@@ -44,7 +44,7 @@ constexpr int kWgWaves = 4;
 constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
-constexpr int kPairTiles = 8;      // pair mode: tiles per wavefront at most
+constexpr int kPairTiles = 20;     // pair mode: tiles per wavefront at most
 constexpr int kMfmaWgWaves = 8;    // matrix-core pass 1 with workgroup combine: wavefronts per CU
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
 constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
@@ -1721,19 +1721,28 @@ int resident_waves_per_cu(PartialKernel k, size_t shmem) {
   return blocks * kWgWaves;
 }
 
-// Shared validation and planning for both layouts.
-kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtype,
-                        kvc_dtype kv_dtype, const int32_t *ctx_lens, int32_t B, int32_t H,
-                        int32_t G, int32_t D,
-                        int32_t cap, int32_t max_ctx, int32_t window, float scale, void *out,
-                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes, PartialPlan &pl) {
+// The launch shape of pass 1 from the problem's sizes alone (no pointer is read): the kernel, the
+// work split, and whether one workgroup per pair finishes every row (pair mode: nothing left for
+// the merge). The partial calls and kvc_decode_merge_needed take it from here, so they agree.
+struct ShapePlan {
+  PartialKernel kern;
+  GroupPlan gp;
+  int32_t Hp;           // pairs per sequence
+  int stage_rows;       // staged output rows per wavefront
+  size_t shmem;         // LDS bytes per workgroup
+  bool pair_mode, wg_combine;
+  int64_t pairs, P;     // (sequence, pair) count; wavefronts of the split
+};
+
+kvc_status plan_shape(bool paged, bool append, kvc_dtype q_dtype, kvc_dtype kv_dtype, int32_t B,
+                      int32_t H, int32_t G, int32_t D, int32_t cap, int32_t max_ctx,
+                      int32_t window, ShapePlan &sp) {
   if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0 || window < 0) return KVC_E_INVALID;
   if (static_cast<int64_t>(H) * G > (1 << 20)) return KVC_E_INVALID;
   if (B > kMaxBatch) return KVC_E_INVALID;
-  if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
+  if (!is_f32_or_f16(q_dtype)) return KVC_E_UNSUPPORTED;
   if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
   if (!paged && is_q8(kv_dtype)) return KVC_E_UNSUPPORTED;
-  if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
   const bool q_f16 = q_dtype == KVC_F16;
   const GroupPlan gp = group_plan(G, kv_dtype, q_f16, paged);
   const int GQ = gp.gq;
@@ -1741,15 +1750,10 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   const int64_t tiles_cap =
       static_cast<int64_t>(B) * Hp * ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
   if (tiles_cap + kMaxWorkers >= INT32_MAX) return KVC_E_INVALID;
-  if (B == 0) {
-    pl.grid = 0;
-    return KVC_OK;
-  }
-  if (!q || !out || !ctx_lens || !workspace) return KVC_E_INVALID;
-  if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
-    return KVC_E_INVALID;
-  const WsLayout wl = ws_layout(B, D, ws_group(G));
-  if (ws_bytes < wl.total) return KVC_E_INVALID;
+  sp = ShapePlan{};
+  sp.gp = gp;
+  sp.Hp = Hp;
+  if (B == 0) return KVC_OK;  // nothing to launch (sp.kern stays null)
 
   // a window covers at most window + 15 positions' blocks
   const int64_t span = window > 0 ? std::min<int64_t>(std::min(max_ctx, cap),
@@ -1794,6 +1798,60 @@ kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtyp
   int64_t P = std::min<int64_t>(kMaxWorkers, static_cast<int64_t>(device_cu_count()) * wpc);
   P = std::min<int64_t>(P, std::max<int64_t>(1, (tiles_hint + kMinChunk - 1) / kMinChunk));
   P = (P + kWgWaves - 1) / kWgWaves * kWgWaves;
+  sp.kern = kern;
+  sp.stage_rows = stage_rows;
+  sp.shmem = shmem;
+  sp.pair_mode = pair_mode;
+  sp.wg_combine = wg_combine;
+  sp.pairs = pairs;
+  sp.P = P;
+  return KVC_OK;
+}
+
+// Shared validation and planning for both layouts.
+kvc_status plan_partial(bool paged, bool append, const void *q, kvc_dtype q_dtype,
+                        kvc_dtype kv_dtype, const int32_t *ctx_lens, int32_t B, int32_t H,
+                        int32_t G, int32_t D,
+                        int32_t cap, int32_t max_ctx, int32_t window, float scale, void *out,
+                        kvc_dtype out_dtype, void *workspace, size_t ws_bytes, PartialPlan &pl) {
+  if (B < 0 || H < 1 || G < 1 || max_ctx < 0 || cap < 0 || window < 0) return KVC_E_INVALID;
+  if (static_cast<int64_t>(H) * G > (1 << 20)) return KVC_E_INVALID;
+  if (B > kMaxBatch) return KVC_E_INVALID;
+  if (!is_f32_or_f16(q_dtype) || !is_f32_or_f16(out_dtype)) return KVC_E_UNSUPPORTED;
+  if (D != 64 && D != 128) return KVC_E_UNSUPPORTED;
+  if (!paged && is_q8(kv_dtype)) return KVC_E_UNSUPPORTED;
+  if (!(scale == scale) || __builtin_isinf(scale)) return KVC_E_INVALID;
+  const bool q_f16 = q_dtype == KVC_F16;
+  // the sizes' own checks again in plan_shape, then (B > 0) the pointers, then the launch shape
+  {
+    const GroupPlan gp = group_plan(G, kv_dtype, q_f16, paged);
+    const int64_t tiles_cap = static_cast<int64_t>(B) * H * (G / gp.gq) *
+                              ((static_cast<int64_t>(cap) + kBlock - 1) / kBlock);
+    if (tiles_cap + kMaxWorkers >= INT32_MAX) return KVC_E_INVALID;
+  }
+  if (B == 0) {
+    pl.grid = 0;
+    return KVC_OK;
+  }
+  if (!q || !out || !ctx_lens || !workspace) return KVC_E_INVALID;
+  if (!aligned16(q) || !aligned16(out) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return KVC_E_INVALID;
+  const WsLayout wl = ws_layout(B, D, ws_group(G));
+  if (ws_bytes < wl.total) return KVC_E_INVALID;
+  ShapePlan sp;
+  const kvc_status ss = plan_shape(paged, append, q_dtype, kv_dtype, B, H, G, D, cap, max_ctx,
+                                   window, sp);
+  if (ss != KVC_OK) return ss;
+  const GroupPlan gp = sp.gp;
+  const int GQ = gp.gq;
+  const int32_t Hp = sp.Hp;
+  const PartialKernel kern = sp.kern;
+  const int stage_rows = sp.stage_rows;
+  const size_t shmem = sp.shmem;
+  const bool pair_mode = sp.pair_mode;
+  const bool wg_combine = sp.wg_combine;
+  const int64_t pairs = sp.pairs;
+  const int64_t P = sp.P;
 
   DecodeArgs &a = pl.a;
   a = DecodeArgs{};
@@ -2038,6 +2096,27 @@ kvc_status kvc_append_decode_partial_paged(const void *q, kvc_dtype q_dtype,
   if (B > 0 && (!k_new || !v_new)) return KVC_E_INVALID;
   return partial_paged(q, q_dtype, 1, layer, block_tables, max_blocks_per_seq, ctx_lens, k_new,
                        v_new, B, max_ctx, 0, scale, out, out_dtype, workspace, ws_bytes, stream);
+}
+
+kvc_status kvc_decode_merge_needed(int32_t paged, int32_t append, kvc_dtype q_dtype,
+                                   kvc_dtype kv_dtype, int32_t B, int32_t H, int32_t G, int32_t D,
+                                   int32_t cap, int32_t max_ctx, int32_t window,
+                                   int32_t *needed) {
+  if (!needed) return KVC_E_INVALID;
+  *needed = 0;
+  if (paged) {
+    if (kv_dtype != KVC_F32 && kv_dtype != KVC_F16 && !is_q8(kv_dtype)) return KVC_E_UNSUPPORTED;
+    if (append && is_q8(kv_dtype)) return KVC_E_UNSUPPORTED;
+  } else if (!is_f32_or_f16(kv_dtype)) {
+    return KVC_E_UNSUPPORTED;
+  }
+  if (append && window > 0) return KVC_E_INVALID;
+  ShapePlan sp;
+  const kvc_status st = plan_shape(paged != 0, append != 0, q_dtype, kv_dtype, B, H, G, D, cap,
+                                   max_ctx, window, sp);
+  if (st != KVC_OK) return st;
+  *needed = (sp.kern && !sp.pair_mode) ? 1 : 0;
+  return KVC_OK;
 }
 
 kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtype out_dtype,

@@ -90,3 +90,73 @@ def test_pair_mode_window_and_fused_append():
             ref_c.K[b, :, :L[b]] = K[b, :L[b]].transpose(1, 0, 2)
             ref_c.V[b, :, :L[b]] = V[b, :L[b]].transpose(1, 0, 2)
         check(fused.cpu().numpy(), ref_c.decode(Q, L, 0.125), TOL["f32"], f"fused max_ctx={max_ctx}")
+
+
+def test_merge_needed_query_matches_what_pass_1_leaves():
+    """kvc_decode_merge_needed against what pass 1 does, for every pass-1 family (multi-head,
+    grouped-query on the matrix cores and on the vector kernel, window, fused append; paged and
+    contiguous), tight and loose bounds: when the query says no merge, pass 1 alone (out
+    poisoned with NaN first) equals the one-shot call bit for bit; when it says a merge is
+    needed, pass 1 alone leaves some rows unwritten. The LLaMA-13B and parallel-sampling bench
+    shapes are asked too."""
+    d = dev()
+    note("merge-needed query")
+    D, H = 128, 4
+    lens = [0, 1, 15, 16, 17, 100, 300, 512]
+    B = len(lens)
+    g, pool, model, seqs, layer, ref, data = _paged_setup(d, "f16", D, lens, H=H, seed=14)
+    layer32 = _paged_setup(d, "f32", D, lens, H=H, seed=14)[4]   # same seed: the same tables
+    tables, tl = pool.block_table(seqs)
+    td, tld = to_dev(tables, d), to_dev(tl, d)
+    cap = tables.shape[1] * 16
+    seen = set()
+
+    def run(name, G, window, max_ctx, kv="f16", lay=layer):
+        q = to_dev(workloads.normal(g, (B, H * G, D), "f16"), d)
+        needed = kvc.decode_merge_needed(True, "f16", kv, B, H, D, cap, max_ctx, G=G,
+                                         window=window)
+        if window:
+            one = kvc.decode_window_paged(q, lay, td, tld, max_ctx, window, scale=scale_of(D))
+            part = kvc.decode_window_partial_paged(q, lay, td, tld, max_ctx, window,
+                                                   scale=scale_of(D),
+                                                   out=torch.full_like(q, float("nan")))[0]
+        else:
+            one = kvc.decode_gqa_paged(q, lay, td, tld, max_ctx, scale=scale_of(D))
+            part = kvc.decode_gqa_partial_paged(q, lay, td, tld, max_ctx, scale=scale_of(D),
+                                                out=torch.full_like(q, float("nan")))[0]
+        torch.cuda.synchronize()
+        if needed:
+            assert torch.isnan(part).any(), f"{name} max_ctx={max_ctx}: nothing left to merge"
+        else:
+            assert torch.equal(part.view(torch.int16), one.view(torch.int16)), \
+                f"{name} max_ctx={max_ctx}"
+        seen.add((name, needed))
+
+    for max_ctx in (TIGHT, LOOSE):
+        run("multi-head", 1, 0, max_ctx)
+        run("grouped-query matrix cores", 8, 0, max_ctx)
+        run("grouped-query vector (fp32 cache)", 2, 0, max_ctx, kv="f32", lay=layer32)
+        run("window", 1, 2000, max_ctx)   # span 512 (tight) or 2015 positions (loose)
+    # fused append on a contiguous fp16 cache: pass 1 alone against the one-shot call
+    S = 600
+    for max_ctx in (TIGHT, LOOSE):
+        kc = torch.zeros((B, H, S, D), dtype=torch.float16, device=d)
+        q = to_dev(workloads.normal(g, (B, H, D), "f16"), d)
+        kn = to_dev(workloads.normal(g, (B, H, D), "f16"), d)
+        vn = to_dev(workloads.normal(g, (B, H, D), "f16"), d)
+        needed = kvc.decode_merge_needed(False, "f16", "f16", B, H, D, S, max_ctx, append=True)
+        one = kvc.append_decode_contig(q, kc, kc.clone(), tld, kn, vn, max_ctx, scale=scale_of(D))
+        part = kvc.append_decode_partial_contig(q, kc, kc.clone(), tld, kn, vn, max_ctx,
+                                                scale=scale_of(D),
+                                                out=torch.full_like(q, float("nan")))[0]
+        torch.cuda.synchronize()
+        if needed:
+            assert torch.isnan(part).any()
+        else:
+            assert torch.equal(part.view(torch.int16), one.view(torch.int16))
+        seen.add(("fused append contiguous", needed))
+    # every family was seen in both modes
+    assert {n for n, _ in seen} == {n for n, k in seen if k} == {n for n, k in seen if not k}
+    # the bench shapes: LLaMA-13B (1280 sequence-heads) merges, parallel sampling (320) does not
+    assert kvc.decode_merge_needed(True, "f16", "f16", 32, 40, 128, 2064, 2064, append=True)
+    assert not kvc.decode_merge_needed(True, "f16", "f16", 8, 40, 128, 1152, 1152, append=True)

@@ -45,8 +45,8 @@ def test_random_paged_decode(seed):
     qd, td, tld = to_dev(q, d), to_dev(tables, d), to_dev(tl, d)
     want = ref.decode(q, tables, tl, scale_of(D), window=window)
     # a tight bound (one workgroup per pair when the pairs are few and short) and a loose one
-    # (equal chunks of the whole work list and the merge)
-    for max_ctx in (max(lens), max(lens) + 1024):
+    # (equal chunks of the whole work list and the merge: over 20 tiles per wavefront)
+    for max_ctx in (max(lens), max(lens) + 4096):
         if window:
             got = kvc.decode_window_paged(qd, layer, td, tld, max_ctx, window, scale=scale_of(D))
         elif G > 1:

@@ -32,6 +32,22 @@ def test_exports_every_declared_symbol(lib):
     assert lib.kvc_status_str(-4).decode() == "block table full"
 
 
+def test_merge_needed_query_checks_its_arguments(lib):
+    """kvc_decode_merge_needed rejects what the matching pass-1 call rejects, before any runtime
+    call: a null result pointer, 8-bit contiguous caches, 8-bit fused appends, a window with the
+    fused append, a negative batch; B = 0 needs no merge."""
+    f = lib.kvc_decode_merge_needed
+    res = ctypes.c_int32(7)
+    assert f(1, 0, kvc.F16, kvc.F16, 4, 8, 1, 128, 256, 256, 0, None) == -1
+    assert f(0, 0, kvc.F16, kvc.E4M3, 4, 8, 1, 128, 256, 256, 0, ctypes.byref(res)) == -5
+    assert f(1, 1, kvc.F16, kvc.I8, 4, 8, 1, 128, 256, 256, 0, ctypes.byref(res)) == -5
+    assert f(1, 1, kvc.F16, kvc.F16, 4, 8, 1, 128, 256, 256, 64, ctypes.byref(res)) == -1
+    assert f(1, 0, kvc.F16, kvc.F16, -1, 8, 1, 128, 256, 256, 0, ctypes.byref(res)) == -1
+    assert f(1, 0, kvc.F16, kvc.F16, 0, 8, 1, 128, 256, 256, 0, ctypes.byref(res)) == 0
+    assert res.value == 0
+    assert not kvc.decode_merge_needed(True, "f16", "f16", 0, 40, 128, 2064, 2064)
+
+
 def test_workspace_size_is_monotone(lib):
     a = kvc.workspace_bytes(32, 40, 128)
     assert a > 0 and kvc.workspace_bytes(64, 40, 128) >= a
