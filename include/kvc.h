@@ -326,9 +326,10 @@ kvc_status kvc_decode_merge(int32_t B, int32_t H, int32_t D, void *out, kvc_dtyp
  *   q_dtype, kv_dtype, B, D, max_ctx, window: as passed to the pass-1 call (window 0: none)
  *   H, G:    K/V heads and query heads per K/V head (G = 1 for the multi-head calls)
  *   cap:     positions a sequence can hold: S_max (contiguous) or 16 * max_blocks_per_seq
- * Returns the status the matching pass-1 call would return for these sizes (KVC_E_INVALID,
- * KVC_E_UNSUPPORTED; the pointer checks aside), KVC_E_INVALID if needed is null. B = 0 gives
- * *needed = 0. */
+ * Returns KVC_E_INVALID or KVC_E_UNSUPPORTED where the matching pass-1 call would for these
+ * sizes and dtypes, KVC_E_INVALID if needed is null; it checks no pointer, layer or table width
+ * (a paged call also rejects max_blocks_per_seq < 1, which this query does not see). B = 0
+ * gives *needed = 0. */
 kvc_status kvc_decode_merge_needed(int32_t paged, int32_t append, kvc_dtype q_dtype,
                                    kvc_dtype kv_dtype, int32_t B, int32_t H, int32_t G, int32_t D,
                                    int32_t cap, int32_t max_ctx, int32_t window,
