@@ -56,6 +56,22 @@ def test_random_paged_decode(seed):
         torch.cuda.synchronize()
         check(got.float().cpu().numpy(), want, TOL["f32"] if dtype == "f32" else TOL["f16"],
               f"seed={seed} max_ctx={max_ctx}")
+        # when kvc_decode_merge_needed says pass 1 leaves nothing to merge, pass 1 alone (out
+        # poisoned first) equals the one-shot output bit for bit
+        cap = tables.shape[1] * 16
+        if not kvc.decode_merge_needed(True, qdt, dtype, B, H, D, cap, max_ctx, G=G,
+                                       window=window):
+            poison = torch.full_like(got, float("nan"))
+            if window:
+                part = kvc.decode_window_partial_paged(qd, layer, td, tld, max_ctx, window,
+                                                       scale=scale_of(D), out=poison)[0]
+            else:
+                part = kvc.decode_gqa_partial_paged(qd, layer, td, tld, max_ctx,
+                                                    scale=scale_of(D), out=poison)[0]
+            torch.cuda.synchronize()
+            bits = torch.int16 if got.dtype == torch.float16 else torch.int32
+            assert torch.equal(part.view(bits), got.view(bits)), f"seed={seed} max_ctx={max_ctx}"
+
         # empty sequences give zero rows
         for b, L in enumerate(lens):
             if L == 0:
