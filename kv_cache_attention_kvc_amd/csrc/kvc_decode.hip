@@ -45,7 +45,7 @@ constexpr int kWgThreads = kWave * kWgWaves;
 constexpr int kMaxWorkers = 8192;  // pass-1 wavefronts at most (records in a workspace)
 constexpr int kMinChunk = 4;       // tiles per wavefront at least
 constexpr int kPairTiles = 20;     // pair mode: tiles per wavefront at most
-constexpr int kMfmaWgWaves = 8;    // matrix-core pass 1 with workgroup combine: wavefronts per CU
+constexpr int kMfmaWgWaves = 4;    // matrix-core pass 1 with workgroup combine: wavefronts per CU
 constexpr int kStageRows = 8;      // finished output rows a wavefront holds in LDS before storing
 constexpr int kMaxGroup = 16;      // query heads one wavefront serves from one K/V head
 constexpr int kMaxBatch = 4096;
@@ -1685,9 +1685,10 @@ struct PartialPlan {
 // Pass-1 wavefronts per compute unit: each wavefront has about one tile of loads in flight, so
 // small tiles (K+V of 16 positions) need more wavefronts to keep enough bytes in flight: 8 for
 // tiles of 8 KiB or more, 12 for 4 KiB, 16 for 2 KiB (register use allows each). The matrix-core
-// kernel over fp16 caches runs 4 (one workgroup, one wavefront per SIMD): a wavefront there
-// serves up to 16 query heads, so each split pair costs up to 16 records and merges, and at the
-// grouped-query workload (64 query heads over 8 K/V heads) 4 measured faster than 8 and 6.
+// kernel over fp16 caches runs 4 (one workgroup, one wavefront per SIMD; with the workgroup
+// combine below as well): a wavefront there serves up to 16 query heads, so each split pair costs
+// up to 16 records and merges, and at the grouped-query workload (64 query heads over 8 K/V
+// heads) 4 measured faster than 8 and 6.
 // A contiguous cache with 8 KiB tiles (fp16, D = 128) runs 12: there a wavefront's chunk is one
 // run of consecutive tiles, and at 16 sequences x 32 heads x 2048 positions 12 measured 3 %
 // faster than 8 (16 slower); the paged pool at the same tile size is fastest at 8.
@@ -1781,10 +1782,12 @@ kvc_status plan_shape(bool paged, bool append, kvc_dtype q_dtype, kvc_dtype kv_d
   const int64_t pair_tiles = (pair_span + kBlock - 1) / kBlock;
   const bool pair_mode = pair_tiles <= static_cast<int64_t>(kWgWaves) * kPairTiles &&
                          pairs * kWgWaves <= static_cast<int64_t>(device_cu_count()) * wpc;
-  // The matrix-core kernel holds one tile in flight per wavefront; with one wavefront per SIMD
-  // that is too few bytes in flight, and with two, twice the cut pairs, each leaving up to 16
-  // records. So it runs two wavefronts per SIMD whose workgroups combine the pairs cut between
-  // their own wavefronts in LDS: only pairs cut at workgroup edges leave records for the merge.
+  // The matrix-core kernel's wavefronts each serve up to 16 query heads, so every pair cut between
+  // two wavefronts would leave up to 16 records for the merge. Its workgroups therefore combine
+  // the pairs cut between their own wavefronts in LDS, and only pairs cut at workgroup edges
+  // leave records. One workgroup per CU (one wavefront per SIMD): at the grouped-query workload
+  // (64 query heads over 8 K/V heads, B = 32) it measured 0.9-1.3 % faster per step than two,
+  // with half the workgroup edges.
   bool wg_combine = false;
   if (gp.mfma && !pair_mode) {
     const size_t sh_wg = lds_plan(B, D, stage_rows, GQ, true, true).total;
